@@ -1,0 +1,58 @@
+"""Build libconv2d.so for gfx950 with hipcc (in-tree, next to this file).
+
+    python -m convolution_conv2d_forward_amd.build [-v]
+
+Every HIP source is compiled with packed-fp32 instructions disabled
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass
+warns that it does not know that feature, which is harmless.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libconv2d.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["conv2d_api.cpp", "igemm_f32.hip", "igemm_bf16.hip", "depthwise.hip", "qpointwise.hip",
+           "direct.hip", "fused_pw_dw.hip"]
+
+FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-ffp-contract=fast"]
+
+
+def _compile(src, verbose):
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, flush=True)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

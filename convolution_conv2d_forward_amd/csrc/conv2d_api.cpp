@@ -1,0 +1,396 @@
+// C ABI of libconv2d.so: descriptor creation and validation, kernel choice,
+// pointer and alias checks, dispatch.  Host code only.
+//
+// The descriptor follows the "validate once, run unchecked" pattern of the
+// onnx-light-cpu "Binary Kernel Design" page (section "Prepared execution":
+// a descriptor built once per node validates attributes and binds the typed
+// function; section "Compute, scheduling, and safety": invalid inputs are
+// rejected before unchecked loops, and an input may alias the output only
+// when nothing is overwritten before its last read).  Status codes mirror
+// the Go "ops" page's error returns (PReluOp rejects a slope it cannot
+// broadcast per channel with ErrIncompatibleShapes).
+#include <cfloat>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "conv2d_internal.h"
+
+using namespace conv2d;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+conv_status_t fail(conv_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+conv_status_t ok() {
+    g_last_error[0] = '\0';
+    return CONV_OK;
+}
+
+const char* kernel_name(const Desc& d) {
+    switch (d.kclass) {
+    case KC_IGEMM_F32: return d.flatten_1x1 ? "igemm_f32_pointwise" : "igemm_f32";
+    case KC_IGEMM_BF16: return d.flatten_1x1 ? "igemm_bf16_pointwise" : "igemm_bf16";
+    case KC_DW: return d.p.dtype == CONV_DTYPE_BF16 ? "depthwise_bf16" : "depthwise_f32";
+    case KC_QDW: return "depthwise_i8";
+    case KC_QPW: return "pointwise_i8_mfma";
+    case KC_DIRECT: return "direct";
+    }
+    return "?";
+}
+
+size_t elem_size(int32_t dtype) {
+    return dtype == CONV_DTYPE_F32 ? 4 : dtype == CONV_DTYPE_BF16 ? 2 : 1;
+}
+
+// Byte ranges of a tensor view: n blocks of `len` bytes, `stride` apart.
+struct View {
+    uintptr_t base;
+    int64_t n;
+    int64_t stride;
+    int64_t len;
+    int64_t first() const { return 0; }
+};
+
+// Do two strided views overlap?  Both are lists of n equal-length blocks at a
+// constant stride; walk them in address order (two pointers, O(n1 + n2)).
+bool views_overlap(const View& a, const View& b) {
+    if (a.len == 0 || b.len == 0 || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a_end = a.base + (uintptr_t)((a.n - 1) * a.stride + a.len);
+    const uintptr_t b_end = b.base + (uintptr_t)((b.n - 1) * b.stride + b.len);
+    if (a_end <= b.base || b_end <= a.base) return false;
+    int64_t i = 0, j = 0;
+    while (i < a.n && j < b.n) {
+        const uintptr_t as = a.base + (uintptr_t)(i * a.stride), ae = as + (uintptr_t)a.len;
+        const uintptr_t bs = b.base + (uintptr_t)(j * b.stride), be = bs + (uintptr_t)b.len;
+        if (as < be && bs < ae) return true;
+        if (ae <= be) ++i; else ++j;
+    }
+    return false;
+}
+
+View flat(const void* p, int64_t bytes) { return View{(uintptr_t)p, 1, 0, bytes}; }
+
+View x_view(const Desc& d, const void* x) {
+    const int64_t plane = (int64_t)d.p.h * d.p.w * (int64_t)elem_size(d.p.dtype);
+    return View{(uintptr_t)x + (uintptr_t)(d.p.in_channel_offset * plane), d.p.n,
+                (int64_t)d.in_total * plane, (int64_t)d.p.c_in * plane};
+}
+
+View y_view(const Desc& d, const void* y) {
+    const int64_t plane = (int64_t)d.ho * d.wo * (int64_t)elem_size(d.p.dtype);
+    return View{(uintptr_t)y + (uintptr_t)(d.p.out_channel_offset * plane), d.p.n,
+                (int64_t)d.out_total * plane, (int64_t)d.p.c_out * plane};
+}
+
+int64_t w_bytes(const Desc& d) {
+    return (int64_t)d.p.c_out * d.cin_g * d.p.k_h * d.p.k_w * (int64_t)elem_size(d.p.dtype);
+}
+
+ConvArgs make_args(const Desc& d, const void* x, const void* w, const float* bias, const float* slope,
+                   void* y) {
+    ConvArgs a;
+    memset(&a, 0, sizeof(a));
+    const conv2d_params_t& p = d.p;
+    a.xptr = x; a.wptr = w; a.bias = p.has_bias ? bias : nullptr;
+    a.slope = p.act_type == CONV_ACT_PRELU ? slope : nullptr;
+    a.yptr = y;
+    a.n = p.n; a.c_in = p.c_in; a.h = p.h; a.w = p.w; a.c_out = p.c_out; a.k_h = p.k_h; a.k_w = p.k_w;
+    a.pad_top = p.pad_top; a.pad_left = p.pad_left;
+    a.stride_h = p.stride_h; a.stride_w = p.stride_w; a.dilation_h = p.dilation_h; a.dilation_w = p.dilation_w;
+    a.groups = p.groups; a.cin_g = d.cin_g; a.cout_g = d.cout_g;
+    a.ho = d.ho; a.wo = d.wo;
+    a.in_total = d.in_total; a.in_off = p.in_channel_offset;
+    a.out_total = d.out_total; a.out_off = p.out_channel_offset;
+    a.pad_value = p.pad_value;
+    a.act = p.act_type; a.act_a = p.act_params[0]; a.act_b = p.act_params[1];
+    a.slope_count = p.prelu_slope_count;
+    return a;
+}
+
+conv_status_t hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(CONV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+conv_status_t check_desc(conv2d_desc_t d) {
+    if (!d) return fail(CONV_ERR_INVALID_ARG, "null descriptor");
+    return CONV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void conv2d_params_init(conv2d_params_t* p) {
+    if (!p) return;
+    memset(p, 0, sizeof(*p));
+    p->stride_h = p->stride_w = 1;
+    p->dilation_h = p->dilation_w = 1;
+    p->groups = 1;
+    p->pad_value = 0.0f;
+    p->act_type = CONV_ACT_NONE;
+    // NaN selects the activation's default at descriptor creation.
+    p->act_params[0] = NAN;
+    p->act_params[1] = NAN;
+    p->prelu_slope_count = 1;
+    p->dtype = CONV_DTYPE_F32;
+    p->int8_rounding = CONV_ROUND_HALF_EVEN;
+}
+
+conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out) {
+    if (!pin || !out) return fail(CONV_ERR_INVALID_ARG, "null params or output pointer");
+    *out = nullptr;
+    conv2d_params_t p = *pin;
+    // Activation defaults: LeakyReLU alpha 0.01 (Go ops LeakyReluOp); Clip
+    // -FLT_MAX / FLT_MAX (ncnn clip).  Unused slots are zeroed.
+    if (p.act_type == CONV_ACT_LEAKY_RELU) {
+        if (std::isnan(p.act_params[0])) p.act_params[0] = 0.01f;
+        p.act_params[1] = 0.0f;
+    } else if (p.act_type == CONV_ACT_CLIP) {
+        if (std::isnan(p.act_params[0])) p.act_params[0] = -FLT_MAX;
+        if (std::isnan(p.act_params[1])) p.act_params[1] = FLT_MAX;
+    } else {
+        p.act_params[0] = p.act_params[1] = 0.0f;
+    }
+    if (p.n <= 0 || p.c_in <= 0 || p.h <= 0 || p.w <= 0 || p.c_out <= 0)
+        return fail(CONV_ERR_INVALID_ARG, "n, c_in, h, w, c_out must be positive");
+    if (p.k_h <= 0 || p.k_w <= 0) return fail(CONV_ERR_INVALID_ARG, "kernel size must be positive");
+    if (p.stride_h <= 0 || p.stride_w <= 0) return fail(CONV_ERR_INVALID_ARG, "stride must be >= 1");
+    if (p.dilation_h <= 0 || p.dilation_w <= 0) return fail(CONV_ERR_INVALID_ARG, "dilation must be >= 1");
+    if (p.pad_top < 0 || p.pad_left < 0 || p.pad_bottom < 0 || p.pad_right < 0)
+        return fail(CONV_ERR_INVALID_ARG, "pads must be >= 0");
+    if (p.dtype < CONV_DTYPE_F32 || p.dtype > CONV_DTYPE_I8) return fail(CONV_ERR_INVALID_ARG, "unknown dtype %d", p.dtype);
+    if (p.act_type < CONV_ACT_NONE || p.act_type > CONV_ACT_CLIP)
+        return fail(CONV_ERR_INVALID_ARG, "unknown activation %d", p.act_type);
+    if (p.int8_rounding != CONV_ROUND_HALF_EVEN && p.int8_rounding != CONV_ROUND_HALF_AWAY)
+        return fail(CONV_ERR_INVALID_ARG, "unknown rounding %d", p.int8_rounding);
+    if (p.has_bias != 0 && p.has_bias != 1) return fail(CONV_ERR_INVALID_ARG, "has_bias must be 0 or 1");
+    if (!std::isfinite(p.pad_value)) return fail(CONV_ERR_INVALID_ARG, "pad_value must be finite");
+    if (p.groups <= 0) return fail(CONV_ERR_INVALID_ARG, "groups must be >= 1");
+    if (p.c_in % p.groups || p.c_out % p.groups)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "groups (%d) must divide c_in (%d) and c_out (%d)", p.groups,
+                    p.c_in, p.c_out);
+    if (p.act_type == CONV_ACT_LEAKY_RELU && !std::isfinite(p.act_params[0]))
+        return fail(CONV_ERR_INVALID_ARG, "leaky alpha must be finite");
+    if (p.act_type == CONV_ACT_CLIP) {
+        if (p.act_params[0] > p.act_params[1]) return fail(CONV_ERR_INVALID_ARG, "clip lo > hi");
+    }
+    if (p.act_type == CONV_ACT_PRELU && p.prelu_slope_count != 1 && p.prelu_slope_count != p.c_out)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "PReLU slope count %d is neither 1 nor c_out (%d)",
+                    p.prelu_slope_count, p.c_out);
+    const int32_t in_total = p.in_total_channels ? p.in_total_channels : p.c_in;
+    const int32_t out_total = p.out_total_channels ? p.out_total_channels : p.c_out;
+    if (p.in_total_channels < 0 || p.out_total_channels < 0 || p.in_channel_offset < 0 || p.out_channel_offset < 0)
+        return fail(CONV_ERR_INVALID_ARG, "channel offsets and totals must be >= 0");
+    if ((int64_t)p.in_channel_offset + p.c_in > in_total)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "input channels [%d, %d) exceed in_total_channels %d",
+                    p.in_channel_offset, p.in_channel_offset + p.c_in, in_total);
+    if ((int64_t)p.out_channel_offset + p.c_out > out_total)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "output channels [%d, %d) exceed out_total_channels %d",
+                    p.out_channel_offset, p.out_channel_offset + p.c_out, out_total);
+    const int64_t hnum = (int64_t)p.h + p.pad_top + p.pad_bottom - (int64_t)p.dilation_h * (p.k_h - 1) - 1;
+    const int64_t wnum = (int64_t)p.w + p.pad_left + p.pad_right - (int64_t)p.dilation_w * (p.k_w - 1) - 1;
+    if (hnum < 0 || wnum < 0) return fail(CONV_ERR_INVALID_ARG, "empty output: kernel extent exceeds padded input");
+    const int64_t ho = hnum / p.stride_h + 1, wo = wnum / p.stride_w + 1;
+    if (ho > INT32_MAX || wo > INT32_MAX) return fail(CONV_ERR_UNSUPPORTED, "output too large");
+    if ((int64_t)p.n * in_total * p.h * p.w >= (int64_t)1 << 40 ||
+        (int64_t)p.n * out_total * ho * wo >= (int64_t)1 << 40)
+        return fail(CONV_ERR_UNSUPPORTED, "tensor too large");
+    if ((int64_t)p.h * p.w > INT32_MAX || ho * wo > INT32_MAX || (int64_t)p.c_in * p.k_h * p.k_w > INT32_MAX)
+        return fail(CONV_ERR_UNSUPPORTED, "plane or filter too large");
+    if (p.dtype == CONV_DTYPE_I8) {
+        if (p.pad_value != 0.0f)
+            return fail(CONV_ERR_UNSUPPORTED, "int8: padded taps read the zero point (0); pad_value must be 0");
+        if (p.act_type != CONV_ACT_NONE && p.act_type != CONV_ACT_RELU)
+            return fail(CONV_ERR_UNSUPPORTED, "int8: only NONE or RELU may follow the requant");
+    }
+
+    Desc* d = new (std::nothrow) Desc();
+    if (!d) return fail(CONV_ERR_INVALID_ARG, "out of host memory");
+    d->p = p;
+    d->ho = (int32_t)ho;
+    d->wo = (int32_t)wo;
+    d->cin_g = p.c_in / p.groups;
+    d->cout_g = p.c_out / p.groups;
+    d->in_total = in_total;
+    d->out_total = out_total;
+    d->flatten_1x1 = false;
+    const bool depthwise = p.groups == p.c_in && p.groups == p.c_out;
+
+    bool planned = false;
+    if (p.dtype == CONV_DTYPE_I8) {
+        if (depthwise) { d->kclass = KC_QDW; planned = plan_qdw(*d); }
+        else { d->kclass = KC_QPW; planned = plan_qpw(*d); }
+    } else if (depthwise) {
+        d->kclass = KC_DW;
+        planned = plan_dw(*d);
+    } else if (p.dtype == CONV_DTYPE_F32) {
+        d->kclass = KC_IGEMM_F32;
+        planned = plan_igemm_f32(*d);
+    } else {
+        d->kclass = KC_IGEMM_BF16;
+        planned = plan_igemm_bf16(*d);
+    }
+    if (!planned) {
+        d->kclass = KC_DIRECT;
+        d->flatten_1x1 = false;
+    }
+    *out = (conv2d_desc_t)d;
+    return ok();
+}
+
+void conv2d_desc_destroy(conv2d_desc_t d) { delete (Desc*)d; }
+
+conv_status_t conv2d_desc_get_output_shape(conv2d_desc_t dd, int32_t out[4]) {
+    if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
+    if (!out) return fail(CONV_ERR_INVALID_ARG, "null output array");
+    const Desc& d = *(const Desc*)dd;
+    out[0] = d.p.n;
+    out[1] = d.out_total;
+    out[2] = d.ho;
+    out[3] = d.wo;
+    return ok();
+}
+
+const char* conv2d_desc_kernel_name(conv2d_desc_t dd) {
+    if (!dd) return "";
+    return kernel_name(*(const Desc*)dd);
+}
+
+conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, const float* bias,
+                             const float* slope, void* y, void* stream) {
+    if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
+    const Desc& d = *(const Desc*)dd;
+    if (d.p.dtype == CONV_DTYPE_I8) return fail(CONV_ERR_INVALID_ARG, "int8 descriptor: use qconv2d_forward");
+    if (!x || !w || !y) return fail(CONV_ERR_INVALID_ARG, "null x, w or y");
+    if (d.p.has_bias && !bias) return fail(CONV_ERR_INVALID_ARG, "has_bias set but bias is null");
+    if (d.p.act_type == CONV_ACT_PRELU && !slope) return fail(CONV_ERR_INVALID_ARG, "PReLU needs a slope pointer");
+    const View yv = y_view(d, y);
+    if (views_overlap(yv, x_view(d, x))) return fail(CONV_ERR_ALIAS, "y overlaps the input channels read");
+    if (views_overlap(yv, flat(w, w_bytes(d)))) return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if (d.p.has_bias && views_overlap(yv, flat(bias, 4 * (int64_t)d.p.c_out)))
+        return fail(CONV_ERR_ALIAS, "y overlaps the bias");
+    if (d.p.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope, 4 * (int64_t)d.p.prelu_slope_count)))
+        return fail(CONV_ERR_ALIAS, "y overlaps the PReLU slopes");
+    ConvArgs a = make_args(d, x, w, bias, slope, y);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (d.kclass) {
+    case KC_IGEMM_F32: e = launch_igemm_f32(d, a, s); break;
+    case KC_IGEMM_BF16: e = launch_igemm_bf16(d, a, s); break;
+    case KC_DW: e = launch_dw(d, a, s); break;
+    default: e = launch_direct(d, a, s); break;
+    }
+    return hip_status(e, kernel_name(d));
+}
+
+conv_status_t fused_pw_dw_forward(conv2d_desc_t dpw, conv2d_desc_t ddw, const void* x, const void* w_pw,
+                                  const float* b_pw, const float* slope_pw, const void* w_dw, const float* b_dw,
+                                  const float* slope_dw, void* y, void* stream) {
+    if (!dpw || !ddw) return fail(CONV_ERR_INVALID_ARG, "null descriptor");
+    const Desc& pw = *(const Desc*)dpw;
+    const Desc& dw = *(const Desc*)ddw;
+    const conv2d_params_t& P = pw.p;
+    const conv2d_params_t& D = dw.p;
+    if (P.dtype != D.dtype) return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "pw and dw dtypes differ");
+    if (P.dtype != CONV_DTYPE_F32) return fail(CONV_ERR_UNSUPPORTED, "fused pw->dw supports F32 only");
+    if (P.k_h != 1 || P.k_w != 1 || P.stride_h != 1 || P.stride_w != 1 || P.groups != 1 || P.pad_top ||
+        P.pad_left || P.pad_bottom || P.pad_right)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "first descriptor must be a 1x1, stride 1, unpadded, ungrouped conv");
+    if (!(D.groups == D.c_in && D.groups == D.c_out))
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "second descriptor must be depthwise (groups == c_in == c_out)");
+    if (D.c_in != P.c_out || D.n != P.n || D.h != P.h || D.w != P.w)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "pw output [%d,%d,%d,%d] does not match dw input [%d,%d,%d,%d]",
+                    P.n, P.c_out, P.h, P.w, D.n, D.c_in, D.h, D.w);
+    if (pw.out_total != P.c_out || P.out_channel_offset != 0 || D.in_channel_offset != 0 || dw.in_total != D.c_in)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "the expanded tensor has no buffer: pw output and dw input must be "
+                                                  "plain (no channel offsets)");
+    if (D.stride_h != 1 || D.stride_w != 1) return fail(CONV_ERR_UNSUPPORTED, "fused pw->dw needs dw stride 1");
+    int32_t th = 0, lds = 0;
+    if (!plan_fused_pw_dw(pw, dw, &th, &lds))
+        return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
+    if (!x || !w_pw || !w_dw || !y) return fail(CONV_ERR_INVALID_ARG, "null x, weights or y");
+    if (P.has_bias && !b_pw) return fail(CONV_ERR_INVALID_ARG, "pw has_bias set but bias is null");
+    if (D.has_bias && !b_dw) return fail(CONV_ERR_INVALID_ARG, "dw has_bias set but bias is null");
+    if (P.act_type == CONV_ACT_PRELU && !slope_pw) return fail(CONV_ERR_INVALID_ARG, "pw PReLU needs slopes");
+    if (D.act_type == CONV_ACT_PRELU && !slope_dw) return fail(CONV_ERR_INVALID_ARG, "dw PReLU needs slopes");
+    const View yv = y_view(dw, y);
+    if (views_overlap(yv, x_view(pw, x))) return fail(CONV_ERR_ALIAS, "y overlaps x");
+    if (views_overlap(yv, flat(w_pw, w_bytes(pw))) || views_overlap(yv, flat(w_dw, w_bytes(dw))))
+        return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if ((P.has_bias && views_overlap(yv, flat(b_pw, 4 * (int64_t)P.c_out))) ||
+        (D.has_bias && views_overlap(yv, flat(b_dw, 4 * (int64_t)D.c_out))))
+        return fail(CONV_ERR_ALIAS, "y overlaps a bias");
+    if ((P.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope_pw, 4 * (int64_t)P.prelu_slope_count))) ||
+        (D.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope_dw, 4 * (int64_t)D.prelu_slope_count))))
+        return fail(CONV_ERR_ALIAS, "y overlaps PReLU slopes");
+    ConvArgs apw = make_args(pw, x, w_pw, b_pw, slope_pw, nullptr);
+    ConvArgs adw = make_args(dw, nullptr, w_dw, b_dw, slope_dw, y);
+    return hip_status(launch_fused_pw_dw(pw, dw, apw, adw, (hipStream_t)stream), "fused_pw_dw");
+}
+
+conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, int8_t x_zp, const int8_t* w,
+                              float w_scale, int8_t w_zp, const int32_t* bias, float y_scale, int8_t y_zp,
+                              int8_t* y, void* stream) {
+    if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
+    const Desc& d = *(const Desc*)dd;
+    if (d.p.dtype != CONV_DTYPE_I8) return fail(CONV_ERR_INVALID_ARG, "qconv2d_forward needs an I8 descriptor");
+    if (x_zp != 0 || w_zp != 0)
+        return fail(CONV_ERR_UNSUPPORTED, "symmetric int8 only: x and w zero points must be 0 (got %d, %d)", x_zp, w_zp);
+    if (!(std::isfinite(x_scale) && x_scale > 0) || !(std::isfinite(w_scale) && w_scale > 0) ||
+        !(std::isfinite(y_scale) && y_scale > 0))
+        return fail(CONV_ERR_INVALID_ARG, "scales must be finite and positive");
+    // composite = f32(f32(x_scale * w_scale) / y_scale), each step rounded to f32.
+    volatile float prod = x_scale * w_scale;
+    volatile float comp = prod / y_scale;
+    const float composite = comp;
+    if (!(std::isfinite(composite) && composite > 0))
+        return fail(CONV_ERR_INVALID_ARG, "composite scale x_scale*w_scale/y_scale is not a positive finite float");
+    if (!x || !w || !y) return fail(CONV_ERR_INVALID_ARG, "null x, w or y");
+    if (d.p.has_bias && !bias) return fail(CONV_ERR_INVALID_ARG, "has_bias set but bias is null");
+    const View yv = y_view(d, y);
+    if (views_overlap(yv, x_view(d, x))) return fail(CONV_ERR_ALIAS, "y overlaps the input channels read");
+    if (views_overlap(yv, flat(w, w_bytes(d)))) return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if (d.p.has_bias && views_overlap(yv, flat(bias, 4 * (int64_t)d.p.c_out)))
+        return fail(CONV_ERR_ALIAS, "y overlaps the bias");
+    ConvArgs a = make_args(d, x, w, nullptr, nullptr, y);
+    a.qbias = d.p.has_bias ? bias : nullptr;
+    a.composite = composite;
+    a.y_zp = y_zp;
+    a.rounding = d.p.int8_rounding;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (d.kclass) {
+    case KC_QDW: e = launch_qdw(d, a, s); break;
+    case KC_QPW: e = launch_qpw(d, a, s); break;
+    default: e = launch_direct(d, a, s); break;
+    }
+    return hip_status(e, kernel_name(d));
+}
+
+const char* conv2d_status_string(conv_status_t s) {
+    switch (s) {
+    case CONV_OK: return "CONV_OK";
+    case CONV_ERR_INVALID_ARG: return "CONV_ERR_INVALID_ARG";
+    case CONV_ERR_INCOMPATIBLE_SHAPES: return "CONV_ERR_INCOMPATIBLE_SHAPES";
+    case CONV_ERR_UNSUPPORTED: return "CONV_ERR_UNSUPPORTED";
+    case CONV_ERR_ALIAS: return "CONV_ERR_ALIAS";
+    case CONV_ERR_HIP: return "CONV_ERR_HIP";
+    }
+    return "CONV_ERR_UNKNOWN";
+}
+
+const char* conv2d_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the C ABI layer and the gfx950 kernels.
+// Nothing here is part of the public ABI (include/conv2d.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/conv2d.h"
+
+namespace conv2d {
+
+// Kernel classes chosen by the descriptor.
+enum KernelClass : int32_t {
+    KC_IGEMM_F32 = 0,    // implicit GEMM, fp32 MFMA (dense, grouped, pointwise)
+    KC_IGEMM_BF16 = 1,   // implicit GEMM, bf16 MFMA, fp32 accumulate
+    KC_DW = 2,           // depthwise (groups == c_in == c_out), VALU, LDS halo tiles
+    KC_QDW = 3,          // int8 depthwise, VALU int32 MACs
+    KC_QPW = 4,          // int8 pointwise 1x1, i8 MFMA
+    KC_DIRECT = 5,       // direct convolution, one thread per output (any shape)
+};
+
+// Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
+// numerators below 2^16: q = umulhi(x, m) with m = ceil(2^32 / d).
+struct FastDiv {
+    uint32_t d;
+    uint32_t m;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.m = (uint32_t)((((uint64_t)1 << 32) + d - 1) / d);
+    return f;
+}
+
+// Everything a forward kernel needs, passed by value.  Sizes are element
+// counts; offsets into x and y are computed in 64-bit inside the kernels.
+struct ConvArgs {
+    const void* xptr;      // input (n, in_total, h, w)
+    const void* wptr;      // weights OIHW
+    const float* bias;     // null when absent
+    const float* slope;    // null unless PReLU
+    void* yptr;            // output (n, out_total, ho, wo)
+
+    int32_t n, c_in, h, w, c_out, k_h, k_w;
+    int32_t pad_top, pad_left;
+    int32_t stride_h, stride_w, dilation_h, dilation_w;
+    int32_t groups, cin_g, cout_g;
+    int32_t ho, wo;
+    int32_t in_total, in_off, out_total, out_off;
+    float pad_value;
+    int32_t act;
+    float act_a, act_b;    // leaky alpha / clip lo, clip hi
+    int32_t slope_count;
+
+    // Tiling decided on the host.
+    int32_t tile_h, tile_w;          // output pixels per tile (rows, cols)
+    int32_t tiles_h, tiles_w;        // tiles per image
+    int32_t co_tiles;                // output-channel tiles per group
+    int32_t patch_h, patch_w;        // input window of one tile (rows, cols)
+    int32_t patch_stride;            // LDS stride between channel planes
+    int32_t chunks;                  // number of input-channel chunks
+    int32_t stages;                  // LDS pipeline stages (1 or 2)
+    uint32_t num_blocks;             // grid size (for the XCD remap)
+    FastDiv div_patch_hw, div_patch_w, div_tile_w;
+
+    // int8 requant
+    float composite;
+    int32_t y_zp;
+    int32_t rounding;
+    const int32_t* qbias;
+};
+
+// Host-side descriptor (opaque to callers).
+struct Desc {
+    conv2d_params_t p;
+    int32_t ho, wo;
+    int32_t cin_g, cout_g, in_total, out_total;
+    KernelClass kclass;
+    // tiling choice for the implicit GEMM / depthwise kernels
+    int32_t cfg;                 // kernel variant index within the class
+    int32_t tile_h, tile_w;
+    int32_t lds_bytes;
+    int32_t stages;
+    bool flatten_1x1;            // 1x1/s1/p0: treat [h][w] as one row of h*w pixels
+};
+
+// Launchers (implemented next to their kernels).  Each returns the
+// hipError_t of the launch.
+hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw,
+                              hipStream_t s);
+
+// Tile planners (host): fill the tiling fields of d; return false if the
+// shape cannot use the class (the caller then falls back to KC_DIRECT).
+bool plan_igemm_f32(Desc& d);
+bool plan_igemm_bf16(Desc& d);
+bool plan_dw(Desc& d);
+bool plan_qdw(Desc& d);
+bool plan_qpw(Desc& d);
+bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
+
+// Fill the tile-dependent ConvArgs fields from a planned descriptor.
+void fill_tiling(const Desc& d, ConvArgs& a);
+
+}  // namespace conv2d

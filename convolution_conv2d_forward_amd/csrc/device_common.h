@@ -1,0 +1,76 @@
+// Device helpers shared by the gfx950 kernels: bias + activation epilogue,
+// requant epilogue, XCD-aware block remap, fast division.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include "conv2d_internal.h"
+
+namespace conv2d {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
+    return f.d == 1 ? x : __umulhi(x, f.m);
+}
+
+// MI355X has 8 XCDs and the dispatcher hands consecutive workgroups to
+// consecutive XCDs.  Remap so that consecutive logical tiles (which share
+// input patches) land on the same XCD and hit its L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
+    const uint32_t full = nblocks & ~7u;
+    if (b >= full) return b;
+    const uint32_t per = full >> 3;
+    return (b & 7u) * per + (b >> 3);
+}
+
+// Bias add then the fused activation (ncnn convolution: y = act(conv + bias);
+// Go ops ConvLeakyReluOp / ConvPReluOp fuse them into the GEMM write).
+__device__ __forceinline__ float bias_act(const ConvArgs& a, float v, int co) {
+    if (a.bias) v += a.bias[co];
+    switch (a.act) {
+    case CONV_ACT_RELU:
+        v = v > 0.0f ? v : 0.0f;
+        break;
+    case CONV_ACT_LEAKY_RELU:
+        v = v >= 0.0f ? v : a.act_a * v;
+        break;
+    case CONV_ACT_PRELU: {
+        const float s = a.slope[a.slope_count == 1 ? 0 : co];
+        v = v >= 0.0f ? v : s * v;
+        break;
+    }
+    case CONV_ACT_CLIP:
+        v = fminf(fmaxf(v, a.act_a), a.act_b);
+        break;
+    default:
+        break;
+    }
+    return v;
+}
+
+// int8 requant: q = sat8(round(f32(acc) * composite) + y_zp), ReLU as
+// max(q, y_zp) (yscv requant epilogue).  The product is a plain f32 multiply
+// (no contraction); rintf rounds ties to even, roundf away from zero.
+__device__ __forceinline__ int8_t requant(int32_t acc, float composite, int rounding, int y_zp,
+                                          bool relu) {
+    const float yf = __fmul_rn((float)acc, composite);
+    const float r = rounding == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
+    int q = (int)r + y_zp;
+    q = q < -128 ? -128 : (q > 127 ? 127 : q);
+    if (relu && q < y_zp) q = y_zp;
+    return (int8_t)q;
+}
+
+__host__ __device__ __forceinline__ float bf16_to_f32(__hip_bfloat16 v) {
+    return __bfloat162float(v);
+}
+
+__host__ __device__ __forceinline__ __hip_bfloat16 f32_to_bf16(float v) {
+    return __float2bfloat16(v);   // round to nearest even
+}
+
+}  // namespace conv2d

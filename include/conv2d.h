@@ -1,0 +1,181 @@
+/*
+ * conv2d.h -- C ABI of libconv2d.so: NCHW 2-D convolution forward on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources: the ncnn developer guide
+ * "operators.md", sections "convolution" and "convolutiondepthwise"; the Go
+ * package docs "ops" of github.com/0verkilll/onnx, sections ConvOp,
+ * ConvLeakyReluOp, ConvPReluOp, ConcatFusedTailOp, ReluOp, LeakyReluOp,
+ * PReluOp, ClipOp; the yscv page "ONNX CPU Kernels (Conv/MatMul) -- Runtime
+ * Map", section "Hot kernel paths"):
+ *
+ *   x2 = pad(x, pads, pad_value)
+ *   x3 = correlate(x2, weight, kernel, stride, dilation, group) + bias
+ *   y  = activation(x3)     (none, ReLU, LeakyReLU, PReLU, Clip)
+ *
+ * Layouts (all tensors dense, row-major):
+ *   x       [n][in_total_channels][h][w]; the convolution reads channels
+ *           [in_channel_offset, in_channel_offset + c_in).
+ *   weight  OIHW: [c_out][c_in/groups][k_h][k_w].
+ *   y       [n][out_total_channels][Ho][Wo]; the convolution writes channels
+ *           [out_channel_offset, out_channel_offset + c_out) and no others
+ *           (ConcatFusedTail: the producer writes the tail slice of a concat
+ *           buffer directly, for any n).
+ *   Ho = floor((h + pad_top + pad_bottom - dilation_h*(k_h-1) - 1)/stride_h) + 1,
+ *   and likewise Wo.
+ *   Output channel co belongs to group g = co / (c_out/groups) and reads input
+ *   channels [g*c_in/groups, (g+1)*c_in/groups).
+ *
+ * Ownership: the caller allocates and owns every device buffer.  No entry
+ * point allocates device memory; forward calls launch kernels asynchronously
+ * on the caller's HIP stream and return.  Descriptors are host objects owned
+ * by the library from conv2d_desc_create until conv2d_desc_destroy; they are
+ * immutable after creation and may be shared across threads.
+ *
+ * Errors: every call returns a conv_status_t and never aborts; no C++
+ * exception crosses the ABI.  conv2d_last_error() returns a thread-local
+ * message for the last failing call on the calling thread.  Validation is
+ * done once at descriptor creation; forward calls only check pointers and
+ * aliasing, then launch.
+ */
+#ifndef CONV2D_MI355X_H
+#define CONV2D_MI355X_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define CONV2D_API __attribute__((visibility("default")))
+#else
+#define CONV2D_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV_OK = 0,
+    CONV_ERR_INVALID_ARG = 1,          /* bad attribute value or null pointer */
+    CONV_ERR_INCOMPATIBLE_SHAPES = 2,  /* channel/group/slope/offset shapes disagree */
+    CONV_ERR_UNSUPPORTED = 3,          /* valid request outside this library's scope */
+    CONV_ERR_ALIAS = 4,                /* output overlaps an input */
+    CONV_ERR_HIP = 5                   /* a HIP runtime call or kernel launch failed */
+} conv_status_t;
+
+/* Activation codes of this library (ncnn does not print its numeric codes). */
+typedef enum {
+    CONV_ACT_NONE = 0,
+    CONV_ACT_RELU = 1,        /* max(0, v) */
+    CONV_ACT_LEAKY_RELU = 2,  /* v >= 0 ? v : act_params[0] * v        (alpha, default 0.01) */
+    CONV_ACT_PRELU = 3,       /* v >= 0 ? v : slope[co or 0] * v       (slope passed at forward) */
+    CONV_ACT_CLIP = 4         /* min(max(v, act_params[0]), act_params[1]) (defaults -FLT_MAX, FLT_MAX) */
+} conv_act_t;
+
+typedef enum {
+    CONV_DTYPE_F32 = 0,   /* x, weight, y float32; fp32 accumulate */
+    CONV_DTYPE_BF16 = 1,  /* x, weight, y bfloat16; fp32 accumulate and epilogue; y rounded to nearest even */
+    CONV_DTYPE_I8 = 2     /* x, weight, y int8; int32 accumulate; requant (qconv2d_forward only) */
+} conv_dtype_t;
+
+typedef enum {
+    CONV_ROUND_HALF_EVEN = 0,  /* default requant rounding */
+    CONV_ROUND_HALF_AWAY = 1   /* ties away from zero, as the yscv requant epilogue does */
+} conv_rounding_t;
+
+/* Convolution attributes.  Fill with conv2d_params_init() and then set what
+ * differs from the defaults.  Pads are ONNX order (top, left, bottom, right);
+ * ncnn's chained defaults (pad_top = pad_left, ...) are the caller's job. */
+typedef struct {
+    int32_t n, c_in, h, w;        /* input batch, channels, height, width */
+    int32_t c_out, k_h, k_w;      /* output channels, kernel size */
+    int32_t pad_top, pad_left, pad_bottom, pad_right;   /* >= 0, default 0 */
+    int32_t stride_h, stride_w;   /* >= 1, default 1 */
+    int32_t dilation_h, dilation_w; /* >= 1, default 1 */
+    int32_t groups;               /* divides c_in and c_out, default 1 */
+    int32_t has_bias;             /* 0/1, default 0 */
+    float pad_value;              /* value of padded taps, default 0 (float paths only) */
+    int32_t act_type;             /* conv_act_t, default CONV_ACT_NONE */
+    float act_params[2];          /* leaky alpha; clip lo/hi.  NaN (the init value) selects
+                                     the default: alpha 0.01; clip -FLT_MAX / FLT_MAX */
+    int32_t prelu_slope_count;    /* 1 or c_out, default 1 */
+    int32_t in_channel_offset;    /* default 0 */
+    int32_t in_total_channels;    /* 0 means c_in */
+    int32_t out_channel_offset;   /* default 0 */
+    int32_t out_total_channels;   /* 0 means c_out */
+    int32_t dtype;                /* conv_dtype_t, default CONV_DTYPE_F32 */
+    int32_t int8_rounding;        /* conv_rounding_t, default CONV_ROUND_HALF_EVEN */
+} conv2d_params_t;
+
+typedef struct conv2d_desc* conv2d_desc_t;
+
+/* Fill *p with the defaults listed above (all sizes 0).  p must not be null. */
+CONV2D_API void conv2d_params_init(conv2d_params_t* p);
+
+/* Validate *p, infer Ho/Wo and choose the kernel.  On success *out receives a
+ * new descriptor owned by the library.  Errors:
+ *   INVALID_ARG           null pointer; size <= 0; negative pad; stride,
+ *                         dilation or kernel < 1; unknown act/dtype/rounding;
+ *                         clip lo > hi; non-finite pad_value or leaky alpha;
+ *                         Ho or Wo < 1 (empty output)
+ *   INCOMPATIBLE_SHAPES   groups not dividing c_in and c_out; slope count not
+ *                         1 or c_out; channel offset + count beyond the total
+ *   UNSUPPORTED           I8 with pad_value != 0 or an activation other than
+ *                         NONE/RELU; tensors beyond 2^31 elements */
+CONV2D_API conv_status_t conv2d_desc_create(const conv2d_params_t* p, conv2d_desc_t* out);
+
+/* Release a descriptor (null is allowed). */
+CONV2D_API void conv2d_desc_destroy(conv2d_desc_t d);
+
+/* out[0..3] = n, out_total_channels, Ho, Wo of the output buffer. */
+CONV2D_API conv_status_t conv2d_desc_get_output_shape(conv2d_desc_t d, int32_t out[4]);
+
+/* Name of the kernel class chosen at creation (static string; for logs). */
+CONV2D_API const char* conv2d_desc_kernel_name(conv2d_desc_t d);
+
+/* Float convolution (dtype F32 or BF16).
+ *   x, w, y   device pointers of the dtype's element type, layouts above
+ *   bias      device float32[c_out]; required iff has_bias, else ignored
+ *   slope     device float32[prelu_slope_count]; required iff act is PRELU
+ *   stream    hipStream_t (null = default stream)
+ * y may be the same buffer as x only when their channel ranges are disjoint
+ * (ConcatFusedTail with in/out offsets); any other overlap of y with x, w,
+ * bias or slope returns CONV_ERR_ALIAS.  A dtype of I8 returns INVALID_ARG. */
+CONV2D_API conv_status_t conv2d_forward(conv2d_desc_t d, const void* x, const void* w, const float* bias,
+                             const float* slope, void* y, void* stream);
+
+/* Fused pointwise 1x1 -> depthwise kxk (the yscv FusedPwDw step).  desc_pw:
+ * 1x1, stride 1, pads 0, groups 1; desc_dw: groups == c_in == c_out ==
+ * desc_pw.c_out, same n/h/w, same dtype (F32).  The expanded tensor stays in
+ * on-chip memory; the depthwise padding applies to the pointwise output, so
+ * taps outside the image read desc_dw.pad_value.  y layout is desc_dw's.
+ * Pointers as in conv2d_forward (b_* / slope_* nullable per descriptor).
+ * Errors: INCOMPATIBLE_SHAPES for a pair that does not chain; UNSUPPORTED for
+ * a dtype other than F32 or a dw stride other than 1; ALIAS as above. */
+CONV2D_API conv_status_t fused_pw_dw_forward(conv2d_desc_t desc_pw, conv2d_desc_t desc_dw, const void* x,
+                                  const void* w_pw, const float* b_pw, const float* slope_pw,
+                                  const void* w_dw, const float* b_dw, const float* slope_dw,
+                                  void* y, void* stream);
+
+/* Symmetric int8 QLinearConv (dtype I8): int32 accumulation, + int32 bias,
+ * then q = saturate_int8(round(f32(acc + bias) * composite) + y_zp), with
+ * composite = f32(f32(x_scale * w_scale) / y_scale) computed on the host and
+ * round = the descriptor's int8_rounding; ReLU (if set) is max(q, y_zp).
+ *   x, w, y   device int8 pointers (layouts above)
+ *   bias      device int32[c_out] or null
+ * Errors: UNSUPPORTED if x_zp != 0 or w_zp != 0 (symmetric scheme only);
+ * INVALID_ARG if a scale is not finite and positive or dtype is not I8. */
+CONV2D_API conv_status_t qconv2d_forward(conv2d_desc_t d, const int8_t* x, float x_scale, int8_t x_zp,
+                              const int8_t* w, float w_scale, int8_t w_zp, const int32_t* bias,
+                              float y_scale, int8_t y_zp, int8_t* y, void* stream);
+
+/* Human-readable name of a status code (static string). */
+CONV2D_API const char* conv2d_status_string(conv_status_t s);
+
+/* Detail of the last error on this thread ("" if none). */
+CONV2D_API const char* conv2d_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV2D_MI355X_H */

@@ -1,0 +1,411 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+fp32: max |gpu - ref| <= 1e-4 * (1 + |ref|); bf16 inputs with fp32
+accumulation: <= 2e-2 * (1 + |ref|) (the oracle is given the same
+bf16-rounded inputs); int8: bit-exact.  Outputs sit between NaN / sentinel
+guard bands, every run is repeated and must be bitwise identical, and
+concat-buffer prefixes must be untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import (BF16_TOL, FP32_TOL, Guarded, assert_bitexact, assert_close, bf16_round, dev,
+                     gpu_layer, layer_params, oracle_layer, to_dev, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def cc():
+    import convolution_conv2d_forward_amd as m
+    return m
+
+
+# --------------------------------------------------------- single conv ----
+
+def test_single_conv_config():
+    wl = workloads.single_conv()
+    L = wl.layers[0]
+    a = wl.arrays
+    y, kname, runs = gpu_layer(L, a["x"], a["w"], a["b"], None, repeat=2)
+    ref = oracle_layer(L, a["x"], a["w"], a["b"], None)
+    assert kname.startswith("igemm_f32")
+    assert_close(y, ref, FP32_TOL, "single conv")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+# ---------------------------------------------------- random fp32 sweep ----
+
+SWEEP = 48
+
+
+@pytest.mark.parametrize("seed", range(SWEEP))
+def test_random_layer_fp32(seed):
+    rng = np.random.default_rng(1000 + seed)
+    L = workloads.random_layer(rng)
+    x, w, b, s = workloads.layer_arrays(rng, L)
+    print(f"case seed={seed} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, w, b, s, repeat=2)
+    ref = oracle_layer(L, x, w, b, s)
+    assert_close(y, ref, FP32_TOL, f"seed {seed} ({kname})")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+# Explicit shapes that reach every tile configuration and the fallbacks:
+# (n, c_in, h, w, c_out, k, stride, pads, dilation, groups, act)
+CLASS_CASES = [
+    (2, 16, 19, 23, 8, 3, 1, 1, 1, 1, workloads.ACT_RELU),          # 3x3, M <= 16
+    (1, 24, 17, 40, 32, 3, 1, 1, 1, 1, workloads.ACT_LEAKY_RELU),   # 3x3, M 32, ragged
+    (2, 40, 13, 21, 48, 3, 2, (0, 1, 2, 1), 1, 1, workloads.ACT_PRELU),  # 3x3 s2 asymmetric pads
+    (1, 12, 30, 33, 64, 3, 1, 2, 2, 1, workloads.ACT_CLIP),         # dilation 2
+    (2, 20, 9, 70, 136, 3, 1, 1, 1, 1, workloads.ACT_NONE),         # M 136: two 128 tiles
+    (3, 36, 11, 7, 24, 1, 1, 0, 1, 1, workloads.ACT_RELU),          # pointwise, flattened
+    (2, 50, 10, 12, 72, 1, 1, 0, 1, 1, workloads.ACT_PRELU),        # pointwise M 72
+    (1, 33, 8, 8, 260, 1, 1, 0, 1, 1, workloads.ACT_NONE),          # pointwise M 260
+    (2, 8, 12, 12, 16, 1, 2, 1, 1, 1, workloads.ACT_RELU),          # 1x1 strided + padded (not flattened)
+    (2, 12, 15, 16, 20, 5, 1, 2, 1, 1, workloads.ACT_LEAKY_RELU),   # 5x5: generic kernel
+    (1, 6, 9, 9, 10, (2, 4), (2, 3), (1, 0, 2, 3), (1, 2), 2, workloads.ACT_CLIP),  # 2x4 grouped
+    (2, 64, 12, 12, 64, 3, 1, 1, 1, 8, workloads.ACT_PRELU),        # grouped, cout_g 8
+    (2, 64, 10, 10, 128, 3, 1, 1, 1, 2, workloads.ACT_RELU),        # grouped, cout_g 64
+    (1, 7, 31, 29, 7, 3, 1, 1, 1, 7, workloads.ACT_CLIP),           # depthwise ragged
+    (2, 5, 17, 16, 5, 3, 2, 1, 1, 5, workloads.ACT_NONE),           # depthwise s2
+    (1, 4, 20, 24, 4, 5, 1, 2, 2, 4, workloads.ACT_RELU),           # depthwise 5x5 d2
+    (1, 6, 12, 12, 12, 3, 1, 1, 1, 6, workloads.ACT_NONE),          # multiplier 2: grouped path
+    (1, 1, 1, 1, 1, 1, 1, 0, 1, 1, workloads.ACT_NONE),             # smallest possible
+    (1, 3, 2, 2, 4, 3, 1, 1, 1, 1, workloads.ACT_RELU),             # kernel larger than image
+    (1, 2, 3, 3, 3, 7, 1, 3, 1, 1, workloads.ACT_NONE),             # 7x7 on 3x3: direct path
+]
+
+
+@pytest.mark.parametrize("i", range(len(CLASS_CASES)))
+@pytest.mark.parametrize("pad_value", [0.0, -0.75])
+def test_kernel_classes_fp32(i, pad_value):
+    n, ci, h, w, co, k, s, p, d, g, act = CLASS_CASES[i]
+    k2 = k if isinstance(k, tuple) else (k, k)
+    s2 = s if isinstance(s, tuple) else (s, s)
+    d2 = d if isinstance(d, tuple) else (d, d)
+    p4 = p if isinstance(p, tuple) else (p, p, p, p)
+    L = workloads.Layer("case", n, ci, h, w, co, k2, stride=s2, pads=p4, dilation=d2, groups=g,
+                        has_bias=True, act=act, alpha=0.1, clip=(-0.5, 0.75), pad_value=pad_value)
+    rng = np.random.default_rng(77 + i)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    print(f"case {i} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, wt, b, sl, repeat=2)
+    ref = oracle_layer(L, x, wt, b, sl)
+    assert_close(y, ref, FP32_TOL, f"case {i} ({kname})")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+# ---------------------------------------------------- ConcatFusedTail ----
+
+@pytest.mark.parametrize("n,co,k", [(1, 16, 3), (3, 12, 3), (2, 24, 1), (2, 6, 3)])
+def test_concat_tail_any_batch(n, co, k):
+    """Conv writing channels [off, off+co) of a [n, T, H, W] buffer equals the
+    conv followed by a channel concat; every other channel is untouched."""
+    t = torch()
+    ci, h, w, off = 10, 13, 17, 21
+    total = off + co + 7
+    groups = co if k == 3 and co == 6 else 1
+    if groups > 1:
+        ci = co
+    L = workloads.Layer("tail", n, ci, h, w, co, (k, k), pads=(k // 2,) * 4, groups=groups, has_bias=True,
+                        act=workloads.ACT_LEAKY_RELU, alpha=0.2)
+    rng = np.random.default_rng(5 + n * 7 + co)
+    x, wt, b, _ = workloads.layer_arrays(rng, L)
+    buf_host = rng.standard_normal((n, total, h, w)).astype(np.float32)
+    buf = to_dev(buf_host)
+    p = layer_params(L, out_total_channels=total, out_channel_offset=off)
+    d = cc().conv2d_desc_create(p)
+    cc().conv2d_forward(d, to_dev(x), to_dev(wt), to_dev(b), None, buf)
+    t.cuda.synchronize()
+    out = buf.cpu().numpy()
+    ref = oracle_layer(L, x, wt, b, None)
+    expect = np.concatenate([buf_host[:, :off], ref, buf_host[:, off + co:]], axis=1)
+    assert_bitexact(out[:, :off], buf_host[:, :off], "prefix channels")
+    assert_bitexact(out[:, off + co:], buf_host[:, off + co:], "suffix channels")
+    assert_close(out, expect, FP32_TOL, "tail slice")
+
+
+def _dense_block(h, w):
+    """The dense-block chain in one concat buffer: layer k reads channels
+    [0, 64+32k) and writes the next slice."""
+    t = torch()
+    wl = workloads.dense_block(h, w)
+    total = workloads.DENSE_TOTAL_CHANNELS
+    buf = t.full((1, total, h, w), float("nan"), device=dev())
+    buf[:, :64] = to_dev(wl.arrays["x"])
+    descs, wts = [], []
+    for k, L in enumerate(wl.layers):
+        p = layer_params(L, in_total_channels=total, out_total_channels=total, out_channel_offset=L.c_in)
+        descs.append(cc().conv2d_desc_create(p))
+        wts.append(to_dev(wl.arrays[f"w{k}"]))
+    for d, wt in zip(descs, wts):
+        cc().conv2d_forward(d, buf, wt, None, None, buf)
+    t.cuda.synchronize()
+    return wl, buf.cpu().numpy()
+
+
+def test_dense_block_chain_reduced_spatial():
+    """Whole chain at 1x{64..256}x24x40 against an oracle chain built by explicit
+    concatenation of independently computed layer outputs (fp32 between layers)."""
+    wl, out = _dense_block(24, 40)
+    cur = wl.arrays["x"].astype(np.float32)
+    for k, L in enumerate(wl.layers):
+        ref = oracle_layer(L, cur, wl.arrays[f"w{k}"], None, None)
+        assert_close(out[:, L.c_in:L.c_in + L.c_out], ref, FP32_TOL, f"layer {k}")
+        cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
+    assert_bitexact(out[:, :64], wl.arrays["x"], "input slice untouched")
+
+
+def test_dense_block_chain_full_size_sampled():
+    """Full 128x128 chain in the launch configuration the benchmark times;
+    each layer is checked at 3000 sampled outputs against the oracle evaluated
+    on the oracle's own chain (full oracle chain, fp32 between layers)."""
+    wl, out = _dense_block(128, 128)
+    rng = np.random.default_rng(0)
+    cur = wl.arrays["x"].astype(np.float32)
+    for k, L in enumerate(wl.layers):
+        ref_full = oracle_layer(L, cur, wl.arrays[f"w{k}"], None, None)   # needed for the next layer's input
+        idx = rng.choice(ref_full.size, 3000, replace=False)
+        got = out[:, L.c_in:L.c_in + L.c_out].reshape(-1)[idx]
+        assert_close(got, ref_full.reshape(-1)[idx], FP32_TOL, f"layer {k}")
+        cur = np.concatenate([cur, ref_full.astype(np.float32)], axis=1)
+
+
+# ------------------------------------------------ inverted bottleneck ----
+
+def _bottleneck_oracle(wl):
+    a = wl.arrays
+    L1, L2, L3 = wl.layers
+    e = oracle_layer(L1, a["x"], a["w_pw1"], None, None).astype(np.float32)
+    d = oracle_layer(L2, e, a["w_dw"], None, None).astype(np.float32)
+    o = oracle_layer(L3, d, a["w_pw2"], None, None)
+    return e, d, o
+
+
+def _run_bottleneck(wl, fused):
+    t = torch()
+    a = wl.arrays
+    L1, L2, L3 = wl.layers
+    d1, d2, d3 = (cc().conv2d_desc_create(layer_params(L)) for L in wl.layers)
+    x = to_dev(a["x"])
+    w1, w2, w3 = to_dev(a["w_pw1"]), to_dev(a["w_dw"]), to_dev(a["w_pw2"])
+    ho, wo = L2.out_hw
+    mid = Guarded(L2.n * L2.c_out * ho * wo, t.float32, float("nan"))
+    out = Guarded(L3.n * L3.c_out * ho * wo, t.float32, float("nan"))
+    exp = None
+    if fused:
+        cc().fused_pw_dw_forward(d1, d2, x, w1, None, None, w2, None, None, mid.view)
+    else:
+        exp = Guarded(L1.n * L1.c_out * L1.h * L1.w, t.float32, float("nan"))
+        cc().conv2d_forward(d1, x, w1, None, None, exp.view)
+        cc().conv2d_forward(d2, exp.view, w2, None, None, mid.view)
+    cc().conv2d_forward(d3, mid.view, w3, None, None, out.view)
+    t.cuda.synchronize()
+    mid.check_guards()
+    out.check_guards()
+    shp = (L2.n, L2.c_out, ho, wo)
+    e = exp.host().numpy().reshape(L1.n, L1.c_out, L1.h, L1.w) if exp is not None else None
+    return e, mid.host().numpy().reshape(shp), out.host().numpy().reshape(L3.n, L3.c_out, ho, wo)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_bottleneck_full_size(fused):
+    wl = workloads.bottleneck()
+    e_ref, d_ref, o_ref = _bottleneck_oracle(wl)
+    e, d, o = _run_bottleneck(wl, fused)
+    if e is not None:
+        assert_close(e, e_ref, FP32_TOL, "pw1")
+    assert_close(d, d_ref, FP32_TOL, "fused pw->dw" if fused else "dw")
+    assert_close(o, o_ref, FP32_TOL, "pw2")
+
+
+FUSED_CASES = [
+    # n, c_in, h, w, c_exp, k, pads, dilation, pw act, dw act, bias, pad_value
+    (1, 8, 9, 13, 40, 3, 1, 1, workloads.ACT_RELU, workloads.ACT_CLIP, True, 0.0),
+    (2, 40, 17, 11, 24, 3, (0, 2, 1, 0), 1, workloads.ACT_PRELU, workloads.ACT_LEAKY_RELU, True, -0.5),
+    (1, 3, 30, 7, 16, 5, 2, 1, workloads.ACT_NONE, workloads.ACT_RELU, False, 0.25),
+    (2, 16, 12, 20, 33, 3, 2, 2, workloads.ACT_CLIP, workloads.ACT_NONE, True, 0.0),
+    (1, 70, 5, 64, 64, 3, 1, 1, workloads.ACT_LEAKY_RELU, workloads.ACT_PRELU, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("i", range(len(FUSED_CASES)))
+def test_fused_pw_dw_cases(i):
+    t = torch()
+    n, ci, h, w, ce, k, p, dil, a1, a2, bias, pv = FUSED_CASES[i]
+    p4 = p if isinstance(p, tuple) else (p,) * 4
+    L1 = workloads.Layer("pw", n, ci, h, w, ce, (1, 1), has_bias=bias, act=a1, alpha=0.1, clip=(-0.3, 0.9))
+    L2 = workloads.Layer("dw", n, ce, h, w, ce, (k, k), pads=p4, dilation=(dil, dil), groups=ce, has_bias=bias,
+                         act=a2, alpha=0.2, clip=(-1.0, 0.5), pad_value=pv)
+    rng = np.random.default_rng(300 + i)
+    x, w1, b1, s1 = workloads.layer_arrays(rng, L1)
+    _, w2, b2, s2 = workloads.layer_arrays(rng, L2)
+    e_ref = oracle_layer(L1, x, w1, b1, s1).astype(np.float32)
+    ref = oracle_layer(L2, e_ref, w2, b2, s2)
+    p1 = layer_params(L1, prelu_slope_count=s1.size)
+    p2 = layer_params(L2, prelu_slope_count=s2.size)
+    d1, d2 = cc().conv2d_desc_create(p1), cc().conv2d_desc_create(p2)
+    ho, wo = L2.out_hw
+    out = Guarded(n * ce * ho * wo, t.float32, float("nan"))
+    dv = lambda v: None if v is None else to_dev(v)
+    cc().fused_pw_dw_forward(d1, d2, to_dev(x), to_dev(w1), dv(b1 if bias else None),
+                             dv(s1 if a1 == workloads.ACT_PRELU else None), to_dev(w2),
+                             dv(b2 if bias else None), dv(s2 if a2 == workloads.ACT_PRELU else None), out.view)
+    t.cuda.synchronize()
+    out.check_guards()
+    assert_close(out.host().numpy().reshape(n, ce, ho, wo), ref, FP32_TOL, f"fused case {i}")
+
+
+# ------------------------------------------------------ mixed sweep ----
+
+def _mixed(name, n):
+    wl = workloads.mixed_sweep(n=n, which={name})
+    L = [l for l in wl.layers if l.name == name][0]
+    a = wl.arrays
+    return L, a[f"x_{name}"], a[f"w_{name}"], a[f"b_{name}"], a[f"s_{name}"]
+
+
+@pytest.mark.parametrize("name", ["s2", "d2", "g32", "pw"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mixed_sweep_reduced_batch(name, dtype):
+    """Each mixed-sweep layer at N=2, fully compared."""
+    L, x, w, b, s = _mixed(name, 2)
+    if dtype == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    y, kname, runs = gpu_layer(L, x, w, b, s, dtype=dtype, repeat=2)
+    ref = oracle_layer(L, x, w, b, s)
+    assert_close(y, ref, FP32_TOL if dtype == "f32" else BF16_TOL, f"{name} {dtype} ({kname})")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+@pytest.mark.parametrize("name", ["s2", "d2", "g32", "pw"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mixed_sweep_full_size_sampled(name, dtype):
+    """Full N=32 layers (the benchmark's launch configuration), 4000 sampled
+    outputs against the oracle evaluated point by point."""
+    L, x, w, b, s = _mixed(name, 32)
+    if dtype == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    y, kname, _ = gpu_layer(L, x, w, b, s, dtype=dtype)
+    rng = np.random.default_rng(1)
+    idx = rng.choice(y.size, 4000, replace=False)
+    ref = oracle.conv2d_points(x, w, b, idx, stride=L.stride, pads=L.pads, dilation=L.dilation,
+                               groups=L.groups, act=L.act, slope=s)
+    assert_close(y.reshape(-1)[idx], ref, FP32_TOL if dtype == "f32" else BF16_TOL, f"{name} {dtype} ({kname})")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_layer_bf16(seed):
+    rng = np.random.default_rng(5000 + seed)
+    L = workloads.random_layer(rng, max_c=40)
+    x, w, b, s = workloads.layer_arrays(rng, L)
+    x, w = bf16_round(x), bf16_round(w)
+    pv = float(bf16_round(np.array([L.pad_value], np.float32))[0])
+    print(f"case seed={seed} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, w, b, s, dtype="bf16", repeat=2)
+    ref = oracle_layer(L, x, w, b, s, pad_value=pv)
+    assert_close(y, ref, BF16_TOL, f"bf16 seed {seed} ({kname})")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+# --------------------------------------------------------------- int8 ----
+
+def _qrun(L, x, w, b, scales, *, rounding=0, y_zp=0, relu=False):
+    t = torch()
+    sx, sw, sy = scales
+    p = layer_params(L, "i8", int8_rounding=rounding)
+    if relu:
+        p.act_type = 1
+    d = cc().conv2d_desc_create(p)
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
+    y = Guarded(n * ot * ho * wo, t.int8, 0x5A)
+    cc().qconv2d_forward(d, to_dev(x), sx, 0, to_dev(w), sw, 0, to_dev(b) if L.has_bias else None, sy, y_zp, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    return y.host().numpy().reshape(n, ot, ho, wo), cc().conv2d_desc_kernel_name(d)
+
+
+def test_int8_chain_full_size():
+    """The int8 chain (dw s1 -> dw s2 -> pw) at full size, bit-exact at every
+    stage; the oracle runs its own chain from the seeded input."""
+    wl = workloads.int8_chain()
+    a = wl.arrays
+    cur_ref = a["x"]
+    cur_gpu = a["x"]
+    sat = []
+    for L in wl.layers:
+        ref = oracle.qconv2d(cur_ref, a[f"w_{L.name}"], a[f"b_{L.name}"], *workloads.INT8_SCALES,
+                             stride=L.stride, pads=L.pads, groups=L.groups)
+        got, kname = _qrun(L, cur_gpu, a[f"w_{L.name}"], a[f"b_{L.name}"], workloads.INT8_SCALES)
+        assert_bitexact(got, ref, f"{L.name} ({kname})")
+        sat.append(float(np.mean((ref == 127) | (ref == -128))))
+        cur_ref, cur_gpu = ref, got
+    print("saturated fraction per stage", sat, flush=True)
+
+
+INT8_CASES = [
+    # n, c, h, w, c_out, k, stride, pads, groups
+    (2, 12, 19, 33, 12, 3, 1, 1, 12),      # dw s1, W not a multiple of 16
+    (2, 8, 32, 32, 8, 3, 2, 1, 8),         # dw s2, vector path
+    (1, 5, 17, 9, 5, 5, 1, 2, 5),          # dw 5x5
+    (2, 144, 10, 10, 48, 1, 1, 0, 1),      # pw K 144
+    (1, 20, 7, 9, 30, 1, 1, 0, 1),         # pw K not multiple of 16, HW odd
+    (1, 200, 4, 8, 70, 1, 1, 0, 1),        # pw K 200 (4 chunks), M 70
+    (2, 6, 9, 11, 10, 3, 1, 1, 2),         # grouped int8 3x3: direct path
+]
+
+
+@pytest.mark.parametrize("i", range(len(INT8_CASES)))
+@pytest.mark.parametrize("mode", ["rne", "away_relu_zp"])
+def test_int8_cases(i, mode):
+    n, c, h, w, co, k, s, p, g = INT8_CASES[i]
+    L = workloads.Layer("q", n, c, h, w, co, (k, k), stride=(s, s), pads=(p,) * 4, groups=g, has_bias=True)
+    rng = np.random.default_rng(900 + i)
+    x = rng.integers(-128, 127, size=L.x_shape, endpoint=True).astype(np.int8)
+    wt = rng.integers(-127, 127, size=L.w_shape, endpoint=True).astype(np.int8)
+    b = rng.integers(-500, 500, size=co, endpoint=True).astype(np.int32)
+    # composite 0.5 exactly for the tie-heavy mode, the symmetric scales otherwise
+    scales = (1.0, 1.0, 2.0 * 127 * k * k) if mode != "rne" else workloads.INT8_SCALES
+    rounding = 0 if mode == "rne" else 1
+    y_zp = 0 if mode == "rne" else 3
+    relu = mode != "rne"
+    ref = oracle.qconv2d(x, wt, b, *scales, stride=L.stride, pads=L.pads, groups=g, y_zp=y_zp,
+                         rounding=rounding, relu=relu)
+    got, kname = _qrun(L, x, wt, b, scales, rounding=rounding, y_zp=y_zp, relu=relu)
+    assert_bitexact(got, ref, f"int8 case {i} {mode} ({kname})")
+
+
+def test_int8_ties_exact():
+    """composite = 0.5 and odd accumulators: every output is a tie."""
+    L = workloads.Layer("q", 1, 4, 6, 6, 4, (1, 1), has_bias=True)
+    x = np.array([1, 3, 5, -1, -3, -5, 7, 9] * 18, dtype=np.int8).reshape(L.x_shape)
+    wt = np.zeros(L.w_shape, dtype=np.int8)
+    for c in range(4):
+        wt[c, c] = 1
+    b = np.zeros(4, dtype=np.int32)
+    for rounding in (0, 1):
+        ref = oracle.qconv2d(x, wt, b, 1.0, 1.0, 2.0, rounding=rounding)
+        got, _ = _qrun(L, x, wt, b, (1.0, 1.0, 2.0), rounding=rounding)
+        assert_bitexact(got, ref, f"ties rounding={rounding}")
+
+
+# ------------------------------------------------------------ errors ----
+
+def test_forward_rejects_alias_and_bad_zero_points():
+    t = torch()
+    L = workloads.Layer("a", 1, 4, 8, 8, 4, (3, 3), pads=(1,) * 4)
+    d = cc().conv2d_desc_create(layer_params(L))
+    x = t.zeros(4 * 64, device=dev())
+    w = t.zeros(4 * 4 * 9, device=dev())
+    with pytest.raises(cc().ConvError) as e:
+        cc().conv2d_forward(d, x, w, None, None, x)
+    assert e.value.status == cc().CONV_ERR_ALIAS
+    qd = cc().conv2d_desc_create(layer_params(L, "i8"))
+    xi = t.zeros(4 * 64, dtype=t.int8, device=dev())
+    wi = t.zeros(4 * 4 * 9, dtype=t.int8, device=dev())
+    yi = t.zeros(4 * 64, dtype=t.int8, device=dev())
+    with pytest.raises(cc().ConvError) as e:
+        cc().qconv2d_forward(qd, xi, 0.1, 1, wi, 0.1, 0, None, 0.1, 0, yi)
+    assert e.value.status == cc().CONV_ERR_UNSUPPORTED
