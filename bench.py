@@ -1,0 +1,459 @@
+"""Benchmark of the conv2d forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline] [--no-extra]
+
+A step is one pass of the dense-block chain: input 1x64x128x128 in a
+1x256x128x128 fp32 concat buffer, five 3x3 s1 p1 convolutions with
+Cin = 64+32k and Cout = 32 (last 64), LeakyReLU(0.2) on all but the last,
+each writing the buffer's next channel slice (ConcatFusedTail), no bias.
+`value` is conv GFLOP/s (2 * MACs, padded taps counted) over K timed steps.
+Steps rotate over buffer sets (>= 1 GiB in all) so that inputs come from HBM,
+not from the 256 MB last-level cache.
+
+The JSON line also carries:
+  roofline      the dominant kernel of the step against the fp32 MFMA peak;
+                its duration comes from HIP events recorded around every launch
+                on the launch stream inside the timed region
+  cpu_baseline  the float64 CPU oracle timed on this host's cores on a sample
+                of the same workload's outputs
+  per_config    the other synthetic workloads (single conv, inverted
+                bottleneck fused/unfused, mixed sweep fp32/bf16, int8 chain),
+                each layer timed with events, with its binding roofline
+Everything on stdout except the final JSON line goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv GFLOP/s (2·MACs) and depthwise GB/s, % of MFMA/HBM roofline"
+PEAK = {"f32": 157.3e12, "bf16": 2516.6e12, "i8": 5033.2e12, "hbm": 8.0e12}
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="all",
+                    help="all | dense_block | single_conv | bottleneck | mixed_f32 | mixed_bf16 | int8_chain | copy")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--reps", type=int, default=20, help="timed launches per layer for per_config")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ setup --
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev():
+    return torch_mod().device("cuda:0")
+
+
+def t_(a, dtype=None):
+    t = torch_mod().from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev())
+
+
+def params_of(L, dtype="f32", **kw):
+    import convolution_conv2d_forward_amd as cc
+    import workloads
+    return cc.make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride, pads=L.pads, dilation=L.dilation,
+                          groups=L.groups, has_bias=L.has_bias, pad_value=L.pad_value, act=L.act,
+                          alpha=L.alpha if L.act == workloads.ACT_LEAKY_RELU else None,
+                          clip=L.clip if L.act == workloads.ACT_CLIP else None, dtype=dtype,
+                          prelu_slope_count=L.c_out if L.act == workloads.ACT_PRELU else 1, **kw)
+
+
+def layer_bytes(L, esize, wsize=None, extra=0):
+    """Algorithmic HBM bytes: x once + weights + bias/slope + y once."""
+    ho, wo = L.out_hw
+    wsize = esize if wsize is None else wsize
+    b = L.n * L.c_in * L.h * L.w * esize + L.c_out * (L.c_in // L.groups) * L.k[0] * L.k[1] * wsize
+    b += L.n * L.c_out * ho * wo * esize
+    if L.has_bias:
+        b += 4 * L.c_out
+    if L.act == 3:
+        b += 4 * L.c_out
+    return b + extra
+
+
+class EventTimer:
+    """HIP events around each launch, on the current (launch) stream."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def run(self, key, fn):
+        torch = torch_mod()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.setdefault(key, []).append((s, e))
+
+    def mean_us(self, key):
+        torch_mod().cuda.synchronize()
+        ts = [s.elapsed_time(e) * 1e3 for s, e in self.pairs[key]]
+        return float(np.mean(ts)), float(np.median(ts)), len(ts)
+
+
+def roofline_entry(flops, bytes_, t_us, dtype, bound=None):
+    t = t_us * 1e-6
+    mf = flops / t / PEAK[dtype]
+    hb = bytes_ / t / PEAK["hbm"]
+    t_roof = max(flops / PEAK[dtype], bytes_ / PEAK["hbm"])
+    if bound is None:
+        bound = "mfma" if flops / PEAK[dtype] >= bytes_ / PEAK["hbm"] else "hbm"
+    return {"us": round(t_us, 3), "gflops": round(flops / t / 1e9, 1), "gbps": round(bytes_ / t / 1e9, 1),
+            "mfma_frac": round(mf, 4), "hbm_frac": round(hb, 4), "bound": bound,
+            "roofline_frac": round(t_roof / t, 4), "flops": int(flops), "bytes": int(bytes_)}
+
+
+# ------------------------------------------------------------ dense block --
+
+class DenseBlock:
+    """The chain: 5 convs into one concat buffer, rotated over buffer sets."""
+
+    def __init__(self, h=128, w=128):
+        import convolution_conv2d_forward_amd as cc
+        import workloads
+        torch = torch_mod()
+        self.cc = cc
+        wl = workloads.dense_block(h, w)
+        self.layers = wl.layers
+        total = workloads.DENSE_TOTAL_CHANNELS
+        buf_bytes = total * h * w * 4
+        self.nsets = max(1, -(-ROTATE_BYTES // buf_bytes))
+        x = t_(wl.arrays["x"])
+        self.bufs = []
+        for _ in range(self.nsets):
+            b = torch.zeros((1, total, h, w), device=dev())
+            b[:, :64] = x
+            self.bufs.append(b)
+        self.descs = [cc.conv2d_desc_create(params_of(L, in_total_channels=total, out_total_channels=total,
+                                                       out_channel_offset=L.c_in)) for L in self.layers]
+        self.kernels = [cc.conv2d_desc_kernel_name(d) for d in self.descs]
+        self.w = [t_(wl.arrays[f"w{k}"]) for k in range(len(self.layers))]
+        self.flops = [L.flops for L in self.layers]
+        # x slice read once + weights + the written slice
+        self.bytes = [4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w) for L in self.layers]
+        self.i = 0
+
+    def step(self, timer=None):
+        buf = self.bufs[self.i % self.nsets]
+        self.i += 1
+        for k, (d, w) in enumerate(zip(self.descs, self.w)):
+            fn = lambda d=d, w=w: self.cc.conv2d_forward(d, buf, w, None, None, buf)
+            if timer is None:
+                fn()
+            else:
+                timer.run(k, fn)
+
+
+def bench_dense_block(steps, warmup):
+    torch = torch_mod()
+    db = DenseBlock()
+    log(f"dense block: {db.nsets} buffer sets, kernels {db.kernels}")
+    for _ in range(warmup):
+        db.step()
+    torch.cuda.synchronize()
+    # Wall-clock pass: K steps, no events.
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        db.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # Event pass over the same number of steps: per-launch durations.
+    timer = EventTimer()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        db.step(timer)
+    torch.cuda.synchronize()
+    per = [timer.mean_us(k) for k in range(len(db.layers))]
+    return db, wall, per
+
+
+def dense_roofline(db, per):
+    """Roofline of the dominant kernel: the instantiation with the largest
+    total event time in the step (layers sharing a kernel are pooled)."""
+    groups = {}
+    for k, name in enumerate(db.kernels):
+        cfg = f"{name}/M{64 if db.layers[k].c_out > 32 else 32}"
+        g = groups.setdefault(cfg, {"layers": [], "flops": 0, "bytes": 0, "us": 0.0})
+        g["layers"].append(db.layers[k].name)
+        g["flops"] += db.flops[k]
+        g["bytes"] += db.bytes[k]
+        g["us"] += per[k][0]
+    dom = max(groups, key=lambda g: groups[g]["us"])
+    g = groups[dom]
+    n = len(g["layers"])
+    achieved = g["flops"] / (g["us"] * 1e-6) / 1e12
+    return dom, g, {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["f32"] / 1e12, "unit": "TFLOP/s",
+        "frac": round(achieved * 1e12 / PEAK["f32"], 4), "traffic": traffic_for(dom, n),
+        "kernel": dom, "launches_per_step": n, "avg_launch_us": round(g["us"] / n, 3),
+        "flops_per_launch": int(g["flops"] / n), "layers": g["layers"],
+    }
+
+
+def _source_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, launches):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else null."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_sha") != _source_sha(rec["source"]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# -------------------------------------------------------------- per config --
+
+def _rotating(make, footprint, target=ROTATE_BYTES, cap=64):
+    n = int(min(cap, max(1, -(-target // max(1, footprint)))))
+    return [make() for _ in range(n)]
+
+
+def time_layer(key, fn_sets, reps, warm=3):
+    """fn_sets: list of callables (one per rotating buffer set)."""
+    torch = torch_mod()
+    for i in range(warm):
+        fn_sets[i % len(fn_sets)]()
+    torch.cuda.synchronize()
+    timer = EventTimer()
+    for i in range(reps):
+        timer.run(key, fn_sets[i % len(fn_sets)])
+    return timer.mean_us(key)[0]
+
+
+def float_layer_fns(L, x, w, b, s, dtype, reps):
+    import convolution_conv2d_forward_amd as cc
+    torch = torch_mod()
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    esize = 4 if dtype == "f32" else 2
+    d = cc.conv2d_desc_create(params_of(L, dtype))
+    ho, wo = L.out_hw
+    wd = t_(w, tdt)
+    bd = t_(b) if L.has_bias else None
+    sd = t_(s) if L.act == 3 else None
+    xs = t_(x, tdt)
+    foot = (x.size + L.n * L.c_out * ho * wo) * esize
+
+    def make():
+        xi = xs.clone()
+        yi = torch.empty((L.n, L.c_out, ho, wo), dtype=tdt, device=dev())
+        return lambda: cc.conv2d_forward(d, xi, wd, bd, sd, yi)
+
+    fns = _rotating(make, foot)
+    t = time_layer(L.name, fns, reps)
+    return t, cc.conv2d_desc_kernel_name(d)
+
+
+def per_config(reps):
+    import convolution_conv2d_forward_amd as cc
+    import workloads
+    torch = torch_mod()
+    out = {}
+
+    # single conv (latency)
+    wl = workloads.single_conv()
+    L = wl.layers[0]
+    t, k = float_layer_fns(L, wl.arrays["x"], wl.arrays["w"], wl.arrays["b"], None, "f32", reps)
+    out["single_conv"] = {"conv": dict(roofline_entry(L.flops, layer_bytes(L, 4), t, "f32", bound="latency"),
+                                       kernel=k)}
+    log("single_conv", out["single_conv"])
+
+    # inverted bottleneck
+    wl = workloads.bottleneck()
+    L1, L2, L3 = wl.layers
+    a = wl.arrays
+    res = {}
+    for L, wk in ((L1, "w_pw1"), (L2, "w_dw"), (L3, "w_pw2")):
+        rng = np.random.default_rng(3)
+        x = a["x"] if L is L1 else rng.standard_normal(L.x_shape).astype(np.float32)
+        t, k = float_layer_fns(L, x, a[wk], None, None, "f32", reps)
+        res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 4), t, "f32"), kernel=k)
+    d1, d2 = cc.conv2d_desc_create(params_of(L1)), cc.conv2d_desc_create(params_of(L2))
+    w1, w2 = t_(a["w_pw1"]), t_(a["w_dw"])
+    xs = t_(a["x"])
+
+    def make_fused():
+        xi = xs.clone()
+        yi = torch.empty((L2.n, L2.c_out, L2.h, L2.w), device=dev())
+        return lambda: cc.fused_pw_dw_forward(d1, d2, xi, w1, None, None, w2, None, None, yi)
+
+    fns = _rotating(make_fused, (L1.n * L1.c_in + L2.n * L2.c_out) * L1.h * L1.w * 4)
+    t = time_layer("fused", fns, reps)
+    fb = 4 * (L1.n * L1.c_in * L1.h * L1.w + L1.c_out * L1.c_in + L2.c_out * 9 + L2.n * L2.c_out * L2.h * L2.w)
+    res["fused_pw_dw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "f32"), kernel="fused_pw_dw")
+    out["bottleneck"] = res
+    log("bottleneck", res)
+
+    # mixed sweep fp32 / bf16
+    for dtype in ("f32", "bf16"):
+        res = {}
+        for name in ("s2", "d2", "g32", "pw"):
+            wl = workloads.mixed_sweep(which={name})
+            L = [l for l in wl.layers if l.name == name][0]
+            a = wl.arrays
+            t, k = float_layer_fns(L, a[f"x_{name}"], a[f"w_{name}"], a[f"b_{name}"], a[f"s_{name}"], dtype, reps)
+            es = 4 if dtype == "f32" else 2
+            res[name] = dict(roofline_entry(L.flops, layer_bytes(L, es), t, dtype), kernel=k)
+            log("mixed", dtype, name, res[name])
+        out[f"mixed_sweep_{dtype}"] = res
+
+    # int8 chain
+    wl = workloads.int8_chain()
+    a = wl.arrays
+    res = {}
+    for L in wl.layers:
+        d = cc.conv2d_desc_create(params_of(L, "i8"))
+        ho, wo = L.out_hw
+        rng = np.random.default_rng(5)
+        x = a["x"] if L.name == "dw_s1" else rng.integers(-128, 128, size=L.x_shape).astype(np.int8)
+        xs = t_(x)
+        wd, bd = t_(a[f"w_{L.name}"]), t_(a[f"b_{L.name}"])
+
+        def make(d=d, xs=xs, wd=wd, bd=bd, L=L, ho=ho, wo=wo):
+            xi = xs.clone()
+            yi = torch.empty((L.n, L.c_out, ho, wo), dtype=torch.int8, device=dev())
+            return lambda: cc.qconv2d_forward(d, xi, 0.02, 0, wd, 0.01, 0, bd, 0.05, 0, yi)
+
+        fns = _rotating(make, x.size + L.n * L.c_out * ho * wo)
+        t = time_layer(L.name, fns, reps)
+        res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 1, extra=0), t, "i8"),
+                           kernel=cc.conv2d_desc_kernel_name(d))
+        log("int8", L.name, res[L.name])
+    out["int8_chain"] = res
+    return out
+
+
+def copy_probe(reps):
+    """A plain device copy of known size (calibrates the HBM byte counters)."""
+    torch = torch_mod()
+    n = 256 << 20   # 1 GiB of float32
+    a = torch.ones(n, device=dev())
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    timer = EventTimer()
+    for _ in range(reps):
+        timer.run("copy", lambda: b.copy_(a))
+    t = timer.mean_us("copy")[0]
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "us": t, "gbps": 8 * n / (t * 1e-6) / 1e9}
+
+
+# ------------------------------------------------------------ cpu baseline --
+
+def cpu_baseline(target_s=12.0):
+    """The oracle (as it stands) on whole passes of the same step: the five
+    dense-block layers, each computed in full in float64 from the previous
+    layers' float32 outputs, with the concat buffer assembled by plain
+    concatenation.  Passes repeat until about target_s seconds have run."""
+    import oracle
+    import workloads
+    layers = workloads.dense_block_layers()
+    wl = workloads.dense_block()
+    step_flops = sum(L.flops for L in layers)
+
+    def one_pass():
+        buf = wl.arrays["x"]
+        for k, L in enumerate(layers):
+            y = oracle.conv2d(buf, wl.arrays[f"w{k}"], None, pads=L.pads, act=L.act, alpha=L.alpha)
+            buf = np.concatenate([buf, y.astype(np.float32)], axis=1)
+        return buf
+
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        passes += 1
+        s = time.perf_counter() - t0
+        if s >= target_s:
+            break
+    f = passes * step_flops
+    return {"value": round(f / s / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the 5-layer dense-block chain "
+                      f"({f / 1e9:.2f} GFLOP in {s:.1f} s, float64 direct loops, OpenMP over (n, c_out))",
+            "seconds": round(s, 2)}
+
+
+# ------------------------------------------------------------------- main --
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described, not built).", file=sys.stderr)
+        sys.exit(2)
+    torch = torch_mod()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import convolution_conv2d_forward_amd as cc   # noqa: F401  (fails loudly if the library is missing)
+
+    if args.only == "copy":
+        log(json.dumps(copy_probe(args.steps)))
+        return
+    if args.only not in ("all", "dense_block"):
+        log(json.dumps(per_config_only(args.only, args.reps)))
+        return
+
+    db, wall, per = bench_dense_block(args.steps, args.warmup)
+    step_flops = sum(db.flops)
+    value = step_flops * args.steps / wall / 1e9
+    dom, g, roof = dense_roofline(db, per)
+    layers = {L.name: dict(roofline_entry(db.flops[k], db.bytes[k], per[k][0], "f32"), kernel=db.kernels[k])
+              for k, L in enumerate(db.layers)}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "dense_block_chain_fp32: 1x64x128x128 input in a 1x256x128x128 concat buffer; "
+                               "5 conv3x3 s1 p1, Cin=64+32k, Cout=32 (last 64), LeakyReLU(0.2) except last, "
+                               "ConcatFusedTail writes, no bias",
+                   "gflop_per_step": round(step_flops / 1e9, 4), "buffer_sets": db.nsets,
+                   "kernel_sum_us_per_step": round(sum(p[0] for p in per), 2)},
+        "roofline": roof,
+        "layers": layers,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+        log("cpu_baseline", line["cpu_baseline"])
+    if not args.no_extra and args.only == "all":
+        line["per_config"] = per_config(args.reps)
+    print(json.dumps(line), flush=True)
+
+
+def per_config_only(name, reps):
+    return {"note": f"--only {name}: use --only all for the per-config table"}
+
+
+if __name__ == "__main__":
+    main()
