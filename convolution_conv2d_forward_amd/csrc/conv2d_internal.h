@@ -33,6 +33,31 @@ inline FastDiv make_fastdiv(uint32_t d) {
     return f;
 }
 
+// Division of any 32-bit unsigned numerator by a runtime constant d >= 1
+// (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994, round-up method): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, the quotient is
+// (t + ((x - t) >> 1)) >> (l - 1), t = umulhi(x, m).
+struct DivU32 {
+    uint32_t d;
+    uint32_t m;
+    uint32_t s;   // l - 1 (unused for d == 1)
+};
+
+inline DivU32 make_divu32(uint32_t d) {
+    DivU32 r;
+    r.d = d;
+    r.m = 0;
+    r.s = 0;
+    if (d > 1) {
+        uint32_t l = 0;
+        while (((uint64_t)1 << l) < d) ++l;
+        r.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+        r.s = l - 1;
+    }
+    return r;
+}
+
 // Everything a forward kernel needs, passed by value.  Sizes are element
 // counts; offsets into x and y are computed in 64-bit inside the kernels.
 struct ConvArgs {
@@ -63,6 +88,10 @@ struct ConvArgs {
     int32_t stages;                  // LDS pipeline stages (1 or 2)
     uint32_t num_blocks;             // grid size (for the XCD remap)
     FastDiv div_patch_hw, div_patch_w, div_tile_w;
+    int32_t patch_shift;             // fp32 igemm: input column of LDS column 0 is iw_lo - patch_shift
+    int32_t pt_vertical;             // fp32 igemm: a block's pixel sub-tiles stack along rows (1) or columns (0)
+    int32_t vec_store;               // outputs may be written as 16-byte vectors
+    DivU32 dv_co_tiles, dv_groups, dv_tiles_w, dv_tiles_h;   // block index decomposition
 
     // int8 requant
     float composite;
@@ -82,6 +111,7 @@ struct Desc {
     int32_t tile_h, tile_w;
     int32_t lds_bytes;
     int32_t stages;
+    int32_t pt_vertical;
     bool flatten_1x1;            // 1x1/s1/p0: treat [h][w] as one row of h*w pixels
 };
 

@@ -17,6 +17,12 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
     return f.d == 1 ? x : __umulhi(x, f.m);
 }
 
+__device__ __forceinline__ uint32_t divu(uint32_t x, DivU32 f) {
+    if (f.d == 1) return x;
+    const uint32_t t = __umulhi(x, f.m);
+    return (t + ((x - t) >> 1)) >> f.s;
+}
+
 // MI355X has 8 XCDs and the dispatcher hands consecutive workgroups to
 // consecutive XCDs.  Remap so that consecutive logical tiles (which share
 // input patches) land on the same XCD and hit its L2.

@@ -292,7 +292,34 @@ const CfgInfo& cfg(int i) {
     return t[i];
 }
 
+
+int patch_stride_for(int phw) {
+    // Smallest stride >= phw with stride % 64 == 16: the four channel planes
+    // read by one MFMA operand fetch then start 16 banks apart.
+    int s = ((phw + 63 - 16) / 64) * 64 + 16;
+    if (s < phw) s += 64;
+    return s;
+}
+
 }  // namespace
+
+void fill_tiling(const Desc& d, ConvArgs& a) {
+    // Per-tile geometry of the bf16 implicit GEMM.
+    const conv2d_params_t& p = d.p;
+    if (d.flatten_1x1) {
+        a.h = 1; a.w = p.h * p.w; a.ho = 1; a.wo = d.ho * d.wo;
+    }
+    a.tile_h = d.tile_h;
+    a.tile_w = d.tile_w;
+    a.tiles_h = (a.ho + d.tile_h - 1) / d.tile_h;
+    a.tiles_w = (a.wo + d.tile_w - 1) / d.tile_w;
+    a.patch_h = (d.tile_h - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
+    a.patch_w = (d.tile_w - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
+    a.patch_stride = patch_stride_for(a.patch_h * a.patch_w);
+    a.div_patch_hw = make_fastdiv((uint32_t)(a.patch_h * a.patch_w));
+    a.div_patch_w = make_fastdiv((uint32_t)a.patch_w);
+    a.div_tile_w = make_fastdiv((uint32_t)d.tile_w);
+}
 
 bool plan_igemm_bf16(Desc& d) {
     const conv2d_params_t& p = d.p;

@@ -2,172 +2,236 @@
 //
 // The Go "ops" page (section ConvOp) runs Conv as im2col + GEMM and fuses the
 // bias and activation into the GEMM write (ConvLeakyReluOp, ConvPReluOp).
-// Here the im2col matrix is never built: per output tile the kernel stages a
-// halo patch of the input (pad_value outside the image, ncnn "convolution")
-// and a slice of the OIHW weights in LDS, then feeds v_mfma_f32_16x16x4f32
-// straight from those tiles.  Per group g the GEMM is
+// Here the im2col matrix is never built.  Per group g the GEMM is
 //   Y_g[co, pixel] = sum_k W_g[co, k] * Xhat_g[k, pixel],  k = (ci, r, s),
-// with M = output channels (rows of the MFMA), N = output pixels (columns:
-// consecutive pixels of a row give coalesced stores), K = input channels x
-// kernel taps.  Inside a channel chunk the K order is (r, s) outer, ci inner,
-// so four consecutive K of one MFMA step are four channels at the same tap.
+// with M = output channels, N = output pixels, K = input channels x taps, and
+// Xhat read out of an input patch staged in LDS: the B operand of tap (r, s)
+// is the patch shifted by (r*dilation_h, s*dilation_w), and patch positions
+// outside the image hold pad_value (ncnn "convolution": pad, then correlate).
 //
-// Tile: BM output channels x BN output pixels (tile_h rows x tile_w cols of
-// one image), 4 waves arranged WAVES_M x WAVES_N x WAVES_K; waves that share
-// an output sub-tile split the channel chunk and are summed through LDS at
-// the end.  The epilogue adds the bias, applies the activation and writes
-// channel out_off + g*cout_g + co of a buffer with out_total channels (the
-// ConcatFusedTail store of the Go "ops" page, for any batch size).
+// Work split.  A workgroup owns BM output channels x PT pixel sub-tiles of
+// TH x TW outputs; its four waves are KS-way split-K x PT pixel sub-tiles.
+// Each wave streams its own slice of the input channels, CW channels at a
+// time, through a private double-buffered LDS stage:
+//   weights  [co][ci*KHW + rs]     (OIHW order, row stride KP)
+//   patch    [ci][row][col]        (channel stride PS)
+// so the main loop has no workgroup barrier at all; the waves only meet in
+// the epilogue, where the split-K partial sums are added through LDS.
+// One MFMA step (v_mfma_f32_16x16x4f32) takes four channels at one tap: lane
+// group q = lane/16 supplies channel 4*step+q of both operands.  The strides
+// are chosen so that every operand fetch hits 64 distinct LDS banks:
+// KP is a multiple of 4 with KP/4 odd (16 rows x 4 k-slots), PS = 16 mod 64
+// (4 channel planes x 16 consecutive pixels).
+//
+// Global traffic per chunk is a few 16-byte loads per lane at offsets
+// computed once per workgroup (the patch geometry does not change from one
+// chunk to the next); the loads of chunk c+1 are in flight while chunk c is
+// multiplied out of LDS.
+//
+// The epilogue adds the bias, applies the activation and writes channel
+// out_off + g*cout_g + co of a buffer with out_total channels (the
+// ConcatFusedTail store of the Go "ops" page, any batch size), four
+// consecutive pixels per lane so that a row of 16 lanes writes 256 bytes.
 #include "device_common.h"
 
 namespace conv2d {
 
 namespace {
 
-constexpr int kThreads = 256;
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int WAVES_K_, int CK_, int KH_, int KW_,
-          int XPT_, int WPT_>
-struct IgemmF32Cfg {
-    static constexpr int BM = BM_, BN = BN_;
-    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES_K = WAVES_K_;
-    static constexpr int CK = CK_, KH = KH_, KW = KW_;
-    static constexpr int XPT = XPT_, WPT = WPT_;
-    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    static constexpr int MI = WM / 16, NI = WN / 16;
-    static constexpr int CKW = CK / WAVES_K;            // channels of a chunk per wave
-    static constexpr int BMP = BM == 16 ? 16 : BM + 16; // LDS row stride of the weight tile
-    static_assert(WAVES_M * WAVES_N * WAVES_K == 4, "4 waves per workgroup");
-    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 fragments");
-    static_assert(CKW % 4 == 0, "each wave needs whole 4-channel MFMA steps");
+// LDS row stride of the weight tile: >= k, a multiple of 4, stride/4 odd.
+__host__ __device__ constexpr int a_stride(int k) {
+    return ((k + 3) / 4) % 2 ? (k + 3) / 4 * 4 : (k + 3) / 4 * 4 + 4;
+}
+
+template <int BM_, int BN_, int TW_, int CW_, int KH_, int KW_, int NW_, int WM_, int KS_, int ST_, int XS_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, TW = TW_, TH = BN_ / TW_, CW = CW_;
+    static constexpr int KH = KH_, KW = KW_, KHW = KH_ * KW_;
+    static constexpr int NW = NW_, NT = 64 * NW_;  // waves and threads per workgroup
+    static constexpr int WM = WM_;                 // waves splitting the BM rows
+    static constexpr int KS = KS_;                 // waves splitting K
+    static constexpr int PT = NW_ / (WM_ * KS_);   // pixel sub-tiles per workgroup
+    static constexpr int ST = ST_;                 // LDS stages per wave (1 or 2)
+    static constexpr int WR = BM / WM;             // rows of one wave tile
+    static constexpr int MI = WR / 16, NI = BN / 16;
+    static constexpr int K = CW * KHW;            // K values of one wave chunk
+    static constexpr int KP = a_stride(K);        // weight row stride in LDS
+    static constexpr int AF4 = WR * K / 4;        // 16-byte weight units per wave chunk
+    static constexpr int AS = (AF4 + 63) / 64;    // weight units per lane
+    static constexpr int XS = XS_;                // patch units per lane (upper bound)
+    static constexpr int ASZ = WR * KP;           // LDS floats of the weight tile
+    static constexpr int RS = BN + 4;             // row stride of the reduction tile
+    static_assert(WR % 16 == 0 && BN % 16 == 0, "whole 16x16 fragments");
+    static_assert(NW % (WM * KS) == 0, "waves split into row halves, K slices and pixel sub-tiles");
+    static_assert(TW % 16 == 0 && BN % TW == 0, "a fragment is 16 pixels of one row");
+    static_assert(CW % 4 == 0, "a wave chunk is whole 4-channel MFMA steps");
+    static_assert((PT * BM * BN / 4) % 64 == 0, "epilogue units fill whole waves");
+    static_assert(ST == 1 || ST == 2, "one or two LDS stages");
 };
 
-// Floats of LDS one pipeline stage needs.
-template <class C>
-__host__ __device__ inline int stage_floats(int patch_stride, int khw) {
-    return C::CK * patch_stride + khw * C::CK * C::BMP;
+__device__ __forceinline__ void wave_lds_sync() {
+    // The LDS stage is private to the wave; order its writes before the reads
+    // of other lanes of the same wave.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void igemm_f32_kernel(ConvArgs a) {
-    extern __shared__ float lds[];
-    constexpr int BM = C::BM, CK = C::CK, BMP = C::BMP, MI = C::MI, NI = C::NI;
-    const int kh = C::KH > 0 ? C::KH : a.k_h;
-    const int kw = C::KW > 0 ? C::KW : a.k_w;
-    const int khw = kh * kw;
+__global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
+    extern __shared__ __align__(16) float lds[];
+    constexpr int BM = C::BM, BN = C::BN, TW = C::TW, TH = C::TH, CW = C::CW;
+    constexpr int KW = C::KW, KHW = C::KHW, KP = C::KP;
+    constexpr int MI = C::MI, NI = C::NI;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wk = wave % C::WAVES_K;
-    const int wmn = wave / C::WAVES_K;
-    const int wm = wmn % C::WAVES_M;
-    const int wn = wmn / C::WAVES_M;
+    const int lane = threadIdx.x & 63;
+    // The wave index is uniform across the wave; saying so keeps the loop
+    // bounds and chunk offsets derived from it in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wk = wave % C::KS;                  // K slice of this wave
+    const int wm = (wave / C::KS) % C::WM;        // row slice of this wave
+    const int pt = wave / (C::KS * C::WM);        // pixel sub-tile of this wave
 
-    // Block -> (co tile, group, pixel tile, image), output-channel tiles fastest
-    // so that blocks reading the same input patch are neighbours on one XCD.
+    // Block -> (co tile, group, column block, row block, image); output-channel
+    // tiles fastest so that blocks reading the same patch are neighbours.
     uint32_t L = xcd_remap(blockIdx.x, a.num_blocks);
-    const int cot = L % a.co_tiles;  L /= a.co_tiles;
-    const int g = L % a.groups;      L /= a.groups;
-    const int twi = L % a.tiles_w;   L /= a.tiles_w;
-    const int thi = L % a.tiles_h;   L /= a.tiles_h;
-    const int n = L;
+    uint32_t Q = divu(L, a.dv_co_tiles);
+    const int cot = L - Q * a.co_tiles;
+    L = Q; Q = divu(L, a.dv_groups);
+    const int g = L - Q * a.groups;
+    L = Q; Q = divu(L, a.dv_tiles_w);
+    const int twi = L - Q * a.tiles_w;
+    L = Q; Q = divu(L, a.dv_tiles_h);
+    const int thi = L - Q * a.tiles_h;
+    const int n = Q;
 
-    const int co0 = cot * BM;
-    const int ho0 = thi * a.tile_h, wo0 = twi * a.tile_w;
+    const int co0 = cot * BM + wm * C::WR;        // first output channel of this wave
+    const int ho0 = a.pt_vertical ? (thi * C::PT + pt) * TH : thi * TH;
+    const int wo0 = a.pt_vertical ? twi * TW : (twi * C::PT + pt) * TW;
     const int ih0 = ho0 * a.stride_h - a.pad_top;
-    const int iw0 = wo0 * a.stride_w - a.pad_left;
-    const int PS = a.patch_stride, PW = a.patch_w;
-    const int PHW = a.patch_h * PW;
-    const int x_total = CK * PHW;
-    const int w_row = CK * khw;                 // weight floats per output channel per chunk
-    const int w_total = BM * w_row;
-    const int stage = stage_floats<C>(PS, khw);
-    const int64_t HW = (int64_t)a.h * a.w;
+    const int ca = wo0 * a.stride_w - a.pad_left - a.patch_shift;   // multiple of 4
+    const int PWA = a.patch_w, PS = a.patch_stride;
+    const int xf4 = CW * a.patch_h * (PWA >> 2);
+    const int HW = a.h * a.w;
+    const int SF = C::ASZ + CW * PS;      // floats of one LDS stage
+    // LDS: the per-wave stages, later reused for the split-K reduction.
+    float* pipe = lds;
 
     const float* __restrict__ xg =
         (const float*)a.xptr + ((int64_t)n * a.in_total + a.in_off + (int64_t)g * a.cin_g) * HW;
-    const float* __restrict__ wg =
-        (const float*)a.wptr + ((int64_t)g * a.cout_g + co0) * a.cin_g * khw;
-    const int co_valid = min(BM, a.cout_g - co0);
+    const float* __restrict__ wg = (const float*)a.wptr + ((int64_t)g * a.cout_g + co0) * a.cin_g * KHW;
+    const bool vx = a.w % 4 == 0 && ((uintptr_t)a.xptr % 16) == 0;
+    const bool vw = (a.cin_g * KHW) % 4 == 0 && ((uintptr_t)a.wptr % 16) == 0;
 
-    float xr[C::XPT];
-    float wr[C::WPT];
+    // Patch unit e of this wave's chunk: channel, row and 4-column group.
+    // (Numerators stay below 2^16, so the host-made magic divisions are exact.)
+    struct XPos { int ci, ih, iw, lo; };
+    auto xpos = [&](int e) {
+        XPos q;
+        q.ci = (int)fdiv(e, a.div_patch_hw);
+        const int rem = e - q.ci * (int)a.div_patch_hw.d;
+        const int row = (int)fdiv(rem, a.div_patch_w);
+        const int cv = rem - row * (int)a.div_patch_w.d;
+        q.ih = ih0 + row;
+        q.iw = ca + 4 * cv;
+        q.lo = q.ci * PS + row * PWA + 4 * cv;
+        return q;
+    };
 
-    // Global -> registers for the channel chunk starting at c0.
-    auto load_chunk = [&](int c0) {
+    // ---- per-lane load plan, fixed for all chunks ----
+    int xgo[C::XS];    // patch unit: element offset from the chunk's first channel, -1 = padding
+    int xlo[C::XS];    // its LDS offset in the patch tile, -1 = no unit
 #pragma unroll
-        for (int i = 0; i < C::XPT; ++i) {
-            const int e = tid + i * kThreads;
-            float v = 0.0f;
-            if (e < x_total) {
-                const int ci = (int)fdiv(e, a.div_patch_hw);
-                const int rem = e - ci * PHW;
-                const int pr = (int)fdiv(rem, a.div_patch_w);
-                const int pc = rem - pr * PW;
-                const int ih = ih0 + pr, iw = iw0 + pc;
-                if (c0 + ci < a.cin_g) {
-                    if ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
-                        v = xg[(int64_t)(c0 + ci) * HW + (int64_t)ih * a.w + iw];
-                    else
-                        v = a.pad_value;
+    for (int i = 0; i < C::XS; ++i) {
+        const int e = lane + 64 * i;
+        xgo[i] = -1; xlo[i] = -1;
+        if (e < xf4) {
+            const XPos q = xpos(e);
+            xlo[i] = q.lo;
+            if ((unsigned)q.ih < (unsigned)a.h && q.iw >= 0 && q.iw < a.w) xgo[i] = q.ci * HW + q.ih * a.w + q.iw;
+        }
+    }
+    constexpr int K4 = C::K / 4;
+    int wgo[C::AS];    // weight unit: offset within the co tile at the chunk's first channel, -1 = none
+#pragma unroll
+    for (int i = 0; i < C::AS; ++i) {
+        const int e = lane + 64 * i;
+        const int co = e / K4, j4 = e - (e / K4) * K4;
+        wgo[i] = (e < C::AF4 && co0 + co < a.cout_g) ? co * a.cin_g * KHW + 4 * j4 : -1;
+    }
+
+    const float pv = a.pad_value;
+    float4 xr[C::XS];
+    float4 wr[C::AS];
+
+    // Global -> registers for the channels [c0, c0 + CW) of the group.
+    auto load = [&](int c0) {
+        const float* __restrict__ xc = xg + (int64_t)c0 * HW;
+        const float* __restrict__ wc = wg + (int64_t)c0 * KHW;
+        const int cl = a.cin_g - c0;          // channels of the group left
+        if (cl >= CW && vx) {
+#pragma unroll
+            for (int i = 0; i < C::XS; ++i)
+                xr[i] = xgo[i] >= 0 ? *(const float4*)(xc + xgo[i]) : make_float4(pv, pv, pv, pv);
+        } else {
+            // Last, partial chunk or unaligned rows: element by element; channels
+            // past the group read zero (their weights are zero too).
+#pragma unroll
+            for (int i = 0; i < C::XS; ++i) {
+                const int e = lane + 64 * i;
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                if (e < xf4) {
+                    const XPos q = xpos(e);
+                    const bool row_in = (unsigned)q.ih < (unsigned)a.h;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int col = q.iw + t;
+                        if (q.ci < cl)
+                            v[t] = (row_in && (unsigned)col < (unsigned)a.w) ? xc[q.ci * HW + q.ih * a.w + col] : pv;
+                    }
                 }
-            }
-            xr[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < C::WPT; ++i) {
-            const int e = tid + i * kThreads;
-            float v = 0.0f;
-            if (e < w_total) {
-                const int co = e % BM;          // output channel fastest: conflict-free LDS rows
-                const int j = e / BM;           // (ci, r, s) within the chunk, OIHW order
-                const int ci = j / khw;
-                if (co < co_valid && c0 + ci < a.cin_g)
-                    v = wg[(int64_t)co * a.cin_g * khw + (int64_t)c0 * khw + j];
-            }
-            wr[i] = v;
-        }
-    };
-
-    // Registers -> LDS stage.  Input plane ci at [ci*PS], weights at
-    // [(rs*CK + ci)*BMP + co] after the input planes.
-    auto store_chunk = [&](int s) {
-        float* xs = lds + s * stage;
-        float* ws = xs + CK * PS;
-#pragma unroll
-        for (int i = 0; i < C::XPT; ++i) {
-            const int e = tid + i * kThreads;
-            if (e < x_total) {
-                const int ci = (int)fdiv(e, a.div_patch_hw);
-                xs[ci * PS + (e - ci * PHW)] = xr[i];
+                xr[i] = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
+        if (cl >= CW && vw) {
 #pragma unroll
-        for (int i = 0; i < C::WPT; ++i) {
-            const int e = tid + i * kThreads;
-            if (e < w_total) {
-                const int co = e % BM;
-                const int j = e / BM;
-                const int ci = j / khw;
-                const int rs = j - ci * khw;
-                ws[(rs * CK + ci) * BMP + co] = wr[i];
+            for (int i = 0; i < C::AS; ++i)
+                wr[i] = wgo[i] >= 0 ? *(const float4*)(wc + wgo[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            const int kl = (cl < CW ? cl : CW) * KHW;   // valid k of this chunk
+#pragma unroll
+            for (int i = 0; i < C::AS; ++i) {
+                const int k0 = 4 * ((lane + 64 * i) % K4);
+                float v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (wgo[i] >= 0 && k0 + t < kl) ? wc[wgo[i] + t] : 0.0f;
+                wr[i] = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
     };
 
-    // Per-lane LDS bases of the MFMA operands.  A (weights): lane holds
-    // row co = lane%16 at k = lane/16.  B (input): lane holds pixel lane%16
-    // at k = lane/16, i.e. channel plane lane/16 of the current 4-channel step.
-    const int a_base = (lane >> 4) * BMP + wm * C::WM + (lane & 15);
-    int b_base[NI];
+    auto store = [&](float* st) {
+#pragma unroll
+        for (int i = 0; i < C::AS; ++i) {
+            const int e = lane + 64 * i;
+            if (e < C::AF4) *(float4*)(st + (e / K4) * KP + 4 * (e % K4)) = wr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < C::XS; ++i)
+            if (xlo[i] >= 0) *(float4*)(st + C::ASZ + xlo[i]) = xr[i];
+    };
+
+    // Operand addresses: A lane reads row co = lane%16 at k = (4*step + lane/16)*KHW + rs;
+    // B lane reads channel plane 4*step + lane/16 at pixel j = ni*16 + lane%16.
+    const int a_lane = (lane & 15) * KP + (lane >> 4) * KHW;
+    int b_lane[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-        const int j = wn * C::WN + ni * 16 + (lane & 15);
-        const int th = (int)fdiv(j, a.div_tile_w);
-        const int tw = j - th * a.tile_w;
-        b_base[ni] = (lane >> 4) * PS + th * a.stride_h * PW + tw * a.stride_w;
+        const int j = ni * 16 + (lane & 15);
+        b_lane[ni] = (lane >> 4) * PS + (j / TW) * a.stride_h * PWA + (j % TW) * a.stride_w + a.patch_shift;
     }
+    const int rstep = a.dilation_h * PWA, sstep = a.dilation_w;
 
     f32x4 acc[MI][NI];
 #pragma unroll
@@ -175,91 +239,122 @@ __global__ __launch_bounds__(kThreads) void igemm_f32_kernel(ConvArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](int s) {
-        const float* xs = lds + s * stage;
-        const float* ws = xs + CK * PS;
-        for (int rs = 0; rs < khw; ++rs) {
-            const int r = rs / kw;
-            const int sc = rs - r * kw;
-            const int uoff = r * a.dilation_h * PW + sc * a.dilation_w;
+    // One MFMA step: tap rs, channels 4q..4q+3 of the chunk.  Operands of
+    // step t+1 are fetched from LDS while the MFMAs of step t run.
+    constexpr int STEPS = KHW * (CW / 4);
+    auto fetch = [&](const float* st, int t, float (&av)[MI], float (&bv)[NI]) {
+        const int rs = t / (CW / 4), q = t % (CW / 4);
+        const int boff = (rs / KW) * rstep + (rs % KW) * sstep;
 #pragma unroll
-            for (int cq = 0; cq < C::CKW / 4; ++cq) {
-                const int ci = wk * C::CKW + cq * 4;
-                float av[MI], bv[NI];
+        for (int mi = 0; mi < MI; ++mi) av[mi] = st[a_lane + mi * 16 * KP + q * 4 * KHW + rs];
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi) av[mi] = ws[(rs * CK + ci) * BMP + a_base + mi * 16];
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) bv[ni] = xs[ci * PS + uoff + b_base[ni]];
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[ni], acc[mi][ni],
-                                                                           0, 0, 0);
-            }
-        }
+        for (int ni = 0; ni < NI; ++ni) bv[ni] = st[C::ASZ + b_lane[ni] + q * 4 * PS + boff];
     };
-
-    // Two-stage pipeline: the next chunk's global loads are in flight while
-    // the current chunk is multiplied out of LDS.
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-    for (int kc = 0; kc < a.chunks; ++kc) {
-        const int s = kc & 1;
-        const bool more = kc + 1 < a.chunks;
-        if (more) load_chunk((kc + 1) * CK);
-        compute(s);
-        if (more) store_chunk(s ^ 1);
-        __syncthreads();
-    }
-
-    // Epilogue.  D layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+v
-    // (v = 0..3) of column lane%16.
-    float* __restrict__ yg = (float*)a.yptr;
-    const int64_t out_plane = (int64_t)a.ho * a.wo;
-    auto emit = [&](int mi, int ni, int v, float val) {
-        const int co = co0 + wm * C::WM + mi * 16 + (lane >> 4) * 4 + v;
-        const int j = wn * C::WN + ni * 16 + (lane & 15);
-        const int th = (int)fdiv(j, a.div_tile_w);
-        const int tw = j - th * a.tile_w;
-        const int ho = ho0 + th, wo = wo0 + tw;
-        if (co < a.cout_g && ho < a.ho && wo < a.wo) {
-            const int cg = g * a.cout_g + co;
-            yg[((int64_t)n * a.out_total + a.out_off + cg) * out_plane + (int64_t)ho * a.wo + wo] =
-                bias_act(a, val, cg);
-        }
-    };
-
-    if constexpr (C::WAVES_K == 1) {
+    auto mfmas = [&](const float (&av)[MI], const float (&bv)[NI]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+    };
+
+    // ---- main loop over this wave's chunks [kb, ke) ----
+    // Registers hold chunk kc+1 (loaded one chunk ahead).  With two LDS
+    // stages it is written to the other stage halfway through chunk kc's
+    // MFMAs and chunk kc+2 is loaded right after; with one stage the writes
+    // follow the last reads of chunk kc (the LDS executes a wave's accesses in
+    // order).  The static chunk split keeps the summation order, and so the
+    // result, identical from run to run.
+    const int nch = a.chunks;
+    const int kb = (nch * wk) / C::KS, ke = (nch * (wk + 1)) / C::KS;
+    float* st0 = pipe + wave * C::ST * SF;
+    float* st1 = st0 + (C::ST - 1) * SF;
+    if (kb < ke) {
+        load(kb * CW);
+        store(st0);
+        if (kb + 1 < ke) load((kb + 1) * CW);
+        for (int kc = kb; kc < ke; ++kc) {
+            const bool odd = (kc - kb) & 1;
+            const float* cur = odd ? st1 : st0;
+            float* nxt = odd ? st0 : st1;
+            const bool more = kc + 1 < ke;
+            wave_lds_sync();
+            float a0[MI], b0[NI], a1[MI], b1[NI];
+            fetch(cur, 0, a0, b0);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) emit(mi, ni, v, acc[mi][ni][v]);
-    } else {
-        // Waves that split K park their partial sums in LDS (the pipeline
-        // buffers are free after the last barrier); each then finishes the
-        // fragments f with f % WAVES_K == wk.
-        constexpr int FR = MI * NI * 4;
-        float* red = lds;
+            for (int t = 0; t < STEPS; ++t) {
+                if (t + 1 < STEPS) {
+                    if (t & 1) fetch(cur, t + 1, a0, b0);
+                    else fetch(cur, t + 1, a1, b1);
+                }
+                // Keep the fetches of step t+1 ahead of the MFMAs of step t.
+                __builtin_amdgcn_sched_barrier(0);
+                if (t & 1) mfmas(a1, b1);
+                else mfmas(a0, b0);
+                if (C::ST == 2 && t == STEPS / 2 && more) {
+                    store(nxt);
+                    if (kc + 2 < ke) load((kc + 2) * CW);
+                }
+            }
+            if (C::ST == 1 && more) {
+                wave_lds_sync();
+                store(nxt);
+                if (kc + 2 < ke) load((kc + 2) * CW);
+            }
+        }
+    }
+
+    // ---- epilogue: split-K sum through LDS, bias, activation, store ----
+    // Wave w parks its WR x BN partial tile at red[w]; wave index is
+    // ((pt * WM) + wm) * KS + wk.
+    __syncthreads();
+    {
+        float* red = pipe + wave * C::WR * C::RS;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    red[((wmn * C::WAVES_K + wk) * FR + (mi * NI + ni) * 4 + v) * 64 + lane] =
-                        acc[mi][ni][v];
-        __syncthreads();
+                    red[(mi * 16 + (lane >> 4) * 4 + v) * C::RS + ni * 16 + (lane & 15)] = acc[mi][ni][v];
+    }
+    __syncthreads();
+
+    float* __restrict__ yg = (float*)a.yptr;
+    const int64_t out_plane = (int64_t)a.ho * a.wo;
+    constexpr int UNITS = C::PT * BM * BN / 4;
+    constexpr int ROW4 = BN / 4;
 #pragma unroll
-        for (int f = 0; f < FR; ++f) {
-            if (f % C::WAVES_K != wk) continue;
-            float sum = 0.0f;
+    for (int u0 = 0; u0 < UNITS; u0 += C::NT) {
+        const int u = u0 + threadIdx.x;
+        if (UNITS % C::NT != 0 && u >= UNITS) break;
+        const int p = u / (BM * ROW4);
+        const int rem = u - p * (BM * ROW4);
+        const int co = rem / ROW4;                // row within the workgroup's BM
+        const int j = 4 * (rem - co * ROW4);
+        const int w0 = (p * C::WM + co / C::WR) * C::KS;
+        const float* src = pipe + (co % C::WR) * C::RS + j;
+        float4 s = *(const float4*)(src + w0 * C::WR * C::RS);
 #pragma unroll
-            for (int k2 = 0; k2 < C::WAVES_K; ++k2) sum += red[((wmn * C::WAVES_K + k2) * FR + f) * 64 + lane];
-            emit(f / (NI * 4), (f / 4) % NI, f % 4, sum);
+        for (int k = 1; k < C::KS; ++k) {
+            const float4 t = *(const float4*)(src + (w0 + k) * C::WR * C::RS);
+            s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+        }
+        const int cog = cot * BM + co;
+        const int pho = a.pt_vertical ? (thi * C::PT + p) * TH : thi * TH;
+        const int pwo = a.pt_vertical ? twi * TW : (twi * C::PT + p) * TW;
+        const int ho = pho + j / TW, wo = pwo + (j % TW);
+        if (cog < a.cout_g && ho < a.ho) {
+            const int cg = g * a.cout_g + cog;
+            float v[4] = {bias_act(a, s.x, cg), bias_act(a, s.y, cg), bias_act(a, s.z, cg), bias_act(a, s.w, cg)};
+            float* dst = yg + ((int64_t)n * a.out_total + a.out_off + cg) * out_plane + (int64_t)ho * a.wo + wo;
+            if (a.vec_store && wo + 3 < a.wo) {
+                *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (wo + t < a.wo) dst[t] = v[t];
+            }
         }
     }
 }
@@ -267,83 +362,85 @@ __global__ __launch_bounds__(kThreads) void igemm_f32_kernel(ConvArgs a) {
 // ------------------------------------------------------------ configs ---
 
 struct CfgInfo {
-    int bm, bn, waves_k, ck, kh, kw, xpt, wpt;
-    int red_floats;   // LDS floats of the split-K reduction (0 if none)
+    int bm, bn, tw, cw, kh, kw, nw, wm, ks, st, xs, asz;
     const void* fn;
-    int stage_floats(int ps, int khw) const {
-        const int bmp = bm == 16 ? 16 : bm + 16;
-        return ck * ps + khw * ck * bmp;
+    int stage_floats(int ps) const { return asz + cw * ps; }
+    int lds_floats(int ps) const {
+        const int pipe = nw * st * stage_floats(ps);
+        const int red = nw * (bm / wm) * (bn + 4);
+        return pipe > red ? pipe : red;
     }
 };
 
 template <class C>
 CfgInfo info() {
-    CfgInfo i;
-    i.bm = C::BM; i.bn = C::BN; i.waves_k = C::WAVES_K; i.ck = C::CK; i.kh = C::KH; i.kw = C::KW;
-    i.xpt = C::XPT; i.wpt = C::WPT;
-    i.red_floats = C::WAVES_K > 1 ? 4 * C::MI * C::NI * 4 * 64 : 0;
-    i.fn = (const void*)igemm_f32_kernel<C>;
-    return i;
+    return CfgInfo{C::BM, C::BN, C::TW, C::CW, C::KH, C::KW, C::NW, C::WM, C::KS, C::ST, C::XS, C::ASZ,
+                   (const void*)igemm_f32_kernel<C>};
 }
 
-//                       BM  BN  WM WN WK  CK KH KW XPT WPT
-using K3_M32  = IgemmF32Cfg<32,  64, 1, 2, 2,  8, 3, 3, 8, 9>;
-using K3_M64  = IgemmF32Cfg<64,  64, 2, 2, 1,  8, 3, 3, 8, 18>;
-using K3_M128 = IgemmF32Cfg<128, 128, 2, 2, 1, 4, 3, 3, 12, 18>;
-using K3_M16  = IgemmF32Cfg<16,  64, 1, 4, 1,  8, 3, 3, 8, 5>;
-using K1_M32  = IgemmF32Cfg<32,  128, 1, 4, 1, 16, 1, 1, 8, 2>;
-using K1_M64  = IgemmF32Cfg<64,  128, 1, 4, 1, 16, 1, 1, 8, 4>;
-using K1_M128 = IgemmF32Cfg<128, 128, 2, 2, 1, 16, 1, 1, 8, 8>;
-using KG_M32  = IgemmF32Cfg<32,  64, 1, 4, 1,  4, 0, 0, 16, 16>;
-using KG_M16  = IgemmF32Cfg<16,  64, 1, 4, 1,  4, 0, 0, 16, 16>;
+// Eight waves (two per SIMD) split K eight ways for the common case, or
+// split the rows in two and K four ways for the wider tiles; four waves split
+// over pixels when the group has too few input channels.
+//                      BM  BN  TW  CW KH KW NW WM KS ST XS
+using K3_M16   = Cfg<16,  64, 16,  4, 3, 3, 8, 1, 8, 2, 3>;
+using K3_M32   = Cfg<32,  64, 16,  4, 3, 3, 8, 1, 8, 2, 3>;
+using K3_M64   = Cfg<64,  64, 16,  4, 3, 3, 8, 2, 4, 2, 3>;
+using K3W_M16  = Cfg<16,  64, 16,  4, 3, 3, 8, 1, 8, 2, 6>;   // wider patches (stride 2)
+using K3W_M32  = Cfg<32,  64, 16,  4, 3, 3, 8, 1, 8, 2, 6>;
+using K3W_M64  = Cfg<64,  64, 16,  4, 3, 3, 8, 2, 4, 1, 6>;
+using K3P_M16  = Cfg<16,  64, 16,  4, 3, 3, 4, 1, 1, 2, 6>;   // few input channels: waves split pixels
+using K3P_M32  = Cfg<32,  64, 16,  4, 3, 3, 4, 1, 1, 2, 6>;
+using K1F_M32  = Cfg<32,  64, 64, 16, 1, 1, 8, 1, 8, 2, 4>;   // flattened 1x1: one row of h*w pixels
+using K1F_M64  = Cfg<64,  64, 64, 16, 1, 1, 8, 2, 4, 2, 4>;
+using K1F_M128 = Cfg<128, 64, 64, 16, 1, 1, 8, 2, 4, 1, 4>;
+using K1FP_M16 = Cfg<16,  64, 64, 16, 1, 1, 4, 1, 1, 2, 4>;
+using K1FP_M32 = Cfg<32,  64, 64, 16, 1, 1, 4, 1, 1, 2, 4>;
+using K1_M32   = Cfg<32,  64, 16,  8, 1, 1, 8, 1, 8, 2, 8>;   // 1x1 with stride or padding
+using K1_M64   = Cfg<64,  64, 16,  8, 1, 1, 8, 2, 4, 2, 8>;
+using K5_M16   = Cfg<16,  64, 16,  4, 5, 5, 8, 1, 8, 1, 4>;
+
+enum {
+    C3_M16, C3_M32, C3_M64, C3W_M16, C3W_M32, C3W_M64, C3P_M16, C3P_M32,
+    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, NCFG
+};
 
 const CfgInfo& cfg(int i) {
-    static const CfgInfo table[] = {
-        info<K3_M32>(), info<K3_M64>(), info<K3_M128>(), info<K3_M16>(),
-        info<K1_M32>(), info<K1_M64>(), info<K1_M128>(),
-        info<KG_M32>(), info<KG_M16>(),
+    static const CfgInfo table[NCFG] = {
+        info<K3_M16>(),   info<K3_M32>(),   info<K3_M64>(),    info<K3W_M16>(),  info<K3W_M32>(),
+        info<K3W_M64>(),  info<K3P_M16>(),  info<K3P_M32>(),   info<K1F_M32>(),  info<K1F_M64>(),
+        info<K1F_M128>(), info<K1FP_M16>(), info<K1FP_M32>(),  info<K1_M32>(),   info<K1_M64>(),
+        info<K5_M16>(),
     };
     return table[i];
 }
 
-int patch_stride_for(int phw) {
+int patch_stride(int phw) {
     // Smallest stride >= phw with stride % 64 == 16: the four channel planes
-    // read by one MFMA operand fetch then start 16 banks apart.
+    // of one operand fetch then start 16 banks apart.
     int s = ((phw + 63 - 16) / 64) * 64 + 16;
     if (s < phw) s += 64;
     return s;
 }
 
-struct Tiling {
-    int tile_h, tile_w, ph, pw, ps;
-    long waste;
+struct Geom {
+    int tw, th, ph, pwa, ps, shift;
 };
 
-bool choose_tiling(const Desc& d, const CfgInfo& c, int h_eff, int w_eff, int ho_eff, int wo_eff,
-                   Tiling* best) {
-    const conv2d_params_t& p = d.p;
-    bool found = false;
-    for (int tw = 8; tw <= c.bn; tw *= 2) {
-        const int th = c.bn / tw;
-        const int ph = (th - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
-        const int pw = (tw - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
-        if (c.ck * ph * pw > kThreads * c.xpt) continue;
-        if (ph * pw >= 65536 || c.ck * ph * pw >= 65536) continue;
-        const int ps = patch_stride_for(ph * pw);
-        const int khw = p.k_h * p.k_w;
-        if (c.bm * c.ck * khw > kThreads * c.wpt) continue;
-        const int lds = 2 * c.stage_floats(ps, khw);
-        if ((lds > c.red_floats ? lds : c.red_floats) * 4 > 64 * 1024) continue;
-        const long tiles = (long)((ho_eff + th - 1) / th) * ((wo_eff + tw - 1) / tw);
-        const long waste = tiles * c.bn - (long)ho_eff * wo_eff;
-        // Prefer less waste; on ties prefer wider rows (longer coalesced runs).
-        if (!found || waste < best->waste || (waste == best->waste && tw > best->tile_w)) {
-            *best = Tiling{th, tw, ph, pw, ps, waste};
-            found = true;
-        }
+// Patch geometry of a TH x TW output sub-tile (columns aligned down to 4).
+Geom geom(const conv2d_params_t& p, const CfgInfo& c, bool flat) {
+    Geom G;
+    G.tw = c.tw;
+    G.th = c.bn / c.tw;
+    if (flat) {
+        G.ph = 1; G.pwa = c.tw; G.shift = 0;
+    } else {
+        G.ph = (G.th - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
+        const int span = (G.tw - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
+        G.shift = ((-p.pad_left) % 4 + 4) % 4;
+        G.pwa = (G.shift + span + 3) / 4 * 4;
     }
-    (void)h_eff; (void)w_eff;
-    return found;
+    G.ps = patch_stride(G.ph * G.pwa);
+    return G;
 }
 
 }  // namespace
@@ -352,85 +449,92 @@ bool plan_igemm_f32(Desc& d) {
     const conv2d_params_t& p = d.p;
     const bool is3 = p.k_h == 3 && p.k_w == 3;
     const bool is1 = p.k_h == 1 && p.k_w == 1;
-    d.flatten_1x1 = is1 && p.stride_h == 1 && p.stride_w == 1 && p.pad_top == 0 &&
-                    p.pad_left == 0 && p.pad_bottom == 0 && p.pad_right == 0;
-    const int h_eff = d.flatten_1x1 ? 1 : p.h;
-    const int w_eff = d.flatten_1x1 ? p.h * p.w : p.w;
-    const int ho_eff = d.flatten_1x1 ? 1 : d.ho;
-    const int wo_eff = d.flatten_1x1 ? d.ho * d.wo : d.wo;
-    if (d.flatten_1x1 && (int64_t)p.h * p.w > INT32_MAX / 2) return false;
-
-    // Candidate configs in order of preference.
+    const bool is5 = p.k_h == 5 && p.k_w == 5;
+    const bool flat = is1 && p.stride_h == 1 && p.stride_w == 1 && p.pad_top == 0 && p.pad_left == 0 &&
+                      p.pad_bottom == 0 && p.pad_right == 0;
+    const int m = d.cout_g;
     int cands[4];
     int nc = 0;
-    const int m = d.cout_g;
     if (is3) {
-        if (m <= 16) cands[nc++] = 3;
-        else if (m <= 32) cands[nc++] = 0;
-        else if (m <= 64) cands[nc++] = 1;
-        else cands[nc++] = 2;
-        cands[nc++] = m <= 16 ? 8 : 7;
+        if (d.cin_g < 32) {
+            cands[nc++] = m <= 16 ? C3P_M16 : C3P_M32;
+        } else {
+            cands[nc++] = m <= 16 ? C3_M16 : (m <= 32 ? C3_M32 : C3_M64);
+            cands[nc++] = m <= 16 ? C3W_M16 : (m <= 32 ? C3W_M32 : C3W_M64);
+        }
+    } else if (flat) {
+        if (d.cin_g < 128) cands[nc++] = m <= 16 ? C1FP_M16 : C1FP_M32;
+        if (d.cin_g >= 64 || m > 32) cands[nc++] = m <= 32 ? C1F_M32 : (m <= 64 || m % 128 ? C1F_M64 : C1F_M128);
     } else if (is1) {
-        if (m <= 32) cands[nc++] = 4;
-        else if (m <= 64) cands[nc++] = 5;
-        else cands[nc++] = 6;
-        cands[nc++] = m <= 16 ? 8 : 7;
-    } else {
-        cands[nc++] = m <= 16 ? 8 : 7;
+        cands[nc++] = m <= 32 ? C1_M32 : C1_M64;
+    } else if (is5) {
+        cands[nc++] = C5_M16;
     }
     for (int k = 0; k < nc; ++k) {
         const CfgInfo& c = cfg(cands[k]);
-        if (c.kh && (c.kh != p.k_h || c.kw != p.k_w)) continue;
-        Tiling t;
-        if (d.flatten_1x1) {
-            // One row of h*w pixels: the patch is the tile itself.
-            t.tile_h = 1; t.tile_w = c.bn; t.ph = 1; t.pw = c.bn;
-            t.ps = patch_stride_for(c.bn);
-            if (c.ck * c.bn > kThreads * c.xpt || c.bm * c.ck > kThreads * c.wpt) continue;
-        } else if (!choose_tiling(d, c, h_eff, w_eff, ho_eff, wo_eff, &t)) {
-            continue;
-        }
-        const int khw = p.k_h * p.k_w;
-        const int lds = 2 * c.stage_floats(t.ps, khw);
+        const Geom G = geom(p, c, flat);
+        if (c.cw * G.ph * G.pwa / 4 > 64 * c.xs) continue;            // patch units per lane
+        if (c.cw * G.ph * G.pwa / 4 >= 65536 || G.ph * G.pwa >= 65536) continue;   // magic division range
+        if ((int64_t)c.cw * p.h * p.w >= INT32_MAX / 2) continue;      // 32-bit patch offsets
+        if ((int64_t)c.bm * d.cin_g * c.kh * c.kw >= INT32_MAX / 2) continue;
+        const int lds = 4 * c.lds_floats(G.ps);
+        if (lds > 160 * 1024) continue;
         d.cfg = cands[k];
-        d.tile_h = t.tile_h;
-        d.tile_w = t.tile_w;
-        d.lds_bytes = 4 * (lds > c.red_floats ? lds : c.red_floats);
-        (void)h_eff; (void)w_eff;
+        d.flatten_1x1 = flat;
+        d.tile_h = G.th;
+        d.tile_w = G.tw;
+        d.lds_bytes = lds;
+        // Stack a block's pixel sub-tiles along rows unless that wastes more.
+        const int pt = c.nw / (c.wm * c.ks);
+        if (flat || pt == 1) {
+            d.pt_vertical = 0;
+        } else {
+            const long v = (long)((d.ho + G.th * pt - 1) / (G.th * pt)) * ((d.wo + G.tw - 1) / G.tw);
+            const long h = (long)((d.ho + G.th - 1) / G.th) * ((d.wo + G.tw * pt - 1) / (G.tw * pt));
+            d.pt_vertical = v <= h;
+        }
         return true;
     }
     return false;
 }
 
-void fill_tiling(const Desc& d, ConvArgs& a) {
-    // Shared by the implicit-GEMM planners: derive the per-tile geometry.
+hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
+    const CfgInfo& c = cfg(d.cfg);
     const conv2d_params_t& p = d.p;
+    const Geom G = geom(p, c, d.flatten_1x1);
     if (d.flatten_1x1) {
         a.h = 1; a.w = p.h * p.w; a.ho = 1; a.wo = d.ho * d.wo;
     }
-    a.tile_h = d.tile_h;
-    a.tile_w = d.tile_w;
-    a.tiles_h = (a.ho + d.tile_h - 1) / d.tile_h;
-    a.tiles_w = (a.wo + d.tile_w - 1) / d.tile_w;
-    a.patch_h = (d.tile_h - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
-    a.patch_w = (d.tile_w - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
-    a.patch_stride = patch_stride_for(a.patch_h * a.patch_w);
-    a.div_patch_hw = make_fastdiv((uint32_t)(a.patch_h * a.patch_w));
-    a.div_patch_w = make_fastdiv((uint32_t)a.patch_w);
-    a.div_tile_w = make_fastdiv((uint32_t)d.tile_w);
-}
-
-hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
-    const CfgInfo& c = cfg(d.cfg);
-    fill_tiling(d, a);
+    const int pt = c.nw / (c.wm * c.ks);
+    const int bth = d.pt_vertical ? G.th * pt : G.th;
+    const int btw = d.pt_vertical ? G.tw : G.tw * pt;
+    a.tiles_h = (a.ho + bth - 1) / bth;
+    a.tiles_w = (a.wo + btw - 1) / btw;
+    a.patch_h = G.ph;
+    a.patch_w = G.pwa;
+    a.patch_stride = G.ps;
+    a.patch_shift = G.shift;
+    a.div_patch_hw = make_fastdiv((uint32_t)(G.ph * G.pwa / 4));   // patch units per channel
+    a.div_patch_w = make_fastdiv((uint32_t)(G.pwa / 4));           // patch units per row
+    a.pt_vertical = d.pt_vertical;
     a.co_tiles = (d.cout_g + c.bm - 1) / c.bm;
-    a.chunks = (d.cin_g + c.ck - 1) / c.ck;
+    a.chunks = (d.cin_g + c.cw - 1) / c.cw;
+    a.vec_store = (a.wo % 4 == 0) && ((uintptr_t)a.yptr % 16 == 0);
+    a.dv_co_tiles = make_divu32((uint32_t)a.co_tiles);
+    a.dv_groups = make_divu32((uint32_t)a.groups);
+    a.dv_tiles_w = make_divu32((uint32_t)a.tiles_w);
+    a.dv_tiles_h = make_divu32((uint32_t)a.tiles_h);
     const uint64_t blocks = (uint64_t)a.co_tiles * a.groups * a.tiles_h * a.tiles_w * a.n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     a.num_blocks = (uint32_t)blocks;
+    if (d.lds_bytes > 64 * 1024) {
+        const hipError_t e =
+            hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, d.lds_bytes);
+        if (e != hipSuccess) return e;
+    }
     void* args[] = {&a};
-    return hipLaunchKernel(c.fn, dim3((uint32_t)blocks), dim3(kThreads), args, d.lds_bytes, s);
+    return hipLaunchKernel(c.fn, dim3((uint32_t)blocks), dim3(c.nw * 64), args, d.lds_bytes, s);
 }
 
 }  // namespace conv2d
