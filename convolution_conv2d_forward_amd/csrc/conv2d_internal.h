@@ -91,6 +91,7 @@ struct ConvArgs {
     int32_t patch_shift;             // fp32 igemm: input column of LDS column 0 is iw_lo - patch_shift
     int32_t pt_vertical;             // fp32 igemm: a block's pixel sub-tiles stack along rows (1) or columns (0)
     int32_t vec_store;               // outputs may be written as 16-byte vectors
+    int32_t dma;                     // fp32 igemm: copy chunks with direct global->LDS loads
     DivU32 dv_co_tiles, dv_groups, dv_tiles_w, dv_tiles_h;   // block index decomposition
 
     // int8 requant

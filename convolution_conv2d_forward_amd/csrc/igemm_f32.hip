@@ -70,6 +70,16 @@ struct Cfg {
     static_assert(ST == 1 || ST == 2, "one or two LDS stages");
 };
 
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane l writes lds_base + 16*l; completion is
+// counted by vmcnt.  The builtin exists only for the device target, so the
+// host pass of this single-source file sees an empty body it never runs.
+__device__ __forceinline__ void copy16_to_lds(const float* src, float* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     // The LDS stage is private to the wave; order its writes before the reads
     // of other lanes of the same wave.
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     // Patch unit e of this wave's chunk: channel, row and 4-column group.
     // (Numerators stay below 2^16, so the host-made magic divisions are exact.)
     struct XPos { int ci, ih, iw, lo; };
-    auto xpos = [&](int e) {
+    auto xpos = [&](int e) __attribute__((always_inline)) {
         XPos q;
         q.ci = (int)fdiv(e, a.div_patch_hw);
         const int rem = e - q.ci * (int)a.div_patch_hw.d;
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     float4 wr[C::AS];
 
     // Global -> registers for the channels [c0, c0 + CW) of the group.
-    auto load = [&](int c0) {
+    auto load = [&](int c0) __attribute__((always_inline)) {
         const float* __restrict__ xc = xg + (int64_t)c0 * HW;
         const float* __restrict__ wc = wg + (int64_t)c0 * KHW;
         const int cl = a.cin_g - c0;          // channels of the group left
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
         }
     };
 
-    auto store = [&](float* st) {
+    auto store = [&](float* st) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::AS; ++i) {
             const int e = lane + 64 * i;
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     // One MFMA step: tap rs, channels 4q..4q+3 of the chunk.  Operands of
     // step t+1 are fetched from LDS while the MFMAs of step t run.
     constexpr int STEPS = KHW * (CW / 4);
-    auto fetch = [&](const float* st, int t, float (&av)[MI], float (&bv)[NI]) {
+    auto fetch = [&](const float* st, int t, float (&av)[MI], float (&bv)[NI]) __attribute__((always_inline)) {
         const int rs = t / (CW / 4), q = t % (CW / 4);
         const int boff = (rs / KW) * rstep + (rs % KW) * sstep;
 #pragma unroll
@@ -250,7 +260,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) bv[ni] = st[C::ASZ + b_lane[ni] + q * 4 * PS + boff];
     };
-    auto mfmas = [&](const float (&av)[MI], const float (&bv)[NI]) {
+    auto mfmas = [&](const float (&av)[MI], const float (&bv)[NI]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -259,17 +269,85 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     };
 
     // ---- main loop over this wave's chunks [kb, ke) ----
-    // Registers hold chunk kc+1 (loaded one chunk ahead).  With two LDS
-    // stages it is written to the other stage halfway through chunk kc's
-    // MFMAs and chunk kc+2 is loaded right after; with one stage the writes
-    // follow the last reads of chunk kc (the LDS executes a wave's accesses in
-    // order).  The static chunk split keeps the summation order, and so the
-    // result, identical from run to run.
     const int nch = a.chunks;
     const int kb = (nch * wk) / C::KS, ke = (nch * (wk + 1)) / C::KS;
     float* st0 = pipe + wave * C::ST * SF;
     float* st1 = st0 + (C::ST - 1) * SF;
-    if (kb < ke) {
+    // One chunk of MFMAs out of LDS stage cur.  With copy_mid, halfway
+    // through the registers are written to stage nxt and, if load_next, chunk
+    // kn's copy is loaded into them.
+    auto run_chunk = [&](const float* cur, bool copy_mid, float* nxt, bool load_next, int kn) __attribute__((always_inline)) {
+        float a0[MI], b0[NI], a1[MI], b1[NI];
+        fetch(cur, 0, a0, b0);
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            if (t + 1 < STEPS) {
+                if (t & 1) fetch(cur, t + 1, a0, b0);
+                else fetch(cur, t + 1, a1, b1);
+            }
+            // Keep the fetches of step t+1 ahead of the MFMAs of step t.
+            __builtin_amdgcn_sched_barrier(0);
+            if (t & 1) mfmas(a1, b1);
+            else mfmas(a0, b0);
+            if (t == STEPS / 2 && copy_mid) {
+                store(nxt);
+                if (load_next) load(kn * CW);
+            }
+        }
+    };
+    if (C::ST == 2 && a.dma) {
+        // Direct global->LDS copies (global_load_lds_dwordx4): lane l of copy
+        // unit i writes 16 bytes at stage + 1024*i + 16*l, which is exactly the
+        // unit-major layout of both tiles here (weight rows of K = KP floats,
+        // patch planes of PS = patch_h*patch_w floats).  Padding positions are
+        // the same for every chunk, so they are written once per stage and the
+        // copies skip them.  Chunk kc+1 is issued right after chunk kc's copy
+        // has landed and runs under chunk kc's MFMAs.
+        auto pad_fill = [&](float* st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < C::XS; ++i)
+                if (xlo[i] >= 0 && xgo[i] < 0) *(float4*)(st + C::ASZ + xlo[i]) = make_float4(pv, pv, pv, pv);
+        };
+        auto dma = [&](int c0, float* st) __attribute__((always_inline)) {
+            const float* __restrict__ wc = wg + (int64_t)c0 * KHW;
+            const float* __restrict__ xc = xg + (int64_t)c0 * HW;
+#pragma unroll
+            for (int i = 0; i < C::AS; ++i)
+                if (wgo[i] >= 0) copy16_to_lds(wc + wgo[i], st + 256 * i);
+#pragma unroll
+            for (int i = 0; i < C::XS; ++i)
+                if (xgo[i] >= 0) copy16_to_lds(xc + xgo[i], st + C::ASZ + 256 * i);
+        };
+        // Chunks that are not whole (the last one when CW does not divide the
+        // group's channels) go through registers.
+        auto copy_chunk = [&](int kc, float* st) __attribute__((always_inline)) {
+            if (a.cin_g - kc * CW >= CW) {
+                dma(kc * CW, st);
+            } else {
+                load(kc * CW);
+                store(st);
+            }
+        };
+        if (kb < ke) {
+            pad_fill(st0);
+            pad_fill(st1);
+            copy_chunk(kb, st0);
+            for (int kc = kb; kc < ke; ++kc) {
+                const bool odd = (kc - kb) & 1;
+                const float* cur = odd ? st1 : st0;
+                float* nxt = odd ? st0 : st1;
+                __builtin_amdgcn_s_waitcnt(0);      // chunk kc (and any register copy) has landed
+                wave_lds_sync();
+                if (kc + 1 < ke) copy_chunk(kc + 1, nxt);
+                run_chunk(cur, false, nullptr, false, 0);
+            }
+        }
+    } else if (kb < ke) {
+        // Register copies.  Registers hold chunk kc+1 (loaded one chunk
+        // ahead).  With two LDS stages it is written to the other stage
+        // halfway through chunk kc's MFMAs and chunk kc+2 is loaded right
+        // after; with one stage the writes follow the last reads of chunk kc
+        // (the LDS executes a wave's accesses in order).
         load(kb * CW);
         store(st0);
         if (kb + 1 < ke) load((kb + 1) * CW);
@@ -279,23 +357,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
             float* nxt = odd ? st0 : st1;
             const bool more = kc + 1 < ke;
             wave_lds_sync();
-            float a0[MI], b0[NI], a1[MI], b1[NI];
-            fetch(cur, 0, a0, b0);
-#pragma unroll
-            for (int t = 0; t < STEPS; ++t) {
-                if (t + 1 < STEPS) {
-                    if (t & 1) fetch(cur, t + 1, a0, b0);
-                    else fetch(cur, t + 1, a1, b1);
-                }
-                // Keep the fetches of step t+1 ahead of the MFMAs of step t.
-                __builtin_amdgcn_sched_barrier(0);
-                if (t & 1) mfmas(a1, b1);
-                else mfmas(a0, b0);
-                if (C::ST == 2 && t == STEPS / 2 && more) {
-                    store(nxt);
-                    if (kc + 2 < ke) load((kc + 2) * CW);
-                }
-            }
+            run_chunk(cur, C::ST == 2 && more, nxt, kc + 2 < ke, kc + 2);
             if (C::ST == 1 && more) {
                 wave_lds_sync();
                 store(nxt);
@@ -303,6 +365,8 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
             }
         }
     }
+    // The static chunk split keeps the summation order, and so the result,
+    // identical from run to run.
 
     // ---- epilogue: split-K sum through LDS, bias, activation, store ----
     // Wave w parks its WR x BN partial tile at red[w]; wave index is
@@ -520,6 +584,14 @@ hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
     a.co_tiles = (d.cout_g + c.bm - 1) / c.bm;
     a.chunks = (d.cin_g + c.cw - 1) / c.cw;
     a.vec_store = (a.wo % 4 == 0) && ((uintptr_t)a.yptr % 16 == 0);
+    // Direct global->LDS copies need the unit-major layout to be the tile
+    // layout (weight row stride K, patch plane stride patch_h*patch_w, which
+    // must keep the four planes of an operand fetch 16 banks apart) and
+    // 16-byte aligned sources.
+    const int kdma = c.cw * c.kh * c.kw;
+    a.dma = c.st == 2 && !d.flatten_1x1 && kdma % 4 == 0 && a_stride(kdma) == kdma &&
+            G.ph * G.pwa == G.ps && p.w % 4 == 0 && (d.cin_g * c.kh * c.kw) % 4 == 0 &&
+            (uintptr_t)a.xptr % 16 == 0 && (uintptr_t)a.wptr % 16 == 0;
     a.dv_co_tiles = make_divu32((uint32_t)a.co_tiles);
     a.dv_groups = make_divu32((uint32_t)a.groups);
     a.dv_tiles_w = make_divu32((uint32_t)a.tiles_w);
