@@ -2,57 +2,90 @@
 // "convolutiondepthwise" with one filter per channel, and the yscv int8
 // depthwise QLinearConv (3x3 s1 / s2, int32 accumulate, requant).
 //
-// There is one multiply-add per input byte or so: the kernel is bound by HBM,
-// so the design is about moving bytes once, in wide coalesced transactions.
-// A workgroup owns a tile of one (n, c) plane: it copies the input window
-// (halo included) into LDS with 16-byte loads (pad_value, or zero for int8,
-// outside the image), then each thread produces VO consecutive outputs of a
-// row from LDS and writes them with one vector store.  No MFMA: there is no
-// reduction dimension to feed it.
+// There is about one multiply-add per byte moved, so the kernel is bound by
+// HBM and is built to keep HBM busy: a workgroup owns a tile of one (n, c)
+// plane, every thread first issues all of its 16-byte loads of the input
+// window (pad_value, or the zero point for int8, outside the image) and only
+// then writes them to LDS, so a plane's worth of reads is in flight at once.
+// Each thread then computes an R x VO block of outputs from a register
+// window read out of LDS (R rows share their input rows, VO columns share
+// their columns) and writes each output row with one vector store.  No MFMA:
+// there is no reduction dimension to feed it.
 #include "device_common.h"
+
+#include <type_traits>
 
 namespace conv2d {
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int VO = 4;   // consecutive outputs per thread
+constexpr int VO = 4;        // consecutive outputs per thread and row
+constexpr int NVMAX = 8;     // 16-byte input vectors per thread (window <= 2048 vectors)
 
 template <typename T> struct Elem;
-template <> struct Elem<float> { using lds_t = float; static constexpr int VL = 4; };
-template <> struct Elem<__hip_bfloat16> { using lds_t = float; static constexpr int VL = 8; };
-template <> struct Elem<int8_t> { using lds_t = int8_t; static constexpr int VL = 16; };
+template <> struct Elem<float> { using lds_t = float; using acc_t = float; static constexpr int VL = 4; };
+template <> struct Elem<__hip_bfloat16> { using lds_t = float; using acc_t = float; static constexpr int VL = 8; };
+template <> struct Elem<int8_t> { using lds_t = int32_t; using acc_t = int32_t; static constexpr int VL = 16; };
 
-struct DwGeom {
-    int rows, cols;      // LDS window
-    int col_shift;       // iw_lo - iw_a
-};
+// Convert one 16-byte input vector to VL LDS values.
+template <typename T>
+__device__ __forceinline__ void widen(uint4 raw, typename Elem<T>::lds_t* out) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = __uint_as_float(w[q]);
+    } else if constexpr (std::is_same<T, int8_t>::value) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) out[q] = (int32_t)(int8_t)(w[q >> 2] >> (8 * (q & 3)));
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            out[2 * q] = __uint_as_float(w[q] << 16);
+            out[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+    }
+}
 
-// VEC: true when rows can be moved as 16-byte vectors (w % VL == 0 and x
-// 16-byte aligned); KH/KW/SH/SW: compile-time kernel and stride (0 = runtime).
-template <typename T, bool VEC, int KH, int KW, int SH, int SW>
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::lds_t load_scalar(const T* p, int64_t i) {
+    if constexpr (std::is_same<T, __hip_bfloat16>::value) return bf16_to_f32(p[i]);
+    else return (typename Elem<T>::lds_t)p[i];
+}
+
+// VEC: rows move as 16-byte vectors (w % VL == 0, 16-byte aligned x).
+// KH/KW/SH/SW: compile-time kernel and stride with dilation 1 (0 = runtime
+// kernel, stride and dilation, one output row per thread).  R: output rows
+// per thread.
+template <typename T, bool VEC, int KH, int KW, int SH, int SW, int R>
 __global__ __launch_bounds__(kThreads) void dw_kernel(ConvArgs a) {
     using LT = typename Elem<T>::lds_t;
+    using AT = typename Elem<T>::acc_t;
     constexpr int VL = VEC ? Elem<T>::VL : 1;
+    constexpr bool FIXED = KH > 0;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     LT* tile = (LT*)lds_raw;
 
-    const int kh = KH ? KH : a.k_h, kw = KW ? KW : a.k_w;
-    const int sh = SH ? SH : a.stride_h, sw = SW ? SW : a.stride_w;
-    const int dh = a.dilation_h, dwl = a.dilation_w;
+    const int kh = FIXED ? KH : a.k_h, kw = FIXED ? KW : a.k_w;
+    const int sh = FIXED ? SH : a.stride_h, sw = FIXED ? SW : a.stride_w;
+    const int dh = FIXED ? 1 : a.dilation_h, dwl = FIXED ? 1 : a.dilation_w;
 
     // block -> (tile col, tile row, channel, image)
     uint32_t L = blockIdx.x;
-    const int twi = L % a.tiles_w;  L /= a.tiles_w;
-    const int thi = L % a.tiles_h;  L /= a.tiles_h;
-    const int c = L % a.c_out;      L /= a.c_out;
-    const int n = L;
+    uint32_t Q = divu(L, a.dv_tiles_w);
+    const int twi = L - Q * a.tiles_w;
+    L = Q; Q = divu(L, a.dv_tiles_h);
+    const int thi = L - Q * a.tiles_h;
+    L = Q; Q = divu(L, a.dv_co_tiles);       // co_tiles holds c_out here
+    const int c = L - Q * a.c_out;
+    const int n = Q;
 
     const int ho0 = thi * a.tile_h, wo0 = twi * a.tile_w;
     const int th_n = min(a.tile_h, a.ho - ho0);
     const int tw_n = min(a.tile_w, a.wo - wo0);
     const int ih_lo = ho0 * sh - a.pad_top;
     const int iw_lo = wo0 * sw - a.pad_left;
+    // First LDS column: iw_lo rounded down to a multiple of VL.
     const int iw_a = VL > 1 ? (iw_lo >= 0 ? iw_lo / VL * VL : -((-iw_lo + VL - 1) / VL) * VL) : iw_lo;
     const int rows = (th_n - 1) * sh + (kh - 1) * dh + 1;
     const int iw_hi = (wo0 + tw_n - 1) * sw - a.pad_left + (kw - 1) * dwl;
@@ -64,129 +97,154 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(ConvArgs a) {
     const T* __restrict__ xp = (const T*)a.xptr + ((int64_t)n * a.in_total + a.in_off + c) * HW;
 
     LT padv;
-    if constexpr (sizeof(T) == 1) padv = 0;          // symmetric int8: the pad is the zero point
+    if constexpr (std::is_same<T, int8_t>::value) padv = 0;   // symmetric int8: the pad is the zero point
     else padv = (LT)a.pad_value;
 
-    // Input window -> LDS.
+    // ---- input window -> LDS: all loads first, then the LDS writes ----
     const int nvec = rows * lwv;
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-        const int r = v / lwv;
-        const int cv = v - r * lwv;
-        const int ih = ih_lo + r;
-        const int iw = iw_a + cv * VL;
-        LT* dst = tile + r * lw + cv * VL;
-        const bool row_in = (unsigned)ih < (unsigned)a.h;
-        if constexpr (VL > 1) {
+    if constexpr (VL > 1) {
+        uint4 buf[NVMAX];
+        bool inb[NVMAX];
+#pragma unroll
+        for (int i = 0; i < NVMAX; ++i) {
+            const int v = threadIdx.x + i * kThreads;
+            const int r = v / lwv;
+            const int iw = iw_a + (v - r * lwv) * VL;
+            const int ih = ih_lo + r;
             // Vectors never straddle the image edge: w % VL == 0 and iw % VL == 0.
-            if (row_in && iw >= 0 && iw < a.w) {
-                const T* src = xp + (int64_t)ih * a.w + iw;
-                if constexpr (sizeof(T) == 4) {
-                    *(float4*)dst = *(const float4*)src;
-                } else if constexpr (sizeof(T) == 1) {
-                    *(int4*)dst = *(const int4*)src;
-                } else {
-                    const uint4 raw = *(const uint4*)src;
-                    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+            inb[i] = v < nvec && (unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w;
+            buf[i] = inb[i] ? *(const uint4*)(xp + (int64_t)ih * a.w + iw) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        dst[2 * q] = __uint_as_float(wv[q] << 16);
-                        dst[2 * q + 1] = __uint_as_float(wv[q] & 0xFFFF0000u);
-                    }
-                }
-            } else {
+        for (int i = 0; i < NVMAX; ++i) {
+            const int v = threadIdx.x + i * kThreads;
+            if (v < nvec) {
+                LT vals[VL];
+                widen<T>(buf[i], vals);
+                LT* dst = tile + v * VL;
 #pragma unroll
-                for (int q = 0; q < VL; ++q) dst[q] = padv;
+                for (int q = 0; q < VL; ++q) dst[q] = inb[i] ? vals[q] : padv;
             }
-        } else {
-            LT val = padv;
-            if (row_in && (unsigned)iw < (unsigned)a.w) {
-                if constexpr (sizeof(T) == 2) val = bf16_to_f32(xp[(int64_t)ih * a.w + iw]);
-                else val = (LT)xp[(int64_t)ih * a.w + iw];
-            }
-            *dst = val;
+        }
+    } else {
+        for (int v = threadIdx.x; v < nvec; v += kThreads) {
+            const int r = v / lwv;
+            const int iw = iw_a + (v - r * lwv);
+            const int ih = ih_lo + r;
+            tile[v] = ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
+                          ? load_scalar<T>(xp, (int64_t)ih * a.w + iw)
+                          : padv;
         }
     }
 
     // Filter taps of this channel (OIHW with one input channel per group).
     const int khw = kh * kw;
-    constexpr int KMAX = (KH && KW) ? KH * KW : 25;
-    using AT = typename std::conditional<sizeof(T) == 1, int32_t, float>::type;
+    constexpr int KMAX = FIXED ? KH * KW : 25;
     AT wt[KMAX];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-        if (i < khw) {
-            if constexpr (sizeof(T) == 2) wt[i] = bf16_to_f32(((const T*)a.wptr)[(int64_t)c * khw + i]);
-            else wt[i] = (AT)((const T*)a.wptr)[(int64_t)c * khw + i];
-        } else {
-            wt[i] = 0;
-        }
+    for (int i = 0; i < KMAX; ++i) wt[i] = i < khw ? (AT)load_scalar<T>((const T*)a.wptr, (int64_t)c * khw + i) : (AT)0;
+    AT bias = 0;
+    if constexpr (std::is_same<T, int8_t>::value) {
+        if (a.qbias) bias = a.qbias[c];
     }
     __syncthreads();
 
-    // Outputs: each thread makes VO consecutive outputs of one row.
+    // ---- outputs: R rows x VO columns per thread ----
     const int uw = (tw_n + VO - 1) / VO;
-    const int units = th_n * uw;
+    const int uh = (th_n + R - 1) / R;
+    const int units = uh * uw;
     const int64_t oplane = (int64_t)a.ho * a.wo;
     T* __restrict__ yp = (T*)a.yptr + ((int64_t)n * a.out_total + a.out_off + c) * oplane;
     const bool relu8 = a.act == CONV_ACT_RELU;
     for (int u = threadIdx.x; u < units; u += kThreads) {
-        const int th = u / uw;
-        const int q0 = (u - th * uw) * VO;
-        AT acc[VO];
+        const int rr = u / uw;
+        const int q0 = (u - rr * uw) * VO;
+        const int r0 = rr * R;
+        AT acc[R][VO];
 #pragma unroll
-        for (int q = 0; q < VO; ++q) acc[q] = 0;
-        for (int r = 0; r < kh; ++r) {
-            const LT* row = tile + (th * sh + r * dh) * lw + shift;
+        for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int s = 0; s < KMAX; ++s) {
-                if (!(KH && KW) && s >= kw) break;
-                if ((KH && KW) && s >= KW) break;
+            for (int q = 0; q < VO; ++q) acc[i][q] = 0;
+        if constexpr (FIXED) {
+            // Register window: RIN rows x CIN columns of the LDS tile.
+            constexpr int RIN = (R - 1) * SH + KH;
+            constexpr int CIN = (VO - 1) * SW + KW;
+            const int cmax = lw - shift - 1;     // last readable column of the window
 #pragma unroll
-                for (int q = 0; q < VO; ++q) {
-                    const int col = (q0 + q) * sw + s * dwl;
-                    const AT xv = (AT)row[col < lw - shift ? col : 0];
-                    if constexpr (sizeof(T) == 1) acc[q] += xv * wt[r * kw + s];
-                    else acc[q] = fmaf(xv, wt[r * kw + s], acc[q]);
+            for (int i = 0; i < RIN; ++i) {
+                const int row = r0 * SH + i;
+                if (row >= rows) break;
+                const LT* src = tile + row * lw + shift + q0 * SW;
+                LT win[CIN];
+#pragma unroll
+                for (int j = 0; j < CIN; ++j) win[j] = src[q0 * SW + j <= cmax ? j : 0];
+#pragma unroll
+                for (int orow = 0; orow < R; ++orow) {
+                    const int r = i - orow * SH;       // filter row this input row feeds
+                    if (r < 0 || r >= KH) continue;
+#pragma unroll
+                    for (int s = 0; s < KW; ++s)
+#pragma unroll
+                        for (int q = 0; q < VO; ++q) {
+                            if constexpr (std::is_same<AT, int32_t>::value) acc[orow][q] += win[q * SW + s] * wt[r * KW + s];
+                            else acc[orow][q] = fmaf(win[q * SW + s], wt[r * KW + s], acc[orow][q]);
+                        }
+                }
+            }
+        } else {
+            for (int r = 0; r < kh; ++r) {
+                const LT* row = tile + (r0 * sh + r * dh) * lw + shift;
+                for (int s = 0; s < kw; ++s) {
+#pragma unroll
+                    for (int q = 0; q < VO; ++q) {
+                        const int col = (q0 + q) * sw + s * dwl;
+                        const AT xv = (AT)row[col < lw - shift ? col : 0];
+                        if constexpr (std::is_same<AT, int32_t>::value) acc[0][q] += xv * wt[r * kw + s];
+                        else acc[0][q] = fmaf(xv, wt[r * kw + s], acc[0][q]);
+                    }
                 }
             }
         }
-        const int ho = ho0 + th;
-        const int wo = wo0 + q0;
-        T outv[VO];
 #pragma unroll
-        for (int q = 0; q < VO; ++q) {
-            if constexpr (sizeof(T) == 1) {
-                const int32_t v = acc[q] + (a.qbias ? a.qbias[c] : 0);
-                outv[q] = requant(v, a.composite, a.rounding, a.y_zp, relu8);
-            } else if constexpr (sizeof(T) == 2) {
-                outv[q] = f32_to_bf16(bias_act(a, acc[q], c));
-            } else {
-                outv[q] = bias_act(a, acc[q], c);
-            }
-        }
-        T* dst = yp + (int64_t)ho * a.wo + wo;
-        const bool full = q0 + VO <= tw_n;
-        if (VEC && full && (a.wo % VO) == 0) {
-            if constexpr (sizeof(T) == 4) {
-                *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
-            } else if constexpr (sizeof(T) == 1) {
-                const uint32_t packed = (uint32_t)(uint8_t)outv[0] | ((uint32_t)(uint8_t)outv[1] << 8) |
-                                        ((uint32_t)(uint8_t)outv[2] << 16) | ((uint32_t)(uint8_t)outv[3] << 24);
-                *(uint32_t*)dst = packed;
-            } else {
-                uint2 packed;
-                packed.x = (uint32_t)__bfloat16_as_ushort(outv[0]) | ((uint32_t)__bfloat16_as_ushort(outv[1]) << 16);
-                packed.y = (uint32_t)__bfloat16_as_ushort(outv[2]) | ((uint32_t)__bfloat16_as_ushort(outv[3]) << 16);
-                *(uint2*)dst = packed;
-            }
-        } else {
+        for (int orow = 0; orow < R; ++orow) {
+            const int th = r0 + orow;
+            if (th >= th_n) break;
+            const int ho = ho0 + th;
+            const int wo = wo0 + q0;
+            T outv[VO];
 #pragma unroll
-            for (int q = 0; q < VO; ++q)
-                if (q0 + q < tw_n) dst[q] = outv[q];
+            for (int q = 0; q < VO; ++q) {
+                if constexpr (std::is_same<T, int8_t>::value) {
+                    outv[q] = requant(acc[orow][q] + bias, a.composite, a.rounding, a.y_zp, relu8);
+                } else if constexpr (std::is_same<T, __hip_bfloat16>::value) {
+                    outv[q] = f32_to_bf16(bias_act(a, acc[orow][q], c));
+                } else {
+                    outv[q] = bias_act(a, acc[orow][q], c);
+                }
+            }
+            T* dst = yp + (int64_t)ho * a.wo + wo;
+            if (a.vec_store && q0 + VO <= tw_n) {
+                if constexpr (sizeof(T) == 4) {
+                    *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
+                } else if constexpr (sizeof(T) == 1) {
+                    *(uint32_t*)dst = (uint32_t)(uint8_t)outv[0] | ((uint32_t)(uint8_t)outv[1] << 8) |
+                                      ((uint32_t)(uint8_t)outv[2] << 16) | ((uint32_t)(uint8_t)outv[3] << 24);
+                } else {
+                    uint2 packed;
+                    packed.x = (uint32_t)__bfloat16_as_ushort(outv[0]) | ((uint32_t)__bfloat16_as_ushort(outv[1]) << 16);
+                    packed.y = (uint32_t)__bfloat16_as_ushort(outv[2]) | ((uint32_t)__bfloat16_as_ushort(outv[3]) << 16);
+                    *(uint2*)dst = packed;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < VO; ++q)
+                    if (q0 + q < tw_n) dst[q] = outv[q];
+            }
         }
     }
 }
 
+// LDS bytes of the window of a tile (worst-case alignment slack).
 template <typename T>
 size_t window_bytes(const conv2d_params_t& p, int tile_h, int tile_w, int ho, int wo) {
     using LT = typename Elem<T>::lds_t;
@@ -195,23 +253,30 @@ size_t window_bytes(const conv2d_params_t& p, int tile_h, int tile_w, int ho, in
     const int tw = tile_w < wo ? tile_w : wo;
     const int rows = (th - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
     const int span = (tw - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
-    const int lw = (span + 2 * VL - 2 + VL - 1) / VL * VL;   // worst-case alignment slack
+    const int lw = (span + 2 * VL - 2 + VL - 1) / VL * VL;
     return (size_t)rows * lw * sizeof(LT);
+}
+
+// Input vectors of the window (for the NVMAX bound of the vector path).
+template <typename T>
+int window_vectors(const conv2d_params_t& p, int tile_h, int tile_w, int ho, int wo) {
+    return (int)(window_bytes<T>(p, tile_h, tile_w, ho, wo) / sizeof(typename Elem<T>::lds_t) / Elem<T>::VL);
 }
 
 template <typename T>
 bool plan_dw_t(Desc& d) {
     const conv2d_params_t& p = d.p;
     if (p.k_h * p.k_w > 25) return false;
-    // Whole rows when they fit; otherwise 256-wide column strips.
-    int tw = d.wo <= 512 ? d.wo : 256;
-    const int uw = (tw + VO - 1) / VO;
-    // About four output vectors per thread.
-    int th = (4 * kThreads) / uw;
-    if (th < 1) th = 1;
-    if (th > d.ho) th = d.ho;
-    while (th > 1 && window_bytes<T>(p, th, tw, d.ho, d.wo) > 32 * 1024) th = (th + 1) / 2;
-    if (window_bytes<T>(p, th, tw, d.ho, d.wo) > 48 * 1024) return false;
+    // Whole rows when they fit; otherwise 256-wide column strips.  Halve the
+    // rows until the window fits both LDS and the per-thread load budget.
+    const int tw = d.wo <= 256 ? d.wo : 256;
+    int th = d.ho;
+    while (th > 1 && (window_bytes<T>(p, th, tw, d.ho, d.wo) > 32 * 1024 ||
+                      window_vectors<T>(p, th, tw, d.ho, d.wo) > NVMAX * kThreads))
+        th = (th + 1) / 2;
+    if (window_bytes<T>(p, th, tw, d.ho, d.wo) > 48 * 1024 ||
+        window_vectors<T>(p, th, tw, d.ho, d.wo) > NVMAX * kThreads)
+        return false;
     d.tile_h = th;
     d.tile_w = tw;
     d.lds_bytes = (int)window_bytes<T>(p, th, tw, d.ho, d.wo);
@@ -220,11 +285,14 @@ bool plan_dw_t(Desc& d) {
 
 template <typename T, bool VEC>
 const void* pick(const conv2d_params_t& p) {
-    if (p.k_h == 3 && p.k_w == 3 && p.stride_h == 1 && p.stride_w == 1)
-        return (const void*)dw_kernel<T, VEC, 3, 3, 1, 1>;
-    if (p.k_h == 3 && p.k_w == 3 && p.stride_h == 2 && p.stride_w == 2)
-        return (const void*)dw_kernel<T, VEC, 3, 3, 2, 2>;
-    return (const void*)dw_kernel<T, VEC, 0, 0, 0, 0>;
+    const bool d1 = p.dilation_h == 1 && p.dilation_w == 1;
+    if (d1 && p.k_h == 3 && p.k_w == 3 && p.stride_h == 1 && p.stride_w == 1)
+        return (const void*)dw_kernel<T, VEC, 3, 3, 1, 1, 4>;
+    if (d1 && p.k_h == 3 && p.k_w == 3 && p.stride_h == 2 && p.stride_w == 2)
+        return (const void*)dw_kernel<T, VEC, 3, 3, 2, 2, 2>;
+    if (d1 && p.k_h == 5 && p.k_w == 5 && p.stride_h == 1 && p.stride_w == 1)
+        return (const void*)dw_kernel<T, VEC, 5, 5, 1, 1, 4>;
+    return (const void*)dw_kernel<T, VEC, 0, 0, 0, 0, 1>;
 }
 
 template <typename T>
@@ -236,7 +304,13 @@ hipError_t launch_t(const Desc& d, ConvArgs a, hipStream_t s) {
     const uint64_t blocks = (uint64_t)a.tiles_w * a.tiles_h * a.c_out * a.n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
-    const bool vec = (d.p.w % Elem<T>::VL) == 0 && ((uintptr_t)a.xptr % 16) == 0 && ((uintptr_t)a.yptr % 16) == 0;
+    a.dv_tiles_w = make_divu32((uint32_t)a.tiles_w);
+    a.dv_tiles_h = make_divu32((uint32_t)a.tiles_h);
+    a.dv_co_tiles = make_divu32((uint32_t)a.c_out);
+    const bool vec = (d.p.w % Elem<T>::VL) == 0 && ((uintptr_t)a.xptr % 16) == 0;
+    // Output rows move as one VO-element vector when every row start keeps
+    // the vector alignment.
+    a.vec_store = (d.wo % VO) == 0 && ((uintptr_t)a.yptr % (VO * sizeof(T))) == 0;
     const void* fn = vec ? pick<T, true>(d.p) : pick<T, false>(d.p);
     void* args[] = {&a};
     return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kThreads), args, d.lds_bytes, s);

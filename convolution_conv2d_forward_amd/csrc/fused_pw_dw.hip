@@ -3,17 +3,23 @@
 // expansion followed by its depthwise conv, with the expanded tensor never
 // written to main memory).
 //
-// Workgroup tile: one image, TH output rows, CE expanded channels.
-//   1. For each chunk of KC input channels, stage the input rows the tile
-//      needs (TH + (kh-1)*dh rows, full width) and the CE x KC pointwise
-//      weights in LDS, and accumulate E = W_pw * X on the fp32 matrix cores
-//      (v_mfma_f32_16x16x4f32; M = CE channels, N = flattened row pixels).
-//   2. Bias + activation of the pointwise conv; the result goes to LDS as
-//      rows of W + pad_left + pad_right floats.  Rows and columns outside the
-//      image hold the depthwise pad_value: the depthwise padding applies to
-//      the pointwise output, not to pw(pad).
-//   3. Depthwise taps from LDS, bias + activation, 16-byte stores of VO
-//      consecutive outputs.
+// Workgroup tile: one image, TH output rows, CE = 32 expanded channels, the
+// full image width.
+//   1. The pointwise input rows the tile needs (TH + (kh-1)*dh rows, halo
+//      included) are loaded for a chunk of KC input channels, every thread
+//      issuing all of its 16-byte loads before writing any of them to LDS,
+//      together with the CE x KC pointwise weights.  E = W_pw * X runs on the
+//      fp32 matrix cores (v_mfma_f32_16x16x4f32; M = the CE channels, N = the
+//      rows' pixels): each of the eight waves owns every 16-pixel fragment
+//      j == wave (mod 8) for both 16-channel halves, so its MFMAs accumulate
+//      into independent registers.
+//   2. Bias + activation of the pointwise conv go into an LDS tile of
+//      W + pad_left + pad_right columns per row.  Rows and columns outside
+//      the image hold the depthwise pad_value: the depthwise padding applies
+//      to the pointwise output, not to pw(pad).
+//   3. The depthwise conv reads R x VO output blocks out of that tile through
+//      a register window, adds its bias, applies its activation and writes
+//      each output row with a 16-byte store.
 // The halo rows are recomputed by the tiles above and below
 // ((TH + kh - 1) / TH pointwise work) instead of being exchanged.
 #include "device_common.h"
@@ -22,22 +28,29 @@ namespace conv2d {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int CE = 32;      // expanded channels per workgroup
-constexpr int KC = 32;      // input channels per pointwise chunk
-constexpr int CEP = CE + 16;
-constexpr int NFW = 14;     // max 16x16 pointwise fragments per wave
-constexpr int VO = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int CE = 32;       // expanded channels per workgroup
+constexpr int KC = 32;       // input channels per pointwise chunk
+constexpr int CEP = 48;      // LDS row stride of the weight tile (4 k-rows land 16 banks apart)
+constexpr int NJMAX = 8;     // max 16-pixel fragments per wave (the NJ template parameter)
+constexpr int NVX = 8;       // max 16-byte input loads per thread and chunk
+constexpr int VO = 4;        // depthwise outputs per thread and row
+constexpr int RR = 4;        // depthwise output rows per thread
 
 struct FusedArgs {
     ConvArgs pw, dw;
     int32_t tile_h, tiles_h, ce_tiles;
     int32_t rows;          // pointwise rows per tile: TH + (kh-1)*dh
-    int32_t xs_stride;     // LDS floats per input-channel plane (rows * w, padded)
+    int32_t xs_stride;     // LDS floats per input-channel plane (rows * w, = 16 mod 64)
     int32_t ew;            // LDS row length of the expanded tile
     int32_t es_stride;     // LDS floats per expanded channel
+    int32_t vec;           // input rows move as 16-byte vectors
     uint32_t num_blocks;
-    FastDiv div_w, div_units_row;
+    DivU32 dv_ce_tiles, dv_tiles_h;
+    FastDiv div_w;         // division by the image width (pixel -> row)
+    FastDiv div_w4;        // division by w/4 (load unit -> row)
+    FastDiv div_rw4;       // division by rows*w/4 (load unit -> channel)
 };
 
 __device__ __forceinline__ float act_f(int act, float v, float a0, float a1, float slope) {
@@ -50,50 +63,86 @@ __device__ __forceinline__ float act_f(int act, float v, float a0, float a1, flo
     }
 }
 
-template <int KH, int KW>
+// NJ: 16-pixel pointwise fragments per wave (register budget: 4 keeps two
+// workgroups per compute unit).
+template <int KH, int KW, int NJ>
 __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) float lds[];
     const ConvArgs& P = f.pw;
     const ConvArgs& D = f.dw;
-    const int kh = KH ? KH : D.k_h, kw = KW ? KW : D.k_w;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr bool FIXED = KH > 0;
+    const int kh = FIXED ? KH : D.k_h, kw = FIXED ? KW : D.k_w;
+    const int dh = FIXED ? 1 : D.dilation_h, dwl = FIXED ? 1 : D.dilation_w;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     uint32_t L = xcd_remap(blockIdx.x, f.num_blocks);
-    const int cet = L % f.ce_tiles;  L /= f.ce_tiles;
-    const int tht = L % f.tiles_h;   L /= f.tiles_h;
-    const int n = L;
+    uint32_t Q = divu(L, f.dv_ce_tiles);
+    const int cet = L - Q * f.ce_tiles;
+    L = Q; Q = divu(L, f.dv_tiles_h);
+    const int tht = L - Q * f.tiles_h;
+    const int n = Q;
     const int ce0 = cet * CE;
     const int ho0 = tht * f.tile_h;
-    const int ih_lo = ho0 - D.pad_top;          // input row of pointwise row 0
+    const int ih_lo = ho0 - D.pad_top;          // image row of pointwise row 0
     const int W = P.w, H = P.h;
     const int npix = f.rows * W;                 // pointwise pixels of the tile
-    const int nfrag_n = (npix + 15) / 16;
-    const int nfrag = (CE / 16) * nfrag_n;
+    const int nfn = (npix + 15) / 16;
     const int ce_valid = min(CE, P.c_out - ce0);
     const int64_t HW = (int64_t)H * W;
+    const int XS = f.xs_stride;
 
     const float* __restrict__ xg = (const float*)P.xptr + ((int64_t)n * P.in_total + P.in_off) * HW;
     const float* __restrict__ wpw = (const float*)P.wptr;
 
-    float* xs = lds;                       // [KC][xs_stride]
-    float* ws = lds + KC * f.xs_stride;    // [KC][CEP]
+    float* xs = lds;                       // [KC][XS]
+    float* ws = lds + KC * XS;             // [KC][CEP]
 
-    f32x4 acc[NFW];
+    f32x4 acc[2][NJ];
 #pragma unroll
-    for (int i = 0; i < NFW; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[m][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // ---- 1. pointwise on the matrix cores ----
     for (int k0 = 0; k0 < P.c_in; k0 += KC) {
-        // input rows (zeros for rows outside the image: replaced in step 2)
-        for (int e = tid; e < KC * npix; e += kThreads) {
-            const int kc = e / npix;
-            const int p = e - kc * npix;
-            const int r = (int)fdiv(p, f.div_w);
-            const int c = p - r * W;
-            const int ih = ih_lo + r;
-            float v = 0.0f;
-            if (k0 + kc < P.c_in && (unsigned)ih < (unsigned)H) v = xg[(int64_t)(k0 + kc) * HW + (int64_t)ih * W + c];
-            xs[kc * f.xs_stride + p] = v;
+        if (f.vec) {
+            // Units of four pixels: (channel, row, column group); all loads first.
+            const int w4 = W >> 2;
+            const int units = KC * f.rows * w4;
+            float4 buf[NVX];
+#pragma unroll
+            for (int i = 0; i < NVX; ++i) {
+                const int u = tid + i * kThreads;
+                const int kc = (int)fdiv(u, f.div_rw4);
+                const int rem = u - kc * (f.rows * w4);
+                const int r = (int)fdiv(rem, f.div_w4);
+                const int c4 = rem - r * w4;
+                const int ih = ih_lo + r;
+                buf[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (u < units && k0 + kc < P.c_in && (unsigned)ih < (unsigned)H)
+                    buf[i] = *(const float4*)(xg + (int64_t)(k0 + kc) * HW + (int64_t)ih * W + 4 * c4);
+            }
+#pragma unroll
+            for (int i = 0; i < NVX; ++i) {
+                const int u = tid + i * kThreads;
+                if (u < units) {
+                    const int kc = (int)fdiv(u, f.div_rw4);
+                    const int rem = u - kc * (f.rows * w4);
+                    *(float4*)(xs + kc * XS + 4 * rem) = buf[i];
+                }
+            }
+        } else {
+            for (int e = tid; e < KC * npix; e += kThreads) {
+                const int kc = e / npix;
+                const int p = e - kc * npix;
+                const int r = (int)fdiv(p, f.div_w);
+                const int c = p - r * W;
+                const int ih = ih_lo + r;
+                float v = 0.0f;
+                if (k0 + kc < P.c_in && (unsigned)ih < (unsigned)H) v = xg[(int64_t)(k0 + kc) * HW + (int64_t)ih * W + c];
+                xs[kc * XS + p] = v;
+            }
         }
         for (int e = tid; e < KC * CE; e += kThreads) {
             const int ce = e % CE;
@@ -103,52 +152,51 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
             ws[kc * CEP + ce] = v;
         }
         __syncthreads();
+        // A lane reads weight row ce = lane%16 (+16) at k = lane/16; B lane reads
+        // input plane k = lane/16 at pixel 16*frag + lane%16.
 #pragma unroll
-        for (int i = 0; i < NFW; ++i) {
-            const int fi = wave + 4 * i;
-            if (fi < nfrag) {
-                const int mf = fi % (CE / 16);
-                const int nf = fi / (CE / 16);
-                f32x4 a = acc[i];
-#pragma unroll 8
-                for (int kq = 0; kq < KC; kq += 4) {
-                    const float av = ws[(kq + (lane >> 4)) * CEP + mf * 16 + (lane & 15)];
-                    const float bv = xs[(kq + (lane >> 4)) * f.xs_stride + nf * 16 + (lane & 15)];
-                    a = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, a, 0, 0, 0);
+        for (int kq = 0; kq < KC; kq += 4) {
+            const int kr = kq + (lane >> 4);
+            const float a0 = ws[kr * CEP + (lane & 15)];
+            const float a1 = ws[kr * CEP + 16 + (lane & 15)];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int fj = wave + kWaves * j;
+                if (fj < nfn) {
+                    const float b = xs[kr * XS + fj * 16 + (lane & 15)];
+                    acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b, acc[0][j], 0, 0, 0);
+                    acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc[1][j], 0, 0, 0);
                 }
-                acc[i] = a;
             }
         }
         __syncthreads();
     }
 
     // ---- 2. pointwise epilogue into the expanded tile (aliases xs/ws) ----
-    float* es = lds;   // [CE][es_stride], row r at r*ew, image column c at c + pad_left
+    float* es = lds;   // [CE][es_stride], pointwise row r at r*ew, image column c at c + pad_left
     const float dpad = D.pad_value;
 #pragma unroll
-    for (int i = 0; i < NFW; ++i) {
-        const int fi = wave + 4 * i;
-        if (fi < nfrag) {
-            const int mf = fi % (CE / 16);
-            const int nf = fi / (CE / 16);
-            const int p = nf * 16 + (lane & 15);
-            if (p < npix) {
-                const int r = (int)fdiv(p, f.div_w);
-                const int c = p - r * W;
-                const bool inside = (unsigned)(ih_lo + r) < (unsigned)H;
+    for (int j = 0; j < NJ; ++j) {
+        const int fj = wave + kWaves * j;
+        const int p = fj * 16 + (lane & 15);
+        if (fj < nfn && p < npix) {
+            const int r = (int)fdiv(p, f.div_w);
+            const int c = p - r * W;
+            const bool inside = (unsigned)(ih_lo + r) < (unsigned)H;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int ce = mf * 16 + (lane >> 4) * 4 + v;
+                    const int ce = m * 16 + (lane >> 4) * 4 + v;
                     float val = dpad;
                     if (inside && ce < ce_valid) {
                         const int cg = ce0 + ce;
-                        float t = acc[i][v] + (P.bias ? P.bias[cg] : 0.0f);
+                        const float t = acc[m][j][v] + (P.bias ? P.bias[cg] : 0.0f);
                         const float sl = P.act == CONV_ACT_PRELU ? P.slope[P.slope_count == 1 ? 0 : cg] : 0.0f;
                         val = act_f(P.act, t, P.act_a, P.act_b, sl);
                     }
                     es[ce * f.es_stride + r * f.ew + c + D.pad_left] = val;
                 }
-            }
         }
     }
     // pad columns of every row
@@ -157,57 +205,100 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
         const int ce = e / (f.rows * padc);
         const int rem = e - ce * f.rows * padc;
         const int r = rem / padc;
-        const int j = rem - r * padc;
-        const int col = j < D.pad_left ? j : W + j;
+        const int jj = rem - r * padc;
+        const int col = jj < D.pad_left ? jj : W + jj;
         es[ce * f.es_stride + r * f.ew + col] = dpad;
     }
     __syncthreads();
 
-    // ---- 3. depthwise from LDS ----
+    // ---- 3. depthwise from LDS, R x VO outputs per thread ----
     const int th_n = min(f.tile_h, D.ho - ho0);
     const int uw = (D.wo + VO - 1) / VO;
-    const int units = ce_valid * th_n * uw;
+    const int uh = (th_n + RR - 1) / RR;
+    const int units = ce_valid * uh * uw;
     const int64_t oplane = (int64_t)D.ho * D.wo;
     float* __restrict__ yg = (float*)D.yptr;
     const float* __restrict__ wdw = (const float*)D.wptr;
     const bool vec_ok = (D.wo % VO) == 0 && (((uintptr_t)D.yptr) % 16) == 0;
     for (int u = tid; u < units; u += kThreads) {
-        const int ce = u / (th_n * uw);
-        const int rem = u - ce * th_n * uw;
-        const int th = rem / uw;
-        const int q0 = (rem - th * uw) * VO;
+        const int ce = u / (uh * uw);
+        const int rem = u - ce * uh * uw;
+        const int rr = rem / uw;
+        const int q0 = (rem - rr * uw) * VO;
+        const int r0 = rr * RR;
         const int cg = ce0 + ce;
-        float accd[VO];
+        float accd[RR][VO];
 #pragma unroll
-        for (int q = 0; q < VO; ++q) accd[q] = 0.0f;
+        for (int i = 0; i < RR; ++i)
+#pragma unroll
+            for (int q = 0; q < VO; ++q) accd[i][q] = 0.0f;
         const float* ech = es + ce * f.es_stride;
         const float* wch = wdw + (int64_t)cg * kh * kw;
+        if constexpr (FIXED) {
+            float wt[KH * KW];
 #pragma unroll
-        for (int r = 0; r < kh; ++r) {
-            const float* row = ech + (th + r * D.dilation_h) * f.ew;
+            for (int i = 0; i < KH * KW; ++i) wt[i] = wch[i];
+            constexpr int RIN = RR + KH - 1, CIN = VO + KW - 1;
+            const int cmax = f.ew - 1;
 #pragma unroll
-            for (int s2 = 0; s2 < kw; ++s2) {
-                const float wv = wch[r * kw + s2];
+            for (int i = 0; i < RIN; ++i) {
+                const int row = r0 + i;
+                if (row >= f.rows) break;
+                const float* src = ech + row * f.ew;
+                float win[CIN];
 #pragma unroll
-                for (int q = 0; q < VO; ++q) {
-                    // Columns past the row end belong to masked outputs; clamp the read.
-                    const int col = min(q0 + q, D.wo - 1) + s2 * D.dilation_w;
-                    accd[q] = fmaf(row[col], wv, accd[q]);
+                for (int jj = 0; jj < CIN; ++jj) win[jj] = src[q0 + jj <= cmax ? q0 + jj : cmax];
+#pragma unroll
+                for (int orow = 0; orow < RR; ++orow) {
+                    const int r = i - orow;
+                    if (r < 0 || r >= KH) continue;
+#pragma unroll
+                    for (int s2 = 0; s2 < KW; ++s2)
+#pragma unroll
+                        for (int q = 0; q < VO; ++q) accd[orow][q] = fmaf(win[q + s2], wt[r * KW + s2], accd[orow][q]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int orow = 0; orow < RR; ++orow) {
+                if (r0 + orow >= th_n) break;
+                for (int r = 0; r < kh; ++r) {
+                    const float* row = ech + (r0 + orow + r * dh) * f.ew;
+                    for (int s2 = 0; s2 < kw; ++s2) {
+                        const float wv = wch[r * kw + s2];
+#pragma unroll
+                        for (int q = 0; q < VO; ++q) {
+                            // Columns past the row end belong to masked outputs; clamp the read.
+                            const int col = min(q0 + q, D.wo - 1) + s2 * dwl;
+                            accd[orow][q] = fmaf(row[col], wv, accd[orow][q]);
+                        }
+                    }
                 }
             }
         }
-        float outv[VO];
 #pragma unroll
-        for (int q = 0; q < VO; ++q) outv[q] = bias_act(D, accd[q], cg);
-        float* dst = yg + ((int64_t)n * D.out_total + D.out_off + cg) * oplane + (int64_t)(ho0 + th) * D.wo + q0;
-        if (vec_ok && q0 + VO <= D.wo) {
-            *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
-        } else {
+        for (int orow = 0; orow < RR; ++orow) {
+            const int th = r0 + orow;
+            if (th >= th_n) break;
+            float outv[VO];
 #pragma unroll
-            for (int q = 0; q < VO; ++q)
-                if (q0 + q < D.wo) dst[q] = outv[q];
+            for (int q = 0; q < VO; ++q) outv[q] = bias_act(D, accd[orow][q], cg);
+            float* dst = yg + ((int64_t)n * D.out_total + D.out_off + cg) * oplane + (int64_t)(ho0 + th) * D.wo + q0;
+            if (vec_ok && q0 + VO <= D.wo) {
+                *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < VO; ++q)
+                    if (q0 + q < D.wo) dst[q] = outv[q];
+            }
         }
     }
+}
+
+// Channel stride of the expanded tile: >= rows * ew and = 4 (mod 16), so the
+// four lane groups of an MFMA result (four channels apart) write 16 banks apart.
+int es_stride_for(int n) {
+    return n % 16 <= 4 ? n - n % 16 + 4 : n - n % 16 + 20;
 }
 
 int xs_stride_for(int npix) {
@@ -217,31 +308,54 @@ int xs_stride_for(int npix) {
 }
 
 struct FusedPlan {
-    int tile_h, rows, xs_stride, ew, es_stride, lds_floats;
+    int tile_h, rows, xs_stride, ew, es_stride, lds_floats, vec;
 };
+
+// Compute units of the current device (256 on MI355X; also the answer when
+// no device is visible, e.g. when descriptors are built on a host without one).
+int cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cached = v;
+        else
+            cached = 256;
+    }
+    return cached;
+}
 
 bool plan(const Desc& pw, const Desc& dw, FusedPlan* out) {
     const conv2d_params_t& d = dw.p;
     const int W = pw.p.w;
     const int ew = W + d.pad_left + d.pad_right;
+    const bool vec = W % 4 == 0;
+    const long per_image = (long)((pw.p.c_out + CE - 1) / CE) * pw.p.n;
     bool ok = false;
     long best_cost = 0;
     for (int th = 1; th <= dw.ho; ++th) {
         const int rows = th + (d.k_h - 1) * d.dilation_h;
         const int npix = rows * W;
-        if ((CE / 16) * ((npix + 15) / 16) > 4 * NFW) break;
+        if ((npix + 15) / 16 > NJMAX * kWaves) break;               // fragments per wave
+        if (vec && KC * rows * (W / 4) > NVX * kThreads) break;     // loads per thread
         if (npix >= 65536) break;
         const int xs = xs_stride_for(npix);
-        const int es = rows * ew;
+        const int es = es_stride_for(rows * ew);
         const int fl1 = KC * xs + KC * CEP;
         const int fl2 = CE * es;
         const int lds = fl1 > fl2 ? fl1 : fl2;
-        if (lds * 4 > 64 * 1024) break;
-        // Pointwise rows computed over the whole image (halo recompute and
-        // the ragged last tile included): the smaller the better.
-        const long cost = (long)((dw.ho + th - 1) / th) * rows;
-        if (!ok || cost <= best_cost) {
-            *out = FusedPlan{th, rows, xs, ew, es, lds};
+        if (lds * 4 > 96 * 1024) break;
+        // Time ~ rounds of resident workgroups x pointwise rows per workgroup
+        // (halo recompute included).
+        const long blocks = per_image * ((dw.ho + th - 1) / th);
+        long per_cu = (160 * 1024) / (lds * 4) > 0 ? (160 * 1024) / (lds * 4) : 1;
+        const long per_cu_regs = (npix + 15) / 16 <= 4 * kWaves ? 2 : 1;   // NJ = 4 or 8 register budget
+        if (per_cu > per_cu_regs) per_cu = per_cu_regs;
+        const long rounds = (blocks + per_cu * cu_count() - 1) / (per_cu * cu_count());
+        const long cost = rounds * rows;
+        if (!ok || cost < best_cost) {
+            *out = FusedPlan{th, rows, xs, ew, es, lds, vec ? 1 : 0};
             best_cost = cost;
             ok = true;
         }
@@ -273,14 +387,24 @@ hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, Conv
     f.xs_stride = fp.xs_stride;
     f.ew = fp.ew;
     f.es_stride = fp.es_stride;
+    f.vec = fp.vec && ((uintptr_t)apw.xptr % 16) == 0;
     f.div_w = make_fastdiv((uint32_t)pw.p.w);
-    f.div_units_row = make_fastdiv(1);
+    f.div_w4 = make_fastdiv((uint32_t)(pw.p.w / 4 > 0 ? pw.p.w / 4 : 1));
+    f.div_rw4 = make_fastdiv((uint32_t)(fp.rows * (pw.p.w / 4) > 0 ? fp.rows * (pw.p.w / 4) : 1));
+    f.dv_ce_tiles = make_divu32((uint32_t)f.ce_tiles);
+    f.dv_tiles_h = make_divu32((uint32_t)f.tiles_h);
     const uint64_t blocks = (uint64_t)f.ce_tiles * f.tiles_h * apw.n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     f.num_blocks = (uint32_t)blocks;
-    const void* fn = (dw.p.k_h == 3 && dw.p.k_w == 3) ? (const void*)fused_pw_dw_kernel<3, 3>
-                                                     : (const void*)fused_pw_dw_kernel<0, 0>;
+    const bool k3 = dw.p.k_h == 3 && dw.p.k_w == 3 && dw.p.dilation_h == 1 && dw.p.dilation_w == 1;
+    const bool nj4 = (fp.rows * pw.p.w + 15) / 16 <= 4 * kWaves;
+    const void* fn = k3 ? (nj4 ? (const void*)fused_pw_dw_kernel<3, 3, 4> : (const void*)fused_pw_dw_kernel<3, 3, 8>)
+                        : (nj4 ? (const void*)fused_pw_dw_kernel<0, 0, 4> : (const void*)fused_pw_dw_kernel<0, 0, 8>);
+    if (fp.lds_floats * 4 > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, fp.lds_floats * 4);
+        if (e != hipSuccess) return e;
+    }
     void* args[] = {&f};
     return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kThreads), args, fp.lds_floats * 4, s);
 }
