@@ -137,6 +137,6 @@ bool plan_qpw(Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.
-void fill_tiling(const Desc& d, ConvArgs& a);
+
 
 }  // namespace conv2d
