@@ -276,48 +276,57 @@ def float_layer_fns(L, x, w, b, s, dtype, reps):
     return t, cc.conv2d_desc_kernel_name(d)
 
 
-def per_config(reps):
+def per_config(reps, only="all"):
+    """Per-configuration table; `only` selects one section (single_conv,
+    bottleneck, mixed_f32, mixed_bf16, int8_chain) or all of them."""
     import convolution_conv2d_forward_amd as cc
     import workloads
     torch = torch_mod()
     out = {}
 
+    def want(name):
+        return only in ("all", name)
+
     # single conv (latency)
-    wl = workloads.single_conv()
-    L = wl.layers[0]
-    t, k = float_layer_fns(L, wl.arrays["x"], wl.arrays["w"], wl.arrays["b"], None, "f32", reps)
-    out["single_conv"] = {"conv": dict(roofline_entry(L.flops, layer_bytes(L, 4), t, "f32", bound="latency"),
-                                       kernel=k)}
-    log("single_conv", out["single_conv"])
+    if want("single_conv"):
+        wl = workloads.single_conv()
+        L = wl.layers[0]
+        t, k = float_layer_fns(L, wl.arrays["x"], wl.arrays["w"], wl.arrays["b"], None, "f32", reps)
+        out["single_conv"] = {"conv": dict(roofline_entry(L.flops, layer_bytes(L, 4), t, "f32", bound="latency"),
+                                           kernel=k)}
+        log("single_conv", out["single_conv"])
 
     # inverted bottleneck
-    wl = workloads.bottleneck()
-    L1, L2, L3 = wl.layers
-    a = wl.arrays
-    res = {}
-    for L, wk in ((L1, "w_pw1"), (L2, "w_dw"), (L3, "w_pw2")):
-        rng = np.random.default_rng(3)
-        x = a["x"] if L is L1 else rng.standard_normal(L.x_shape).astype(np.float32)
-        t, k = float_layer_fns(L, x, a[wk], None, None, "f32", reps)
-        res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 4), t, "f32"), kernel=k)
-    d1, d2 = cc.conv2d_desc_create(params_of(L1)), cc.conv2d_desc_create(params_of(L2))
-    w1, w2 = t_(a["w_pw1"]), t_(a["w_dw"])
-    xs = t_(a["x"])
+    if want("bottleneck"):
+        wl = workloads.bottleneck()
+        L1, L2, L3 = wl.layers
+        a = wl.arrays
+        res = {}
+        for L, wk in ((L1, "w_pw1"), (L2, "w_dw"), (L3, "w_pw2")):
+            rng = np.random.default_rng(3)
+            x = a["x"] if L is L1 else rng.standard_normal(L.x_shape).astype(np.float32)
+            t, k = float_layer_fns(L, x, a[wk], None, None, "f32", reps)
+            res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 4), t, "f32"), kernel=k)
+        d1, d2 = cc.conv2d_desc_create(params_of(L1)), cc.conv2d_desc_create(params_of(L2))
+        w1, w2 = t_(a["w_pw1"]), t_(a["w_dw"])
+        xs = t_(a["x"])
 
-    def make_fused():
-        xi = xs.clone()
-        yi = torch.empty((L2.n, L2.c_out, L2.h, L2.w), device=dev())
-        return lambda: cc.fused_pw_dw_forward(d1, d2, xi, w1, None, None, w2, None, None, yi)
+        def make_fused():
+            xi = xs.clone()
+            yi = torch.empty((L2.n, L2.c_out, L2.h, L2.w), device=dev())
+            return lambda: cc.fused_pw_dw_forward(d1, d2, xi, w1, None, None, w2, None, None, yi)
 
-    fns = _rotating(make_fused, (L1.n * L1.c_in + L2.n * L2.c_out) * L1.h * L1.w * 4)
-    t = time_layer("fused", fns, reps)
-    fb = 4 * (L1.n * L1.c_in * L1.h * L1.w + L1.c_out * L1.c_in + L2.c_out * 9 + L2.n * L2.c_out * L2.h * L2.w)
-    res["fused_pw_dw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "f32"), kernel="fused_pw_dw")
-    out["bottleneck"] = res
-    log("bottleneck", res)
+        fns = _rotating(make_fused, (L1.n * L1.c_in + L2.n * L2.c_out) * L1.h * L1.w * 4)
+        t = time_layer("fused", fns, reps)
+        fb = 4 * (L1.n * L1.c_in * L1.h * L1.w + L1.c_out * L1.c_in + L2.c_out * 9 + L2.n * L2.c_out * L2.h * L2.w)
+        res["fused_pw_dw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "f32"), kernel="fused_pw_dw")
+        out["bottleneck"] = res
+        log("bottleneck", res)
 
     # mixed sweep fp32 / bf16
     for dtype in ("f32", "bf16"):
+        if not want(f"mixed_{dtype}"):
+            continue
         res = {}
         for name in ("s2", "d2", "g32", "pw"):
             wl = workloads.mixed_sweep(which={name})
@@ -330,28 +339,29 @@ def per_config(reps):
         out[f"mixed_sweep_{dtype}"] = res
 
     # int8 chain
-    wl = workloads.int8_chain()
-    a = wl.arrays
-    res = {}
-    for L in wl.layers:
-        d = cc.conv2d_desc_create(params_of(L, "i8"))
-        ho, wo = L.out_hw
-        rng = np.random.default_rng(5)
-        x = a["x"] if L.name == "dw_s1" else rng.integers(-128, 128, size=L.x_shape).astype(np.int8)
-        xs = t_(x)
-        wd, bd = t_(a[f"w_{L.name}"]), t_(a[f"b_{L.name}"])
+    if want("int8_chain"):
+        wl = workloads.int8_chain()
+        a = wl.arrays
+        res = {}
+        for L in wl.layers:
+            d = cc.conv2d_desc_create(params_of(L, "i8"))
+            ho, wo = L.out_hw
+            rng = np.random.default_rng(5)
+            x = a["x"] if L.name == "dw_s1" else rng.integers(-128, 128, size=L.x_shape).astype(np.int8)
+            xs = t_(x)
+            wd, bd = t_(a[f"w_{L.name}"]), t_(a[f"b_{L.name}"])
 
-        def make(d=d, xs=xs, wd=wd, bd=bd, L=L, ho=ho, wo=wo):
-            xi = xs.clone()
-            yi = torch.empty((L.n, L.c_out, ho, wo), dtype=torch.int8, device=dev())
-            return lambda: cc.qconv2d_forward(d, xi, 0.02, 0, wd, 0.01, 0, bd, 0.05, 0, yi)
+            def make(d=d, xs=xs, wd=wd, bd=bd, L=L, ho=ho, wo=wo):
+                xi = xs.clone()
+                yi = torch.empty((L.n, L.c_out, ho, wo), dtype=torch.int8, device=dev())
+                return lambda: cc.qconv2d_forward(d, xi, 0.02, 0, wd, 0.01, 0, bd, 0.05, 0, yi)
 
-        fns = _rotating(make, x.size + L.n * L.c_out * ho * wo)
-        t = time_layer(L.name, fns, reps)
-        res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 1, extra=0), t, "i8"),
-                           kernel=cc.conv2d_desc_kernel_name(d))
-        log("int8", L.name, res[L.name])
-    out["int8_chain"] = res
+            fns = _rotating(make, x.size + L.n * L.c_out * ho * wo)
+            t = time_layer(L.name, fns, reps)
+            res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 1, extra=0), t, "i8"),
+                               kernel=cc.conv2d_desc_kernel_name(d))
+            log("int8", L.name, res[L.name])
+        out["int8_chain"] = res
     return out
 
 
@@ -422,7 +432,7 @@ def main():
         log(json.dumps(copy_probe(args.steps)))
         return
     if args.only not in ("all", "dense_block"):
-        log(json.dumps(per_config_only(args.only, args.reps)))
+        log(json.dumps(per_config(args.reps, args.only)))
         return
 
     db, wall, per = bench_dense_block(args.steps, args.warmup)
@@ -449,10 +459,6 @@ def main():
     if not args.no_extra and args.only == "all":
         line["per_config"] = per_config(args.reps)
     print(json.dumps(line), flush=True)
-
-
-def per_config_only(name, reps):
-    return {"note": f"--only {name}: use --only all for the per-config table"}
 
 
 if __name__ == "__main__":

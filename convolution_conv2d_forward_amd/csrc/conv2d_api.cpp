@@ -245,12 +245,36 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
     if (!planned) {
         d->kclass = KC_DIRECT;
         d->flatten_1x1 = false;
+        d->wpack_bytes = 0;
+    }
+    if (d->kclass == KC_IGEMM_BF16) {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipMalloc(&d->wpack, (size_t)d->wpack_bytes);
+        if (e != hipSuccess) {
+            d->wpack = nullptr;
+            delete d;
+            return fail(CONV_ERR_HIP, "allocating %lld bytes for the packed bf16 weights: %s",
+                        (long long)d->wpack_bytes, hipGetErrorString(e));
+        }
+        d->wpack_device = dev;
     }
     *out = (conv2d_desc_t)d;
     return ok();
 }
 
-void conv2d_desc_destroy(conv2d_desc_t d) { delete (Desc*)d; }
+void conv2d_desc_destroy(conv2d_desc_t dd) {
+    Desc* d = (Desc*)dd;
+    if (!d) return;
+    if (d->wpack) {
+        int cur = -1;
+        const bool switched = hipGetDevice(&cur) == hipSuccess && cur != d->wpack_device &&
+                              hipSetDevice(d->wpack_device) == hipSuccess;
+        (void)hipFree(d->wpack);
+        if (switched) (void)hipSetDevice(cur);
+    }
+    delete d;
+}
 
 conv_status_t conv2d_desc_get_output_shape(conv2d_desc_t dd, int32_t out[4]) {
     if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
@@ -283,6 +307,12 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
         return fail(CONV_ERR_ALIAS, "y overlaps the bias");
     if (d.p.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope, 4 * (int64_t)d.p.prelu_slope_count)))
         return fail(CONV_ERR_ALIAS, "y overlaps the PReLU slopes");
+    if (d.kclass == KC_IGEMM_BF16) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || dev != d.wpack_device)
+            return fail(CONV_ERR_INVALID_ARG, "bf16 descriptor was created on device %d, current device is %d",
+                        d.wpack_device, dev);
+    }
     ConvArgs a = make_args(d, x, w, bias, slope, y);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;

@@ -93,6 +93,7 @@ struct ConvArgs {
     int32_t vec_store;               // outputs may be written as 16-byte vectors
     int32_t dma;                     // fp32 igemm: copy chunks with direct global->LDS loads
     DivU32 dv_co_tiles, dv_groups, dv_tiles_w, dv_tiles_h;   // block index decomposition
+    int32_t lds_rs, lds_plane, col_half;  // bf16 igemm: patch row / plane strides in LDS cells, stride-2 split
 
     // int8 requant
     float composite;
@@ -114,6 +115,15 @@ struct Desc {
     int32_t stages;
     int32_t pt_vertical;
     bool flatten_1x1;            // 1x1/s1/p0: treat [h][w] as one row of h*w pixels
+    // bf16 implicit GEMM: device buffer for the weights in the kernel's LDS
+    // layout, refilled by every forward call (allocated at creation).
+    void* wpack = nullptr;
+    int64_t wpack_bytes = 0;
+    int wpack_device = -1;
+    // bf16 implicit GEMM: patch geometry fixed at planning (rows, columns,
+    // column shift, 8-pixel vectors per row, LDS row / plane stride in cells,
+    // stride-2 half width)
+    int32_t g_ph = 0, g_span = 0, g_shift = 0, g_nvr = 0, g_rs = 0, g_plane = 0, g_half = 0;
 };
 
 // Launchers (implemented next to their kernels).  Each returns the

@@ -58,6 +58,22 @@ __device__ __forceinline__ float bias_act(const ConvArgs& a, float v, int co) {
     return v;
 }
 
+// The activation alone, with the channel's PReLU slope already loaded.
+__device__ __forceinline__ float apply_act(const ConvArgs& a, float v, float slope) {
+    switch (a.act) {
+    case CONV_ACT_RELU:
+        return v > 0.0f ? v : 0.0f;
+    case CONV_ACT_LEAKY_RELU:
+        return v >= 0.0f ? v : a.act_a * v;
+    case CONV_ACT_PRELU:
+        return v >= 0.0f ? v : slope * v;
+    case CONV_ACT_CLIP:
+        return fminf(fmaxf(v, a.act_a), a.act_b);
+    default:
+        return v;
+    }
+}
+
 // int8 requant: q = sat8(round(f32(acc) * composite) + y_zp), ReLU as
 // max(q, y_zp) (yscv requant epilogue).  The product is a plain f32 multiply
 // (no contraction); rintf rounds ties to even, roundf away from zero.

@@ -2,29 +2,31 @@
 // cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation, fp32 bias and
 // activation, bf16 output rounded to nearest even.
 //
-// The GEMM view is the one of the fp32 kernel (M = output channels, N =
-// output pixels, K = input channels x taps; ncnn "convolution": pad with
-// pad_value, correlate, + bias, activation), but a bf16 MFMA step takes 32
-// K values and each lane supplies 8 consecutive ones, and at bf16 rates the
-// LDS bandwidth is the first limit.  So:
-//   * the tiles are shared by the whole workgroup and every wave owns a
-//     WR x 64 output tile (WR/16 x 4 MFMA fragments; WR = 64 in the wide
-//     configurations), which keeps LDS reads at one 16-byte read per two
-//     MFMAs;
-//   * inside a chunk of CC input channels, K runs tap-major and channel-minor,
-//     and both LDS tiles keep the channels innermost:
-//       weights  [tap][output channel][CC + 8]
-//       patch    [patch position][CC + 8]
-//     so an MFMA operand is one 16-byte LDS read, and the row strides (80 or
-//     144 bytes) put 16 consecutive rows on 16 distinct 16-byte bank groups;
-//   * the copy from global memory (16-byte loads of OIHW weights and of NCHW
-//     rows) transposes into that layout with 2-byte LDS writes, the lanes of
-//     a write walking along output channels (weights) or input channels
-//     (patch) so that the writes spread over the banks.  The next chunk's
-//     loads are in flight while the current one is multiplied out.
+// GEMM view (ncnn "convolution": pad with pad_value, correlate, + bias,
+// activation): M = output channels of a group, N = output pixels, K = input
+// channels x taps.  A bf16 MFMA step takes 32 K values and every lane
+// supplies 8 consecutive ones, so both operands are kept in LDS as 16-byte
+// cells of 8 consecutive input channels:
+//   weights  [tap*G + group-of-8][output channel]      (one cell each)
+//   patch    [group-of-8][patch position]              (one cell each)
+// K runs tap-major inside a chunk of CC = 8*G input channels; an MFMA operand
+// is one 16-byte LDS read and 16 lanes of a read touch 16 consecutive cells.
+//
+// Copy path.  The weights are re-laid once per call (pack kernel below) into
+// exactly the LDS image of each (output-channel tile, channel chunk), so a
+// chunk's weights move with direct global->LDS loads (no registers, no
+// transposition).  The NCHW input is transposed on the fly: a lane loads 8
+// channels x 8 pixels (eight 16-byte row loads), permutes them in registers
+// and writes eight 16-byte cells.  Stride-2 patches keep even and odd columns
+// in separate halves of a row, so a stride-2 read of 16 output pixels is
+// still 16 consecutive cells.  The row and plane strides of the patch are
+// chosen on the host to spread those cell writes over the LDS banks.
+//
+// Pipeline: two LDS stages; the copy of chunk c+1 (DMA and row loads) is in
+// flight while chunk c is multiplied out, one workgroup barrier per chunk.
 // The epilogue adds the bias, applies the activation, rounds to bf16 and
 // writes channel out_off + g*cout_g + co of a buffer with out_total channels
-// (ConcatFusedTail).
+// (ConcatFusedTail), 4 pixels of a row per 8-byte store.
 #include "device_common.h"
 
 namespace conv2d {
@@ -33,34 +35,51 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int BM_, int WM_, int WN_, int NI_, int TW_, int CC_, int KH_, int KW_, int XS_>
+template <int BM_, int WM_, int WN_, int NI_, int TW_, int CC_, int KH_, int KW_, int SD_, int XS_>
 struct BCfg {
-    static constexpr int BM = BM_, WM = WM_, WN = WN_, TW = TW_, CC = CC_, KH = KH_, KW = KW_;
-    static constexpr int KHW = KH_ * KW_;
+    static constexpr int BM = BM_, WM = WM_, WN = WN_, NI = NI_, TW = TW_, CC = CC_, KH = KH_, KW = KW_;
+    static constexpr bool SD = SD_ != 0;               // stride-2 column split
+    static constexpr int XS = XS_;                     // input tasks per thread (upper bound)
+    static constexpr int KHW = KH * KW;
     static constexpr int NW = WM * WN, NT = 64 * NW;   // waves, threads
-    static constexpr int WR = BM / WM;                 // rows of a wave tile
-    static constexpr int MI = WR / 16, NI = NI_;       // MFMA fragments of a wave tile
-    static constexpr int WC = 16 * NI;                 // pixels of a wave tile
-    static constexpr int BN = WC * WN;                 // pixels of the workgroup tile
+    static constexpr int WR = BM / WM, MI = WR / 16;   // rows / row fragments of a wave tile
+    static constexpr int WC = 16 * NI, BN = WC * WN;   // pixels of a wave tile / of the workgroup tile
     static constexpr int TH = BN / TW;
-    static constexpr int CCP = CC + 8;                 // bf16 per LDS row
+    static constexpr int G = CC / 8;                   // 8-channel groups per chunk
     static constexpr int STEPS = (KHW * CC + 31) / 32; // K steps of 32 per chunk
-    static constexpr int KHWP = STEPS * 32 / CC;       // taps incl. the zero padding of the last step
-    static constexpr int RV = CC * KHW / 8;            // 16-byte vectors per weight row and chunk
-    static constexpr int AV = BM * RV;                 // 16-byte weight vectors per chunk
-    static constexpr int AS = (AV + NT - 1) / NT;      // per thread
-    static constexpr int XS = XS_;                     // 16-byte input vectors per thread (upper bound)
-    static constexpr int ALDS = KHWP * BM * CCP;       // bf16 of the weight tile
-    static_assert(CC % 16 == 0 && (CC >= 32 ? CC % 32 == 0 : 32 % CC == 0), "K steps of 32 tile the chunk");
-    static_assert((CC * KHW) % 8 == 0, "whole 16-byte weight vectors");
-    static_assert(WR % 16 == 0 && BN % TW == 0 && TW % 16 == 0, "whole fragments");
+    static constexpr int TGP = 4 * STEPS;              // (tap, group) slots incl. the zero K padding
+    static constexpr int ACELLS = TGP * BM;            // 16-byte cells of a chunk's weight image
+    static constexpr int DMAR = ACELLS / 64;           // 1 KB wave copies per weight image
+    static_assert(CC % 8 == 0 && TGP % G == 0, "K steps tile whole (tap, group) slots");
+    static_assert(ACELLS % 64 == 0, "weight image in whole 1 KB pieces");
+    static_assert(WR % 16 == 0 && TW % 16 == 0 && BN % TW == 0, "whole fragments");
 };
+
+// Input task v of a chunk: 8 channels (group g) x 8 pixels (vector vc) of
+// patch row `row`.  Vectors run fastest, then rows, then groups.
+__host__ __device__ inline void input_task(int v, int nvr, int ph, int& vc, int& row, int& g) {
+    vc = v % nvr;
+    const int rest = v / nvr;
+    row = rest % ph;
+    g = rest / ph;
+}
+
+// Cell of patch column pc inside its row (stride-2 patches: evens, then odds).
+__host__ __device__ inline int col_cell(int pc, int half, bool split) {
+    return split ? (pc & 1) * half + (pc >> 1) : pc;
+}
+
+__device__ __forceinline__ void copy16_to_lds(const uint4* src, uint4* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds((const float*)src, (float*)lds_base, 16, 0, 0);
+#endif
+}
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
-    extern __shared__ __align__(16) uint16_t lds16[];
-    constexpr int BM = C::BM, TW = C::TW, TH = C::TH, CC = C::CC, CCP = C::CCP;
-    constexpr int KHW = C::KHW, KW = C::KW, MI = C::MI, NI = C::NI, RV = C::RV;
+    extern __shared__ __align__(16) uint4 lds[];
+    constexpr int BM = C::BM, TW = C::TW, TH = C::TH, G = C::G;
+    constexpr int KHW = C::KHW, KW = C::KW, MI = C::MI, NI = C::NI, STEPS = C::STEPS;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -81,147 +100,126 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
     const int ho0 = thi * TH, wo0 = twi * TW;
     const int ih0 = ho0 * a.stride_h - a.pad_top;
     const int iw_lo = wo0 * a.stride_w - a.pad_left;      // input column of patch column 0
-    const int span = a.patch_w;                           // patch columns kept in LDS
-    const int PH = a.patch_h;
+    const int PH = a.patch_h, span = a.patch_w;
     const int shift = a.patch_shift;                      // iw_lo minus its 8-aligned floor
     const int nvr = a.patch_stride;                       // 8-pixel vectors per patch row
-    const int xv = CC * PH * nvr;                         // input vectors per chunk
+    const int RS = a.lds_rs, PL = a.lds_plane, HALF = a.col_half;
+    const int scells = C::ACELLS + G * PL;                // cells per stage
     const int HW = a.h * a.w;
 
     const uint16_t* __restrict__ xg = (const uint16_t*)a.xptr +
                                       ((int64_t)n * a.in_total + a.in_off + (int64_t)g * a.cin_g) * HW;
-    const uint16_t* __restrict__ wg = (const uint16_t*)a.wptr + ((int64_t)g * a.cout_g + co0) * a.cin_g * KHW;
+    const uint4* __restrict__ wp = (const uint4*)a.wptr + (int64_t)(g * a.co_tiles + cot) * a.chunks * C::ACELLS;
     const bool vx = a.w % 8 == 0 && ((uintptr_t)a.xptr % 16) == 0;
-    const bool vw = (a.cin_g * KHW) % 8 == 0 && ((uintptr_t)a.wptr % 16) == 0;
     const uint32_t padb = __bfloat16_as_ushort(f32_to_bf16(a.pad_value));
     const uint32_t pad2 = padb | (padb << 16);
 
-    uint16_t* As = lds16;                 // [tap][BM][CCP]
-    uint16_t* Bs = lds16 + C::ALDS;       // [pos][CCP]
-
-    // ---- per-lane input plan: vector i = 8 pixels of one row of one channel,
-    // channels fastest across the lanes ----
-    int xgo[C::XS];    // element offset from the chunk's first channel plane, -1 = outside the image
-    int xpk[C::XS];    // packed (row << 20) | ((patch column of the first pixel + 8) << 8) | channel; -1 = none
+    // ---- per-thread input tasks ----
+    int tcell[C::XS];   // cell (in the patch part of a stage) of the task's row start; -1 = no task
+    int tpc[C::XS];     // patch column of the vector's first pixel
+    int tg8[C::XS];     // first channel of the task's group
+    int trow[C::XS];    // patch row
+    int txo[C::XS];     // element offset of (channel tg8, row, first pixel); -1 = outside the image
 #pragma unroll
     for (int i = 0; i < C::XS; ++i) {
         const int v = tid + C::NT * i;
-        xgo[i] = -1; xpk[i] = -1;
-        if (v < xv) {
-            const int ci = v % CC;
-            const int rest = v / CC;
-            const int row = rest / nvr;
-            const int vc = rest - row * nvr;
+        tcell[i] = -1; tpc[i] = 0; tg8[i] = 0; trow[i] = 0; txo[i] = -1;
+        if (v < G * PH * nvr) {
+            int vc, row, gg;
+            input_task(v, nvr, PH, vc, row, gg);
             const int ih = ih0 + row, iw = iw_lo - shift + 8 * vc;
-            xpk[i] = (row << 20) | ((8 * vc - shift + 8) << 8) | ci;
-            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w) xgo[i] = ci * HW + ih * a.w + iw;
+            tcell[i] = gg * PL + row * RS;
+            tpc[i] = 8 * vc - shift;
+            tg8[i] = 8 * gg;
+            trow[i] = row;
+            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w) txo[i] = 8 * gg * HW + ih * a.w + iw;
         }
     }
-    auto pk_ci = [](int pk) { return pk & 255; };
-    auto pk_pc = [](int pk) { return ((pk >> 8) & 4095) - 8; };
-    auto pk_row = [](int pk) { return pk >> 20; };
-    // Zero the padding taps of the weight tile once (K steps past the last tap).
-    if constexpr (C::KHWP > KHW) {
-        for (int e = tid; e < (C::KHWP - KHW) * BM * CCP; e += C::NT) As[KHW * BM * CCP + e] = 0;
-    }
 
-    uint4 ar[C::AS];
-    uint4 xr[C::XS];
-
-    // Global -> registers for the channels [c0, c0 + CC) of the group.
-    // Weight vector i: output channel v % BM (fastest), 8 elements 8*(v / BM)..
-    // of the channel chunk's OIHW row.
-    auto load = [&](int c0) __attribute__((always_inline)) {
+    uint4 xr[C::XS][8];
+    // Global -> registers: channels c0 + tg8 .. +7 of each task.
+    auto load_x = [&](int c0) __attribute__((always_inline)) {
         const int cl = a.cin_g - c0;
-        const uint16_t* __restrict__ wc = wg + (int64_t)c0 * KHW;
-#pragma unroll
-        for (int i = 0; i < C::AS; ++i) {
-            const int v = tid + C::NT * i;
-            const int co = v % BM, j = v / BM;
-            uint4 r = make_uint4(0, 0, 0, 0);
-            if (v < C::AV && co0 + co < a.cout_g) {
-                const uint16_t* src = wc + (int64_t)co * a.cin_g * KHW + 8 * j;
-                if (vw && cl >= CC) {
-                    r = *(const uint4*)src;
-                } else {
-                    uint32_t e[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) e[t] = (8 * j + t) / KHW < cl ? src[t] : 0u;
-                    r = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
-                }
-            }
-            ar[i] = r;
-        }
         const uint16_t* __restrict__ xc = xg + (int64_t)c0 * HW;
 #pragma unroll
         for (int i = 0; i < C::XS; ++i) {
-            uint4 r = make_uint4(0, 0, 0, 0);
-            if (xpk[i] >= 0 && pk_ci(xpk[i]) < cl) {
-                if (vx) {
-                    r = xgo[i] >= 0 ? *(const uint4*)(xc + xgo[i]) : make_uint4(pad2, pad2, pad2, pad2);
-                } else {
-                    const int ih = ih0 + pk_row(xpk[i]);
-                    const int iw0 = iw_lo + pk_pc(xpk[i]);
-                    uint32_t e[8];
+            if (tcell[i] < 0) continue;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const int iw = iw0 + t;
-                        e[t] = ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
-                                   ? (uint32_t)xc[pk_ci(xpk[i]) * HW + ih * a.w + iw]
-                                   : padb;
+            for (int t = 0; t < 8; ++t) {
+                uint4 r = make_uint4(0, 0, 0, 0);
+                if (tg8[i] + t < cl) {
+                    if (vx) {
+                        r = txo[i] >= 0 ? *(const uint4*)(xc + txo[i] + t * HW) : make_uint4(pad2, pad2, pad2, pad2);
+                    } else {
+                        const int ih = ih0 + trow[i];
+                        const int iw0 = iw_lo + tpc[i];
+                        const uint16_t* plane = xc + (int64_t)(tg8[i] + t) * HW;
+                        uint32_t e[8];
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const int iw = iw0 + p;
+                            e[p] = ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
+                                       ? (uint32_t)plane[ih * a.w + iw]
+                                       : padb;
+                        }
+                        r = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
                     }
-                    r = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
                 }
+                xr[i][t] = r;
             }
-            xr[i] = r;
         }
     };
-
-    // Registers -> LDS, transposing to channel-innermost rows.
-    auto store = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < C::AS; ++i) {
-            const int v = tid + C::NT * i;
-            if (v < C::AV) {
-                const int co = v % BM, j = v / BM;
-                if constexpr (KHW == 1) {
-                    *(uint4*)(As + co * CCP + 8 * j) = ar[i];
-                } else {
-                    const uint32_t w4[4] = {ar[i].x, ar[i].y, ar[i].z, ar[i].w};
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const int e = 8 * j + t;          // OIHW order within the row: e = ci*KHW + rs
-                        const int ci = e / KHW, rs = e - (e / KHW) * KHW;
-                        As[(rs * BM + co) * CCP + ci] = (uint16_t)(w4[t >> 1] >> (16 * (t & 1)));
-                    }
-                }
-            }
-        }
+    // Registers -> LDS: 8 channels x 8 pixels become 8 cells of 8 channels.
+    auto store_x = [&](uint4* bst) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::XS; ++i) {
-            if (xpk[i] >= 0) {
-                const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-                const int pc0 = pk_pc(xpk[i]);
-                uint16_t* dst = Bs + (pk_row(xpk[i]) * span + pc0) * CCP + pk_ci(xpk[i]);
+            if (tcell[i] < 0) continue;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int pc = pc0 + t;
-                    if (pc >= 0 && pc < span) dst[t * CCP] = (uint16_t)(w4[t >> 1] >> (16 * (t & 1)));
+            for (int p = 0; p < 8; ++p) {
+                const int pc = tpc[i] + p;
+                uint32_t d[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint4 lo = xr[i][2 * k], hi = xr[i][2 * k + 1];
+                    const uint32_t wl = (p >> 1) == 0 ? lo.x : (p >> 1) == 1 ? lo.y : (p >> 1) == 2 ? lo.z : lo.w;
+                    const uint32_t wh = (p >> 1) == 0 ? hi.x : (p >> 1) == 1 ? hi.y : (p >> 1) == 2 ? hi.z : hi.w;
+                    d[k] = (p & 1) ? ((wl >> 16) | (wh & 0xffff0000u)) : ((wl & 0xffffu) | (wh << 16));
                 }
+                if (pc >= 0 && pc < span) bst[tcell[i] + col_cell(pc, HALF, C::SD)] = make_uint4(d[0], d[1], d[2], d[3]);
             }
         }
     };
+    // Weight image of chunk kc -> LDS (1 KB per wave instruction).
+    auto dma_w = [&](int kc, uint4* ast) __attribute__((always_inline)) {
+        const uint4* src = wp + (int64_t)kc * C::ACELLS + lane;
+#pragma unroll
+        for (int r = 0; r < C::DMAR; r += C::NW)
+            if (r + wave < C::DMAR) copy16_to_lds(src + (r + wave) * 64, ast + (r + wave) * 64);
+    };
 
-    // Operand addresses.  Chunk K index k = tap*CC + channel; step s takes
-    // k in [32s, 32s + 32) and lane group q = lane/16 supplies k = 32s + 8q..+7,
-    // i.e. tap (32s + 8q) / CC, channels (32s + 8q) % CC.. of that tap.
-    // A: row co = wm*WR + mi*16 + lane%16.  B: pixel j = wn*WC + ni*16 + lane%16.
-    const int a_lane = (wm * C::WR + (lane & 15)) * CCP;
+    // ---- operand offsets (cells) ----
+    // Step s, lane group q = lane/16 supplies K slot tg = 4s + q: tap tg / G,
+    // channel group tg % G.  A row co = wm*WR + mi*16 + lane%16; B pixel
+    // j = wn*WC + ni*16 + lane%16.
+    const int q = lane >> 4, l16 = lane & 15;
+    const int a_lane = q * BM + wm * C::WR + l16;
     int b_lane[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-        const int j = wn * C::WC + ni * 16 + (lane & 15);
-        b_lane[ni] = ((j / TW) * a.stride_h * span + (j % TW) * a.stride_w) * CCP;
+        const int j = wn * C::WC + ni * 16 + l16;
+        const int jr = j / TW, jc = j % TW;
+        b_lane[ni] = C::SD ? jr * a.stride_h * RS + jc : jr * a.stride_h * RS + jc * a.stride_w;
+    }
+    int b_step[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int tg = 4 * s + q;
+        int tap = tg / G;
+        const int gg = tg - (tg / G) * G;
+        if (tap >= KHW) tap = 0;     // K padding: zero weights, finite inputs of tap 0
+        const int r = tap / KW, sc = tap - (tap / KW) * KW;
+        const int cdx = sc * a.dilation_w;
+        b_step[s] = gg * PL + r * a.dilation_h * RS + (C::SD ? (cdx & 1) * HALF + (cdx >> 1) : cdx);
     }
 
     f32x4 acc[MI][NI];
@@ -230,119 +228,197 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto fetch = [&](int s, int al, const int (&bl)[NI], bf16x8 (&av)[MI], bf16x8 (&bv)[NI])
-                     __attribute__((always_inline)) {
-        const int k = 32 * s + 8 * (lane >> 4);
-        const int rs = k / CC, kc = k % CC;
-        // Padding taps (rs >= KHW) have zero weights; read tap 0's finite inputs.
-        const int rv = rs < KHW ? rs : 0;
-        const int r = rv / KW, sc = rv % KW;
-        const int boff = (r * a.dilation_h * span + sc * a.dilation_w) * CCP + kc;
+    auto fetch = [&](const uint4* st, int s, bf16x8 (&av)[MI], bf16x8 (&bv)[NI]) __attribute__((always_inline)) {
+        const uint4* as = st + a_lane + 4 * s * BM;
+        const uint4* bs = st + C::ACELLS + b_step[s];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) av[mi] = *(const bf16x8*)(As + (rs * BM) * CCP + al + mi * 16 * CCP + kc);
+        for (int mi = 0; mi < MI; ++mi) av[mi] = __builtin_bit_cast(bf16x8, as[16 * mi]);
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bv[ni] = *(const bf16x8*)(Bs + bl[ni] + boff);
+        for (int ni = 0; ni < NI; ++ni) bv[ni] = __builtin_bit_cast(bf16x8, bs[b_lane[ni]]);
     };
     auto mfmas = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NI]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[ni], av[mi], acc[mi][ni], 0, 0, 0);
     };
-
-    // ---- main loop: one LDS stage, next chunk prefetched into registers ----
-    const int nch = a.chunks;
-    load(0);
-    store();
-    __syncthreads();
-    for (int kc = 0; kc < nch; ++kc) {
-        if (kc + 1 < nch) load((kc + 1) * CC);
-        // Operand offsets are re-derived every chunk from copies the compiler
-        // cannot see through, so it does not keep all the steps' addresses
-        // live across the loop.
-        int al = a_lane, bl[NI];
-        asm volatile("" : "+v"(al));
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            bl[ni] = b_lane[ni];
-            asm volatile("" : "+v"(bl[ni]));
-        }
+    auto compute = [&](const uint4* st) __attribute__((always_inline)) {
         bf16x8 a0[MI], b0[NI], a1[MI], b1[NI];
-        fetch(0, al, bl, a0, b0);
+        fetch(st, 0, a0, b0);
 #pragma unroll
-        for (int s = 0; s < C::STEPS; ++s) {
-            if (s + 1 < C::STEPS) {
-                if (s & 1) fetch(s + 1, al, bl, a0, b0);
-                else fetch(s + 1, al, bl, a1, b1);
+        for (int s = 0; s < STEPS; ++s) {
+            if (s + 1 < STEPS) {
+                if (s & 1) fetch(st, s + 1, a0, b0);
+                else fetch(st, s + 1, a1, b1);
             }
             // Keep the fetches of step s+1 ahead of the MFMAs of step s.
             __builtin_amdgcn_sched_barrier(0);
             if (s & 1) mfmas(a1, b1);
             else mfmas(a0, b0);
         }
-        __syncthreads();
-        if (kc + 1 < nch) {
-            store();
-            __syncthreads();
+    };
+
+    // ---- main loop: two stages, chunk c+1 copied while chunk c computes ----
+    const int nch = a.chunks;
+    uint4* const st0 = lds;
+    uint4* const st1 = lds + scells;
+    dma_w(0, st0);
+    load_x(0);
+    store_x(st0 + C::ACELLS);
+    if (nch > 1) {
+        dma_w(1, st1);
+        load_x(C::CC);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        uint4* cur = (c & 1) ? st1 : st0;
+        uint4* nxt = (c & 1) ? st0 : st1;
+        compute(cur);
+        if (c + 1 < nch) {
+            __builtin_amdgcn_s_waitcnt(0);   // chunk c+1: weight image and input rows have landed
+            store_x(nxt + C::ACELLS);
+        }
+        __syncthreads();                     // stage cur is free, stage nxt is complete
+        if (c + 2 < nch) {
+            dma_w(c + 2, cur);
+            load_x((c + 2) * C::CC);
         }
     }
 
     // ---- epilogue: bias, activation, bf16, store ----
-    __hip_bfloat16* __restrict__ yg = (__hip_bfloat16*)a.yptr;
+    // The workgroup's BM biases and PReLU slopes go through LDS (free after
+    // the last barrier), one global load per channel instead of one per output.
+    float* eb = (float*)lds;
+    float* es = eb + BM;
+    for (int i = tid; i < BM; i += C::NT) {
+        const int co = co0 + i;
+        const int cg = g * a.cout_g + (co < a.cout_g ? co : a.cout_g - 1);
+        eb[i] = a.bias ? a.bias[cg] : 0.0f;
+        es[i] = a.act == CONV_ACT_PRELU ? a.slope[a.slope_count == 1 ? 0 : cg] : 0.0f;
+    }
+    __syncthreads();
+    // The MFMA's first operand is the pixel fragment, so lane (q, l16) holds
+    // output channel mi*16 + l16 at the 4 consecutive pixels ni*16 + 4q ..+3
+    // of one output row: one 8-byte store where the row allows it.
+    uint16_t* __restrict__ yg = (uint16_t*)a.yptr;
     const int64_t out_plane = (int64_t)a.ho * a.wo;
+    const bool vy = a.wo % 4 == 0 && ((uintptr_t)a.yptr % 8) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+        const int col = wm * C::WR + mi * 16 + l16;
+        const int co = co0 + col;
+        if (co >= a.cout_g) continue;
+        const int cg = g * a.cout_g + co;
+        const float bb = eb[col], ss = es[col];
+        uint16_t* yc = yg + ((int64_t)n * a.out_total + a.out_off + cg) * out_plane;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-            const int j = wn * C::WC + ni * 16 + (lane & 15);
+            const int j = wn * C::WC + ni * 16 + 4 * q;
             const int ho = ho0 + j / TW, wo = wo0 + j % TW;
-            if (ho < a.ho && wo < a.wo) {
+            if (ho >= a.ho) continue;
+            uint32_t h[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int co = co0 + wm * C::WR + mi * 16 + (lane >> 4) * 4 + v;
-                    if (co < a.cout_g) {
-                        const int cg = g * a.cout_g + co;
-                        yg[((int64_t)n * a.out_total + a.out_off + cg) * out_plane + (int64_t)ho * a.wo + wo] =
-                            f32_to_bf16(bias_act(a, acc[mi][ni][v], cg));
-                    }
-                }
+            for (int v = 0; v < 4; ++v)
+                h[v] = __bfloat16_as_ushort(f32_to_bf16(apply_act(a, acc[mi][ni][v] + bb, ss)));
+            uint16_t* dst = yc + (int64_t)ho * a.wo + wo;
+            if (vy && wo + 3 < a.wo) {
+                *(uint2*)dst = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (wo + v < a.wo) dst[v] = (uint16_t)h[v];
             }
         }
+    }
+}
+
+// Weight re-layout: OIHW bf16 -> per (group, output-channel tile, chunk) the
+// LDS image [tap*G + group-of-8][BM][8 channels], zero where the tap, the
+// output channel or the input channel lies past the filter.
+__global__ __launch_bounds__(256) void pack_weights_bf16(const uint16_t* __restrict__ w, uint4* __restrict__ out,
+                                                         int64_t total, int bm, int tgp, int gq, int cc, int khw,
+                                                         int chunks, int co_tiles, int cin_g, int cout_g) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    int64_t rest = idx;
+    const int co = rest % bm; rest /= bm;
+    const int tg = rest % tgp; rest /= tgp;
+    const int kc = rest % chunks; rest /= chunks;
+    const int cot = rest % co_tiles;
+    const int grp = rest / co_tiles;
+    const int tap = tg / gq, g8 = tg % gq;
+    const int cog = cot * bm + co;
+    uint32_t e[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int ci = kc * cc + g8 * 8 + t;
+        e[t] = (tap < khw && cog < cout_g && ci < cin_g)
+                   ? (uint32_t)w[(((int64_t)grp * cout_g + cog) * cin_g + ci) * khw + tap]
+                   : 0u;
+    }
+    out[idx] = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
 }
 
 // ------------------------------------------------------------ configs ---
 
 struct CfgInfo {
-    int bm, bn, tw, cc, kh, kw, xs, nt, alds;
+    int bm, bn, tw, cc, kh, kw, sd, xs, nt, tgp;
     const void* fn;
 };
 
 template <class C>
 CfgInfo info() {
-    return CfgInfo{C::BM, C::BN, C::TW, C::CC, C::KH, C::KW, C::XS, C::NT, C::ALDS,
+    return CfgInfo{C::BM, C::BN, C::TW, C::CC, C::KH, C::KW, C::SD ? 1 : 0, C::XS, C::NT, C::TGP,
                    (const void*)igemm_bf16_kernel<C>};
 }
 
-// Four waves (one per SIMD, up to 512 registers each) in a 2 x 2 grid of
-// 64 x 128 or 64 x 64 wave tiles.
-//                      BM WM WN NI   TW  CC KH KW  XS
-using B3_128x128 = BCfg<128, 2, 2, 4,  16, 16, 3, 3,  6>;   // 3x3 any stride: 8 x 16 output pixels
-using B3_32x256  = BCfg<32,  1, 4, 4,  16, 16, 3, 3,  6>;   // few output channels per group
-using B1_128x256 = BCfg<128, 2, 2, 8, 256, 64, 1, 1,  8>;   // flattened 1x1
-using B1_32x256  = BCfg<32,  1, 4, 4, 256, 64, 1, 1,  8>;
+// Four waves (one per SIMD, up to 512 registers each).
+//                   BM WM WN NI   TW  CC KH KW SD XS
+using B3_128 = BCfg<128, 2, 2, 8,  16, 16, 3, 3, 0, 2>;   // 3x3 stride 1: 16 x 16 output pixels
+using B3S_128 = BCfg<128, 2, 2, 8, 16, 16, 3, 3, 1, 2>;   // 3x3 stride 2 (column split)
+using B3_32 = BCfg<32, 1, 4, 4,  16, 16, 3, 3, 0, 2>;     // 3x3, few output channels per group
+using B3_16 = BCfg<16, 1, 4, 4,  16, 8, 3, 3, 0, 2>;      // 3x3, <= 16 output and <= 8 input channels per group
+using B1_128 = BCfg<128, 2, 2, 8, 256, 64, 1, 1, 0, 1>;   // flattened 1x1
+using B1_32 = BCfg<32, 1, 4, 4, 256, 64, 1, 1, 0, 1>;
 
-enum { C3_128x128, C3_32x256, C1_128x256, C1_32x256, NCFG };
+enum { C3_128, C3S_128, C3_32, C3_16, C1_128, C1_32, NCFG };
 
 const CfgInfo& cfg(int i) {
-    static const CfgInfo t[NCFG] = {info<B3_128x128>(), info<B3_32x256>(), info<B1_128x256>(),
-                                    info<B1_32x256>()};
+    static const CfgInfo t[NCFG] = {info<B3_128>(), info<B3S_128>(), info<B3_32>(),
+                                    info<B3_16>(),  info<B1_128>(),  info<B1_32>()};
     return t[i];
 }
 
 struct Geom {
-    int ph, span, shift, nvr;
+    int ph, span, shift, nvr, half, rs, plane;
 };
+
+// LDS cell-write cost of one chunk's input tasks for row stride rs and
+// plane stride pl: per 16-lane pass of a 16-byte write, the largest number
+// of lanes that fall on the same 16-byte bank group.
+int64_t write_cost(const Geom& G, const CfgInfo& c, int rs, int pl) {
+    const int tasks = (c.cc / 8) * G.ph * G.nvr;
+    int64_t cost = 0;
+    for (int base = 0; base < tasks; base += 16) {
+        for (int p = 0; p < 8; ++p) {
+            int hits[16] = {0};
+            int worst = 0;
+            for (int l = 0; l < 16 && base + l < tasks; ++l) {
+                int vc, row, gg;
+                input_task(base + l, G.nvr, G.ph, vc, row, gg);
+                const int pc = 8 * vc - G.shift + p;
+                if (pc < 0 || pc >= G.span) continue;
+                const int cell = gg * pl + row * rs + col_cell(pc, G.half, c.sd != 0);
+                const int h = ++hits[cell & 15];
+                worst = h > worst ? h : worst;
+            }
+            cost += worst;
+        }
+    }
+    return cost;
+}
 
 Geom geom(const conv2d_params_t& p, const CfgInfo& c, bool flat) {
     Geom G;
@@ -355,7 +431,27 @@ Geom geom(const conv2d_params_t& p, const CfgInfo& c, bool flat) {
         G.shift = ((-p.pad_left) % 8 + 8) % 8;
         G.nvr = (G.shift + G.span + 7) / 8;
     }
+    G.half = (G.span + 1) / 2;
+    const int rs0 = c.sd ? 2 * G.half : G.span;
+    // Smallest write cost over row strides rs0..rs0+15 and plane padding 0..15.
+    int64_t best = -1;
+    G.rs = rs0;
+    G.plane = G.ph * rs0;
+    for (int rs = rs0; rs < rs0 + 16; ++rs)
+        for (int pad = 0; pad < (c.cc > 8 ? 16 : 1); ++pad) {
+            const int pl = G.ph * rs + pad;
+            const int64_t cost = write_cost(G, c, rs, pl);
+            if (best < 0 || cost < best || (cost == best && pl < G.plane)) {
+                best = cost; G.rs = rs; G.plane = pl;
+            }
+        }
     return G;
+}
+
+int64_t wpack_cells(const Desc& d, const CfgInfo& c) {
+    const int64_t co_tiles = (d.cout_g + c.bm - 1) / c.bm;
+    const int64_t chunks = (d.cin_g + c.cc - 1) / c.cc;
+    return (int64_t)d.p.groups * co_tiles * chunks * c.tgp * c.bm;
 }
 
 }  // namespace
@@ -367,27 +463,33 @@ bool plan_igemm_bf16(Desc& d) {
                       p.pad_left == 0 && p.pad_bottom == 0 && p.pad_right == 0;
     int cands[3];
     int nc = 0;
-    const bool small_m = d.cout_g <= 32;
-    if (is3) {
-        if (small_m) cands[nc++] = C3_32x256;
-        cands[nc++] = C3_128x128;
+    if (is3 && p.stride_h == p.stride_w) {
+        if (p.stride_w == 2) {
+            cands[nc++] = C3S_128;
+        } else if (p.stride_w == 1) {
+            if (d.cout_g <= 16 && d.cin_g <= 8) cands[nc++] = C3_16;
+            if (d.cout_g <= 32) cands[nc++] = C3_32;
+            cands[nc++] = C3_128;
+        }
     } else if (flat) {
-        cands[nc++] = small_m ? C1_32x256 : C1_128x256;
+        cands[nc++] = d.cout_g <= 32 ? C1_32 : C1_128;
     }
     for (int k = 0; k < nc; ++k) {
         const CfgInfo& c = cfg(cands[k]);
         const Geom G = geom(p, c, flat);
-        if (c.cc * G.ph * G.nvr > c.xs * c.nt) continue;                    // input vectors per thread
-        if (G.ph >= 2048 || 8 * G.nvr + 8 >= 4096 || c.cc > 256) continue;  // packed vector plan fields
-        const int lds = 2 * (c.alds + G.ph * G.span * (c.cc + 8));
-        if (lds > 160 * 1024) continue;
+        if ((c.cc / 8) * G.ph * G.nvr > c.xs * c.nt) continue;         // input tasks per thread
+        const int64_t stage = 16 * ((int64_t)c.tgp * c.bm + (int64_t)(c.cc / 8) * G.plane);
+        if (2 * stage > 160 * 1024) continue;
         if ((int64_t)c.cc * p.h * p.w >= INT32_MAX / 2) continue;
-        if ((int64_t)c.bm * d.cin_g * p.k_h * p.k_w >= INT32_MAX / 2) continue;
+        if (wpack_cells(d, c) * 16 >= ((int64_t)1 << 40)) continue;
         d.cfg = cands[k];
         d.flatten_1x1 = flat;
         d.tile_w = c.tw;
         d.tile_h = c.bn / c.tw;
-        d.lds_bytes = lds;
+        d.lds_bytes = (int32_t)(2 * stage);
+        d.wpack_bytes = wpack_cells(d, c) * 16;
+        d.g_ph = G.ph; d.g_span = G.span; d.g_shift = G.shift; d.g_nvr = G.nvr;
+        d.g_rs = G.rs; d.g_plane = G.plane; d.g_half = G.half;
         return true;
     }
     return false;
@@ -396,16 +498,18 @@ bool plan_igemm_bf16(Desc& d) {
 hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s) {
     const CfgInfo& c = cfg(d.cfg);
     const conv2d_params_t& p = d.p;
-    const Geom G = geom(p, c, d.flatten_1x1);
     if (d.flatten_1x1) {
         a.h = 1; a.w = p.h * p.w; a.ho = 1; a.wo = d.ho * d.wo;
     }
     a.tiles_h = (a.ho + d.tile_h - 1) / d.tile_h;
     a.tiles_w = (a.wo + d.tile_w - 1) / d.tile_w;
-    a.patch_h = G.ph;
-    a.patch_w = G.span;
-    a.patch_shift = G.shift;
-    a.patch_stride = G.nvr;
+    a.patch_h = d.g_ph;
+    a.patch_w = d.g_span;
+    a.patch_shift = d.g_shift;
+    a.patch_stride = d.g_nvr;
+    a.lds_rs = d.g_rs;
+    a.lds_plane = d.g_plane;
+    a.col_half = d.g_half;
     a.co_tiles = (d.cout_g + c.bm - 1) / c.bm;
     a.chunks = (d.cin_g + c.cc - 1) / c.cc;
     a.dv_co_tiles = make_divu32((uint32_t)a.co_tiles);
@@ -416,8 +520,24 @@ hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s) {
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     a.num_blocks = (uint32_t)blocks;
+    if (!d.wpack || d.wpack_bytes != wpack_cells(d, c) * 16) return hipErrorInvalidValue;
+
+    // 1) weights -> per-chunk LDS images
+    const int64_t total = d.wpack_bytes / 16;
+    const void* w_src = a.wptr;
+    uint4* pk = (uint4*)d.wpack;
+    int64_t tot = total;
+    int bm = c.bm, tgp = c.tgp, gq = c.cc / 8, cc = c.cc, khw = p.k_h * p.k_w, chunks = a.chunks,
+        co_tiles = a.co_tiles, cin_g = d.cin_g, cout_g = d.cout_g;
+    void* pargs[] = {&w_src, &pk, &tot, &bm, &tgp, &gq, &cc, &khw, &chunks, &co_tiles, &cin_g, &cout_g};
+    hipError_t e = hipLaunchKernel((const void*)pack_weights_bf16, dim3((uint32_t)((total + 255) / 256)), dim3(256),
+                                   pargs, 0, s);
+    if (e != hipSuccess) return e;
+
+    // 2) the convolution
+    a.wptr = d.wpack;
     if (d.lds_bytes > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, d.lds_bytes);
+        e = hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, d.lds_bytes);
         if (e != hipSuccess) return e;
     }
     void* args[] = {&a};

@@ -26,11 +26,19 @@
  *   Output channel co belongs to group g = co / (c_out/groups) and reads input
  *   channels [g*c_in/groups, (g+1)*c_in/groups).
  *
- * Ownership: the caller allocates and owns every device buffer.  No entry
- * point allocates device memory; forward calls launch kernels asynchronously
- * on the caller's HIP stream and return.  Descriptors are host objects owned
- * by the library from conv2d_desc_create until conv2d_desc_destroy; they are
- * immutable after creation and may be shared across threads.
+ * Ownership: the caller allocates and owns every input and output buffer;
+ * forward calls launch kernels asynchronously on the caller's HIP stream and
+ * return, and allocate nothing.  Descriptors are owned by the library from
+ * conv2d_desc_create until conv2d_desc_destroy and are immutable after
+ * creation.  One exception to "no library device memory": a BF16 descriptor
+ * whose kernel is the implicit GEMM (any BF16 dense or grouped convolution
+ * that is not depthwise; conv2d_desc_kernel_name starts with "igemm_bf16")
+ * allocates, at creation and on the current device, a buffer for the weights
+ * in the kernel's layout, freed by conv2d_desc_destroy.  Every forward call
+ * refills it from w before the convolution reads it, so forward calls that
+ * use one such descriptor must be ordered (one stream, or events); calls on
+ * other descriptors are independent.  Such a descriptor must be used with the
+ * device it was created on (INVALID_ARG otherwise).
  *
  * Errors: every call returns a conv_status_t and never aborts; no C++
  * exception crosses the ABI.  conv2d_last_error() returns a thread-local
@@ -120,7 +128,9 @@ CONV2D_API void conv2d_params_init(conv2d_params_t* p);
  *   INCOMPATIBLE_SHAPES   groups not dividing c_in and c_out; slope count not
  *                         1 or c_out; channel offset + count beyond the total
  *   UNSUPPORTED           I8 with pad_value != 0 or an activation other than
- *                         NONE/RELU; tensors beyond 2^31 elements */
+ *                         NONE/RELU; tensors beyond 2^31 elements
+ *   HIP                   BF16 implicit-GEMM descriptor: no current device,
+ *                         or its packed-weight buffer could not be allocated */
 CONV2D_API conv_status_t conv2d_desc_create(const conv2d_params_t* p, conv2d_desc_t* out);
 
 /* Release a descriptor (null is allowed). */
