@@ -22,8 +22,9 @@
 // still 16 consecutive cells.  The row and plane strides of the patch are
 // chosen on the host to spread those cell writes over the LDS banks.
 //
-// Pipeline: two LDS stages; the copy of chunk c+1 (DMA and row loads) is in
-// flight while chunk c is multiplied out, one workgroup barrier per chunk.
+// Pipeline: two LDS stages; the copy instructions of chunk c+1 (DMA and row
+// loads) are interleaved with the MFMAs of chunk c, then its rows are
+// transposed into the free stage; one workgroup barrier per chunk.
 // The epilogue adds the bias, applies the activation, rounds to bf16 and
 // writes channel out_off + g*cout_g + co of a buffer with out_total channels
 // (ConcatFusedTail), 4 pixels of a row per 8-byte store.
@@ -50,6 +51,10 @@ struct BCfg {
     static constexpr int TGP = 4 * STEPS;              // (tap, group) slots incl. the zero K padding
     static constexpr int ACELLS = TGP * BM;            // 16-byte cells of a chunk's weight image
     static constexpr int DMAR = ACELLS / 64;           // 1 KB wave copies per weight image
+    // One wave per SIMD: double-buffer the MFMA operands and spread the copy
+    // instructions over the MFMAs.  Two waves per SIMD: the other wave covers
+    // those stalls, and the registers are needed elsewhere.
+    static constexpr bool PIPE = NW <= 4;
     static_assert(CC % 8 == 0 && TGP % G == 0, "K steps tile whole (tap, group) slots");
     static_assert(ACELLS % 64 == 0, "weight image in whole 1 KB pieces");
     static_assert(WR % 16 == 0 && TW % 16 == 0 && BN % TW == 0, "whole fragments");
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
     int tpc[C::XS];     // patch column of the vector's first pixel
     int tg8[C::XS];     // first channel of the task's group
     int trow[C::XS];    // patch row
-    int txo[C::XS];     // element offset of (channel tg8, row, first pixel); -1 = outside the image
+    int txo[C::XS];     // offset of the vector's first pixel in a channel plane; -1 = outside the image
 #pragma unroll
     for (int i = 0; i < C::XS; ++i) {
         const int v = tid + C::NT * i;
@@ -132,42 +137,34 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
             tpc[i] = 8 * vc - shift;
             tg8[i] = 8 * gg;
             trow[i] = row;
-            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w) txo[i] = 8 * gg * HW + ih * a.w + iw;
+            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w) txo[i] = ih * a.w + iw;
         }
     }
 
     uint4 xr[C::XS][8];
-    // Global -> registers: channels c0 + tg8 .. +7 of each task.
-    auto load_x = [&](int c0) __attribute__((always_inline)) {
-        const int cl = a.cin_g - c0;
-        const uint16_t* __restrict__ xc = xg + (int64_t)c0 * HW;
+    // Global -> register: channel c0 + tg8 + t of input task i (8 pixels).
+    auto load_op = [&](int i, int t, int c0) __attribute__((always_inline)) {
+        if (tcell[i] < 0) return;
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (tg8[i] + t < a.cin_g - c0) {
+            const uint16_t* __restrict__ plane = xg + (int64_t)(c0 + tg8[i] + t) * HW;
+            if (vx) {
+                r = txo[i] >= 0 ? *(const uint4*)(plane + txo[i]) : make_uint4(pad2, pad2, pad2, pad2);
+            } else {
+                const int ih = ih0 + trow[i];
+                const int iw0 = iw_lo + tpc[i];
+                uint32_t e[8];
 #pragma unroll
-        for (int i = 0; i < C::XS; ++i) {
-            if (tcell[i] < 0) continue;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                uint4 r = make_uint4(0, 0, 0, 0);
-                if (tg8[i] + t < cl) {
-                    if (vx) {
-                        r = txo[i] >= 0 ? *(const uint4*)(xc + txo[i] + t * HW) : make_uint4(pad2, pad2, pad2, pad2);
-                    } else {
-                        const int ih = ih0 + trow[i];
-                        const int iw0 = iw_lo + tpc[i];
-                        const uint16_t* plane = xc + (int64_t)(tg8[i] + t) * HW;
-                        uint32_t e[8];
-#pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-                            const int iw = iw0 + p;
-                            e[p] = ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
-                                       ? (uint32_t)plane[ih * a.w + iw]
-                                       : padb;
-                        }
-                        r = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
-                    }
+                for (int p = 0; p < 8; ++p) {
+                    const int iw = iw0 + p;
+                    e[p] = ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
+                               ? (uint32_t)plane[ih * a.w + iw]
+                               : padb;
                 }
-                xr[i][t] = r;
+                r = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
             }
         }
+        xr[i][t] = r;
     };
     // Registers -> LDS: 8 channels x 8 pixels become 8 cells of 8 channels.
     auto store_x = [&](uint4* bst) __attribute__((always_inline)) {
@@ -189,12 +186,17 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
             }
         }
     };
-    // Weight image of chunk kc -> LDS (1 KB per wave instruction).
-    auto dma_w = [&](int kc, uint4* ast) __attribute__((always_inline)) {
-        const uint4* src = wp + (int64_t)kc * C::ACELLS + lane;
-#pragma unroll
-        for (int r = 0; r < C::DMAR; r += C::NW)
-            if (r + wave < C::DMAR) copy16_to_lds(src + (r + wave) * 64, ast + (r + wave) * 64);
+    // Weight image of chunk kc -> LDS: the wave's k-th 1 KB piece.
+    constexpr int ND = (C::DMAR + C::NW - 1) / C::NW;    // DMA pieces per wave
+    constexpr int NOPS = ND + C::XS * 8;                  // copy instructions per wave and chunk
+    auto dma_op = [&](int k, int kc, uint4* ast) __attribute__((always_inline)) {
+        const int r = wave + C::NW * k;
+        if (r < C::DMAR) copy16_to_lds(wp + (int64_t)kc * C::ACELLS + r * 64 + lane, ast + r * 64);
+    };
+    // Copy instruction k of chunk kc: DMA pieces first, then the input loads.
+    auto copy_op = [&](int k, int kc, uint4* ast) __attribute__((always_inline)) {
+        if (k < ND) dma_op(k, kc, ast);
+        else load_op((k - ND) / 8, (k - ND) % 8, kc * C::CC);
     };
 
     // ---- operand offsets (cells) ----
@@ -236,14 +238,33 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) bv[ni] = __builtin_bit_cast(bf16x8, bs[b_lane[ni]]);
     };
-    auto mfmas = [&](const bf16x8 (&av)[MI], const bf16x8 (&bv)[NI]) __attribute__((always_inline)) {
+    // Chunk from stage st.  With `copy`, the copy instructions of chunk kn
+    // (DMA into stage nst, input rows into registers) are spread over the
+    // MFMAs of the first half of the steps, so the memory pipe drains while
+    // the matrix cores run.
+    auto compute = [&](const uint4* st, bool copy, int kn, uint4* nst) __attribute__((always_inline)) {
+        constexpr int SP = STEPS > 1 ? (STEPS + 1) / 2 : 1;
+        constexpr int SLOTS = SP * MI * NI;                      // MFMAs that may carry copy instructions
+        constexpr int PER = (NOPS + SLOTS - 1) / SLOTS;          // copy instructions per carrying MFMA
+        constexpr int NGRP = (NOPS + PER - 1) / PER;
+        constexpr int STRIDE = SLOTS / NGRP;
+        if constexpr (!C::PIPE) {
+            if (copy) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+                for (int k = 0; k < NOPS; ++k) copy_op(k, kn, nst);
+            }
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[ni], av[mi], acc[mi][ni], 0, 0, 0);
-    };
-    auto compute = [&](const uint4* st) __attribute__((always_inline)) {
+            for (int s = 0; s < STEPS; ++s) {
+                bf16x8 av[MI], bv[NI];
+                fetch(st, s, av, bv);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[ni], av[mi], acc[mi][ni], 0, 0, 0);
+            }
+            return;
+        }
         bf16x8 a0[MI], b0[NI], a1[MI], b1[NI];
         fetch(st, 0, a0, b0);
 #pragma unroll
@@ -254,8 +275,22 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
             }
             // Keep the fetches of step s+1 ahead of the MFMAs of step s.
             __builtin_amdgcn_sched_barrier(0);
-            if (s & 1) mfmas(a1, b1);
-            else mfmas(a0, b0);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    if (s & 1)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[ni], a1[mi], acc[mi][ni], 0, 0, 0);
+                    else
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[ni], a0[mi], acc[mi][ni], 0, 0, 0);
+                    const int gm = (s * MI + mi) * NI + ni;
+                    if (copy && gm % STRIDE == 0 && gm / STRIDE < NGRP) {
+#pragma unroll
+                        for (int u = 0; u < PER; ++u)
+                            if ((gm / STRIDE) * PER + u < NOPS) copy_op((gm / STRIDE) * PER + u, kn, nst);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
         }
     };
 
@@ -263,28 +298,22 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
     const int nch = a.chunks;
     uint4* const st0 = lds;
     uint4* const st1 = lds + scells;
-    dma_w(0, st0);
-    load_x(0);
-    store_x(st0 + C::ACELLS);
-    if (nch > 1) {
-        dma_w(1, st1);
-        load_x(C::CC);
-    }
+#pragma unroll
+    for (int k = 0; k < NOPS; ++k) copy_op(k, 0, st0);
     __builtin_amdgcn_s_waitcnt(0);
+    store_x(st0 + C::ACELLS);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         uint4* cur = (c & 1) ? st1 : st0;
         uint4* nxt = (c & 1) ? st0 : st1;
-        compute(cur);
         if (c + 1 < nch) {
+            compute(cur, true, c + 1, nxt);
             __builtin_amdgcn_s_waitcnt(0);   // chunk c+1: weight image and input rows have landed
             store_x(nxt + C::ACELLS);
+        } else {
+            compute(cur, false, 0, nxt);
         }
         __syncthreads();                     // stage cur is free, stage nxt is complete
-        if (c + 2 < nch) {
-            dma_w(c + 2, cur);
-            load_x((c + 2) * C::CC);
-        }
     }
 
     // ---- epilogue: bias, activation, bf16, store ----
@@ -374,20 +403,23 @@ CfgInfo info() {
                    (const void*)igemm_bf16_kernel<C>};
 }
 
-// Four waves (one per SIMD, up to 512 registers each).
+// Eight waves (two per SIMD, so one wave's memory or barrier stalls are
+// covered by the other's MFMAs) in a 2 x 4 grid of 64 x 64 wave tiles; the
+// small-channel variants use four waves.
 //                   BM WM WN NI   TW  CC KH KW SD XS
-using B3_128 = BCfg<128, 2, 2, 8,  16, 16, 3, 3, 0, 2>;   // 3x3 stride 1: 16 x 16 output pixels
-using B3S_128 = BCfg<128, 2, 2, 8, 16, 16, 3, 3, 1, 2>;   // 3x3 stride 2 (column split)
+using B3_128 = BCfg<128, 2, 4, 4,  16, 16, 3, 3, 0, 2>;   // 3x3 stride 1: 16 x 16 output pixels
+using B3_128s = BCfg<128, 2, 4, 4, 16, 16, 3, 3, 0, 1>;   // the same for patches of <= 512 input tasks
+using B3S_128 = BCfg<128, 2, 4, 4, 16, 16, 3, 3, 1, 1>;   // 3x3 stride 2 (column split)
 using B3_32 = BCfg<32, 1, 4, 4,  16, 16, 3, 3, 0, 2>;     // 3x3, few output channels per group
 using B3_16 = BCfg<16, 1, 4, 4,  16, 8, 3, 3, 0, 2>;      // 3x3, <= 16 output and <= 8 input channels per group
-using B1_128 = BCfg<128, 2, 2, 8, 256, 64, 1, 1, 0, 1>;   // flattened 1x1
+using B1_128 = BCfg<128, 2, 4, 4, 256, 64, 1, 1, 0, 1>;   // flattened 1x1
 using B1_32 = BCfg<32, 1, 4, 4, 256, 64, 1, 1, 0, 1>;
 
-enum { C3_128, C3S_128, C3_32, C3_16, C1_128, C1_32, NCFG };
+enum { C3_128, C3_128s, C3S_128, C3_32, C3_16, C1_128, C1_32, NCFG };
 
 const CfgInfo& cfg(int i) {
-    static const CfgInfo t[NCFG] = {info<B3_128>(), info<B3S_128>(), info<B3_32>(),
-                                    info<B3_16>(),  info<B1_128>(),  info<B1_32>()};
+    static const CfgInfo t[NCFG] = {info<B3_128>(), info<B3_128s>(), info<B3S_128>(), info<B3_32>(),
+                                    info<B3_16>(),  info<B1_128>(),   info<B1_32>()};
     return t[i];
 }
 
@@ -461,7 +493,7 @@ bool plan_igemm_bf16(Desc& d) {
     const bool is3 = p.k_h == 3 && p.k_w == 3;
     const bool flat = p.k_h == 1 && p.k_w == 1 && p.stride_h == 1 && p.stride_w == 1 && p.pad_top == 0 &&
                       p.pad_left == 0 && p.pad_bottom == 0 && p.pad_right == 0;
-    int cands[3];
+    int cands[4];
     int nc = 0;
     if (is3 && p.stride_h == p.stride_w) {
         if (p.stride_w == 2) {
@@ -469,6 +501,7 @@ bool plan_igemm_bf16(Desc& d) {
         } else if (p.stride_w == 1) {
             if (d.cout_g <= 16 && d.cin_g <= 8) cands[nc++] = C3_16;
             if (d.cout_g <= 32) cands[nc++] = C3_32;
+            cands[nc++] = C3_128s;
             cands[nc++] = C3_128;
         }
     } else if (flat) {
