@@ -8,23 +8,29 @@
 // supplies 8 consecutive ones, so both operands are kept in LDS as 16-byte
 // cells of 8 consecutive input channels:
 //   weights  [tap*G + group-of-8][output channel]      (one cell each)
-//   patch    [group-of-8][patch position]              (one cell each)
+//   patch    [group-of-8][patch row][patch column]    (one cell each)
 // K runs tap-major inside a chunk of CC = 8*G input channels; an MFMA operand
 // is one 16-byte LDS read and 16 lanes of a read touch 16 consecutive cells.
+// K slots past the last tap (when taps*G is not a multiple of 4) read a
+// block of zero cells instead of stored zeros.
 //
 // Copy path.  The weights are re-laid once per call (pack kernel below) into
 // exactly the LDS image of each (output-channel tile, channel chunk), so a
 // chunk's weights move with direct global->LDS loads (no registers, no
 // transposition).  The NCHW input is transposed on the fly: a lane loads 8
-// channels x 8 pixels (eight 16-byte row loads), permutes them in registers
-// and writes eight 16-byte cells.  Stride-2 patches keep even and odd columns
-// in separate halves of a row, so a stride-2 read of 16 output pixels is
-// still 16 consecutive cells.  The row and plane strides of the patch are
-// chosen on the host to spread those cell writes over the LDS banks.
+// channels x 8 pixels (eight 16-byte row loads from wave-uniform plane
+// pointers), permutes them in registers and writes eight 16-byte cells.
+// Patch rows hold whole 8-pixel vectors (the row starts at the 8-aligned
+// input column below the tile's first one), so no cell write needs a range
+// check; vectors entirely outside the image are pad cells written once per
+// stage.  Stride-2 patches keep even and odd columns in separate halves of a
+// row, so a stride-2 read of 16 output pixels is still 16 consecutive cells.
+// The row and plane strides are chosen on the host to spread the cell writes
+// over the LDS banks.
 //
-// Pipeline: two LDS stages; the copy instructions of chunk c+1 (DMA and row
-// loads) are interleaved with the MFMAs of chunk c, then its rows are
-// transposed into the free stage; one workgroup barrier per chunk.
+// Pipeline: eight waves, two per SIMD, 64 x 64 wave tiles; two LDS stages,
+// the copy of chunk c+1 issued at the start of chunk c, its rows transposed
+// into the free stage after chunk c's MFMAs; one barrier per chunk.
 // The epilogue adds the bias, applies the activation, rounds to bf16 and
 // writes channel out_off + g*cout_g + co of a buffer with out_total channels
 // (ConcatFusedTail), 4 pixels of a row per 8-byte store.
@@ -35,6 +41,9 @@ namespace conv2d {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
 
 template <int BM_, int WM_, int WN_, int NI_, int TW_, int CC_, int KH_, int KW_, int SD_, int XS_>
 struct BCfg {
@@ -48,14 +57,13 @@ struct BCfg {
     static constexpr int TH = BN / TW;
     static constexpr int G = CC / 8;                   // 8-channel groups per chunk
     static constexpr int STEPS = (KHW * CC + 31) / 32; // K steps of 32 per chunk
-    static constexpr int TGP = 4 * STEPS;              // (tap, group) slots incl. the zero K padding
-    static constexpr int ACELLS = TGP * BM;            // 16-byte cells of a chunk's weight image
+    // Stored (tap, group) slots: taps*G rounded up so the image is whole 1 KB pieces.
+    static constexpr int SQ = 64 / cgcd(BM, 64);
+    static constexpr int TGA = (KHW * G + SQ - 1) / SQ * SQ;
+    static constexpr int ACELLS = TGA * BM;            // 16-byte cells of a chunk's weight image
     static constexpr int DMAR = ACELLS / 64;           // 1 KB wave copies per weight image
-    // One wave per SIMD: double-buffer the MFMA operands and spread the copy
-    // instructions over the MFMAs.  Two waves per SIMD: the other wave covers
-    // those stalls, and the registers are needed elsewhere.
-    static constexpr bool PIPE = NW <= 4;
-    static_assert(CC % 8 == 0 && TGP % G == 0, "K steps tile whole (tap, group) slots");
+    static constexpr int ZCELLS = 16 * MI;             // zero cells read by K slots past TGA
+    static_assert(CC % 8 == 0 && TGA <= 4 * STEPS, "K steps cover the stored slots");
     static_assert(ACELLS % 64 == 0, "weight image in whole 1 KB pieces");
     static_assert(WR % 16 == 0 && TW % 16 == 0 && BN % TW == 0, "whole fragments");
 };
@@ -69,16 +77,34 @@ __host__ __device__ inline void input_task(int v, int nvr, int ph, int& vc, int&
     g = rest / ph;
 }
 
+// Input task of lane slot u (= lane + 64*i) of wave w: the tasks of a chunk
+// are dealt to the waves in equal contiguous runs.  -1 = none.
+__host__ __device__ inline int task_of(int w, int u, int tasks, int nw) {
+    const int per = (tasks + nw - 1) / nw;
+    const int v = w * per + u;
+    return (u < per && v < tasks) ? v : -1;
+}
+
 // Cell of patch column pc inside its row (stride-2 patches: evens, then odds).
 __host__ __device__ inline int col_cell(int pc, int half, bool split) {
     return split ? (pc & 1) * half + (pc >> 1) : pc;
 }
 
-__device__ __forceinline__ void copy16_to_lds(const uint4* src, uint4* lds_base) {
+// Direct global->LDS copy of 16 bytes per lane: lane l writes lds_base + 16*l
+// (lds_base wave-uniform).  Issued as inline assembly so that the compiler
+// does not order every later LDS read of the workgroup behind it (it cannot
+// tell that the reads go to the other stage); the kernel's own s_waitcnt
+// before the barrier is what orders the copy.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, const uint4* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds((const float*)src, (float*)lds_base, 16, 0, 0);
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
+                 : "memory", "m0");
 #endif
 }
+#pragma clang diagnostic pop
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
@@ -104,76 +130,96 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
     const int co0 = cot * BM;
     const int ho0 = thi * TH, wo0 = twi * TW;
     const int ih0 = ho0 * a.stride_h - a.pad_top;
-    const int iw_lo = wo0 * a.stride_w - a.pad_left;      // input column of patch column 0
-    const int PH = a.patch_h, span = a.patch_w;
-    const int shift = a.patch_shift;                      // iw_lo minus its 8-aligned floor
-    const int nvr = a.patch_stride;                       // 8-pixel vectors per patch row
+    const int shift = a.patch_shift;                         // 8-aligned patch start: iw_lo - shift
+    const int iw8 = wo0 * a.stride_w - a.pad_left - shift;  // input column of patch column 0
+    const int PH = a.patch_h;
+    const int nvr = a.patch_stride;                          // 8-pixel vectors per patch row
     const int RS = a.lds_rs, PL = a.lds_plane, HALF = a.col_half;
-    const int scells = C::ACELLS + G * PL;                // cells per stage
+    const int scells = C::ACELLS + G * PL;                   // cells per stage
     const int HW = a.h * a.w;
 
-    const uint16_t* __restrict__ xg = (const uint16_t*)a.xptr +
-                                      ((int64_t)n * a.in_total + a.in_off + (int64_t)g * a.cin_g) * HW;
-    const uint4* __restrict__ wp = (const uint4*)a.wptr + (int64_t)(g * a.co_tiles + cot) * a.chunks * C::ACELLS;
-    const bool vx = a.w % 8 == 0 && ((uintptr_t)a.xptr % 16) == 0;
+    uint4* const st0 = lds;
+    uint4* const st1 = lds + scells;
+    uint4* const zero = lds + 2 * scells;                    // C::ZCELLS zero cells
+
+    const char* __restrict__ xg = (const char*)a.xptr +
+                                  2 * ((int64_t)n * a.in_total + a.in_off + (int64_t)g * a.cin_g) * HW;
+    const char* __restrict__ wp =
+        (const char*)a.wptr + 16 * (int64_t)(g * a.co_tiles + cot) * a.chunks * C::ACELLS;
     const uint32_t padb = __bfloat16_as_ushort(f32_to_bf16(a.pad_value));
     const uint32_t pad2 = padb | (padb << 16);
 
     // ---- per-thread input tasks ----
-    int tcell[C::XS];   // cell (in the patch part of a stage) of the task's row start; -1 = no task
-    int tpc[C::XS];     // patch column of the vector's first pixel
-    int tg8[C::XS];     // first channel of the task's group
-    int trow[C::XS];    // patch row
-    int txo[C::XS];     // offset of the vector's first pixel in a channel plane; -1 = outside the image
+    int tcell[C::XS];   // cell (in the patch part of a stage) of the vector's first pixel; -1 = no task
+    int toff[C::XS];    // byte offset of the vector in the task's first channel plane; -1 = outside the image
 #pragma unroll
     for (int i = 0; i < C::XS; ++i) {
-        const int v = tid + C::NT * i;
-        tcell[i] = -1; tpc[i] = 0; tg8[i] = 0; trow[i] = 0; txo[i] = -1;
-        if (v < G * PH * nvr) {
+        const int v = task_of(wave, lane + 64 * i, G * PH * nvr, C::NW);
+        tcell[i] = -1; toff[i] = -1;
+        if (v >= 0) {
             int vc, row, gg;
             input_task(v, nvr, PH, vc, row, gg);
-            const int ih = ih0 + row, iw = iw_lo - shift + 8 * vc;
-            tcell[i] = gg * PL + row * RS;
-            tpc[i] = 8 * vc - shift;
-            tg8[i] = 8 * gg;
-            trow[i] = row;
-            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w) txo[i] = ih * a.w + iw;
+            const int ih = ih0 + row, iw = iw8 + 8 * vc;
+            tcell[i] = gg * PL + row * RS + (C::SD ? 4 * vc : 8 * vc);
+            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w) toff[i] = 2 * (8 * gg * HW + ih * a.w + iw);
         }
     }
+    // Buffer over the group's input channels (byte size < 2^31, checked when
+    // planning).  tvo = per-lane byte offset; 2^31 for lanes that load
+    // nothing, so that offset + channel offset stays past the buffer.
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xg, (short)0, 2 * a.cin_g * HW, 0x00020000);
+    int tvo[C::XS];
+#pragma unroll
+    for (int i = 0; i < C::XS; ++i) tvo[i] = toff[i] >= 0 ? toff[i] : INT32_MIN;
+    // Cell of pixel p of a task's vector, relative to tcell.
+    auto pcell = [&](int p) __attribute__((always_inline)) { return C::SD ? (p & 1) * HALF + (p >> 1) : p; };
 
-    uint4 xr[C::XS][8];
-    // Global -> register: channel c0 + tg8 + t of input task i (8 pixels).
-    auto load_op = [&](int i, int t, int c0) __attribute__((always_inline)) {
-        if (tcell[i] < 0) return;
-        uint4 r = make_uint4(0, 0, 0, 0);
-        if (tg8[i] + t < a.cin_g - c0) {
-            const uint16_t* __restrict__ plane = xg + (int64_t)(c0 + tg8[i] + t) * HW;
-            if (vx) {
-                r = txo[i] >= 0 ? *(const uint4*)(plane + txo[i]) : make_uint4(pad2, pad2, pad2, pad2);
-            } else {
-                const int ih = ih0 + trow[i];
-                const int iw0 = iw_lo + tpc[i];
-                uint32_t e[8];
+    // Zero cells, and pad cells of vectors outside the image in both stages
+    // (no chunk writes them again).
+    for (int e = tid; e < C::ZCELLS; e += C::NT) zero[e] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const int iw = iw0 + p;
-                    e[p] = ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
-                               ? (uint32_t)plane[ih * a.w + iw]
-                               : padb;
-                }
-                r = make_uint4(e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16);
-            }
-        }
-        xr[i][t] = r;
-    };
-    // Registers -> LDS: 8 channels x 8 pixels become 8 cells of 8 channels.
-    auto store_x = [&](uint4* bst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < C::XS; ++i) {
-            if (tcell[i] < 0) continue;
+    for (int i = 0; i < C::XS; ++i)
+        if (tcell[i] >= 0 && toff[i] < 0) {
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
-                const int pc = tpc[i] + p;
+                st0[C::ACELLS + tcell[i] + pcell(p)] = make_uint4(pad2, pad2, pad2, pad2);
+                st1[C::ACELLS + tcell[i] + pcell(p)] = make_uint4(pad2, pad2, pad2, pad2);
+            }
+        }
+
+    // Chunk kc's weight image -> stage ast (direct to LDS).
+    auto dma_w = [&](int kc, uint4* ast) __attribute__((always_inline)) {
+        const char* src = wp + 16 * ((int64_t)kc * C::ACELLS + lane);
+#pragma unroll
+        for (int k = 0; k < (C::DMAR + C::NW - 1) / C::NW; ++k) {
+            const int r = wave + C::NW * k;
+            if (r < C::DMAR) copy16_to_lds(src + 1024 * r, ast + 64 * r);
+        }
+    };
+    // Chunk kc's input rows -> registers xr.  Unconditional buffer loads:
+    // lanes without an in-image vector, and channels past the group's last
+    // one, read beyond the buffer and get zeros without touching memory (no
+    // per-lane branches, so no register merges that would make the compiler
+    // hold later LDS reads behind these loads).
+    auto load_x = [&](int kc, uint4 (&xr)[C::XS][8]) __attribute__((always_inline)) {
+        const int c0 = kc * C::CC;
+#pragma unroll
+        for (int i = 0; i < C::XS; ++i) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, tvo[i] + 2 * (c0 + t) * HW, 0, 0);
+                xr[i][t] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+        }
+    };
+    // Registers -> LDS: 8 channels x 8 pixels become 8 cells of 8 channels.
+    auto store_x = [&](const uint4 (&xr)[C::XS][8], uint4* bst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < C::XS; ++i) {
+            if (toff[i] < 0) continue;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
                 uint32_t d[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -182,21 +228,9 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
                     const uint32_t wh = (p >> 1) == 0 ? hi.x : (p >> 1) == 1 ? hi.y : (p >> 1) == 2 ? hi.z : hi.w;
                     d[k] = (p & 1) ? ((wl >> 16) | (wh & 0xffff0000u)) : ((wl & 0xffffu) | (wh << 16));
                 }
-                if (pc >= 0 && pc < span) bst[tcell[i] + col_cell(pc, HALF, C::SD)] = make_uint4(d[0], d[1], d[2], d[3]);
+                bst[tcell[i] + pcell(p)] = make_uint4(d[0], d[1], d[2], d[3]);
             }
         }
-    };
-    // Weight image of chunk kc -> LDS: the wave's k-th 1 KB piece.
-    constexpr int ND = (C::DMAR + C::NW - 1) / C::NW;    // DMA pieces per wave
-    constexpr int NOPS = ND + C::XS * 8;                  // copy instructions per wave and chunk
-    auto dma_op = [&](int k, int kc, uint4* ast) __attribute__((always_inline)) {
-        const int r = wave + C::NW * k;
-        if (r < C::DMAR) copy16_to_lds(wp + (int64_t)kc * C::ACELLS + r * 64 + lane, ast + r * 64);
-    };
-    // Copy instruction k of chunk kc: DMA pieces first, then the input loads.
-    auto copy_op = [&](int k, int kc, uint4* ast) __attribute__((always_inline)) {
-        if (k < ND) dma_op(k, kc, ast);
-        else load_op((k - ND) / 8, (k - ND) % 8, kc * C::CC);
     };
 
     // ---- operand offsets (cells) ----
@@ -204,13 +238,12 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
     // channel group tg % G.  A row co = wm*WR + mi*16 + lane%16; B pixel
     // j = wn*WC + ni*16 + lane%16.
     const int q = lane >> 4, l16 = lane & 15;
-    const int a_lane = q * BM + wm * C::WR + l16;
     int b_lane[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
         const int j = wn * C::WC + ni * 16 + l16;
         const int jr = j / TW, jc = j % TW;
-        b_lane[ni] = C::SD ? jr * a.stride_h * RS + jc : jr * a.stride_h * RS + jc * a.stride_w;
+        b_lane[ni] = jr * a.stride_h * RS + (C::SD ? jc : jc * a.stride_w);
     }
     int b_step[STEPS];
 #pragma unroll
@@ -220,8 +253,8 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
         const int gg = tg - (tg / G) * G;
         if (tap >= KHW) tap = 0;     // K padding: zero weights, finite inputs of tap 0
         const int r = tap / KW, sc = tap - (tap / KW) * KW;
-        const int cdx = sc * a.dilation_w;
-        b_step[s] = gg * PL + r * a.dilation_h * RS + (C::SD ? (cdx & 1) * HALF + (cdx >> 1) : cdx);
+        const int cdx = shift + sc * a.dilation_w;
+        b_step[s] = C::ACELLS + gg * PL + r * a.dilation_h * RS + (C::SD ? (cdx & 1) * HALF + (cdx >> 1) : cdx);
     }
 
     f32x4 acc[MI][NI];
@@ -230,91 +263,79 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto fetch = [&](const uint4* st, int s, bf16x8 (&av)[MI], bf16x8 (&bv)[NI]) __attribute__((always_inline)) {
-        const uint4* as = st + a_lane + 4 * s * BM;
-        const uint4* bs = st + C::ACELLS + b_step[s];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) av[mi] = __builtin_bit_cast(bf16x8, as[16 * mi]);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bv[ni] = __builtin_bit_cast(bf16x8, bs[b_lane[ni]]);
-    };
-    // Chunk from stage st.  With `copy`, the copy instructions of chunk kn
-    // (DMA into stage nst, input rows into registers) are spread over the
-    // MFMAs of the first half of the steps, so the memory pipe drains while
-    // the matrix cores run.
-    auto compute = [&](const uint4* st, bool copy, int kn, uint4* nst) __attribute__((always_inline)) {
-        constexpr int SP = STEPS > 1 ? (STEPS + 1) / 2 : 1;
-        constexpr int SLOTS = SP * MI * NI;                      // MFMAs that may carry copy instructions
-        constexpr int PER = (NOPS + SLOTS - 1) / SLOTS;          // copy instructions per carrying MFMA
-        constexpr int NGRP = (NOPS + PER - 1) / PER;
-        constexpr int STRIDE = SLOTS / NGRP;
-        if constexpr (!C::PIPE) {
-            if (copy) {
-#pragma unroll
-                for (int k = 0; k < NOPS; ++k) copy_op(k, kn, nst);
-            }
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                bf16x8 av[MI], bv[NI];
-                fetch(st, s, av, bv);
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[ni], av[mi], acc[mi][ni], 0, 0, 0);
-            }
-            return;
-        }
-        bf16x8 a0[MI], b0[NI], a1[MI], b1[NI];
-        fetch(st, 0, a0, b0);
+    auto compute = [&](const uint4* st) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
-            if (s + 1 < STEPS) {
-                if (s & 1) fetch(st, s + 1, a0, b0);
-                else fetch(st, s + 1, a1, b1);
-            }
-            // Keep the fetches of step s+1 ahead of the MFMAs of step s.
-            __builtin_amdgcn_sched_barrier(0);
+            const int tg = 4 * s + q;
+            const uint4* as = (4 * s + 3 < C::TGA || tg < C::TGA) ? st + tg * BM + wm * C::WR + l16 : zero + l16;
+            const uint4* bs = st + b_step[s];
+            bf16x8 av[MI], bv[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) av[mi] = __builtin_bit_cast(bf16x8, as[16 * mi]);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) bv[ni] = __builtin_bit_cast(bf16x8, bs[b_lane[ni]]);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    if (s & 1)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[ni], a1[mi], acc[mi][ni], 0, 0, 0);
-                    else
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[ni], a0[mi], acc[mi][ni], 0, 0, 0);
-                    const int gm = (s * MI + mi) * NI + ni;
-                    if (copy && gm % STRIDE == 0 && gm / STRIDE < NGRP) {
-#pragma unroll
-                        for (int u = 0; u < PER; ++u)
-                            if ((gm / STRIDE) * PER + u < NOPS) copy_op((gm / STRIDE) * PER + u, kn, nst);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[ni], av[mi], acc[mi][ni], 0, 0, 0);
         }
     };
 
-    // ---- main loop: two stages, chunk c+1 copied while chunk c computes ----
+    // ---- main loop ----
+    // Two LDS stages: chunk c computes from stage c%2 while chunk c+1's
+    // weight image lands in the other one and its rows (loaded into
+    // registers one chunk earlier) are transposed into it after the MFMAs.
+    // Input rows are loaded two chunks ahead into two register sets: rows of
+    // chunk k live in R[k%2].  Steady-state steps load and wait
+    // unconditionally, so the compiler sees nothing outstanding at the top of
+    // a step; the wait before the transposition leaves the newest row loads
+    // in flight.
+    constexpr int VMX = 8 * C::XS;   // row loads per chunk and thread
+    static_assert(VMX < 64, "vmcnt field");
+    constexpr int WAIT_ROWS = (VMX & 15) | (7 << 4) | (15 << 8) | ((VMX >> 4) << 14);   // vmcnt(VMX) only
     const int nch = a.chunks;
-    uint4* const st0 = lds;
-    uint4* const st1 = lds + scells;
-#pragma unroll
-    for (int k = 0; k < NOPS; ++k) copy_op(k, 0, st0);
+    uint4 R0[C::XS][8], R1[C::XS][8];
+    auto stage = [&](int k) __attribute__((always_inline)) { return (k & 1) ? st1 : st0; };
+    // Step c with chunk c+2 to prefetch: rows of c+1 are in rs, rows of c+2 go to rl.
+    auto step_full = [&](int c, uint4 (&rl)[C::XS][8], const uint4 (&rs)[C::XS][8]) __attribute__((always_inline)) {
+        dma_w(c + 1, stage(c + 1));
+        load_x(c + 2, rl);
+        compute(stage(c));
+        __builtin_amdgcn_s_waitcnt(WAIT_ROWS);   // weight image and rows of chunk c+1 have landed
+        store_x(rs, stage(c + 1) + C::ACELLS);
+        __syncthreads();
+    };
+    // Step c, c+1 being the last chunk.
+    auto step_last = [&](int c, const uint4 (&rs)[C::XS][8]) __attribute__((always_inline)) {
+        dma_w(c + 1, stage(c + 1));
+        compute(stage(c));
+        __builtin_amdgcn_s_waitcnt(0);
+        store_x(rs, stage(c + 1) + C::ACELLS);
+        __syncthreads();
+    };
+    dma_w(0, st0);
+    load_x(0, R0);
     __builtin_amdgcn_s_waitcnt(0);
-    store_x(st0 + C::ACELLS);
+    store_x(R0, st0 + C::ACELLS);
+    if (nch > 1) load_x(1, R1);
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        uint4* cur = (c & 1) ? st1 : st0;
-        uint4* nxt = (c & 1) ? st0 : st1;
-        if (c + 1 < nch) {
-            compute(cur, true, c + 1, nxt);
-            __builtin_amdgcn_s_waitcnt(0);   // chunk c+1: weight image and input rows have landed
-            store_x(nxt + C::ACELLS);
-        } else {
-            compute(cur, false, 0, nxt);
-        }
-        __syncthreads();                     // stage cur is free, stage nxt is complete
+    int c = 0;
+    for (; c + 3 < nch; c += 2) {
+        step_full(c, R0, R1);
+        step_full(c + 1, R1, R0);
     }
+    // c is even: rows of chunk c+1 (if any) are in R1.
+    if (c + 2 < nch) {           // three chunks left
+        step_full(c, R0, R1);
+        step_last(c + 1, R0);
+        c += 2;
+    } else if (c + 1 < nch) {    // two chunks left
+        step_last(c, R1);
+        c += 1;
+    }
+    compute(stage(c));
+    __syncthreads();
 
     // ---- epilogue: bias, activation, bf16, store ----
     // The workgroup's BM biases and PReLU slopes go through LDS (free after
@@ -364,16 +385,16 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
 }
 
 // Weight re-layout: OIHW bf16 -> per (group, output-channel tile, chunk) the
-// LDS image [tap*G + group-of-8][BM][8 channels], zero where the tap, the
-// output channel or the input channel lies past the filter.
+// LDS image [tap*G + group-of-8][BM][8 channels] with tga slots, zero where
+// the tap, the output channel or the input channel lies past the filter.
 __global__ __launch_bounds__(256) void pack_weights_bf16(const uint16_t* __restrict__ w, uint4* __restrict__ out,
-                                                         int64_t total, int bm, int tgp, int gq, int cc, int khw,
+                                                         int64_t total, int bm, int tga, int gq, int cc, int khw,
                                                          int chunks, int co_tiles, int cin_g, int cout_g) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total) return;
     int64_t rest = idx;
     const int co = rest % bm; rest /= bm;
-    const int tg = rest % tgp; rest /= tgp;
+    const int tg = rest % tga; rest /= tga;
     const int kc = rest % chunks; rest /= chunks;
     const int cot = rest % co_tiles;
     const int grp = rest / co_tiles;
@@ -393,14 +414,14 @@ __global__ __launch_bounds__(256) void pack_weights_bf16(const uint16_t* __restr
 // ------------------------------------------------------------ configs ---
 
 struct CfgInfo {
-    int bm, bn, tw, cc, kh, kw, sd, xs, nt, tgp;
+    int bm, bn, tw, cc, kh, kw, sd, xs, nt, nw, tga, acells, zcells;
     const void* fn;
 };
 
 template <class C>
 CfgInfo info() {
-    return CfgInfo{C::BM, C::BN, C::TW, C::CC, C::KH, C::KW, C::SD ? 1 : 0, C::XS, C::NT, C::TGP,
-                   (const void*)igemm_bf16_kernel<C>};
+    return CfgInfo{C::BM, C::BN, C::TW, C::CC, C::KH, C::KW, C::SD ? 1 : 0, C::XS, C::NT, C::NW, C::TGA,
+                   C::ACELLS, C::ZCELLS, (const void*)igemm_bf16_kernel<C>};
 }
 
 // Eight waves (two per SIMD, so one wave's memory or barrier stalls are
@@ -424,7 +445,7 @@ const CfgInfo& cfg(int i) {
 }
 
 struct Geom {
-    int ph, span, shift, nvr, half, rs, plane;
+    int ph, shift, nvr, half, rs, plane;
 };
 
 // LDS cell-write cost of one chunk's input tasks for row stride rs and
@@ -432,39 +453,43 @@ struct Geom {
 // of lanes that fall on the same 16-byte bank group.
 int64_t write_cost(const Geom& G, const CfgInfo& c, int rs, int pl) {
     const int tasks = (c.cc / 8) * G.ph * G.nvr;
+    const int per = (tasks + c.nw - 1) / c.nw;
     int64_t cost = 0;
-    for (int base = 0; base < tasks; base += 16) {
-        for (int p = 0; p < 8; ++p) {
-            int hits[16] = {0};
-            int worst = 0;
-            for (int l = 0; l < 16 && base + l < tasks; ++l) {
-                int vc, row, gg;
-                input_task(base + l, G.nvr, G.ph, vc, row, gg);
-                const int pc = 8 * vc - G.shift + p;
-                if (pc < 0 || pc >= G.span) continue;
-                const int cell = gg * pl + row * rs + col_cell(pc, G.half, c.sd != 0);
-                const int h = ++hits[cell & 15];
-                worst = h > worst ? h : worst;
+    for (int w = 0; w < c.nw; ++w)
+        for (int base = 0; base < per; base += 16)
+            for (int p = 0; p < 8; ++p) {
+                int hits[16] = {0};
+                int worst = 0;
+                for (int l = 0; l < 16; ++l) {
+                    const int v = task_of(w, base + l, tasks, c.nw);
+                    if (v < 0) continue;
+                    int vc, row, gg;
+                    input_task(v, G.nvr, G.ph, vc, row, gg);
+                    const int cell = gg * pl + row * rs + col_cell(8 * vc + p, G.half, c.sd != 0);
+                    const int h = ++hits[cell & 15];
+                    worst = h > worst ? h : worst;
+                }
+                cost += worst;
             }
-            cost += worst;
-        }
-    }
     return cost;
 }
 
-Geom geom(const conv2d_params_t& p, const CfgInfo& c, bool flat) {
-    Geom G;
+// Patch geometry; the plane stride is kept <= max_plane.  Returns false if
+// even the densest layout does not fit.
+bool geom(const conv2d_params_t& p, const CfgInfo& c, bool flat, int max_plane, Geom& G) {
     const int th = c.bn / c.tw;
+    int span;
     if (flat) {
-        G.ph = 1; G.span = c.tw; G.shift = 0; G.nvr = c.tw / 8;
+        G.ph = 1; G.shift = 0; span = c.tw;
     } else {
         G.ph = (th - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
-        G.span = (c.tw - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
+        span = (c.tw - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1;
         G.shift = ((-p.pad_left) % 8 + 8) % 8;
-        G.nvr = (G.shift + G.span + 7) / 8;
     }
-    G.half = (G.span + 1) / 2;
-    const int rs0 = c.sd ? 2 * G.half : G.span;
+    G.nvr = (G.shift + span + 7) / 8;
+    G.half = 4 * G.nvr;
+    const int rs0 = 8 * G.nvr;
+    if ((int64_t)G.ph * rs0 > max_plane) return false;
     // Smallest write cost over row strides rs0..rs0+15 and plane padding 0..15.
     int64_t best = -1;
     G.rs = rs0;
@@ -472,19 +497,22 @@ Geom geom(const conv2d_params_t& p, const CfgInfo& c, bool flat) {
     for (int rs = rs0; rs < rs0 + 16; ++rs)
         for (int pad = 0; pad < (c.cc > 8 ? 16 : 1); ++pad) {
             const int pl = G.ph * rs + pad;
+            if (pl > max_plane) continue;
             const int64_t cost = write_cost(G, c, rs, pl);
             if (best < 0 || cost < best || (cost == best && pl < G.plane)) {
                 best = cost; G.rs = rs; G.plane = pl;
             }
         }
-    return G;
+    return true;
 }
 
 int64_t wpack_cells(const Desc& d, const CfgInfo& c) {
     const int64_t co_tiles = (d.cout_g + c.bm - 1) / c.bm;
     const int64_t chunks = (d.cin_g + c.cc - 1) / c.cc;
-    return (int64_t)d.p.groups * co_tiles * chunks * c.tgp * c.bm;
+    return (int64_t)d.p.groups * co_tiles * chunks * c.acells;
 }
+
+constexpr int kLdsMax = 160 * 1024;
 
 }  // namespace
 
@@ -493,6 +521,8 @@ bool plan_igemm_bf16(Desc& d) {
     const bool is3 = p.k_h == 3 && p.k_w == 3;
     const bool flat = p.k_h == 1 && p.k_w == 1 && p.stride_h == 1 && p.stride_w == 1 && p.pad_top == 0 &&
                       p.pad_left == 0 && p.pad_bottom == 0 && p.pad_right == 0;
+    // Input rows are read as 16-byte vectors of 8 pixels.
+    if ((flat ? (int64_t)p.h * p.w : p.w) % 8 != 0) return false;
     int cands[4];
     int nc = 0;
     if (is3 && p.stride_h == p.stride_w) {
@@ -509,19 +539,20 @@ bool plan_igemm_bf16(Desc& d) {
     }
     for (int k = 0; k < nc; ++k) {
         const CfgInfo& c = cfg(cands[k]);
-        const Geom G = geom(p, c, flat);
-        if ((c.cc / 8) * G.ph * G.nvr > c.xs * c.nt) continue;         // input tasks per thread
-        const int64_t stage = 16 * ((int64_t)c.tgp * c.bm + (int64_t)(c.cc / 8) * G.plane);
-        if (2 * stage > 160 * 1024) continue;
-        if ((int64_t)c.cc * p.h * p.w >= INT32_MAX / 2) continue;
+        const int gq = c.cc / 8;
+        const int max_plane = (kLdsMax - 16 * c.zcells - 2 * 16 * c.acells) / (2 * 16 * gq);
+        Geom G;
+        if (max_plane <= 0 || !geom(p, c, flat, max_plane, G)) continue;
+        if (gq * G.ph * G.nvr > c.xs * c.nt) continue;                  // input tasks per thread
+        if (2 * (int64_t)d.cin_g * p.h * p.w >= INT32_MAX) continue;      // 32-bit byte offsets in a group
         if (wpack_cells(d, c) * 16 >= ((int64_t)1 << 40)) continue;
         d.cfg = cands[k];
         d.flatten_1x1 = flat;
         d.tile_w = c.tw;
         d.tile_h = c.bn / c.tw;
-        d.lds_bytes = (int32_t)(2 * stage);
+        d.lds_bytes = 16 * (2 * (c.acells + gq * G.plane) + c.zcells);
         d.wpack_bytes = wpack_cells(d, c) * 16;
-        d.g_ph = G.ph; d.g_span = G.span; d.g_shift = G.shift; d.g_nvr = G.nvr;
+        d.g_ph = G.ph; d.g_span = 8 * G.nvr; d.g_shift = G.shift; d.g_nvr = G.nvr;
         d.g_rs = G.rs; d.g_plane = G.plane; d.g_half = G.half;
         return true;
     }
@@ -529,6 +560,8 @@ bool plan_igemm_bf16(Desc& d) {
 }
 
 hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s) {
+    // The kernel reads input rows as 16-byte vectors.
+    if ((uintptr_t)a.xptr % 16 != 0) return launch_direct(d, a, s);
     const CfgInfo& c = cfg(d.cfg);
     const conv2d_params_t& p = d.p;
     if (d.flatten_1x1) {
@@ -560,9 +593,9 @@ hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s) {
     const void* w_src = a.wptr;
     uint4* pk = (uint4*)d.wpack;
     int64_t tot = total;
-    int bm = c.bm, tgp = c.tgp, gq = c.cc / 8, cc = c.cc, khw = p.k_h * p.k_w, chunks = a.chunks,
+    int bm = c.bm, tga = c.tga, gq = c.cc / 8, cc = c.cc, khw = p.k_h * p.k_w, chunks = a.chunks,
         co_tiles = a.co_tiles, cin_g = d.cin_g, cout_g = d.cout_g;
-    void* pargs[] = {&w_src, &pk, &tot, &bm, &tgp, &gq, &cc, &khw, &chunks, &co_tiles, &cin_g, &cout_g};
+    void* pargs[] = {&w_src, &pk, &tot, &bm, &tga, &gq, &cc, &khw, &chunks, &co_tiles, &cin_g, &cout_g};
     hipError_t e = hipLaunchKernel((const void*)pack_weights_bf16, dim3((uint32_t)((total + 255) / 256)), dim3(256),
                                    pargs, 0, s);
     if (e != hipSuccess) return e;
