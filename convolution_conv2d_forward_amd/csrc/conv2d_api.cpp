@@ -45,6 +45,7 @@ const char* kernel_name(const Desc& d) {
     case KC_QDW: return "depthwise_i8";
     case KC_QPW: return "pointwise_i8_mfma";
     case KC_DIRECT: return "direct";
+    case KC_GROUPED: return d.p.dtype == CONV_DTYPE_BF16 ? "grouped_bf16" : "grouped_f32";
     }
     return "?";
 }
@@ -235,6 +236,9 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
     } else if (depthwise) {
         d->kclass = KC_DW;
         planned = plan_dw(*d);
+    } else if (plan_grouped(*d)) {
+        d->kclass = KC_GROUPED;
+        planned = true;
     } else if (p.dtype == CONV_DTYPE_F32) {
         d->kclass = KC_IGEMM_F32;
         planned = plan_igemm_f32(*d);
@@ -320,6 +324,7 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     case KC_IGEMM_F32: e = launch_igemm_f32(d, a, s); break;
     case KC_IGEMM_BF16: e = launch_igemm_bf16(d, a, s); break;
     case KC_DW: e = launch_dw(d, a, s); break;
+    case KC_GROUPED: e = launch_grouped(d, a, s); break;
     default: e = launch_direct(d, a, s); break;
     }
     return hip_status(e, kernel_name(d));

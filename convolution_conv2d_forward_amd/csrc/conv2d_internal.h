@@ -17,6 +17,7 @@ enum KernelClass : int32_t {
     KC_QDW = 3,          // int8 depthwise, VALU int32 MACs
     KC_QPW = 4,          // int8 pointwise 1x1, i8 MFMA
     KC_DIRECT = 5,       // direct convolution, one thread per output (any shape)
+    KC_GROUPED = 6,      // grouped 3x3 with 4 or 8 channels per group, VALU
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -134,6 +135,7 @@ hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw,
                               hipStream_t s);
 
@@ -144,6 +146,7 @@ bool plan_igemm_bf16(Desc& d);
 bool plan_dw(Desc& d);
 bool plan_qdw(Desc& d);
 bool plan_qpw(Desc& d);
+bool plan_grouped(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.

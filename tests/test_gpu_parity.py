@@ -67,6 +67,8 @@ CLASS_CASES = [
     (2, 12, 15, 16, 20, 5, 1, 2, 1, 1, workloads.ACT_LEAKY_RELU),   # 5x5: generic kernel
     (1, 6, 9, 9, 10, (2, 4), (2, 3), (1, 0, 2, 3), (1, 2), 2, workloads.ACT_CLIP),  # 2x4 grouped
     (2, 64, 12, 12, 64, 3, 1, 1, 1, 8, workloads.ACT_PRELU),        # grouped, cout_g 8
+    (1, 32, 15, 17, 32, 3, 2, (0, 1, 2, 1), 1, 8, workloads.ACT_LEAKY_RELU),  # grouped 4/group, s2, odd width
+    (2, 24, 9, 13, 24, 3, 1, 2, 2, 3, workloads.ACT_CLIP),          # grouped 8/group, dilation 2, odd width
     (2, 64, 10, 10, 128, 3, 1, 1, 1, 2, workloads.ACT_RELU),        # grouped, cout_g 64
     (1, 7, 31, 29, 7, 3, 1, 1, 1, 7, workloads.ACT_CLIP),           # depthwise ragged
     (2, 5, 17, 16, 5, 3, 2, 1, 1, 5, workloads.ACT_NONE),           # depthwise s2
@@ -94,6 +96,27 @@ def test_kernel_classes_fp32(i, pad_value):
     y, kname, runs = gpu_layer(L, x, wt, b, sl, repeat=2)
     ref = oracle_layer(L, x, wt, b, sl)
     assert_close(y, ref, FP32_TOL, f"case {i} ({kname})")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+GROUPED_CASES = [i for i, c in enumerate(CLASS_CASES) if c[9] > 1 and c[1] // c[9] in (4, 8)
+                 and c[1] == c[4] and c[5] == 3]
+
+
+@pytest.mark.parametrize("i", GROUPED_CASES)
+def test_grouped_cases_bf16(i):
+    n, ci, h, w, co, k, s, p, d, g, act = CLASS_CASES[i]
+    p4 = p if isinstance(p, tuple) else (p, p, p, p)
+    L = workloads.Layer("case", n, ci, h, w, co, (k, k), stride=(s, s), pads=p4, dilation=(d, d), groups=g,
+                        has_bias=True, act=act, alpha=0.1, clip=(-0.5, 0.75), pad_value=-0.75)
+    rng = np.random.default_rng(177 + i)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    x, wt = bf16_round(x), bf16_round(wt)
+    print(f"case {i} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, wt, b, sl, dtype="bf16", repeat=2)
+    ref = oracle_layer(L, x, wt, b, sl, pad_value=-0.75)
+    assert kname == "grouped_bf16"
+    assert_close(y, ref, BF16_TOL, f"case {i} ({kname})")
     assert_bitexact(runs[1], runs[0], "repeat")
 
 
