@@ -42,7 +42,7 @@ const char* kernel_name(const Desc& d) {
     case KC_IGEMM_F32: return d.flatten_1x1 ? "igemm_f32_pointwise" : "igemm_f32";
     case KC_IGEMM_BF16: return d.flatten_1x1 ? "igemm_bf16_pointwise" : "igemm_bf16";
     case KC_DW: return d.p.dtype == CONV_DTYPE_BF16 ? "depthwise_bf16" : "depthwise_f32";
-    case KC_QDW: return "depthwise_i8";
+    case KC_QDW: return d.cfg == 1 ? "depthwise_i8_dot4" : "depthwise_i8";
     case KC_QPW: return "pointwise_i8_mfma";
     case KC_DIRECT: return "direct";
     case KC_GROUPED: return d.p.dtype == CONV_DTYPE_BF16 ? "grouped_bf16" : "grouped_f32";

@@ -136,6 +136,7 @@ hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw,
                               hipStream_t s);
 
@@ -147,6 +148,7 @@ bool plan_dw(Desc& d);
 bool plan_qdw(Desc& d);
 bool plan_qpw(Desc& d);
 bool plan_grouped(const Desc& d);
+bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.

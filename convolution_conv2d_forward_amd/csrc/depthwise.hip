@@ -322,12 +322,23 @@ bool plan_dw(Desc& d) {
     return d.p.dtype == CONV_DTYPE_BF16 ? plan_dw_t<__hip_bfloat16>(d) : plan_dw_t<float>(d);
 }
 
-bool plan_qdw(Desc& d) { return plan_dw_t<int8_t>(d); }
+// int8: the byte-plane dot-product kernel for 3x3 s1/s2 (cfg 1), else the
+// generic one (cfg 0).
+bool plan_qdw(Desc& d) {
+    if (plan_qdw3(d)) {
+        d.cfg = 1;
+        return true;
+    }
+    d.cfg = 0;
+    return plan_dw_t<int8_t>(d);
+}
 
 hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s) {
     return d.p.dtype == CONV_DTYPE_BF16 ? launch_t<__hip_bfloat16>(d, a, s) : launch_t<float>(d, a, s);
 }
 
-hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s) { return launch_t<int8_t>(d, a, s); }
+hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s) {
+    return d.cfg == 1 ? launch_qdw3(d, a, s) : launch_t<int8_t>(d, a, s);
+}
 
 }  // namespace conv2d

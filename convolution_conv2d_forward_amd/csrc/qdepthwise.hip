@@ -1,0 +1,207 @@
+// int8 depthwise 3x3 (stride 1 or 2, dilation 1): the yscv int8 depthwise
+// QLinearConv (int32 accumulation, + int32 bias, requant) on the VALU
+// dot-product unit.
+//
+//   * A workgroup owns P whole (n, c) planes.  They are staged in LDS as
+//     int8 (not widened), one 16-byte chunk per global load: chunks inside
+//     the image are copied, the margins and the rows outside it are the
+//     zero point (0), so no tap needs a bounds check.
+//   * A thread computes 4 consecutive outputs of one row (one 32-bit store of
+//     4 requantized bytes).  For each filter row it reads the covering LDS
+//     dwords once; the 3 input bytes under output j are cut out with
+//     v_alignbyte and multiplied by the packed (w0, w1, w2, 0) with one
+//     v_dot4_i32_i8, exact in int32 like the oracle's sum.
+//   * The byte offset of the first tap inside its dword depends only on
+//     pad_left, so it is a template parameter and every byte select is a
+//     fixed instruction.
+#include "device_common.h"
+
+namespace conv2d {
+
+namespace {
+
+constexpr int kQT = 256;
+constexpr int kMarg = 16;    // zero bytes left of input column 0 in every LDS row
+constexpr int kNQ = 16;      // 16-byte chunks per thread (bound checked when planning)
+
+// LDS geometry of a plane for stride ss, pad_left pl, input width w, output width wo.
+struct QGeom {
+    int rows, row_bytes, plane_bytes, planes;
+};
+
+__host__ __device__ inline int qdw_q0(int k, int ss, int pl) { return ss * k + ((kMarg - pl) >> 2); }
+
+// Requant with the rounding mode fixed at compile time (same arithmetic as
+// the shared requant(): f32 product, then ties-to-even or ties-away).
+template <int RND>
+__device__ __forceinline__ uint32_t rq(int32_t acc, float comp, int y_zp, bool relu) {
+    const float yf = __fmul_rn((float)acc, comp);
+    const float r = RND == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
+    int q = (int)r + y_zp;
+    q = q < -128 ? -128 : (q > 127 ? 127 : q);
+    if (relu && q < y_zp) q = y_zp;
+    return (uint32_t)(uint8_t)(int8_t)q;
+}
+
+template <int SS, int OFF, int RND>
+__global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row_bytes, int P) {
+    extern __shared__ __align__(16) uint8_t lds8[];
+    const int plane_bytes = rows * row_bytes;
+    int32_t* wpk = (int32_t*)(lds8 + P * plane_bytes);     // [P][3] packed filter rows
+    int32_t* bsh = wpk + 3 * P;                             // [P] bias
+
+    const int cblocks = (a.c_out + P - 1) / P;
+    const int n = blockIdx.x / cblocks;
+    const int c0 = (blockIdx.x - n * cblocks) * P;
+    const int np = min(P, a.c_out - c0);
+    const int64_t HW = (int64_t)a.h * a.w;
+    const int8_t* __restrict__ xp = (const int8_t*)a.xptr + ((int64_t)n * a.in_total + a.in_off + c0) * HW;
+
+    // ---- planes -> LDS: all chunk loads first, then the LDS writes ----
+    const int cpr = row_bytes / 16;                        // chunks per LDS row
+    const int nchunks = np * rows * cpr;
+    uint4 buf[kNQ];
+#pragma unroll
+    for (int i = 0; i < kNQ; ++i) {
+        const int e = threadIdx.x + i * kQT;
+        buf[i] = make_uint4(0, 0, 0, 0);
+        if (e < nchunks) {
+            const int p = e / (rows * cpr);
+            const int rem = e - p * rows * cpr;
+            const int r = rem / cpr, j = rem - r * cpr;
+            const int ih = r - a.pad_top, iw = 16 * j - kMarg;
+            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w)
+                buf[i] = *(const uint4*)(xp + p * HW + (int64_t)ih * a.w + iw);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kNQ; ++i) {
+        const int e = threadIdx.x + i * kQT;
+        if (e < nchunks) {
+            const int p = e / (rows * cpr);
+            const int rem = e - p * rows * cpr;
+            *(uint4*)(lds8 + p * plane_bytes + rem * 16) = buf[i];
+        }
+    }
+    if (threadIdx.x < np * 3) {
+        const int p = threadIdx.x / 3, r = threadIdx.x - p * 3;
+        const int8_t* w = (const int8_t*)a.wptr + (int64_t)(c0 + p) * 9 + 3 * r;
+        wpk[threadIdx.x] = (int32_t)((uint32_t)(uint8_t)w[0] | ((uint32_t)(uint8_t)w[1] << 8) |
+                                     ((uint32_t)(uint8_t)w[2] << 16));
+    }
+    if (threadIdx.x < np) bsh[threadIdx.x] = a.qbias ? a.qbias[c0 + threadIdx.x] : 0;
+    __syncthreads();
+
+    // ---- outputs: 4 consecutive columns of one row per unit ----
+    // A thread keeps one column group k and walks down the rows of the P
+    // planes (rpi rows apart), so its LDS and output addresses only advance.
+    constexpr int ND = SS == 1 ? 3 : 4;                    // dwords covering the taps of 4 outputs
+    const int wq = a.wo / 4;
+    const int rpi = kQT / wq;                              // rows covered by one pass of the workgroup
+    const int t0 = divu((uint32_t)threadIdx.x, a.dv_tiles_w);
+    if (t0 >= rpi) return;                                 // (no barrier follows)
+    const int k = threadIdx.x - t0 * wq;
+    const int64_t oplane = (int64_t)a.ho * a.wo;
+    const bool relu = a.act == CONV_ACT_RELU;
+    const int q0 = qdw_q0(k, SS, a.pad_left);
+    int p = 0, ho = t0;
+    while (ho >= a.ho && p < np) { ho -= a.ho; ++p; }
+    for (; p < np;) {
+        const uint8_t* prow = lds8 + p * plane_bytes + ho * SS * row_bytes + 4 * q0;
+        int32_t acc[4];
+        const int32_t b = bsh[p];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = b;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const uint32_t* src = (const uint32_t*)(prow + r * row_bytes);
+            uint32_t d[ND];
+#pragma unroll
+            for (int t = 0; t < ND; ++t) d[t] = src[t];
+            const int32_t wr = wpk[3 * p + r];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int idx = OFF + SS * j;              // byte of the first tap, from dword q0
+                const uint32_t lo = d[idx >> 2], hi = d[(idx >> 2) + 1 < ND ? (idx >> 2) + 1 : ND - 1];
+                const uint32_t win = (idx & 3) ? __builtin_amdgcn_alignbyte(hi, lo, idx & 3) : lo;
+                acc[j] = __builtin_amdgcn_sdot4((int)win, wr, acc[j], false);
+            }
+        }
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) packed |= rq<RND>(acc[j], a.composite, a.y_zp, relu) << (8 * j);
+        int8_t* y = (int8_t*)a.yptr + ((int64_t)n * a.out_total + a.out_off + c0 + p) * oplane + (int64_t)ho * a.wo;
+        *(uint32_t*)(y + 4 * k) = packed;
+        ho += rpi;
+        while (ho >= a.ho && p < np) { ho -= a.ho; ++p; }
+    }
+}
+
+// Byte offset of output 0's first tap inside dword q0: (kMarg - pad_left) & 3.
+template <int SS, int RND>
+const void* pick_off(int off) {
+    switch (off) {
+    case 0: return (const void*)qdw3_kernel<SS, 0, RND>;
+    case 1: return (const void*)qdw3_kernel<SS, 1, RND>;
+    case 2: return (const void*)qdw3_kernel<SS, 2, RND>;
+    default: return (const void*)qdw3_kernel<SS, 3, RND>;
+    }
+}
+
+template <int SS>
+const void* pick_rnd(int off, int rounding) {
+    return rounding == CONV_ROUND_HALF_AWAY ? pick_off<SS, CONV_ROUND_HALF_AWAY>(off)
+                                            : pick_off<SS, CONV_ROUND_HALF_EVEN>(off);
+}
+
+bool qgeom(const Desc& d, QGeom& G) {
+    const conv2d_params_t& p = d.p;
+    const int ss = p.stride_h;
+    const int pl = p.pad_left;
+    const int wq = d.wo / 4;
+    // Last byte a unit reads in a row: dwords q0 .. q0 + ND - 1 of the last column group.
+    const int nd = ss == 1 ? 3 : 4;
+    const int last = 4 * (qdw_q0(wq - 1, ss, pl) + nd) - 1;
+    int rb = kMarg + p.w + 16;
+    if (last + 1 > rb) rb = last + 1;
+    G.row_bytes = (rb + 15) / 16 * 16;
+    G.rows = (d.ho - 1) * ss + 3;
+    G.plane_bytes = G.rows * G.row_bytes;
+    int P = (32 * 1024) / G.plane_bytes;
+    if (P > 8) P = 8;
+    if (P < 1) P = 1;
+    while (P > 1 && P * G.rows * (G.row_bytes / 16) > kNQ * kQT) --P;
+    G.planes = P;
+    return P * G.rows * (G.row_bytes / 16) <= kNQ * kQT && P * G.plane_bytes + 16 * P <= 64 * 1024;
+}
+
+}  // namespace
+
+bool plan_qdw3(const Desc& d) {
+    const conv2d_params_t& p = d.p;
+    if (p.k_h != 3 || p.k_w != 3 || p.dilation_h != 1 || p.dilation_w != 1) return false;
+    if (p.stride_h != p.stride_w || (p.stride_h != 1 && p.stride_h != 2)) return false;
+    if (p.w % 16 != 0 || d.wo % 4 != 0 || p.pad_left > kMarg) return false;
+    if ((int64_t)p.h * p.w >= INT32_MAX / 16) return false;
+    QGeom G;
+    return qgeom(d, G);
+}
+
+hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s) {
+    if ((uintptr_t)a.xptr % 16 != 0 || (uintptr_t)a.yptr % 4 != 0) return launch_direct(d, a, s);
+    QGeom G;
+    if (!qgeom(d, G)) return hipErrorInvalidConfiguration;
+    const int64_t blocks = (int64_t)a.n * ((a.c_out + G.planes - 1) / G.planes);
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int off = (kMarg - d.p.pad_left) & 3;
+    a.dv_tiles_h = make_divu32((uint32_t)(a.ho * (a.wo / 4)));
+    a.dv_tiles_w = make_divu32((uint32_t)(a.wo / 4));
+    const void* fn = d.p.stride_h == 1 ? pick_rnd<1>(off, a.rounding) : pick_rnd<2>(off, a.rounding);
+    int rows = G.rows, rb = G.row_bytes, P = G.planes;
+    void* args[] = {&a, &rows, &rb, &P};
+    const size_t lds = (size_t)P * G.plane_bytes + 16 * P;
+    return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kQT), args, lds, s);
+}
+
+}  // namespace conv2d

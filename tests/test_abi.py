@@ -120,7 +120,7 @@ def test_kernel_choice_for_the_workloads():
         d = cc().conv2d_desc_create(cc().make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride,
                                                      pads=L.pads, groups=L.groups, dtype="i8"))
         names[L.name] = cc().conv2d_desc_kernel_name(d)
-    assert names["dw_s1"] == names["dw_s2"] == "depthwise_i8" and names["pw"] == "pointwise_i8_mfma"
+    assert names["dw_s1"] == names["dw_s2"] == "depthwise_i8_dot4" and names["pw"] == "pointwise_i8_mfma"
 
 
 def _raw(fn, *args):

@@ -377,6 +377,12 @@ INT8_CASES = [
     (1, 20, 7, 9, 30, 1, 1, 0, 1),         # pw K not multiple of 16, HW odd
     (1, 200, 4, 8, 70, 1, 1, 0, 1),        # pw K 200 (4 chunks), M 70
     (2, 6, 9, 11, 10, 3, 1, 1, 2),         # grouped int8 3x3: direct path
+    # byte-plane 3x3 kernel: every first-tap byte offset (pad_left mod 4), both strides
+    (2, 16, 12, 48, 16, 3, 1, (1, 0, 1, 2), 16),   # s1, pad_left 0
+    (1, 24, 10, 32, 24, 3, 1, (2, 3, 0, 3), 24),   # s1, pad_left 3
+    (2, 8, 17, 64, 8, 3, 2, (1, 2, 1, 0), 8),      # s2, pad_left 2
+    (1, 9, 16, 32, 9, 3, 2, 1, 9),                 # s2, pad_left 1, 9 planes (partial last workgroup)
+    (3, 5, 9, 16, 5, 3, 1, 1, 5),                  # s1, tiny planes
 ]
 
 
@@ -384,7 +390,8 @@ INT8_CASES = [
 @pytest.mark.parametrize("mode", ["rne", "away_relu_zp"])
 def test_int8_cases(i, mode):
     n, c, h, w, co, k, s, p, g = INT8_CASES[i]
-    L = workloads.Layer("q", n, c, h, w, co, (k, k), stride=(s, s), pads=(p,) * 4, groups=g, has_bias=True)
+    p4 = p if isinstance(p, tuple) else (p,) * 4
+    L = workloads.Layer("q", n, c, h, w, co, (k, k), stride=(s, s), pads=p4, groups=g, has_bias=True)
     rng = np.random.default_rng(900 + i)
     x = rng.integers(-128, 127, size=L.x_shape, endpoint=True).astype(np.int8)
     wt = rng.integers(-127, 127, size=L.w_shape, endpoint=True).astype(np.int8)
