@@ -161,10 +161,13 @@ class Desc:
     def __init__(self, handle, params):
         self.handle = handle
         self.params = params
+        # Kept on the instance: module globals may already be gone when the
+        # last descriptors are collected at interpreter exit.
+        self._destroy = _lib.conv2d_desc_destroy
 
     def __del__(self):
-        if getattr(self, "handle", None):
-            _lib.conv2d_desc_destroy(self.handle)
+        if getattr(self, "handle", None) and getattr(self, "_destroy", None) is not None:
+            self._destroy(self.handle)
             self.handle = None
 
 
