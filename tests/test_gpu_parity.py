@@ -99,6 +99,45 @@ def test_kernel_classes_fp32(i, pad_value):
     assert_bitexact(runs[1], runs[0], "repeat")
 
 
+@pytest.mark.parametrize("i", range(len(CLASS_CASES)))
+def test_kernel_classes_bf16(i):
+    """The same shapes in bf16 (fp32 accumulate): the bf16 implicit GEMM's tile
+    configurations, partial channel chunks, ragged tiles, pad cells, stride-2
+    column split, and the fallbacks."""
+    n, ci, h, w, co, k, s, p, d, g, act = CLASS_CASES[i]
+    k2 = k if isinstance(k, tuple) else (k, k)
+    s2 = s if isinstance(s, tuple) else (s, s)
+    d2 = d if isinstance(d, tuple) else (d, d)
+    p4 = p if isinstance(p, tuple) else (p, p, p, p)
+    L = workloads.Layer("case", n, ci, h, w, co, k2, stride=s2, pads=p4, dilation=d2, groups=g,
+                        has_bias=True, act=act, alpha=0.1, clip=(-0.5, 0.75), pad_value=-0.75)
+    rng = np.random.default_rng(277 + i)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    x, wt = bf16_round(x), bf16_round(wt)
+    print(f"case {i} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, wt, b, sl, dtype="bf16", repeat=2)
+    ref = oracle_layer(L, x, wt, b, sl, pad_value=-0.75)
+    assert_close(y, ref, BF16_TOL, f"bf16 case {i} ({kname})")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+@pytest.mark.parametrize("n,ci,co,k", [(1, 40, 48, 3), (3, 24, 20, 3), (2, 64, 136, 1)])
+def test_concat_tail_bf16(n, ci, co, k):
+    """bf16 implicit GEMM writing channels [off, off+co) of a larger buffer:
+    the slice matches the oracle, every other channel keeps its NaN guard."""
+    h, w, off = 11, 24, 5
+    L = workloads.Layer("tail", n, ci, h, w, co, (k, k), pads=(k // 2,) * 4, has_bias=True,
+                        act=workloads.ACT_PRELU)
+    rng = np.random.default_rng(41 + n + co)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    x, wt = bf16_round(x), bf16_round(wt)
+    y, kname, _ = gpu_layer(L, x, wt, b, sl, dtype="bf16", out_total=off + co + 3, out_off=off)
+    assert kname.startswith("igemm_bf16")
+    ref = oracle_layer(L, x, wt, b, sl)
+    assert np.isnan(y[:, :off]).all() and np.isnan(y[:, off + co:]).all(), "channels outside the slice written"
+    assert_close(y[:, off:off + co], ref, BF16_TOL, f"bf16 tail ({kname})")
+
+
 GROUPED_CASES = [i for i, c in enumerate(CLASS_CASES) if c[9] > 1 and c[1] // c[9] in (4, 8)
                  and c[1] == c[4] and c[5] == 3]
 
