@@ -202,22 +202,18 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
     // one, read beyond the buffer and get zeros without touching memory (no
     // per-lane branches, so no register merges that would make the compiler
     // hold later LDS reads behind these loads).
-    auto load_x = [&](int kc, uint4 (&xr)[C::XS][8]) __attribute__((always_inline)) {
-        const int c0 = kc * C::CC;
-#pragma unroll
-        for (int i = 0; i < C::XS; ++i) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, tvo[i] + 2 * (c0 + t) * HW, 0, 0);
-                xr[i][t] = make_uint4(v.x, v.y, v.z, v.w);
-            }
-        }
+    auto load_row = [&](int kc, uint4 (&xr)[C::XS][8], int j) __attribute__((always_inline)) {
+        const int i = j / 8, t = j % 8;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xrs, tvo[i] + 2 * (kc * C::CC + t) * HW, 0, 0);
+        xr[i][t] = make_uint4(v.x, v.y, v.z, v.w);
     };
-    // Registers -> LDS: 8 channels x 8 pixels become 8 cells of 8 channels.
-    auto store_x = [&](const uint4 (&xr)[C::XS][8], uint4* bst) __attribute__((always_inline)) {
+    auto load_x = [&](int kc, uint4 (&xr)[C::XS][8]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::XS; ++i) {
-            if (toff[i] < 0) continue;
+        for (int j = 0; j < 8 * C::XS; ++j) load_row(kc, xr, j);
+    };
+    // Registers -> LDS: 8 channels x 8 pixels of task i become 8 cells of 8 channels.
+    auto store_task = [&](const uint4 (&xr)[C::XS][8], uint4* bst, int i) __attribute__((always_inline)) {
+        if (toff[i] >= 0) {
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 uint32_t d[4];
@@ -231,6 +227,10 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
                 bst[tcell[i] + pcell(p)] = make_uint4(d[0], d[1], d[2], d[3]);
             }
         }
+    };
+    auto store_x = [&](const uint4 (&xr)[C::XS][8], uint4* bst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < C::XS; ++i) store_task(xr, bst, i);
     };
 
     // ---- operand offsets (cells) ----
@@ -263,7 +263,10 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](const uint4* st) __attribute__((always_inline)) {
+    // The MFMAs of one chunk; after step s, between(s) runs (the
+    // transposition of the next chunk's rows goes there, so that its VALU and
+    // LDS writes issue while the matrix core works).
+    auto compute = [&](const uint4* st, auto&& between) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             const int tg = 4 * s + q;
@@ -279,39 +282,71 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[ni], av[mi], acc[mi][ni], 0, 0, 0);
+            between(s);
         }
     };
+    auto nothing = [](int) {};
 
     // ---- main loop ----
     // Two LDS stages: chunk c computes from stage c%2 while chunk c+1's
     // weight image lands in the other one and its rows (loaded into
-    // registers one chunk earlier) are transposed into it after the MFMAs.
-    // Input rows are loaded two chunks ahead into two register sets: rows of
-    // chunk k live in R[k%2].  Steady-state steps load and wait
+    // registers one step earlier) are transposed into it between chunk c's
+    // MFMA steps.  Input rows are loaded two chunks ahead into two register
+    // sets: rows of chunk k live in R[k%2].  Steady-state steps load and wait
     // unconditionally, so the compiler sees nothing outstanding at the top of
-    // a step; the wait before the transposition leaves the newest row loads
-    // in flight.
-    constexpr int VMX = 8 * C::XS;   // row loads per chunk and thread
-    static_assert(VMX < 64, "vmcnt field");
-    constexpr int WAIT_ROWS = (VMX & 15) | (7 << 4) | (15 << 8) | ((VMX >> 4) << 14);   // vmcnt(VMX) only
+    // a step.  Loads complete in issue order, so a wait for "at most n
+    // outstanding" leaves exactly the newest n in flight: right after a
+    // step's copies are issued, waiting down to (this step's weight copies +
+    // row loads) means the previous step's row loads have landed.  A wave
+    // issues DMAR/NW or one more weight copies; the wait counts the smaller
+    // number, which at worst also waits for one of this step's copies.
+    constexpr int VMX = 8 * C::XS;                 // row loads per chunk and thread
+    constexpr int DMA_LO = C::DMAR / C::NW;        // fewest weight copies per wave and chunk
+    static_assert(VMX + DMA_LO < 64, "vmcnt field");
+    auto vm_wait = [](auto n) __attribute__((always_inline)) {
+        constexpr int N = decltype(n)::value;
+        __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));   // vmcnt(N) only
+    };
+    using vm_rows_prev = std::integral_constant<int, VMX + DMA_LO>;
+    using vm_rows_new = std::integral_constant<int, VMX>;
+    using vm_copies = std::integral_constant<int, DMA_LO>;
+    using vm_none = std::integral_constant<int, 0>;
     const int nch = a.chunks;
     uint4 R0[C::XS][8], R1[C::XS][8];
     auto stage = [&](int k) __attribute__((always_inline)) { return (k & 1) ? st1 : st0; };
+    // Between the MFMA steps of chunk c: the row loads of chunk c+2 are
+    // issued a few at a time over steps 0..S_ROWS (issued all at once, they
+    // fill the memory unit's queue and stall the wave, MFMAs included), and
+    // after step S_ROWS the rows of chunk c+1, loaded during the previous
+    // chunk, are waited for and transposed into the free stage.
+    constexpr int S_ROWS = STEPS >= 3 ? STEPS - 2 : STEPS - 1;
+    auto interleave = [&](const uint4 (&rs)[C::XS][8], uint4* bst, int kl, uint4 (*rl)[C::XS][8], auto n)
+        __attribute__((always_inline)) {
+        return [&rs, bst, kl, rl, &store_task, &load_row, &vm_wait, n](int s) __attribute__((always_inline)) {
+            if (rl) {
+#pragma unroll
+                for (int j = 0; j < VMX; ++j)
+                    if (j * (S_ROWS + 1) / VMX == s) load_row(kl, *rl, j);
+            }
+            if (s == S_ROWS) {
+                vm_wait(n);
+#pragma unroll
+                for (int i = 0; i < C::XS; ++i) store_task(rs, bst, i);
+            }
+        };
+    };
     // Step c with chunk c+2 to prefetch: rows of c+1 are in rs, rows of c+2 go to rl.
     auto step_full = [&](int c, uint4 (&rl)[C::XS][8], const uint4 (&rs)[C::XS][8]) __attribute__((always_inline)) {
         dma_w(c + 1, stage(c + 1));
-        load_x(c + 2, rl);
-        compute(stage(c));
-        __builtin_amdgcn_s_waitcnt(WAIT_ROWS);   // weight image and rows of chunk c+1 have landed
-        store_x(rs, stage(c + 1) + C::ACELLS);
+        compute(stage(c), interleave(rs, stage(c + 1) + C::ACELLS, c + 2, &rl, vm_rows_prev{}));   // rows of c+1 landed
+        vm_wait(vm_rows_new{});                  // chunk c+1's weight image has landed
         __syncthreads();
     };
     // Step c, c+1 being the last chunk.
     auto step_last = [&](int c, const uint4 (&rs)[C::XS][8]) __attribute__((always_inline)) {
         dma_w(c + 1, stage(c + 1));
-        compute(stage(c));
-        __builtin_amdgcn_s_waitcnt(0);
-        store_x(rs, stage(c + 1) + C::ACELLS);
+        compute(stage(c), interleave(rs, stage(c + 1) + C::ACELLS, 0, nullptr, vm_copies{}));   // rows of c+1 landed
+        vm_wait(vm_none{});
         __syncthreads();
     };
     dma_w(0, st0);
@@ -334,7 +369,7 @@ __global__ __launch_bounds__(C::NT) void igemm_bf16_kernel(ConvArgs a) {
         step_last(c, R1);
         c += 1;
     }
-    compute(stage(c));
+    compute(stage(c), nothing);
     __syncthreads();
 
     // ---- epilogue: bias, activation, bf16, store ----
