@@ -10,7 +10,8 @@ built, importing this package raises.
 
 Names and argument order follow the C ABI:
     conv2d_params_init, conv2d_desc_create, conv2d_desc_destroy,
-    conv2d_desc_get_output_shape, conv2d_desc_kernel_name, conv2d_forward,
+    conv2d_desc_get_output_shape, conv2d_desc_kernel_name,
+    conv2d_desc_bind_weights, conv2d_forward,
     fused_pw_dw_forward, qconv2d_forward, conv2d_status_string,
     conv2d_last_error
 plus ``make_params`` (keyword construction of a params struct).
@@ -79,6 +80,8 @@ def _load():
     lib.conv2d_desc_get_output_shape.restype = i32
     lib.conv2d_desc_kernel_name.argtypes = [vp]
     lib.conv2d_desc_kernel_name.restype = ctypes.c_char_p
+    lib.conv2d_desc_bind_weights.argtypes = [vp, vp, vp]
+    lib.conv2d_desc_bind_weights.restype = i32
     lib.conv2d_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.conv2d_forward.restype = i32
     lib.fused_pw_dw_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -96,8 +99,8 @@ _lib = _load()
 
 # C ABI symbols this binding relies on (the header declares exactly these).
 EXPORTED = ("conv2d_params_init", "conv2d_desc_create", "conv2d_desc_destroy", "conv2d_desc_get_output_shape",
-            "conv2d_desc_kernel_name", "conv2d_forward", "fused_pw_dw_forward", "qconv2d_forward",
-            "conv2d_status_string", "conv2d_last_error")
+            "conv2d_desc_kernel_name", "conv2d_desc_bind_weights", "conv2d_forward", "fused_pw_dw_forward",
+            "qconv2d_forward", "conv2d_status_string", "conv2d_last_error")
 
 
 def conv2d_status_string(status: int) -> str:
@@ -241,8 +244,17 @@ def _sizes(desc):
     return x_numel, w_numel, y_numel
 
 
+def conv2d_desc_bind_weights(desc: Desc, w, stream=None) -> None:
+    """Copy (and, where the kernel wants it, re-lay) w into the descriptor;
+    forward calls given w=None then use that copy."""
+    p = desc.params
+    _, wn, _ = _sizes(desc)
+    _check(_lib.conv2d_desc_bind_weights(desc.handle, _ptr(w, "w", _ELEM[p.dtype], wn), _stream(stream)))
+
+
 def conv2d_forward(desc: Desc, x, w, bias, slope, y, stream=None) -> None:
-    """Float convolution (F32 or BF16 descriptor), launched on `stream`."""
+    """Float convolution (F32 or BF16 descriptor), launched on `stream`.
+    w=None uses the weights bound with conv2d_desc_bind_weights."""
     p = desc.params
     et = _ELEM[p.dtype]
     xn, wn, yn = _sizes(desc)

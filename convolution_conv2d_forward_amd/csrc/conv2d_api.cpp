@@ -129,6 +129,26 @@ conv_status_t check_desc(conv2d_desc_t d) {
     return CONV_OK;
 }
 
+// Weights a forward call uses: w itself, or (w null) the descriptor's bound
+// copy, which must live on the current device.  what names the operand.
+conv_status_t resolve_weights(const Desc& d, const void*& w, const char* what) {
+    if (w) return CONV_OK;
+    if (!d.bound) return fail(CONV_ERR_INVALID_ARG, "null %s and no weights bound to the descriptor", what);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != d.wbound_device)
+        return fail(CONV_ERR_INVALID_ARG, "%s were bound on device %d, current device is %d", what, d.wbound_device, dev);
+    w = d.wbound;
+    return CONV_OK;
+}
+
+void free_on(void* ptr, int device) {
+    if (!ptr) return;
+    int cur = -1;
+    const bool switched = hipGetDevice(&cur) == hipSuccess && cur != device && hipSetDevice(device) == hipSuccess;
+    (void)hipFree(ptr);
+    if (switched) (void)hipSetDevice(cur);
+}
+
 }  // namespace
 
 extern "C" {
@@ -270,14 +290,49 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
 void conv2d_desc_destroy(conv2d_desc_t dd) {
     Desc* d = (Desc*)dd;
     if (!d) return;
-    if (d->wpack) {
-        int cur = -1;
-        const bool switched = hipGetDevice(&cur) == hipSuccess && cur != d->wpack_device &&
-                              hipSetDevice(d->wpack_device) == hipSuccess;
-        (void)hipFree(d->wpack);
-        if (switched) (void)hipSetDevice(cur);
-    }
+    free_on(d->wpack, d->wpack_device);
+    free_on(d->wbound, d->wbound_device);
     delete d;
+}
+
+conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* stream) {
+    if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
+    Desc& d = *(Desc*)dd;
+    if (!w) return fail(CONV_ERR_INVALID_ARG, "null weights");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(CONV_ERR_HIP, "no current HIP device");
+    if (d.wpack_device >= 0 && dev != d.wpack_device)
+        return fail(CONV_ERR_INVALID_ARG, "descriptor was created on device %d, current device is %d",
+                    d.wpack_device, dev);
+    if (d.wbound && dev != d.wbound_device)
+        return fail(CONV_ERR_INVALID_ARG, "weights were first bound on device %d, current device is %d",
+                    d.wbound_device, dev);
+    const int64_t wb = w_bytes(d);
+    const bool packs = d.kclass == KC_IGEMM_BF16;
+    const int64_t off = packs ? (wb + 255) / 256 * 256 : 0;
+    const int64_t total = packs ? off + d.wpack_bytes : wb;
+    if (views_overlap(flat(w, wb), flat(d.wbound, d.wbound_bytes)))
+        return fail(CONV_ERR_ALIAS, "w is the descriptor's own bound copy");
+    if (!d.wbound) {
+        const hipError_t e = hipMalloc(&d.wbound, (size_t)total);
+        if (e != hipSuccess) {
+            d.wbound = nullptr;
+            return fail(CONV_ERR_HIP, "allocating %lld bytes for the bound weights: %s", (long long)total,
+                        hipGetErrorString(e));
+        }
+        d.wbound_bytes = total;
+        d.wbound_device = dev;
+    }
+    d.wbound_pack_off = packs ? off : 0;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(d.wbound, w, (size_t)wb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && packs) e = pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s);
+    if (e != hipSuccess) {
+        d.bound = false;
+        return hip_status(e, "binding weights");
+    }
+    d.bound = true;
+    return ok();
 }
 
 conv_status_t conv2d_desc_get_output_shape(conv2d_desc_t dd, int32_t out[4]) {
@@ -301,7 +356,9 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
     const Desc& d = *(const Desc*)dd;
     if (d.p.dtype == CONV_DTYPE_I8) return fail(CONV_ERR_INVALID_ARG, "int8 descriptor: use qconv2d_forward");
-    if (!x || !w || !y) return fail(CONV_ERR_INVALID_ARG, "null x, w or y");
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    const bool use_bound = !w;
+    if (resolve_weights(d, w, "weights") != CONV_OK) return CONV_ERR_INVALID_ARG;
     if (d.p.has_bias && !bias) return fail(CONV_ERR_INVALID_ARG, "has_bias set but bias is null");
     if (d.p.act_type == CONV_ACT_PRELU && !slope) return fail(CONV_ERR_INVALID_ARG, "PReLU needs a slope pointer");
     const View yv = y_view(d, y);
@@ -322,7 +379,9 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     hipError_t e;
     switch (d.kclass) {
     case KC_IGEMM_F32: e = launch_igemm_f32(d, a, s); break;
-    case KC_IGEMM_BF16: e = launch_igemm_bf16(d, a, s); break;
+    case KC_IGEMM_BF16:
+        e = launch_igemm_bf16(d, a, s, use_bound ? (const char*)d.wbound + d.wbound_pack_off : nullptr);
+        break;
     case KC_DW: e = launch_dw(d, a, s); break;
     case KC_GROUPED: e = launch_grouped(d, a, s); break;
     default: e = launch_direct(d, a, s); break;
@@ -355,7 +414,10 @@ conv_status_t fused_pw_dw_forward(conv2d_desc_t dpw, conv2d_desc_t ddw, const vo
     int32_t th = 0, lds = 0;
     if (!plan_fused_pw_dw(pw, dw, &th, &lds))
         return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
-    if (!x || !w_pw || !w_dw || !y) return fail(CONV_ERR_INVALID_ARG, "null x, weights or y");
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    if (resolve_weights(pw, w_pw, "pointwise weights") != CONV_OK ||
+        resolve_weights(dw, w_dw, "depthwise weights") != CONV_OK)
+        return CONV_ERR_INVALID_ARG;
     if (P.has_bias && !b_pw) return fail(CONV_ERR_INVALID_ARG, "pw has_bias set but bias is null");
     if (D.has_bias && !b_dw) return fail(CONV_ERR_INVALID_ARG, "dw has_bias set but bias is null");
     if (P.act_type == CONV_ACT_PRELU && !slope_pw) return fail(CONV_ERR_INVALID_ARG, "pw PReLU needs slopes");
@@ -392,14 +454,16 @@ conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, 
     const float composite = comp;
     if (!(std::isfinite(composite) && composite > 0))
         return fail(CONV_ERR_INVALID_ARG, "composite scale x_scale*w_scale/y_scale is not a positive finite float");
-    if (!x || !w || !y) return fail(CONV_ERR_INVALID_ARG, "null x, w or y");
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    const void* wv = w;
+    if (resolve_weights(d, wv, "weights") != CONV_OK) return CONV_ERR_INVALID_ARG;
     if (d.p.has_bias && !bias) return fail(CONV_ERR_INVALID_ARG, "has_bias set but bias is null");
     const View yv = y_view(d, y);
     if (views_overlap(yv, x_view(d, x))) return fail(CONV_ERR_ALIAS, "y overlaps the input channels read");
-    if (views_overlap(yv, flat(w, w_bytes(d)))) return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if (views_overlap(yv, flat(wv, w_bytes(d)))) return fail(CONV_ERR_ALIAS, "y overlaps the weights");
     if (d.p.has_bias && views_overlap(yv, flat(bias, 4 * (int64_t)d.p.c_out)))
         return fail(CONV_ERR_ALIAS, "y overlaps the bias");
-    ConvArgs a = make_args(d, x, w, nullptr, nullptr, y);
+    ConvArgs a = make_args(d, x, wv, nullptr, nullptr, y);
     a.qbias = d.p.has_bias ? bias : nullptr;
     a.composite = composite;
     a.y_zp = y_zp;

@@ -125,12 +125,25 @@ struct Desc {
     // column shift, 8-pixel vectors per row, LDS row / plane stride in cells,
     // stride-2 half width)
     int32_t g_ph = 0, g_span = 0, g_shift = 0, g_nvr = 0, g_rs = 0, g_plane = 0, g_half = 0;
+    // Weights bound with conv2d_desc_bind_weights: an OIHW copy at wbound,
+    // followed for the bf16 implicit GEMM by the packed image at
+    // wbound + wbound_pack_off (0 = no packed image).
+    void* wbound = nullptr;
+    int64_t wbound_bytes = 0;
+    int64_t wbound_pack_off = 0;
+    int wbound_device = -1;
+    bool bound = false;
 };
 
 // Launchers (implemented next to their kernels).  Each returns the
 // hipError_t of the launch.
 hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s);
-hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s);
+// packed: the weights already in the kernel's layout (bound weights), or
+// null to pack a.wptr (OIHW) into d.wpack first.
+hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed);
+// OIHW bf16 weights -> the bf16 implicit GEMM's per-chunk LDS images at dst
+// (d.wpack_bytes bytes).
+hipError_t pack_igemm_bf16_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);

@@ -594,7 +594,23 @@ bool plan_igemm_bf16(Desc& d) {
     return false;
 }
 
-hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s) {
+hipError_t pack_igemm_bf16_weights(const Desc& d, const void* w, void* dst, hipStream_t s) {
+    const CfgInfo& c = cfg(d.cfg);
+    const conv2d_params_t& p = d.p;
+    const int64_t total = d.wpack_bytes / 16;
+    if (total == 0) return hipSuccess;
+    const void* w_src = w;
+    uint4* pk = (uint4*)dst;
+    int64_t tot = total;
+    int bm = c.bm, tga = c.tga, gq = c.cc / 8, cc = c.cc, khw = p.k_h * p.k_w,
+        chunks = (d.cin_g + c.cc - 1) / c.cc, co_tiles = (d.cout_g + c.bm - 1) / c.bm, cin_g = d.cin_g,
+        cout_g = d.cout_g;
+    void* pargs[] = {&w_src, &pk, &tot, &bm, &tga, &gq, &cc, &khw, &chunks, &co_tiles, &cin_g, &cout_g};
+    return hipLaunchKernel((const void*)pack_weights_bf16, dim3((uint32_t)((total + 255) / 256)), dim3(256), pargs,
+                           0, s);
+}
+
+hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed) {
     // The kernel reads input rows as 16-byte vectors.
     if ((uintptr_t)a.xptr % 16 != 0) return launch_direct(d, a, s);
     const CfgInfo& c = cfg(d.cfg);
@@ -621,24 +637,19 @@ hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s) {
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     a.num_blocks = (uint32_t)blocks;
-    if (!d.wpack || d.wpack_bytes != wpack_cells(d, c) * 16) return hipErrorInvalidValue;
-
-    // 1) weights -> per-chunk LDS images
-    const int64_t total = d.wpack_bytes / 16;
-    const void* w_src = a.wptr;
-    uint4* pk = (uint4*)d.wpack;
-    int64_t tot = total;
-    int bm = c.bm, tga = c.tga, gq = c.cc / 8, cc = c.cc, khw = p.k_h * p.k_w, chunks = a.chunks,
-        co_tiles = a.co_tiles, cin_g = d.cin_g, cout_g = d.cout_g;
-    void* pargs[] = {&w_src, &pk, &tot, &bm, &tga, &gq, &cc, &khw, &chunks, &co_tiles, &cin_g, &cout_g};
-    hipError_t e = hipLaunchKernel((const void*)pack_weights_bf16, dim3((uint32_t)((total + 255) / 256)), dim3(256),
-                                   pargs, 0, s);
-    if (e != hipSuccess) return e;
+    if (d.wpack_bytes != wpack_cells(d, c) * 16) return hipErrorInvalidValue;
+    // 1) weights -> per-chunk LDS images (unless they are bound, packed once)
+    if (!packed) {
+        if (!d.wpack) return hipErrorInvalidValue;
+        const hipError_t e = pack_igemm_bf16_weights(d, a.wptr, d.wpack, s);
+        if (e != hipSuccess) return e;
+        packed = d.wpack;
+    }
 
     // 2) the convolution
-    a.wptr = d.wpack;
+    a.wptr = packed;
     if (d.lds_bytes > 64 * 1024) {
-        e = hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, d.lds_bytes);
+        const hipError_t e = hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, d.lds_bytes);
         if (e != hipSuccess) return e;
     }
     void* args[] = {&a};

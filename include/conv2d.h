@@ -29,8 +29,10 @@
  * Ownership: the caller allocates and owns every input and output buffer;
  * forward calls launch kernels asynchronously on the caller's HIP stream and
  * return, and allocate nothing.  Descriptors are owned by the library from
- * conv2d_desc_create until conv2d_desc_destroy and are immutable after
- * creation.  One exception to "no library device memory": a BF16 descriptor
+ * conv2d_desc_create until conv2d_desc_destroy; their attributes are fixed at
+ * creation, and the only later change is weights bound with
+ * conv2d_desc_bind_weights (a device copy the descriptor owns; see there).
+ * Apart from that copy, one exception to "no library device memory": a BF16 descriptor
  * whose kernel is the implicit GEMM (any BF16 dense or grouped convolution
  * that is not depthwise; conv2d_desc_kernel_name starts with "igemm_bf16")
  * allocates, at creation and on the current device, a buffer for the weights
@@ -142,8 +144,29 @@ CONV2D_API conv_status_t conv2d_desc_get_output_shape(conv2d_desc_t d, int32_t o
 /* Name of the kernel class chosen at creation (static string; for logs). */
 CONV2D_API const char* conv2d_desc_kernel_name(conv2d_desc_t d);
 
+/* Bind weights to the descriptor once, as ncnn transforms and packs weights
+ * once when a layer's pipeline is created instead of on every forward (the
+ * yscv page, section "Hot kernel paths", likewise packs int8 weights once at
+ * load).  The library copies w (OIHW, the descriptor's dtype; device
+ * pointer) into a device buffer it allocates on the first bind, on the
+ * current device, and owns until conv2d_desc_destroy; for the BF16 implicit
+ * GEMM it also re-lays the copy into the kernel's per-chunk layout, so
+ * forward calls that use the bound weights skip that step.  Forward calls
+ * (conv2d_forward, fused_pw_dw_forward, qconv2d_forward) use the bound copy
+ * when their weight pointer is null.  The copy and the re-layout are queued
+ * on `stream` (hipStream_t, null = default stream): forward calls on the same
+ * stream see them; calls on other streams must be ordered by the caller.
+ * Binding again replaces the bound weights in place (ordered the same way
+ * against forward calls still reading the old ones).  Errors: INVALID_ARG for
+ * a null descriptor or w, or a device other than the descriptor's; ALIAS if w
+ * is the descriptor's own bound copy; HIP if the buffer cannot be allocated or
+ * a copy/launch fails (no weights are then bound). */
+CONV2D_API conv_status_t conv2d_desc_bind_weights(conv2d_desc_t d, const void* w, void* stream);
+
 /* Float convolution (dtype F32 or BF16).
- *   x, w, y   device pointers of the dtype's element type, layouts above
+ *   x, w, y   device pointers of the dtype's element type, layouts above;
+ *             w null = the weights bound to the descriptor (INVALID_ARG if
+ *             none are bound, or they were bound on another device)
  *   bias      device float32[c_out]; required iff has_bias, else ignored
  *   slope     device float32[prelu_slope_count]; required iff act is PRELU
  *   stream    hipStream_t (null = default stream)
@@ -158,7 +181,8 @@ CONV2D_API conv_status_t conv2d_forward(conv2d_desc_t d, const void* x, const vo
  * desc_pw.c_out, same n/h/w, same dtype (F32).  The expanded tensor stays in
  * on-chip memory; the depthwise padding applies to the pointwise output, so
  * taps outside the image read desc_dw.pad_value.  y layout is desc_dw's.
- * Pointers as in conv2d_forward (b_* / slope_* nullable per descriptor).
+ * Pointers as in conv2d_forward (b_* / slope_* nullable per descriptor; a
+ * null w_pw or w_dw selects that descriptor's bound weights).
  * Errors: INCOMPATIBLE_SHAPES for a pair that does not chain; UNSUPPORTED for
  * a dtype other than F32 or a dw stride other than 1; ALIAS as above. */
 CONV2D_API conv_status_t fused_pw_dw_forward(conv2d_desc_t desc_pw, conv2d_desc_t desc_dw, const void* x,
@@ -170,7 +194,7 @@ CONV2D_API conv_status_t fused_pw_dw_forward(conv2d_desc_t desc_pw, conv2d_desc_
  * then q = saturate_int8(round(f32(acc + bias) * composite) + y_zp), with
  * composite = f32(f32(x_scale * w_scale) / y_scale) computed on the host and
  * round = the descriptor's int8_rounding; ReLU (if set) is max(q, y_zp).
- *   x, w, y   device int8 pointers (layouts above)
+ *   x, w, y   device int8 pointers (layouts above); w null = bound weights
  *   bias      device int32[c_out] or null
  * Errors: UNSUPPORTED if x_zp != 0 or w_zp != 0 (symmetric scheme only);
  * INVALID_ARG if a scale is not finite and positive or dtype is not I8. */

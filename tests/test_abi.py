@@ -29,7 +29,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 11, syms
     lib = ctypes.CDLL(cc().LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), f"{s} declared in conv2d.h but not exported"
@@ -177,6 +177,30 @@ def test_fused_pair_validation():
     assert call(dw, dw, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
     assert call(pw, s2, X + 0x400000) == cc().CONV_ERR_UNSUPPORTED
     assert call(pw, dw, X) == cc().CONV_ERR_ALIAS
+
+
+def test_bound_weights_validation():
+    """Null weights need bound ones; a null bind is refused.  Every call
+    below returns before any HIP call (nothing is bound, so none reaches the
+    device)."""
+    lib = cc()._lib
+    X = 0x30000000
+    xb = 2 * 4 * 64 * 4
+    d = cc().conv2d_desc_create(cc().make_params(2, 4, 8, 8, 4, 3, pads=1))
+    assert _raw(lib.conv2d_desc_bind_weights, d.handle, 0, None) == cc().CONV_ERR_INVALID_ARG
+    assert _raw(lib.conv2d_forward, d.handle, X, 0, None, None, X + 10 * xb, None) == cc().CONV_ERR_INVALID_ARG
+    assert "no weights bound" in cc().conv2d_last_error()
+    assert _raw(lib.conv2d_desc_bind_weights, 0, X, None) == cc().CONV_ERR_INVALID_ARG
+    dq = cc().conv2d_desc_create(cc().make_params(2, 4, 8, 8, 4, 3, pads=1, dtype="i8"))
+    f = ctypes.c_float
+    assert lib.qconv2d_forward(dq.handle, ctypes.c_void_p(X), f(0.1), ctypes.c_int8(0), None, f(0.1),
+                               ctypes.c_int8(0), None, f(0.1), ctypes.c_int8(0), ctypes.c_void_p(X + 9 * xb),
+                               None) == cc().CONV_ERR_INVALID_ARG
+    pw = cc().conv2d_desc_create(cc().make_params(2, 8, 10, 10, 16, 1))
+    dw = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 3, pads=1, groups=16))
+    assert lib.fused_pw_dw_forward(pw.handle, dw.handle, ctypes.c_void_p(X), None, None, None,
+                                   ctypes.c_void_p(X + 0x100000), None, None, ctypes.c_void_p(X + 0x400000),
+                                   None) == cc().CONV_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():
