@@ -327,6 +327,20 @@ def per_config(reps, only="all"):
         t = time_layer("fused", fns, reps)
         fb = 4 * (L1.n * L1.c_in * L1.h * L1.w + L1.c_out * L1.c_in + L2.c_out * 9 + L2.n * L2.c_out * L2.h * L2.w)
         res["fused_pw_dw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "f32"), kernel="fused_pw_dw")
+        # dw -> pw2 fused: the depthwise output stays on chip
+        d3 = cc.conv2d_desc_create(params_of(L3))
+        w3 = t_(a["w_pw2"])
+        xe = t_(np.random.default_rng(3).standard_normal(L2.x_shape).astype(np.float32))
+
+        def make_dwpw():
+            xi = xe.clone()
+            yi = torch.empty((L3.n, L3.c_out, L3.h, L3.w), device=dev())
+            return lambda: cc.fused_dw_pw_forward(d2, d3, xi, w2, None, None, w3, None, None, yi)
+
+        fns = _rotating(make_dwpw, (L2.n * L2.c_in + L3.n * L3.c_out) * L2.h * L2.w * 4)
+        t = time_layer("fused_dw_pw", fns, reps)
+        fb = 4 * (L2.n * L2.c_in * L2.h * L2.w + L2.c_out * 9 + L3.c_out * L3.c_in + L3.n * L3.c_out * L3.h * L3.w)
+        res["fused_dw_pw"] = dict(roofline_entry(L2.flops + L3.flops, fb, t, "f32"), kernel="fused_dw_pw")
         out["bottleneck"] = res
         log("bottleneck", res)
 

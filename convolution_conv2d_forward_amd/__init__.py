@@ -12,7 +12,7 @@ Names and argument order follow the C ABI:
     conv2d_params_init, conv2d_desc_create, conv2d_desc_destroy,
     conv2d_desc_get_output_shape, conv2d_desc_kernel_name,
     conv2d_desc_bind_weights, conv2d_forward,
-    fused_pw_dw_forward, qconv2d_forward, conv2d_status_string,
+    fused_pw_dw_forward, fused_dw_pw_forward, qconv2d_forward, conv2d_status_string,
     conv2d_last_error
 plus ``make_params`` (keyword construction of a params struct).
 """
@@ -86,6 +86,8 @@ def _load():
     lib.conv2d_forward.restype = i32
     lib.fused_pw_dw_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fused_pw_dw_forward.restype = i32
+    lib.fused_dw_pw_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fused_dw_pw_forward.restype = i32
     lib.qconv2d_forward.argtypes = [vp, vp, f32, i8, vp, f32, i8, vp, f32, i8, vp, vp]
     lib.qconv2d_forward.restype = i32
     lib.conv2d_status_string.argtypes = [i32]
@@ -100,7 +102,7 @@ _lib = _load()
 # C ABI symbols this binding relies on (the header declares exactly these).
 EXPORTED = ("conv2d_params_init", "conv2d_desc_create", "conv2d_desc_destroy", "conv2d_desc_get_output_shape",
             "conv2d_desc_kernel_name", "conv2d_desc_bind_weights", "conv2d_forward", "fused_pw_dw_forward",
-            "qconv2d_forward", "conv2d_status_string", "conv2d_last_error")
+            "fused_dw_pw_forward", "qconv2d_forward", "conv2d_status_string", "conv2d_last_error")
 
 
 def conv2d_status_string(status: int) -> str:
@@ -279,6 +281,23 @@ def fused_pw_dw_forward(desc_pw: Desc, desc_dw: Desc, x, w_pw, b_pw, slope_pw, w
         _ptr(w_dw, "w_dw", et, wdn),
         _ptr(b_dw, "b_dw", "float32", pd.c_out) if pd.has_bias else None,
         _ptr(slope_dw, "slope_dw", "float32", pd.prelu_slope_count) if pd.act_type == ACT_PRELU else None,
+        _ptr(y, "y", et, yn), _stream(stream)))
+
+
+def fused_dw_pw_forward(desc_dw: Desc, desc_pw: Desc, x, w_dw, b_dw, slope_dw, w_pw, b_pw, slope_pw, y,
+                        stream=None) -> None:
+    """Fused depthwise kxk -> pointwise 1x1 (F32)."""
+    pd, pp = desc_dw.params, desc_pw.params
+    et = _ELEM[pd.dtype]
+    xn, wdn, _ = _sizes(desc_dw)
+    _, wpn, yn = _sizes(desc_pw)
+    _check(_lib.fused_dw_pw_forward(
+        desc_dw.handle, desc_pw.handle, _ptr(x, "x", et, xn), _ptr(w_dw, "w_dw", et, wdn),
+        _ptr(b_dw, "b_dw", "float32", pd.c_out) if pd.has_bias else None,
+        _ptr(slope_dw, "slope_dw", "float32", pd.prelu_slope_count) if pd.act_type == ACT_PRELU else None,
+        _ptr(w_pw, "w_pw", et, wpn),
+        _ptr(b_pw, "b_pw", "float32", pp.c_out) if pp.has_bias else None,
+        _ptr(slope_pw, "slope_pw", "float32", pp.prelu_slope_count) if pp.act_type == ACT_PRELU else None,
         _ptr(y, "y", et, yn), _stream(stream)))
 
 

@@ -437,6 +437,52 @@ conv_status_t fused_pw_dw_forward(conv2d_desc_t dpw, conv2d_desc_t ddw, const vo
     return hip_status(launch_fused_pw_dw(pw, dw, apw, adw, (hipStream_t)stream), "fused_pw_dw");
 }
 
+conv_status_t fused_dw_pw_forward(conv2d_desc_t ddw, conv2d_desc_t dpw, const void* x, const void* w_dw,
+                                  const float* b_dw, const float* slope_dw, const void* w_pw, const float* b_pw,
+                                  const float* slope_pw, void* y, void* stream) {
+    if (!ddw || !dpw) return fail(CONV_ERR_INVALID_ARG, "null descriptor");
+    const Desc& dw = *(const Desc*)ddw;
+    const Desc& pw = *(const Desc*)dpw;
+    const conv2d_params_t& D = dw.p;
+    const conv2d_params_t& P = pw.p;
+    if (P.dtype != D.dtype) return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "dw and pw dtypes differ");
+    if (D.dtype != CONV_DTYPE_F32) return fail(CONV_ERR_UNSUPPORTED, "fused dw->pw supports F32 only");
+    if (!(D.groups == D.c_in && D.groups == D.c_out))
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "first descriptor must be depthwise (groups == c_in == c_out)");
+    if (P.k_h != 1 || P.k_w != 1 || P.stride_h != 1 || P.stride_w != 1 || P.groups != 1 || P.pad_top ||
+        P.pad_left || P.pad_bottom || P.pad_right)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "second descriptor must be a 1x1, stride 1, unpadded, ungrouped conv");
+    if (P.c_in != D.c_out || P.n != D.n || P.h != dw.ho || P.w != dw.wo)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "dw output [%d,%d,%d,%d] does not match pw input [%d,%d,%d,%d]",
+                    D.n, D.c_out, dw.ho, dw.wo, P.n, P.c_in, P.h, P.w);
+    if (dw.out_total != D.c_out || D.out_channel_offset != 0 || P.in_channel_offset != 0 || pw.in_total != P.c_in)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "the depthwise output has no buffer: dw output and pw input must be "
+                                                  "plain (no channel offsets)");
+    if (D.k_h > 5 || D.k_w > 5) return fail(CONV_ERR_UNSUPPORTED, "fused dw->pw supports depthwise windows up to 5x5");
+    if (!plan_fused_dw_pw(dw, pw)) return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    if (resolve_weights(dw, w_dw, "depthwise weights") != CONV_OK ||
+        resolve_weights(pw, w_pw, "pointwise weights") != CONV_OK)
+        return CONV_ERR_INVALID_ARG;
+    if (D.has_bias && !b_dw) return fail(CONV_ERR_INVALID_ARG, "dw has_bias set but bias is null");
+    if (P.has_bias && !b_pw) return fail(CONV_ERR_INVALID_ARG, "pw has_bias set but bias is null");
+    if (D.act_type == CONV_ACT_PRELU && !slope_dw) return fail(CONV_ERR_INVALID_ARG, "dw PReLU needs slopes");
+    if (P.act_type == CONV_ACT_PRELU && !slope_pw) return fail(CONV_ERR_INVALID_ARG, "pw PReLU needs slopes");
+    const View yv = y_view(pw, y);
+    if (views_overlap(yv, x_view(dw, x))) return fail(CONV_ERR_ALIAS, "y overlaps x");
+    if (views_overlap(yv, flat(w_dw, w_bytes(dw))) || views_overlap(yv, flat(w_pw, w_bytes(pw))))
+        return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if ((D.has_bias && views_overlap(yv, flat(b_dw, 4 * (int64_t)D.c_out))) ||
+        (P.has_bias && views_overlap(yv, flat(b_pw, 4 * (int64_t)P.c_out))))
+        return fail(CONV_ERR_ALIAS, "y overlaps a bias");
+    if ((D.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope_dw, 4 * (int64_t)D.prelu_slope_count))) ||
+        (P.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope_pw, 4 * (int64_t)P.prelu_slope_count))))
+        return fail(CONV_ERR_ALIAS, "y overlaps PReLU slopes");
+    ConvArgs adw = make_args(dw, x, w_dw, b_dw, slope_dw, nullptr);
+    ConvArgs apw = make_args(pw, nullptr, w_pw, b_pw, slope_pw, y);
+    return hip_status(launch_fused_dw_pw(dw, pw, adw, apw, (hipStream_t)stream), "fused_dw_pw");
+}
+
 conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, int8_t x_zp, const int8_t* w,
                               float w_scale, int8_t w_zp, const int32_t* bias, float y_scale, int8_t y_zp,
                               int8_t* y, void* stream) {

@@ -152,6 +152,8 @@ hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw,
                               hipStream_t s);
+hipError_t launch_fused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, ConvArgs apw,
+                              hipStream_t s);
 
 // Tile planners (host): fill the tiling fields of d; return false if the
 // shape cannot use the class (the caller then falls back to KC_DIRECT).
@@ -163,6 +165,7 @@ bool plan_qpw(Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
+bool plan_fused_dw_pw(const Desc& dw, const Desc& pw);
 
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.
 

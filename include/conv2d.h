@@ -190,6 +190,23 @@ CONV2D_API conv_status_t fused_pw_dw_forward(conv2d_desc_t desc_pw, conv2d_desc_
                                   const void* w_dw, const float* b_dw, const float* slope_dw,
                                   void* y, void* stream);
 
+/* Fused depthwise kxk -> pointwise 1x1 (the yscv FusedDwPw step).  desc_dw:
+ * groups == c_in == c_out, window up to 5x5, any stride, dilation and pads;
+ * its input may be a channel slice of a larger buffer (in_channel_offset /
+ * in_total_channels).  desc_pw: 1x1, stride 1, pads 0, groups 1, c_in ==
+ * desc_dw.c_out, h/w == desc_dw's output size, same n and dtype (F32); its
+ * output may be a channel slice (ConcatFusedTail).  The depthwise output stays
+ * in on-chip memory; y layout is desc_pw's.  Pointers as in
+ * fused_pw_dw_forward (a null w_dw or w_pw selects that descriptor's bound
+ * weights).  Errors: INCOMPATIBLE_SHAPES for a pair that does not chain (or a
+ * depthwise output / pointwise input with channel offsets, which have no
+ * buffer here); UNSUPPORTED for a dtype other than F32, a window beyond 5x5
+ * or rows too wide for the on-chip tile; ALIAS as above. */
+CONV2D_API conv_status_t fused_dw_pw_forward(conv2d_desc_t desc_dw, conv2d_desc_t desc_pw, const void* x,
+                                  const void* w_dw, const float* b_dw, const float* slope_dw,
+                                  const void* w_pw, const float* b_pw, const float* slope_pw,
+                                  void* y, void* stream);
+
 /* Symmetric int8 QLinearConv (dtype I8): int32 accumulation, + int32 bias,
  * then q = saturate_int8(round(f32(acc + bias) * composite) + y_zp), with
  * composite = f32(f32(x_scale * w_scale) / y_scale) computed on the host and

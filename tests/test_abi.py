@@ -29,7 +29,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 12, syms
     lib = ctypes.CDLL(cc().LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), f"{s} declared in conv2d.h but not exported"
@@ -201,6 +201,25 @@ def test_bound_weights_validation():
     assert lib.fused_pw_dw_forward(pw.handle, dw.handle, ctypes.c_void_p(X), None, None, None,
                                    ctypes.c_void_p(X + 0x100000), None, None, ctypes.c_void_p(X + 0x400000),
                                    None) == cc().CONV_ERR_INVALID_ARG
+
+
+def test_fused_dw_pw_rejects():
+    lib = cc()._lib
+    X = 0x40000000
+    dw = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 3, pads=1, groups=16))
+    pw = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 8, 1))
+    pw_bad = cc().conv2d_desc_create(cc().make_params(2, 12, 10, 10, 8, 1))
+    dense = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 3, pads=1))
+    dw7 = cc().conv2d_desc_create(cc().make_params(2, 16, 16, 16, 16, 7, pads=3, groups=16))
+    pw16 = cc().conv2d_desc_create(cc().make_params(2, 16, 16, 16, 8, 1))
+    args = [ctypes.c_void_p(X + i * 0x100000) for i in range(3)]
+    call = lambda a, b, y: lib.fused_dw_pw_forward(a.handle, b.handle, args[0], args[1], None, None, args[2],
+                                                   None, None, ctypes.c_void_p(y), None)
+    assert call(dw, pw_bad, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
+    assert call(dense, pw, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
+    assert call(pw, dw, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
+    assert call(dw7, pw16, X + 0x400000) == cc().CONV_ERR_UNSUPPORTED
+    assert call(dw, pw, X) == cc().CONV_ERR_ALIAS
 
 
 def test_binding_refuses_cpu_tensors():
