@@ -459,8 +459,8 @@ conv_status_t fused_dw_pw_forward(conv2d_desc_t ddw, conv2d_desc_t dpw, const vo
         return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "the depthwise output has no buffer: dw output and pw input must be "
                                                   "plain (no channel offsets)");
     if (D.k_h > 5 || D.k_w > 5) return fail(CONV_ERR_UNSUPPORTED, "fused dw->pw supports depthwise windows up to 5x5");
-    if (!plan_fused_dw_pw(dw, pw)) return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
     if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    if (!plan_fused_dw_pw(dw, pw, x)) return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
     if (resolve_weights(dw, w_dw, "depthwise weights") != CONV_OK ||
         resolve_weights(pw, w_pw, "pointwise weights") != CONV_OK)
         return CONV_ERR_INVALID_ARG;

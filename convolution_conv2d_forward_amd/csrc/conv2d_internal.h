@@ -165,7 +165,8 @@ bool plan_qpw(Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
-bool plan_fused_dw_pw(const Desc& dw, const Desc& pw);
+// x: the input pointer (its alignment decides between vector and scalar row loads).
+bool plan_fused_dw_pw(const Desc& dw, const Desc& pw, const void* x);
 
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.
 

@@ -11,9 +11,10 @@
 //      LDS tile whose pad rows and columns hold the depthwise pad_value
 //      (written once: they are the same for every chunk); the chunk's
 //      pointwise weights go to LDS as [k][co] at the same time;
-//   2. the depthwise conv reads VO outputs of one row per thread unit out of
-//      that tile (register window), adds its bias, applies its activation and
-//      writes the result to LDS as the GEMM's B operand, [k][pixel];
+//   2. the depthwise conv reads that tile (lane l of a 16-lane unit computes
+//      columns l, l+16, l+32, l+48 of one output row, so the lanes of a read
+//      touch consecutive LDS words), adds its bias, applies its activation and
+//      writes the result to LDS as the GEMM's A operand, [k][pixel];
 //   3. Y[co, pixel] += W_pw[co, k] * D[k, pixel] runs on the fp32 matrix
 //      cores (v_mfma_f32_16x16x4f32, the pixel fragment as first operand so a
 //      lane ends up holding 4 consecutive pixels of one output channel).
@@ -32,9 +33,10 @@ namespace {
 constexpr int kT = 512;
 constexpr int kWaves = kT / 64;
 constexpr int KC = 32;        // depthwise channels per chunk
-constexpr int VO = 4;         // depthwise outputs per thread unit (one row)
-constexpr int NXV = 8;        // 16-byte input loads per thread and chunk (upper bound)
-constexpr int NSC = 8;        // scalar-path input elements per thread and chunk, in units of kT
+constexpr int NPW = KC * 64 / kT;   // pointwise weights per thread and chunk (KC x up to 64 channels)
+constexpr int KHW_MAX = 25;   // depthwise windows up to 5x5
+constexpr int NDW = (KC * KHW_MAX + kT - 1) / kT;   // depthwise weights per thread and chunk
+constexpr int DWP = KC * KHW_MAX + 2 * KC;          // LDS floats of a chunk's depthwise weights, bias, slopes
 
 struct DwPwArgs {
     ConvArgs dw, pw;
@@ -44,29 +46,43 @@ struct DwPwArgs {
     int32_t xw;            // LDS row stride of the input tile
     int32_t xs_plane;      // LDS floats per channel of the input tile
     int32_t npx, nf;       // pixels of a tile (th * wo) and 16-pixel fragments
-    int32_t es_stride;     // LDS floats per channel of the depthwise result (= 16 mod 64)
-    int32_t cop;           // LDS row stride of the pointwise weight chunk (= 16 mod 64)
-    int32_t vec;           // input rows move as 16-byte vectors
+    int32_t es_stride;     // LDS floats per channel of the depthwise result (= 16 mod 32)
+    int32_t cop;           // LDS row stride of the pointwise weight chunk (= 16 mod 32)
     uint32_t num_blocks;
     DivU32 dv_co_tiles, dv_tiles_h;
+    FastDiv div_cg, div_th;   // 64-column groups per row; output rows per tile
 };
 
-__host__ __device__ inline int stride16(int n) {   // smallest s >= n with s % 64 == 16
-    int s = (n + 47) / 64 * 64 + 16;
-    return s < n ? s + 64 : s;
+// Smallest s >= n with s % 32 == 16: four rows s apart start 16 or 48 banks
+// apart, so a 4 x 16 operand fetch hits 64 distinct banks.
+__host__ __device__ inline int stride16(int n) {
+    const int s = n / 32 * 32 + 16;
+    return s < n ? s + 32 : s;
 }
+
+// One chunk's global data, held in registers between its loads and its LDS
+// writes (loaded two chunks ahead).  VEC: the input moves as 16-byte vectors.
+template <bool VEC, int NX>
+struct ChunkRegs {
+    typename std::conditional<VEC, f32x4, float>::type x[NX];
+    float pw[NPW];
+    float dwt[NDW];
+    float bias, slope;
+};
 
 // KH/KW/SS > 0: fixed 3x3 window with stride SS and dilation 1 (the reads are
 // constant offsets); 0: any window up to 5x5 with the descriptor's stride and
 // dilation.  MI: 16-channel output fragments (COT / 16).  NJ: pixel fragments
-// per wave.
-template <int KH, int KW, int SS, int MI, int NJ>
+// per wave.  VEC/NX: input loads per thread and chunk (16-byte vectors or
+// single floats).
+template <int KH, int KW, int SS, int MI, int NJ, bool VEC, int NX>
 __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     extern __shared__ __align__(16) float lds[];
     const ConvArgs& D = f.dw;
     const ConvArgs& P = f.pw;
     constexpr bool FIXED = KH > 0;
     const int kh = FIXED ? KH : D.k_h, kw = FIXED ? KW : D.k_w;
+    const int khw = kh * kw;
     const int sh = FIXED ? SS : D.stride_h, sw = FIXED ? SS : D.stride_w;
     const int dh = FIXED ? 1 : D.dilation_h, dwl = FIXED ? 1 : D.dilation_w;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -90,6 +106,7 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     float* xs = lds;                                        // [KC][ir][xw]
     float* es0 = xs + KC * f.xs_plane;                      // [KC][es_stride] x 2
     float* ws0 = es0 + 2 * KC * f.es_stride;                // [KC][cop] x 2
+    float* dp0 = ws0 + 2 * KC * f.cop;                      // [KC][khw], bias[KC], slope[KC] x 2
     const float* __restrict__ xg = (const float*)D.xptr + ((int64_t)n * D.in_total + D.in_off) * HW;
     const float* __restrict__ wdw = (const float*)D.wptr;
     const float* __restrict__ wpw = (const float*)P.wptr;
@@ -100,72 +117,83 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     for (int e = tid; e < KC * f.ir * f.xw; e += kT) {
         const int row = (e / f.xw) % f.ir, col = e % f.xw;
         const int ih = ih0 + row, iw = col - f.xoff;
-        if ((unsigned)ih >= (unsigned)H || (unsigned)iw >= (unsigned)W) xs[(e / (f.ir * f.xw)) * f.xs_plane + row * f.xw + col] = pv;
+        if ((unsigned)ih >= (unsigned)H || (unsigned)iw >= (unsigned)W) xs[e] = pv;
     }
 
-    // ---- chunk loads: input rows and pointwise weights into registers ----
-    const int w4 = W >> 2;
-    const int vunits = KC * f.ir * w4;                      // 4-pixel units of a chunk (vector path)
-    float4 xr[NXV];
-    float sr[NSC];
-    float wr[KC * 64 / kT];                                 // pointwise weights: KC x COT (<= 64) / kT per thread
-    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    // ---- chunk loads ----
+    // Every load is issued unconditionally (elements outside the tile read a
+    // valid address and are dropped when written to LDS), so each wave issues
+    // the same loads in the same order for every chunk and the compiler's
+    // waits before the LDS writes leave the next chunk's loads in flight.
+    const int per_ch = VEC ? f.ir * (W >> 2) : f.ir * W;    // load units per channel
+    const int units_x = KC * per_ch;
+    using Regs = ChunkRegs<VEC, NX>;
+    auto load_chunk = [&](int c, Regs& R) __attribute__((always_inline)) {
         const int c0 = c * KC;
-        if (f.vec) {
 #pragma unroll
-            for (int i = 0; i < NXV; ++i) {
-                const int u = tid + i * kT;
-                const int ch = u / (f.ir * w4), rem = u - ch * (f.ir * w4);
-                const int row = rem / w4, c4 = rem - row * w4;
-                const int ih = ih0 + row;
-                xr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (u < vunits && c0 + ch < C && (unsigned)ih < (unsigned)H)
-                    xr[i] = *(const float4*)(xg + (int64_t)(c0 + ch) * HW + (int64_t)ih * W + 4 * c4);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NSC; ++i) {
-                const int e = tid + i * kT;
-                const int ch = e / (f.ir * W), rem = e - ch * (f.ir * W);
-                const int row = rem / W, col = rem - row * W;
-                const int ih = ih0 + row;
-                sr[i] = 0.0f;
-                if (e < KC * f.ir * W && c0 + ch < C && (unsigned)ih < (unsigned)H)
-                    sr[i] = xg[(int64_t)(c0 + ch) * HW + (int64_t)ih * W + col];
-            }
+        for (int i = 0; i < NX; ++i) {
+            const int u = tid + i * kT;
+            const int ch = u / per_ch, rem = u - ch * per_ch;
+            int row, col;
+            if (VEC) { row = rem / (W >> 2); col = 4 * (rem - row * (W >> 2)); }
+            else { row = rem / W; col = rem - row * W; }
+            const bool ok = u < units_x && c0 + ch < C && (unsigned)(ih0 + row) < (unsigned)H;
+            const int64_t off = ok ? (int64_t)(c0 + ch) * HW + (int64_t)(ih0 + row) * W + col : 0;
+            if constexpr (VEC) R.x[i] = *(const f32x4*)(xg + off);
+            else R.x[i] = xg[off];
         }
+        // The loaded values are not touched here: masking them now would make
+        // the compiler wait for every load in flight, the next chunk's included.
 #pragma unroll
-        for (int i = 0; i < KC * 64 / kT; ++i) {
+        for (int i = 0; i < NPW; ++i) {
             const int e = tid + i * kT;                     // k-major: e = k * 64 + co
             const int k = e >> 6, co = e & 63;
-            wr[i] = (co < f.cot && co0 + co < P.c_out && c0 + k < C) ? wpw[(int64_t)(co0 + co) * C + c0 + k] : 0.0f;
+            const bool ok = co < f.cot && co0 + co < P.c_out && c0 + k < C;
+            R.pw[i] = wpw[ok ? (int64_t)(co0 + co) * C + c0 + k : 0];
         }
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) {
+            const int e = tid + i * kT;                     // e = ch * khw + tap
+            const bool ok = e < KC * khw && c0 * khw + e < C * khw;
+            R.dwt[i] = wdw[ok ? (int64_t)c0 * khw + e : 0];
+        }
+        const bool okc = tid < KC && c0 + tid < C;
+        const float* bsrc = D.bias ? D.bias : wdw;
+        const float* ssrc = D.act == CONV_ACT_PRELU ? D.slope : wdw;
+        R.bias = bsrc[okc && D.bias ? c0 + tid : 0];
+        R.slope = ssrc[okc && D.act == CONV_ACT_PRELU ? (D.slope_count == 1 ? 0 : c0 + tid) : 0];
     };
-    auto store_chunk = [&](float* ws) __attribute__((always_inline)) {
-        if (f.vec) {
+    auto store_chunk = [&](int c, const Regs& R, float* ws, float* dp) __attribute__((always_inline)) {
+        const int c0 = c * KC;
 #pragma unroll
-            for (int i = 0; i < NXV; ++i) {
-                const int u = tid + i * kT;
-                const int ch = u / (f.ir * w4), rem = u - ch * (f.ir * w4);
-                const int row = rem / w4, c4 = rem - row * w4;
-                if (u < vunits && (unsigned)(ih0 + row) < (unsigned)H)
-                    *(float4*)(xs + ch * f.xs_plane + row * f.xw + f.xoff + 4 * c4) = xr[i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NSC; ++i) {
-                const int e = tid + i * kT;
-                const int ch = e / (f.ir * W), rem = e - ch * (f.ir * W);
-                const int row = rem / W, col = rem - row * W;
-                if (e < KC * f.ir * W && (unsigned)(ih0 + row) < (unsigned)H)
-                    xs[ch * f.xs_plane + row * f.xw + f.xoff + col] = sr[i];
+        for (int i = 0; i < NX; ++i) {
+            const int u = tid + i * kT;
+            const int ch = u / per_ch, rem = u - ch * per_ch;
+            int row, col;
+            if (VEC) { row = rem / (W >> 2); col = 4 * (rem - row * (W >> 2)); }
+            else { row = rem / W; col = rem - row * W; }
+            if (u < units_x && (unsigned)(ih0 + row) < (unsigned)H) {
+                float* dst = xs + ch * f.xs_plane + row * f.xw + f.xoff + col;
+                if constexpr (VEC) *(f32x4*)dst = R.x[i];
+                else *dst = R.x[i];
             }
         }
 #pragma unroll
-        for (int i = 0; i < KC * 64 / kT; ++i) {
+        for (int i = 0; i < NPW; ++i) {
             const int e = tid + i * kT;
             const int k = e >> 6, co = e & 63;
-            if (co < f.cot) ws[k * f.cop + co] = wr[i];
+            const bool ok = co0 + co < P.c_out && c0 + k < C;
+            if (co < f.cot) ws[k * f.cop + co] = ok ? R.pw[i] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) {
+            const int e = tid + i * kT;
+            if (e < KC * khw) dp[e] = c0 * khw + e < C * khw ? R.dwt[i] : 0.0f;
+        }
+        if (tid < KC) {
+            const bool okc = c0 + tid < C;
+            dp[KC * KHW_MAX + tid] = okc && D.bias ? R.bias : 0.0f;
+            dp[KC * KHW_MAX + KC + tid] = okc ? R.slope : 0.0f;
         }
     };
 
@@ -175,83 +203,116 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[m][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int uw = (WO + VO - 1) / VO;
-    const int units = KC * th_n * uw;
-    load_chunk(0);
-    for (int c = 0; c < nch; ++c) {
-        float* es = es0 + (c & 1) * KC * f.es_stride;
-        float* ws = ws0 + (c & 1) * KC * f.cop;
-        store_chunk(ws);
-        __syncthreads();                                    // input tile and weights of chunk c are in LDS
-        if (c + 1 < nch) load_chunk(c + 1);
-
-        // ---- 2. depthwise into the GEMM operand ----
+    // ---- 2. depthwise into the GEMM operand ----
+    // A thread unit is 16 lanes' worth of one (channel, output row, 64-column
+    // group): lane l computes columns g*64 + l + 16v (v < 4), so the lanes of a
+    // window read touch consecutive LDS words (no bank conflicts at stride 1).
+    const int cgroups = (WO + 63) / 64;
+    const int units = KC * f.th * cgroups * 16;
+    auto depthwise = [&](int c, float* es, const float* dp) __attribute__((always_inline)) {
         const int c0 = c * KC;
         for (int u = tid; u < units; u += kT) {
-            const int ch = u / (th_n * uw), rem = u - ch * (th_n * uw);
-            const int r = rem / uw, q0 = (rem - r * uw) * VO;
-            const int cg = c0 + ch;
-            float outv[VO];
-            if (cg < C) {
-                float a[VO];
-#pragma unroll
-                for (int v = 0; v < VO; ++v) a[v] = 0.0f;
-                const float* src = xs + ch * f.xs_plane + r * sh * f.xw + f.xoff - D.pad_left + q0 * sw;
-                const float* wch = wdw + (int64_t)cg * kh * kw;
+            const int l = u & 15;
+            const int rest = u >> 4;
+            const int rg = (int)fdiv((uint32_t)rest, f.div_cg);        // ch * th + r
+            const int g = rest - rg * cgroups;
+            const int ch = (int)fdiv((uint32_t)rg, f.div_th);
+            const int r = rg - ch * f.th;
+            if (r >= th_n) continue;
+            const int col0 = g * 64 + l;
+            float outv[4];
+            if (c0 + ch < C) {
+                float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float* base = xs + ch * f.xs_plane + r * sh * f.xw + f.xoff - D.pad_left + col0 * sw;
+                const float* wch = dp + ch * khw;
                 if constexpr (FIXED) {
-                    constexpr int CIN = (VO - 1) * SS + KW;
 #pragma unroll
-                    for (int i = 0; i < KH; ++i) {
-                        float win[CIN];
-#pragma unroll
-                        for (int jj = 0; jj < CIN; ++jj) win[jj] = src[i * f.xw + jj];
+                    for (int i = 0; i < KH; ++i)
 #pragma unroll
                         for (int s2 = 0; s2 < KW; ++s2) {
                             const float wv = wch[i * KW + s2];
 #pragma unroll
-                            for (int v = 0; v < VO; ++v) a[v] = fmaf(win[v * SS + s2], wv, a[v]);
+                            for (int v = 0; v < 4; ++v) a[v] = fmaf(base[i * f.xw + 16 * v * SS + s2], wv, a[v]);
                         }
-                    }
                 } else {
                     for (int i = 0; i < kh; ++i)
                         for (int s2 = 0; s2 < kw; ++s2) {
                             const float wv = wch[i * kw + s2];
-                            const float* rp = src + i * dh * f.xw + s2 * dwl;
+                            const float* rp = base + i * dh * f.xw + s2 * dwl;
 #pragma unroll
-                            for (int v = 0; v < VO; ++v) a[v] = fmaf(rp[v * sw], wv, a[v]);
+                            for (int v = 0; v < 4; ++v) a[v] = fmaf(rp[16 * v * sw], wv, a[v]);
                         }
                 }
+                const float bb = dp[KC * KHW_MAX + ch], sl = dp[KC * KHW_MAX + KC + ch];
 #pragma unroll
-                for (int v = 0; v < VO; ++v) outv[v] = bias_act(D, a[v], cg);
+                for (int v = 0; v < 4; ++v) outv[v] = apply_act(D, a[v] + bb, sl);
             } else {
 #pragma unroll
-                for (int v = 0; v < VO; ++v) outv[v] = 0.0f;   // past the last channel: zero weights too
+                for (int v = 0; v < 4; ++v) outv[v] = 0.0f;   // past the last channel: zero weights too
             }
-            float* dst = es + ch * f.es_stride + r * WO + q0;
+            float* dst = es + ch * f.es_stride + r * WO;
 #pragma unroll
-            for (int v = 0; v < VO; ++v)
-                if (q0 + v < WO) dst[v] = outv[v];
+            for (int v = 0; v < 4; ++v)
+                if (col0 + 16 * v < WO) dst[col0 + 16 * v] = outv[v];
         }
-        __syncthreads();                                    // the depthwise rows of chunk c are in LDS
+    };
 
-        // ---- 3. pointwise on the matrix cores ----
-#pragma unroll
-        for (int kq = 0; kq < KC; kq += 4) {
+    // ---- 3. pointwise on the matrix cores ----
+    // The operands of k step t+1 are read from LDS while the MFMAs of step t run.
+    auto pointwise = [&](const float* es, const float* ws) __attribute__((always_inline)) {
+        float bv[2][MI], av[2][NJ];
+        auto fetch = [&](int kq, int set) __attribute__((always_inline)) {
             const int kr = kq + q;
-            float bv[MI];
 #pragma unroll
-            for (int m = 0; m < MI; ++m) bv[m] = ws[kr * f.cop + m * 16 + l16];
+            for (int m = 0; m < MI; ++m) bv[set][m] = ws[kr * f.cop + m * 16 + l16];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int fj = wave + kWaves * j;
-                if (fj < f.nf) {
-                    const float av = es[kr * f.es_stride + fj * 16 + l16];
+                av[set][j] = fj < f.nf ? es[kr * f.es_stride + fj * 16 + l16] : 0.0f;
+            }
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int t = 0; t < KC / 4; ++t) {
+            if (t + 1 < KC / 4) fetch(4 * (t + 1), (t + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                if (wave + kWaves * j < f.nf) {
 #pragma unroll
                     for (int m = 0; m < MI; ++m)
-                        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[m], acc[m][j], 0, 0, 0);
+                        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t & 1][j], bv[t & 1][m], acc[m][j], 0, 0, 0);
                 }
             }
         }
+    };
+
+    // Chunk c: its registers -> LDS (the input tile is free: the depthwise of
+    // chunk c-1 finished before the last barrier; the weight and result
+    // buffers c%2 were last read by chunk c-2's MFMAs), barrier, loads of
+    // chunk cn (two ahead) into the same registers, depthwise, barrier, MFMAs.
+    auto step = [&](int c, Regs& R, int cn) __attribute__((always_inline)) {
+        float* es = es0 + (c & 1) * KC * f.es_stride;
+        float* ws = ws0 + (c & 1) * KC * f.cop;
+        float* dp = dp0 + (c & 1) * DWP;
+        store_chunk(c, R, ws, dp);
+        __syncthreads();
+        load_chunk(cn, R);
+        depthwise(c, es, dp);
+        __syncthreads();
+        pointwise(es, ws);
+    };
+    // An even number of steps, two per iteration with fixed register sets, and
+    // loads in every step (the last two reload the last chunk; with an odd
+    // chunk count the extra chunk lies past the channels and adds zeros): no
+    // load sits behind a condition, so the waits stay exact.
+    const int nch2 = (nch + 1) & ~1;
+    Regs R0, R1;
+    load_chunk(0, R0);
+    load_chunk(1, R1);
+    for (int c = 0; c < nch2; c += 2) {
+        step(c, R0, min(c + 2, nch2 - 1));
+        step(c + 1, R1, min(c + 3, nch2 - 1));
     }
 
     // ---- epilogue: lane (q, l16) of fragment (m, j) holds output channel
@@ -285,7 +346,7 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
 }
 
 struct Plan {
-    int th, ir, xoff, xw, xs_plane, npx, nf, nj, es_stride, cot, cop, lds_floats, vec;
+    int th, ir, xoff, xw, xs_plane, npx, nf, nj, nx, es_stride, cot, cop, lds_floats;
 };
 
 int cu_count_dwpw() {
@@ -301,15 +362,21 @@ int cu_count_dwpw() {
     return cached;
 }
 
-bool plan(const Desc& dw, const Desc& pw, Plan* out) {
+// vec: the input moves as 16-byte vectors (row width and pointer allow it).
+bool plan(const Desc& dw, const Desc& pw, bool vec, Plan* out, int cot = 0) {
     const conv2d_params_t& d = dw.p;
     const int W = d.w, WO = dw.wo;
-    const bool vec = W % 4 == 0;
-    const int cot = pw.p.c_out <= 32 ? 32 : 64;
+    if (cot == 0) {
+        // 64 output channels per tile; 32 when there are few or the 64-wide
+        // variant does not fit the rows (each tile then redoes the depthwise).
+        if (pw.p.c_out > 32 && plan(dw, pw, vec, out, 64)) return true;
+        return plan(dw, pw, vec, out, 32);
+    }
     const int co_tiles = (pw.p.c_out + cot - 1) / cot;
     const int xoff = (d.pad_left + 3) / 4 * 4;
-    // Columns a tile reads: up to xoff - pad_left + (wo_padded-1)*sw + (kw-1)*dw + 1.
-    const int wo_pad = (WO + VO - 1) / VO * VO;
+    // Columns a tile reads (outputs padded to whole 64-column groups):
+    // up to xoff - pad_left + (wo_padded-1)*sw + (kw-1)*dw + 1.
+    const int wo_pad = (WO + 63) / 64 * 64;
     const int need = xoff - d.pad_left + (wo_pad - 1) * d.stride_w + (d.k_w - 1) * d.dilation_w + 1;
     int xw = xoff + W + d.pad_right;
     if (xw < need) xw = need;
@@ -322,11 +389,17 @@ bool plan(const Desc& dw, const Desc& pw, Plan* out) {
         const int nf = (npx + 15) / 16;
         const int nj = (nf + kWaves - 1) / kWaves;
         if (nj > 4) break;
-        if (vec ? KC * ir * (W / 4) > NXV * kT : KC * ir * W > NSC * kT) break;
+        const int units = vec ? KC * ir * (W / 4) : KC * ir * W;
+        const int nx = (units + kT - 1) / kT;
+        const int nxt = vec ? (nx <= 2 ? 2 : (nx <= 4 ? 4 : 8)) : 8;
+        const int njt = nj <= 2 ? 2 : 4;
+        // Variants that keep within 256 registers (larger ones spill).
+        const bool fits = (vec ? (nxt == 8 ? cot == 32 && njt == 2 : njt == 2 || (nxt == 2 && cot == 32)) : njt == 2);
+        if (nx > 8 || !fits) break;
         const int xs_plane = ir * xw;
         const int es_stride = stride16(nf * 16);
         const int cop = stride16(cot);
-        const int lds = KC * xs_plane + 2 * KC * es_stride + 2 * KC * cop;
+        const int lds = KC * xs_plane + 2 * KC * es_stride + 2 * KC * cop + 2 * DWP;
         if (lds * 4 > 160 * 1024) break;
         // One workgroup per compute unit: 8 waves of up to 256 registers.
         const long blocks = (long)d.n * ((dw.ho + th - 1) / th) * co_tiles;
@@ -334,7 +407,7 @@ bool plan(const Desc& dw, const Desc& pw, Plan* out) {
         // Time ~ rounds x input rows a workgroup stages (halo included).
         const long cost = rounds * ir;
         if (!ok || cost < best) {
-            *out = Plan{th, ir, xoff, xw, xs_plane, npx, nf, nj <= 2 ? 2 : 4, es_stride, cot, cop, lds, vec ? 1 : 0};
+            *out = Plan{th, ir, xoff, xw, xs_plane, npx, nf, njt, nxt, es_stride, cot, cop, lds};
             best = cost;
             ok = true;
         }
@@ -342,24 +415,38 @@ bool plan(const Desc& dw, const Desc& pw, Plan* out) {
     return ok;
 }
 
+// The instantiations the planner may pick (see `fits` there).
 template <int KH, int KW, int SS>
-const void* pick_mn(int mi, int nj) {
-    if (mi == 2) return nj == 2 ? (const void*)fused_dw_pw_kernel<KH, KW, SS, 2, 2> : (const void*)fused_dw_pw_kernel<KH, KW, SS, 2, 4>;
-    return nj == 2 ? (const void*)fused_dw_pw_kernel<KH, KW, SS, 4, 2> : (const void*)fused_dw_pw_kernel<KH, KW, SS, 4, 4>;
+const void* pick_x(bool vec, int nx, int mi, int nj) {
+#define K_(MI, NJ, V, NX) (const void*)fused_dw_pw_kernel<KH, KW, SS, MI, NJ, V, NX>
+    if (!vec) return mi == 2 ? K_(2, 2, false, 8) : K_(4, 2, false, 8);
+    if (nx == 8) return K_(2, 2, true, 8);
+    if (nx == 4) return mi == 2 ? K_(2, 2, true, 4) : K_(4, 2, true, 4);
+    if (mi == 2) return nj == 2 ? K_(2, 2, true, 2) : K_(2, 4, true, 2);
+    return K_(4, 2, true, 2);
+#undef K_
+}
+
+bool vec_ok(const Desc& dw, const void* x) {
+    const conv2d_params_t& d = dw.p;
+    const int64_t hw = (int64_t)d.h * d.w;
+    return d.w % 4 == 0 && ((uintptr_t)x % 16) == 0 && ((int64_t)d.in_channel_offset * hw) % 4 == 0 &&
+           ((int64_t)dw.in_total * hw) % 4 == 0;
 }
 
 }  // namespace
 
-bool plan_fused_dw_pw(const Desc& dw, const Desc& pw) {
+bool plan_fused_dw_pw(const Desc& dw, const Desc& pw, const void* x) {
     if (dw.p.k_h > 5 || dw.p.k_w > 5) return false;
     if ((int64_t)dw.p.h * dw.p.w >= INT32_MAX / 2 || (int64_t)dw.ho * dw.wo >= INT32_MAX / 2) return false;
     Plan pl{};
-    return plan(dw, pw, &pl);
+    return plan(dw, pw, vec_ok(dw, x), &pl);
 }
 
 hipError_t launch_fused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, ConvArgs apw, hipStream_t s) {
+    const bool vec = vec_ok(dw, adw.xptr);
     Plan pl{};
-    if (!plan(dw, pw, &pl)) return hipErrorInvalidConfiguration;
+    if (!plan(dw, pw, vec, &pl)) return hipErrorInvalidConfiguration;
     DwPwArgs f;
     f.dw = adw;
     f.pw = apw;
@@ -375,10 +462,10 @@ hipError_t launch_fused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, Conv
     f.nf = pl.nf;
     f.es_stride = pl.es_stride;
     f.cop = pl.cop;
-    f.vec = pl.vec && ((uintptr_t)adw.xptr % 16) == 0 &&
-            ((int64_t)adw.in_off * dw.p.h * dw.p.w) % 4 == 0 && ((int64_t)adw.in_total * dw.p.h * dw.p.w) % 4 == 0;
     f.dv_co_tiles = make_divu32((uint32_t)f.co_tiles);
     f.dv_tiles_h = make_divu32((uint32_t)f.tiles_h);
+    f.div_cg = make_fastdiv((uint32_t)((dw.wo + 63) / 64));
+    f.div_th = make_fastdiv((uint32_t)pl.th);
     const uint64_t blocks = (uint64_t)f.co_tiles * f.tiles_h * adw.n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
@@ -387,8 +474,9 @@ hipError_t launch_fused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, Conv
     const bool k3 = d.k_h == 3 && d.k_w == 3 && d.dilation_h == 1 && d.dilation_w == 1 && d.stride_h == d.stride_w &&
                     (d.stride_h == 1 || d.stride_h == 2);
     const int mi = pl.cot / 16;
-    const void* fn = !k3 ? pick_mn<0, 0, 0>(mi, pl.nj)
-                         : (d.stride_h == 1 ? pick_mn<3, 3, 1>(mi, pl.nj) : pick_mn<3, 3, 2>(mi, pl.nj));
+    const void* fn = !k3 ? pick_x<0, 0, 0>(vec, pl.nx, mi, pl.nj)
+                         : (d.stride_h == 1 ? pick_x<3, 3, 1>(vec, pl.nx, mi, pl.nj)
+                                            : pick_x<3, 3, 2>(vec, pl.nx, mi, pl.nj));
     const int lds = pl.lds_floats * 4;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
