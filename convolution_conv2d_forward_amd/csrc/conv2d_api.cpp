@@ -410,7 +410,6 @@ conv_status_t fused_pw_dw_forward(conv2d_desc_t dpw, conv2d_desc_t ddw, const vo
     if (pw.out_total != P.c_out || P.out_channel_offset != 0 || D.in_channel_offset != 0 || dw.in_total != D.c_in)
         return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "the expanded tensor has no buffer: pw output and dw input must be "
                                                   "plain (no channel offsets)");
-    if (D.stride_h != 1 || D.stride_w != 1) return fail(CONV_ERR_UNSUPPORTED, "fused pw->dw needs dw stride 1");
     int32_t th = 0, lds = 0;
     if (!plan_fused_pw_dw(pw, dw, &th, &lds))
         return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");

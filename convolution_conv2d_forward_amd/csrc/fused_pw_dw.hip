@@ -21,7 +21,9 @@
 //      a register window, adds its bias, applies its activation and writes
 //      each output row with a 16-byte store.
 // The halo rows are recomputed by the tiles above and below
-// ((TH + kh - 1) / TH pointwise work) instead of being exchanged.
+// (((TH-1)*stride + kh) / TH pointwise work) instead of being exchanged.
+// The depthwise may have any stride (the pages' depthwise steps are 3x3 and
+// 5x5 at stride 1 or 2); the fixed 3x3 register-window path is stride 1.
 #include "device_common.h"
 
 namespace conv2d {
@@ -84,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
     const int n = Q;
     const int ce0 = cet * CE;
     const int ho0 = tht * f.tile_h;
-    const int ih_lo = ho0 - D.pad_top;          // image row of pointwise row 0
+    const int sh = FIXED ? 1 : D.stride_h, sw = FIXED ? 1 : D.stride_w;
+    const int ih_lo = ho0 * sh - D.pad_top;     // image row of pointwise row 0
     const int W = P.w, H = P.h;
     const int npix = f.rows * W;                 // pointwise pixels of the tile
     const int nfn = (npix + 15) / 16;
@@ -263,13 +266,13 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
             for (int orow = 0; orow < RR; ++orow) {
                 if (r0 + orow >= th_n) break;
                 for (int r = 0; r < kh; ++r) {
-                    const float* row = ech + (r0 + orow + r * dh) * f.ew;
+                    const float* row = ech + ((r0 + orow) * sh + r * dh) * f.ew;
                     for (int s2 = 0; s2 < kw; ++s2) {
                         const float wv = wch[r * kw + s2];
 #pragma unroll
                         for (int q = 0; q < VO; ++q) {
                             // Columns past the row end belong to masked outputs; clamp the read.
-                            const int col = min(q0 + q, D.wo - 1) + s2 * dwl;
+                            const int col = min(q0 + q, D.wo - 1) * sw + s2 * dwl;
                             accd[orow][q] = fmaf(row[col], wv, accd[orow][q]);
                         }
                     }
@@ -335,7 +338,7 @@ bool plan(const Desc& pw, const Desc& dw, FusedPlan* out) {
     bool ok = false;
     long best_cost = 0;
     for (int th = 1; th <= dw.ho; ++th) {
-        const int rows = th + (d.k_h - 1) * d.dilation_h;
+        const int rows = (th - 1) * d.stride_h + (d.k_h - 1) * d.dilation_h + 1;
         const int npix = rows * W;
         if ((npix + 15) / 16 > NJMAX * kWaves) break;               // fragments per wave
         if (vec && KC * rows * (W / 4) > NVX * kThreads) break;     // loads per thread
@@ -397,7 +400,8 @@ hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, Conv
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     f.num_blocks = (uint32_t)blocks;
-    const bool k3 = dw.p.k_h == 3 && dw.p.k_w == 3 && dw.p.dilation_h == 1 && dw.p.dilation_w == 1;
+    const bool k3 = dw.p.k_h == 3 && dw.p.k_w == 3 && dw.p.dilation_h == 1 && dw.p.dilation_w == 1 &&
+                    dw.p.stride_h == 1 && dw.p.stride_w == 1;
     const bool nj4 = (fp.rows * pw.p.w + 15) / 16 <= 4 * kWaves;
     const void* fn = k3 ? (nj4 ? (const void*)fused_pw_dw_kernel<3, 3, 4> : (const void*)fused_pw_dw_kernel<3, 3, 8>)
                         : (nj4 ? (const void*)fused_pw_dw_kernel<0, 0, 4> : (const void*)fused_pw_dw_kernel<0, 0, 8>);

@@ -183,8 +183,10 @@ CONV2D_API conv_status_t conv2d_forward(conv2d_desc_t d, const void* x, const vo
  * taps outside the image read desc_dw.pad_value.  y layout is desc_dw's.
  * Pointers as in conv2d_forward (b_* / slope_* nullable per descriptor; a
  * null w_pw or w_dw selects that descriptor's bound weights).
+ * The depthwise window is up to 5x5, with any stride, dilation and pads.
  * Errors: INCOMPATIBLE_SHAPES for a pair that does not chain; UNSUPPORTED for
- * a dtype other than F32 or a dw stride other than 1; ALIAS as above. */
+ * a dtype other than F32, a window beyond 5x5 or rows too wide for the
+ * on-chip tile; ALIAS as above. */
 CONV2D_API conv_status_t fused_pw_dw_forward(conv2d_desc_t desc_pw, conv2d_desc_t desc_dw, const void* x,
                                   const void* w_pw, const float* b_pw, const float* slope_pw,
                                   const void* w_dw, const float* b_dw, const float* slope_dw,

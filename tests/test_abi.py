@@ -168,14 +168,14 @@ def test_fused_pair_validation():
     dw = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 3, pads=1, groups=16))
     bad_dw = cc().conv2d_desc_create(cc().make_params(2, 12, 10, 10, 12, 3, pads=1, groups=12))
     dense = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 3, pads=1))
-    s2 = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 3, pads=1, stride=2, groups=16))
+    dw7 = cc().conv2d_desc_create(cc().make_params(2, 16, 10, 10, 16, 7, pads=3, groups=16))
     args = [ctypes.c_void_p(X + i * 0x100000) for i in range(3)]
     call = lambda a, b, y: lib.fused_pw_dw_forward(a.handle, b.handle, args[0], args[1], None, None, args[2],
                                                    None, None, ctypes.c_void_p(y), None)
     assert call(pw, bad_dw, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
     assert call(pw, dense, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
     assert call(dw, dw, X + 0x400000) == cc().CONV_ERR_INCOMPATIBLE_SHAPES
-    assert call(pw, s2, X + 0x400000) == cc().CONV_ERR_UNSUPPORTED
+    assert call(pw, dw7, X + 0x400000) == cc().CONV_ERR_UNSUPPORTED
     assert call(pw, dw, X) == cc().CONV_ERR_ALIAS
 
 

@@ -290,17 +290,21 @@ FUSED_CASES = [
     (1, 3, 30, 7, 16, 5, 2, 1, workloads.ACT_NONE, workloads.ACT_RELU, False, 0.25),
     (2, 16, 12, 20, 33, 3, 2, 2, workloads.ACT_CLIP, workloads.ACT_NONE, True, 0.0),
     (1, 70, 5, 64, 64, 3, 1, 1, workloads.ACT_LEAKY_RELU, workloads.ACT_PRELU, True, 1.0),
+    # depthwise stride 2 (the 7th field): odd and even image sizes, 3x3 and 5x5
+    (2, 16, 13, 20, 48, 3, 1, 1, workloads.ACT_CLIP, workloads.ACT_RELU, True, 0.0, 2),
+    (1, 24, 16, 17, 32, 5, (2, 1, 2, 2), 1, workloads.ACT_RELU, workloads.ACT_CLIP, False, -0.5, 2),
 ]
 
 
 @pytest.mark.parametrize("i", range(len(FUSED_CASES)))
 def test_fused_pw_dw_cases(i):
     t = torch()
-    n, ci, h, w, ce, k, p, dil, a1, a2, bias, pv = FUSED_CASES[i]
+    n, ci, h, w, ce, k, p, dil, a1, a2, bias, pv = FUSED_CASES[i][:12]
+    st = FUSED_CASES[i][12] if len(FUSED_CASES[i]) > 12 else 1
     p4 = p if isinstance(p, tuple) else (p,) * 4
     L1 = workloads.Layer("pw", n, ci, h, w, ce, (1, 1), has_bias=bias, act=a1, alpha=0.1, clip=(-0.3, 0.9))
-    L2 = workloads.Layer("dw", n, ce, h, w, ce, (k, k), pads=p4, dilation=(dil, dil), groups=ce, has_bias=bias,
-                         act=a2, alpha=0.2, clip=(-1.0, 0.5), pad_value=pv)
+    L2 = workloads.Layer("dw", n, ce, h, w, ce, (k, k), stride=(st, st), pads=p4, dilation=(dil, dil), groups=ce,
+                         has_bias=bias, act=a2, alpha=0.2, clip=(-1.0, 0.5), pad_value=pv)
     rng = np.random.default_rng(300 + i)
     x, w1, b1, s1 = workloads.layer_arrays(rng, L1)
     _, w2, b2, s2 = workloads.layer_arrays(rng, L2)
