@@ -12,7 +12,8 @@ Names and argument order follow the C ABI:
     conv2d_params_init, conv2d_desc_create, conv2d_desc_destroy,
     conv2d_desc_get_output_shape, conv2d_desc_kernel_name,
     conv2d_desc_bind_weights, conv2d_forward,
-    fused_pw_dw_forward, fused_dw_pw_forward, qconv2d_forward, conv2d_status_string,
+    fused_pw_dw_forward, fused_dw_pw_forward, qconv2d_forward, qfused_dw_pw_forward,
+    conv2d_status_string,
     conv2d_last_error
 plus ``make_params`` (keyword construction of a params struct).
 """
@@ -90,6 +91,8 @@ def _load():
     lib.fused_dw_pw_forward.restype = i32
     lib.qconv2d_forward.argtypes = [vp, vp, f32, i8, vp, f32, i8, vp, f32, i8, vp, vp]
     lib.qconv2d_forward.restype = i32
+    lib.qfused_dw_pw_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, f32, f32, f32, i8, vp, vp]
+    lib.qfused_dw_pw_forward.restype = i32
     lib.conv2d_status_string.argtypes = [i32]
     lib.conv2d_status_string.restype = ctypes.c_char_p
     lib.conv2d_last_error.argtypes = []
@@ -102,7 +105,8 @@ _lib = _load()
 # C ABI symbols this binding relies on (the header declares exactly these).
 EXPORTED = ("conv2d_params_init", "conv2d_desc_create", "conv2d_desc_destroy", "conv2d_desc_get_output_shape",
             "conv2d_desc_kernel_name", "conv2d_desc_bind_weights", "conv2d_forward", "fused_pw_dw_forward",
-            "fused_dw_pw_forward", "qconv2d_forward", "conv2d_status_string", "conv2d_last_error")
+            "fused_dw_pw_forward", "qconv2d_forward", "qfused_dw_pw_forward", "conv2d_status_string",
+            "conv2d_last_error")
 
 
 def conv2d_status_string(status: int) -> str:
@@ -310,6 +314,21 @@ def qconv2d_forward(desc: Desc, x, x_scale, x_zp, w, w_scale, w_zp, bias, y_scal
         _ptr(w, "w", "int8", wn), ctypes.c_float(w_scale), ctypes.c_int8(int(w_zp)),
         _ptr(bias, "bias", "int32", p.c_out) if p.has_bias else None,
         ctypes.c_float(y_scale), ctypes.c_int8(int(y_zp)), _ptr(y, "y", "int8", yn), _stream(stream)))
+
+
+def qfused_dw_pw_forward(desc_dw: Desc, desc_pw: Desc, x, w_dw, b_dw, dw_scales, w_pw, b_pw, pw_scales, y_zp, y,
+                         stream=None) -> None:
+    """Fused int8 depthwise -> pointwise: two symmetric QLinearConvs, each with
+    its (x_scale, w_scale, y_scale) triple."""
+    pd, pp = desc_dw.params, desc_pw.params
+    xn, wdn, _ = _sizes(desc_dw)
+    _, wpn, yn = _sizes(desc_pw)
+    f = ctypes.c_float
+    _check(_lib.qfused_dw_pw_forward(
+        desc_dw.handle, desc_pw.handle, _ptr(x, "x", "int8", xn), _ptr(w_dw, "w_dw", "int8", wdn),
+        _ptr(b_dw, "b_dw", "int32", pd.c_out) if pd.has_bias else None, *(f(v) for v in dw_scales),
+        _ptr(w_pw, "w_pw", "int8", wpn), _ptr(b_pw, "b_pw", "int32", pp.c_out) if pp.has_bias else None,
+        *(f(v) for v in pw_scales), ctypes.c_int8(int(y_zp)), _ptr(y, "y", "int8", yn), _stream(stream)))
 
 
 def output_shape(desc: Desc):

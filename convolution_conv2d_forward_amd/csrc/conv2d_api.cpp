@@ -482,6 +482,70 @@ conv_status_t fused_dw_pw_forward(conv2d_desc_t ddw, conv2d_desc_t dpw, const vo
     return hip_status(launch_fused_dw_pw(dw, pw, adw, apw, (hipStream_t)stream), "fused_dw_pw");
 }
 
+namespace {
+// composite = f32(f32(in_scale * w_scale) / out_scale), each step rounded to
+// f32 (the requant scale of an int8 stage); false if not positive and finite.
+bool composite_scale(float in_scale, float w_scale, float out_scale, float* out) {
+    if (!(std::isfinite(in_scale) && in_scale > 0) || !(std::isfinite(w_scale) && w_scale > 0) ||
+        !(std::isfinite(out_scale) && out_scale > 0))
+        return false;
+    volatile float prod = in_scale * w_scale;
+    volatile float comp = prod / out_scale;
+    *out = comp;
+    return std::isfinite(*out) && *out > 0;
+}
+}  // namespace
+
+conv_status_t qfused_dw_pw_forward(conv2d_desc_t ddw, conv2d_desc_t dpw, const int8_t* x, const int8_t* w_dw,
+                                   const int32_t* b_dw, float dw_x_scale, float dw_w_scale, float dw_y_scale,
+                                   const int8_t* w_pw, const int32_t* b_pw, float pw_x_scale, float pw_w_scale,
+                                   float pw_y_scale, int8_t y_zp, int8_t* y, void* stream) {
+    if (!ddw || !dpw) return fail(CONV_ERR_INVALID_ARG, "null descriptor");
+    const Desc& dw = *(const Desc*)ddw;
+    const Desc& pw = *(const Desc*)dpw;
+    const conv2d_params_t& D = dw.p;
+    const conv2d_params_t& P = pw.p;
+    if (D.dtype != CONV_DTYPE_I8 || P.dtype != CONV_DTYPE_I8)
+        return fail(CONV_ERR_INVALID_ARG, "qfused_dw_pw_forward needs two I8 descriptors");
+    if (!(D.groups == D.c_in && D.groups == D.c_out))
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "first descriptor must be depthwise (groups == c_in == c_out)");
+    if (P.k_h != 1 || P.k_w != 1 || P.stride_h != 1 || P.stride_w != 1 || P.groups != 1 || P.pad_top ||
+        P.pad_left || P.pad_bottom || P.pad_right)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "second descriptor must be a 1x1, stride 1, unpadded, ungrouped conv");
+    if (P.c_in != D.c_out || P.n != D.n || P.h != dw.ho || P.w != dw.wo)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "dw output [%d,%d,%d,%d] does not match pw input [%d,%d,%d,%d]",
+                    D.n, D.c_out, dw.ho, dw.wo, P.n, P.c_in, P.h, P.w);
+    if (dw.out_total != D.c_out || D.out_channel_offset != 0 || P.in_channel_offset != 0 || pw.in_total != P.c_in)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "the depthwise output has no buffer: dw output and pw input must be "
+                                                  "plain (no channel offsets)");
+    if (D.k_h > 5 || D.k_w > 5) return fail(CONV_ERR_UNSUPPORTED, "fused int8 dw->pw supports windows up to 5x5");
+    if (!plan_qfused_dw_pw(dw, pw)) return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
+    float comp_dw = 0.0f, comp_pw = 0.0f;
+    if (!composite_scale(dw_x_scale, dw_w_scale, dw_y_scale, &comp_dw) ||
+        !composite_scale(pw_x_scale, pw_w_scale, pw_y_scale, &comp_pw))
+        return fail(CONV_ERR_INVALID_ARG, "scales (and their composites) must be finite and positive");
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    const void* wdv = w_dw;
+    const void* wpv = w_pw;
+    if (resolve_weights(dw, wdv, "depthwise weights") != CONV_OK || resolve_weights(pw, wpv, "pointwise weights") != CONV_OK)
+        return CONV_ERR_INVALID_ARG;
+    if (D.has_bias && !b_dw) return fail(CONV_ERR_INVALID_ARG, "dw has_bias set but bias is null");
+    if (P.has_bias && !b_pw) return fail(CONV_ERR_INVALID_ARG, "pw has_bias set but bias is null");
+    const View yv = y_view(pw, y);
+    if (views_overlap(yv, x_view(dw, x))) return fail(CONV_ERR_ALIAS, "y overlaps x");
+    if (views_overlap(yv, flat(wdv, w_bytes(dw))) || views_overlap(yv, flat(wpv, w_bytes(pw))))
+        return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if ((D.has_bias && views_overlap(yv, flat(b_dw, 4 * (int64_t)D.c_out))) ||
+        (P.has_bias && views_overlap(yv, flat(b_pw, 4 * (int64_t)P.c_out))))
+        return fail(CONV_ERR_ALIAS, "y overlaps a bias");
+    ConvArgs adw = make_args(dw, x, wdv, nullptr, nullptr, nullptr);
+    adw.qbias = D.has_bias ? b_dw : nullptr;
+    ConvArgs apw = make_args(pw, nullptr, wpv, nullptr, nullptr, y);
+    apw.qbias = P.has_bias ? b_pw : nullptr;
+    return hip_status(launch_qfused_dw_pw(dw, pw, adw, apw, comp_dw, comp_pw, y_zp, (hipStream_t)stream),
+                      "qfused_dw_pw");
+}
+
 conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, int8_t x_zp, const int8_t* w,
                               float w_scale, int8_t w_zp, const int32_t* bias, float y_scale, int8_t y_zp,
                               int8_t* y, void* stream) {

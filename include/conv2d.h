@@ -221,6 +221,32 @@ CONV2D_API conv_status_t qconv2d_forward(conv2d_desc_t d, const int8_t* x, float
                               const int8_t* w, float w_scale, int8_t w_zp, const int32_t* bias,
                               float y_scale, int8_t y_zp, int8_t* y, void* stream);
 
+/* Fused int8 depthwise kxk -> pointwise 1x1 (the yscv QuantizedDwPw step):
+ * two symmetric QLinearConvs as in qconv2d_forward, each with its own scale
+ * triple, the int8 intermediate kept in on-chip memory.  desc_dw: I8,
+ * groups == c_in == c_out, window up to 5x5, any stride, dilation and pads;
+ * desc_pw: I8, 1x1, stride 1, pads 0, groups 1, c_in == desc_dw.c_out, h/w ==
+ * desc_dw's output size; the depthwise output and pointwise input are plain
+ * (no channel offsets), the depthwise input and pointwise output may be
+ * channel slices.  The depthwise stage requantises with the composite of
+ * (dw_x_scale, dw_w_scale, dw_y_scale), zero point 0 and its descriptor's
+ * rounding and ReLU; the pointwise stage reads that int8 tensor and
+ * requantises with the composite of (pw_x_scale, pw_w_scale, pw_y_scale),
+ * y_zp and its descriptor's rounding and ReLU.  The output is bitwise that
+ * of qconv2d_forward(desc_dw, x, dw_x_scale, 0, w_dw, dw_w_scale, 0, b_dw,
+ * dw_y_scale, 0, tmp) followed by qconv2d_forward(desc_pw, tmp, pw_x_scale,
+ * 0, w_pw, pw_w_scale, 0, b_pw, pw_y_scale, y_zp, y) (pw_x_scale is normally
+ * dw_y_scale; both are taken so that any pair of stages fuses).  Null w_dw /
+ * w_pw select bound weights; biases are device int32 or null.  Errors:
+ * INVALID_ARG for a non-I8 descriptor, a scale or composite that is not
+ * finite and positive, or null pointers; INCOMPATIBLE_SHAPES / UNSUPPORTED /
+ * ALIAS as for fused_dw_pw_forward. */
+CONV2D_API conv_status_t qfused_dw_pw_forward(conv2d_desc_t desc_dw, conv2d_desc_t desc_pw, const int8_t* x,
+                                   const int8_t* w_dw, const int32_t* b_dw, float dw_x_scale,
+                                   float dw_w_scale, float dw_y_scale, const int8_t* w_pw,
+                                   const int32_t* b_pw, float pw_x_scale, float pw_w_scale,
+                                   float pw_y_scale, int8_t y_zp, int8_t* y, void* stream);
+
 /* Human-readable name of a status code (static string). */
 CONV2D_API const char* conv2d_status_string(conv_status_t s);
 

@@ -1,0 +1,141 @@
+"""GPU: the fused int8 depthwise -> pointwise path (qfused_dw_pw_forward).
+
+Bit-exact twice over: against the oracle's two QLinearConvs chained through
+the int8 intermediate, and against the library's own unfused calls
+(qconv2d_forward twice)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import Guarded, assert_bitexact, layer_params, to_dev, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def cc():
+    import convolution_conv2d_forward_amd as m
+    return m
+
+
+CASES = [
+    # n, c, h, w, k, stride, pads, dilation, c_out, scales (x, w_dw, mid, w_pw, y), dw relu, pw relu, y_zp, rounding
+    (2, 144, 20, 16, 3, 2, 1, 1, 48, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 0),   # the chain's dw s2 -> pw
+    (1, 72, 9, 13, 3, 1, 1, 1, 40, (0.02, 0.01, 0.05, 0.01, 0.05), True, False, 0, 0),     # s1, odd width (byte rows)
+    (2, 20, 11, 24, 5, 1, (2, 1, 2, 3), 2, 70, (0.03, 0.02, 0.04, 0.01, 0.09), False, True, 3, 1),  # 5x5 d2, 2 co tiles
+    (1, 130, 6, 8, 3, 2, (0, 1, 1, 0), 1, 16, (1.0, 1.0, 36.0, 1.0, 2.0), True, True, -2, 1),  # ties, 3 chunks
+    (3, 7, 5, 5, 1, 1, 0, 1, 9, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 5, 0),       # 1x1 depthwise window
+    (1, 16, 20, 16, 3, 2, 1, 1, 16, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 0),    # one partial chunk
+    (1, 64, 24, 80, 3, 2, 1, 1, 48, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 0),    # several row tiles
+]
+
+
+def _layers(case):
+    n, c, h, w, k, s, p, d, co = case[:9]
+    p4 = p if isinstance(p, tuple) else (p,) * 4
+    L1 = workloads.Layer("dw", n, c, h, w, c, (k, k), stride=(s, s), pads=p4, dilation=(d, d), groups=c,
+                         has_bias=True)
+    ho, wo = L1.out_hw
+    L2 = workloads.Layer("pw", n, c, ho, wo, co, (1, 1), has_bias=True)
+    return L1, L2
+
+
+def _desc(L, rounding, relu, **kw):
+    p = layer_params(L, "i8", int8_rounding=rounding, **kw)
+    if relu:
+        p.act_type = 1
+    return cc().conv2d_desc_create(p)
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_qfused_dw_pw_cases(i):
+    t = torch()
+    case = CASES[i]
+    L1, L2 = _layers(case)
+    sx, swd, smid, swp, sy = case[9]
+    relu1, relu2, y_zp, rnd = case[10:]
+    rng = np.random.default_rng(700 + i)
+    x = rng.integers(-128, 127, size=L1.x_shape, endpoint=True).astype(np.int8)
+    w1 = rng.integers(-127, 127, size=L1.w_shape, endpoint=True).astype(np.int8)
+    w2 = rng.integers(-127, 127, size=L2.w_shape, endpoint=True).astype(np.int8)
+    b1 = rng.integers(-500, 500, size=L1.c_out, endpoint=True).astype(np.int32)
+    b2 = rng.integers(-500, 500, size=L2.c_out, endpoint=True).astype(np.int32)
+    mid = oracle.qconv2d(x, w1, b1, sx, swd, smid, stride=L1.stride, pads=L1.pads, dilation=L1.dilation,
+                         groups=L1.groups, rounding=rnd, relu=relu1)
+    ref = oracle.qconv2d(mid, w2, b2, smid, swp, sy, y_zp=y_zp, rounding=rnd, relu=relu2)
+    print(f"case {i}: {L1} -> {L2}; intermediate saturated {np.mean(np.abs(mid.astype(int)) >= 127):.3f}",
+          flush=True)
+    d1, d2 = _desc(L1, rnd, relu1), _desc(L2, rnd, relu2)
+    xd, w1d, w2d, b1d, b2d = to_dev(x), to_dev(w1), to_dev(w2), to_dev(b1), to_dev(b2)
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d2)
+    y = Guarded(n * ot * ho * wo, t.int8, 0x5A)
+    cc().qfused_dw_pw_forward(d1, d2, xd, w1d, b1d, (sx, swd, smid), w2d, b2d, (smid, swp, sy), y_zp, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    got = y.host().numpy().reshape(n, ot, ho, wo)
+    assert_bitexact(got, ref, f"case {i}: fused vs oracle chain")
+    # the library's unfused path
+    _, _, h1, w1o = cc().conv2d_desc_get_output_shape(d1)
+    tmp = t.empty(L1.n * L1.c_out * h1 * w1o, dtype=t.int8, device="cuda")
+    y2 = t.empty(n * ot * ho * wo, dtype=t.int8, device="cuda")
+    cc().qconv2d_forward(d1, xd, sx, 0, w1d, swd, 0, b1d, smid, 0, tmp)
+    cc().qconv2d_forward(d2, tmp, smid, 0, w2d, swp, 0, b2d, sy, y_zp, y2)
+    t.cuda.synchronize()
+    assert_bitexact(got, y2.cpu().numpy().reshape(n, ot, ho, wo), f"case {i}: fused vs unfused")
+    # bound weights
+    cc().conv2d_desc_bind_weights(d1, w1d)
+    cc().conv2d_desc_bind_weights(d2, w2d)
+    y3 = Guarded(n * ot * ho * wo, t.int8, 0x5A)
+    cc().qfused_dw_pw_forward(d1, d2, xd, None, b1d, (sx, swd, smid), None, b2d, (smid, swp, sy), y_zp, y3.view)
+    t.cuda.synchronize()
+    y3.check_guards()
+    assert_bitexact(y3.host().numpy().reshape(n, ot, ho, wo), got, f"case {i}: bound weights")
+
+
+def test_qfused_dw_pw_chain_full_size():
+    """The int8 chain's dw s2 -> pw at full size (16 x 144 x 80 x 80 into the
+    s2 depthwise), fed with the oracle's dw s1 output.  Every stage of the
+    chain uses the same (x, w, y) scale triple, so the pointwise stage's input
+    scale is not the depthwise stage's output scale: the fused call takes both
+    triples as they are."""
+    t = torch()
+    wl = workloads.int8_chain()
+    a = wl.arrays
+    L0, L1, L2 = wl.layers
+    sc = workloads.INT8_SCALES
+    s1 = oracle.qconv2d(a["x"], a["w_dw_s1"], a["b_dw_s1"], *sc, stride=L0.stride, pads=L0.pads, groups=L0.groups)
+    s2 = oracle.qconv2d(s1, a["w_dw_s2"], a["b_dw_s2"], *sc, stride=L1.stride, pads=L1.pads, groups=L1.groups)
+    ref = oracle.qconv2d(s2, a["w_pw"], a["b_pw"], *sc)
+    d1, d2 = _desc(L1, 0, False), _desc(L2, 0, False)
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d2)
+    y = Guarded(n * ot * ho * wo, t.int8, 0x5A)
+    cc().qfused_dw_pw_forward(d1, d2, to_dev(s1), to_dev(a["w_dw_s2"]), to_dev(a["b_dw_s2"]), sc,
+                              to_dev(a["w_pw"]), to_dev(a["b_pw"]), sc, 0, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    assert_bitexact(y.host().numpy().reshape(n, ot, ho, wo), ref, "chain dw s2 -> pw fused")
+
+
+def test_qfused_dw_pw_output_slice():
+    """Pointwise output into channels [4, 4 + c_out) of a wider buffer."""
+    t = torch()
+    L1, L2 = _layers(CASES[1])
+    sx, swd, smid, swp, sy = CASES[1][9]
+    rng = np.random.default_rng(760)
+    x = rng.integers(-128, 127, size=L1.x_shape, endpoint=True).astype(np.int8)
+    w1 = rng.integers(-127, 127, size=L1.w_shape, endpoint=True).astype(np.int8)
+    w2 = rng.integers(-127, 127, size=L2.w_shape, endpoint=True).astype(np.int8)
+    mid = oracle.qconv2d(x, w1, None, sx, swd, smid, stride=L1.stride, pads=L1.pads, groups=L1.groups)
+    ref = oracle.qconv2d(mid, w2, None, smid, swp, sy)
+    L1.has_bias = L2.has_bias = False
+    d1 = _desc(L1, 0, False)
+    d2 = _desc(L2, 0, False, out_total_channels=L2.c_out + 7, out_channel_offset=4)
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d2)
+    y = Guarded(n * ot * ho * wo, t.int8, 0x5A)
+    cc().qfused_dw_pw_forward(d1, d2, to_dev(x), to_dev(w1), None, (sx, swd, smid), to_dev(w2), None,
+                              (smid, swp, sy), 0, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    got = y.host().numpy().reshape(n, ot, ho, wo)
+    assert (got[:, :4] == 0x5A).all() and (got[:, 4 + L2.c_out:] == 0x5A).all()
+    assert_bitexact(got[:, 4:4 + L2.c_out], ref, "slice")
