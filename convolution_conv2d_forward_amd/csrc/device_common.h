@@ -79,7 +79,13 @@ __device__ __forceinline__ float apply_act(const ConvArgs& a, float v, float slo
 // (no contraction); rintf rounds ties to even, roundf away from zero.
 __device__ __forceinline__ int8_t requant(int32_t acc, float composite, int rounding, int y_zp,
                                           bool relu) {
-    const float yf = __fmul_rn((float)acc, composite);
+    float yf = __fmul_rn((float)acc, composite);
+    // Materialise the rounded f32 product: under -ffp-contract=fast the
+    // compiler would otherwise fuse it into roundf's own subtraction of the
+    // truncated value (one fma, no intermediate rounding), and a product
+    // that rounds to an exact tie (25.4999994 -> 25.5) would then round
+    // toward zero.
+    asm volatile("" : "+v"(yf));
     const float r = rounding == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
     int q = (int)r + y_zp;
     q = q < -128 ? -128 : (q > 127 ? 127 : q);

@@ -35,7 +35,13 @@ __host__ __device__ inline int qdw_q0(int k, int ss, int pl) { return ss * k + (
 // the shared requant(): f32 product, then ties-to-even or ties-away).
 template <int RND>
 __device__ __forceinline__ uint32_t rq(int32_t acc, float comp, int y_zp, bool relu) {
-    const float yf = __fmul_rn((float)acc, comp);
+    float yf = __fmul_rn((float)acc, comp);
+    // Materialise the rounded f32 product: under -ffp-contract=fast the
+    // compiler would otherwise fuse it into roundf's own subtraction of the
+    // truncated value (one fma, no intermediate rounding), and a product
+    // that rounds to an exact tie (25.4999994 -> 25.5) would then round
+    // toward zero.
+    asm volatile("" : "+v"(yf));
     const float r = RND == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
     int q = (int)r + y_zp;
     q = q < -128 ? -128 : (q > 127 ? 127 : q);
