@@ -392,6 +392,25 @@ def per_config(reps, only="all"):
             res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 1, extra=0), t, "i8"),
                                kernel=cc.conv2d_desc_kernel_name(d))
             log("int8", L.name, res[L.name])
+        # dw s2 -> pw fused: the int8 depthwise output stays on chip
+        L1, L2 = wl.layers[1], wl.layers[2]
+        d1 = cc.conv2d_desc_create(params_of(L1, "i8"))
+        d2 = cc.conv2d_desc_create(params_of(L2, "i8"))
+        w1, b1, w2, b2 = (t_(a[k]) for k in ("w_dw_s2", "b_dw_s2", "w_pw", "b_pw"))
+        xq = t_(np.random.default_rng(5).integers(-128, 128, size=L1.x_shape).astype(np.int8))
+        sc = workloads.INT8_SCALES
+
+        def make_q():
+            xi = xq.clone()
+            yi = torch.empty((L2.n, L2.c_out, L2.h, L2.w), dtype=torch.int8, device=dev())
+            return lambda: cc.qfused_dw_pw_forward(d1, d2, xi, w1, b1, sc, w2, b2, sc, 0, yi)
+
+        fns = _rotating(make_q, L1.n * L1.c_in * L1.h * L1.w + L2.n * L2.c_out * L2.h * L2.w)
+        t = time_layer("qfused_dw_pw", fns, reps)
+        fb = (L1.n * L1.c_in * L1.h * L1.w + L1.c_out * 9 + 4 * L1.c_out + L2.c_out * L2.c_in + 4 * L2.c_out
+              + L2.n * L2.c_out * L2.h * L2.w)
+        res["qfused_dw_pw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "i8"), kernel="qfused_dw_pw")
+        log("int8", "qfused_dw_pw", res["qfused_dw_pw"])
         out["int8_chain"] = res
     return out
 

@@ -27,6 +27,15 @@ CASES = [
     (3, 7, 5, 5, 1, 1, 0, 1, 9, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 5, 0),       # 1x1 depthwise window
     (1, 16, 20, 16, 3, 2, 1, 1, 16, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 0),    # one partial chunk
     (1, 64, 24, 80, 3, 2, 1, 1, 48, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 0),    # several row tiles
+    # 16-byte rows (the vector-copy path): stride, window, pad offset, tails
+    (1, 64, 12, 32, 3, 1, 1, 1, 80, (0.02, 0.01, 0.05, 0.01, 0.05), True, False, 0, 0),     # s1, 2 channel tiles
+    (2, 48, 15, 32, 3, 2, (0, 0, 1, 1), 1, 24, (0.03, 0.02, 0.04, 0.01, 0.09), False, True, -3, 1),  # pad 0
+    (1, 32, 9, 48, 5, 1, 2, 1, 40, (0.02, 0.01, 0.05, 0.01, 0.05), True, True, 2, 0),       # 5x5 s1
+    (1, 16, 10, 32, 5, 2, (2, 1, 2, 1), 1, 16, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 1),  # 5x5 s2, wo 15
+    (1, 128, 4, 112, 3, 1, 1, 1, 32, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 0, 0),   # 8 copy slots
+    (2, 80, 6, 16, 3, 2, (1, 3, 1, 3), 1, 72, (1.0, 1.0, 36.0, 1.0, 2.0), True, True, -2, 1),  # pad 3, ties
+    (3, 160, 7, 64, 3, 2, 1, 1, 64, (0.02, 0.01, 0.05, 0.01, 0.05), False, False, 1, 0),    # 3 chunks
+    (64, 16, 10, 16, 3, 2, 1, 1, 16, (0.02, 0.01, 0.05, 0.01, 0.05), False, True, 0, 0),    # 2-row tiles, last 1 row
 ]
 
 
