@@ -13,12 +13,15 @@ not from the 256 MB last-level cache.
 The JSON line also carries:
   roofline      the dominant kernel of the step against the fp32 MFMA peak;
                 its duration comes from HIP events recorded around every launch
-                on the launch stream inside the timed region
+                on the launch stream, in a pass over the same number of steps
+                queued behind a GPU delay (launches back to back, so no host
+                launch time inside an event pair)
   cpu_baseline  the float64 CPU oracle timed on this host's cores on a sample
                 of the same workload's outputs
   per_config    the other synthetic workloads (single conv, inverted
-                bottleneck fused/unfused, mixed sweep fp32/bf16, int8 chain),
-                each layer timed with events, with its binding roofline
+                bottleneck fused/unfused, mixed sweep fp32/bf16, int8 chain
+                unfused/fused), each layer timed with events the same way,
+                with its binding roofline
 Everything on stdout except the final JSON line goes to stderr.
 """
 import argparse
@@ -94,6 +97,28 @@ def layer_bytes(L, esize, wsize=None, extra=0):
     if L.act == 3:
         b += 4 * L.c_out
     return b + extra
+
+
+_SLEEP_CYCLES_PER_US = None
+
+
+def gpu_delay(us):
+    """Queue a spin kernel of about `us` microseconds on the current stream.
+    Launches enqueued behind it then run back to back, so the HIP events
+    around each one time GPU work rather than waits for the host's next
+    launch call (a 10 us kernel is comparable to one ctypes call)."""
+    global _SLEEP_CYCLES_PER_US
+    torch = torch_mod()
+    if _SLEEP_CYCLES_PER_US is None:
+        n = 2_000_000
+        torch.cuda._sleep(n)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        torch.cuda._sleep(n)
+        e.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = n / (s.elapsed_time(e) * 1e3)
+    torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US))
 
 
 class EventTimer:
@@ -183,12 +208,19 @@ def bench_dense_block(steps, warmup):
         db.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Event pass over the same number of steps: per-launch durations.
+    # Event pass over the same number of steps: per-launch durations, queued
+    # behind a GPU delay so that the launches run back to back.
     timer = EventTimer()
     torch.cuda.synchronize()
+    delay = 300.0 * steps
+    gpu_delay(delay)
+    t0 = time.perf_counter()
     for _ in range(steps):
         db.step(timer)
+    t_enq = (time.perf_counter() - t0) * 1e6
     torch.cuda.synchronize()
+    if t_enq > delay:
+        log(f"dense block: host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
     per = [timer.mean_us(k) for k in range(len(db.layers))]
     return db, wall, per
 
@@ -242,14 +274,21 @@ def _rotating(make, footprint, target=ROTATE_BYTES, cap=64):
 
 
 def time_layer(key, fn_sets, reps, warm=3):
-    """fn_sets: list of callables (one per rotating buffer set)."""
+    """Mean HIP-event time of one launch.  fn_sets: list of callables (one per
+    rotating buffer set); the timed launches are queued behind a GPU delay."""
     torch = torch_mod()
     for i in range(warm):
         fn_sets[i % len(fn_sets)]()
     torch.cuda.synchronize()
     timer = EventTimer()
+    delay = 200.0 * reps
+    gpu_delay(delay)
+    t0 = time.perf_counter()
     for i in range(reps):
         timer.run(key, fn_sets[i % len(fn_sets)])
+    t_enq = (time.perf_counter() - t0) * 1e6
+    if t_enq > delay:
+        log(f"{key}: host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
     return timer.mean_us(key)[0]
 
 
