@@ -29,6 +29,8 @@ CONV_OK, CONV_ERR_INVALID_ARG, CONV_ERR_INCOMPATIBLE_SHAPES, CONV_ERR_UNSUPPORTE
 ACT_NONE, ACT_RELU, ACT_LEAKY_RELU, ACT_PRELU, ACT_CLIP = range(5)
 DTYPE_F32, DTYPE_BF16, DTYPE_I8 = range(3)
 ROUND_HALF_EVEN, ROUND_HALF_AWAY = range(2)
+ALGO_AUTO, ALGO_DIRECT, ALGO_WINOGRAD = range(3)
+ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "winograd": ALGO_WINOGRAD}
 
 _ACT_NAMES = {"none": ACT_NONE, "relu": ACT_RELU, "leaky_relu": ACT_LEAKY_RELU, "prelu": ACT_PRELU,
               "clip": ACT_CLIP}
@@ -51,6 +53,7 @@ class conv2d_params_t(ctypes.Structure):
         ("out_total_channels", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("int8_rounding", ctypes.c_int32),
+        ("algo", ctypes.c_int32),
     ]
 
 
@@ -137,7 +140,7 @@ def _pair(v):
 def make_params(n, c_in, h, w, c_out, k, *, stride=1, pads=0, dilation=1, groups=1, has_bias=False,
                 pad_value=0.0, act="none", alpha=None, clip=None, prelu_slope_count=1, in_channel_offset=0,
                 in_total_channels=0, out_channel_offset=0, out_total_channels=0, dtype="f32",
-                int8_rounding=ROUND_HALF_EVEN) -> conv2d_params_t:
+                int8_rounding=ROUND_HALF_EVEN, algo=0) -> conv2d_params_t:
     """Build a conv2d_params_t.  pads: int, or (top, left, bottom, right)."""
     p = conv2d_params_init()
     p.n, p.c_in, p.h, p.w, p.c_out = int(n), int(c_in), int(h), int(w), int(c_out)
@@ -161,6 +164,7 @@ def make_params(n, c_in, h, w, c_out, k, *, stride=1, pads=0, dilation=1, groups
     p.out_channel_offset, p.out_total_channels = int(out_channel_offset), int(out_total_channels)
     p.dtype = _DTYPE_NAMES[dtype] if isinstance(dtype, str) else int(dtype)
     p.int8_rounding = int(int8_rounding)
+    p.algo = int(ALGOS.get(algo, algo) if isinstance(algo, str) else algo)
     return p
 
 

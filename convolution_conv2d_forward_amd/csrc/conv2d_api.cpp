@@ -46,6 +46,7 @@ const char* kernel_name(const Desc& d) {
     case KC_QPW: return "pointwise_i8_mfma";
     case KC_DIRECT: return "direct";
     case KC_GROUPED: return d.p.dtype == CONV_DTYPE_BF16 ? "grouped_bf16" : "grouped_f32";
+    case KC_WINOGRAD_F32: return "winograd_f32";
     }
     return "?";
 }
@@ -149,6 +150,13 @@ void free_on(void* ptr, int device) {
     if (switched) (void)hipSetDevice(cur);
 }
 
+// AUTO picks Winograd only where it has been measured faster than the
+// implicit GEMM (none yet).
+bool winograd_preferred(const Desc& d) {
+    (void)d;
+    return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +175,7 @@ void conv2d_params_init(conv2d_params_t* p) {
     p->prelu_slope_count = 1;
     p->dtype = CONV_DTYPE_F32;
     p->int8_rounding = CONV_ROUND_HALF_EVEN;
+    p->algo = CONV_ALGO_AUTO;
 }
 
 conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out) {
@@ -197,6 +206,7 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
     if (p.int8_rounding != CONV_ROUND_HALF_EVEN && p.int8_rounding != CONV_ROUND_HALF_AWAY)
         return fail(CONV_ERR_INVALID_ARG, "unknown rounding %d", p.int8_rounding);
     if (p.has_bias != 0 && p.has_bias != 1) return fail(CONV_ERR_INVALID_ARG, "has_bias must be 0 or 1");
+    if (p.algo < CONV_ALGO_AUTO || p.algo > CONV_ALGO_WINOGRAD) return fail(CONV_ERR_INVALID_ARG, "unknown algo %d", p.algo);
     if (!std::isfinite(p.pad_value)) return fail(CONV_ERR_INVALID_ARG, "pad_value must be finite");
     if (p.groups <= 0) return fail(CONV_ERR_INVALID_ARG, "groups must be >= 1");
     if (p.c_in % p.groups || p.c_out % p.groups)
@@ -250,7 +260,18 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
     const bool depthwise = p.groups == p.c_in && p.groups == p.c_out;
 
     bool planned = false;
-    if (p.dtype == CONV_DTYPE_I8) {
+    if (p.algo == CONV_ALGO_WINOGRAD) {
+        if (!plan_winograd_f32(*d)) {
+            delete d;
+            return fail(CONV_ERR_UNSUPPORTED, "Winograd F(2x2,3x3) needs F32, a 3x3 window, stride 1, dilation 1 "
+                                              "and one group");
+        }
+        d->kclass = KC_WINOGRAD_F32;
+        planned = true;
+    } else if (p.algo == CONV_ALGO_AUTO && winograd_preferred(*d)) {
+        d->kclass = KC_WINOGRAD_F32;
+        planned = true;
+    } else if (p.dtype == CONV_DTYPE_I8) {
         if (depthwise) { d->kclass = KC_QDW; planned = plan_qdw(*d); }
         else { d->kclass = KC_QPW; planned = plan_qpw(*d); }
     } else if (depthwise) {
@@ -384,6 +405,7 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
         break;
     case KC_DW: e = launch_dw(d, a, s); break;
     case KC_GROUPED: e = launch_grouped(d, a, s); break;
+    case KC_WINOGRAD_F32: e = launch_winograd_f32(d, a, s); break;
     default: e = launch_direct(d, a, s); break;
     }
     return hip_status(e, kernel_name(d));

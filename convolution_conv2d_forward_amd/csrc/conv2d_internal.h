@@ -18,6 +18,7 @@ enum KernelClass : int32_t {
     KC_QPW = 4,          // int8 pointwise 1x1, i8 MFMA
     KC_DIRECT = 5,       // direct convolution, one thread per output (any shape)
     KC_GROUPED = 6,      // grouped 3x3 with 4 or 8 channels per group, VALU
+    KC_WINOGRAD_F32 = 7, // Winograd F(2x2, 3x3), fp32 MFMA (3x3, stride 1, dilation 1, one group)
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -149,6 +150,7 @@ hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw,
                               hipStream_t s);
@@ -165,6 +167,7 @@ bool plan_dw(Desc& d);
 bool plan_qdw(Desc& d);
 bool plan_qpw(Desc& d);
 bool plan_grouped(const Desc& d);
+bool plan_winograd_f32(const Desc& d);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 // x: the input pointer (its alignment decides between vector and scalar row loads).

@@ -95,6 +95,21 @@ typedef enum {
 /* Convolution attributes.  Fill with conv2d_params_init() and then set what
  * differs from the defaults.  Pads are ONNX order (top, left, bottom, right);
  * ncnn's chained defaults (pad_top = pad_left, ...) are the caller's job. */
+/* Algorithm of a float convolution.  AUTO lets the library choose (the
+ * direct tiled classes unless Winograd is measured faster for the shape);
+ * DIRECT never uses Winograd; WINOGRAD requests the F(2x2, 3x3) minimal
+ * filtering algorithm (Lavin and Gray, CVPR 2016) for the "Winograd cells"
+ * the Go package doc "ops" names among its conv fan-out sites (section
+ * WorkerPool): F32 only, 3x3 window, stride 1, dilation 1, one group, any
+ * pads, bias, activation and channel offsets; conv2d_desc_create returns
+ * CONV_ERR_UNSUPPORTED for any other shape.  Its results differ from the
+ * direct sum by fp32 rounding only. */
+typedef enum {
+    CONV_ALGO_AUTO = 0,
+    CONV_ALGO_DIRECT = 1,
+    CONV_ALGO_WINOGRAD = 2
+} conv_algo_t;
+
 typedef struct {
     int32_t n, c_in, h, w;        /* input batch, channels, height, width */
     int32_t c_out, k_h, k_w;      /* output channels, kernel size */
@@ -114,6 +129,7 @@ typedef struct {
     int32_t out_total_channels;   /* 0 means c_out */
     int32_t dtype;                /* conv_dtype_t, default CONV_DTYPE_F32 */
     int32_t int8_rounding;        /* conv_rounding_t, default CONV_ROUND_HALF_EVEN */
+    int32_t algo;                 /* conv_algo_t, default CONV_ALGO_AUTO */
 } conv2d_params_t;
 
 typedef struct conv2d_desc* conv2d_desc_t;

@@ -6,6 +6,7 @@ import ctypes
 import math
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -36,9 +37,21 @@ def test_header_symbols_exported():
     assert sorted(cc().EXPORTED) == syms
 
 
-def test_params_layout_matches_header():
-    # conv2d_params_t: 17 int32, float, int32, float[2], 7 int32 = 28 * 4 bytes
-    assert ctypes.sizeof(cc().conv2d_params_t) == 28 * 4
+def test_params_layout_matches_header(tmp_path):
+    """The ctypes mirror of conv2d_params_t has the header's size and field
+    offsets (the header compiled with gcc)."""
+    P = cc().conv2d_params_t
+    names = [f[0] for f in P._fields_]
+    src = tmp_path / "layout.c"
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "conv2d.h")
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "%s"\nint main(void) {\n'
+                   '  printf("%%zu\\n", sizeof(conv2d_params_t));\n%s  return 0;\n}\n'
+                   % (hdr, "".join('  printf("%%zu\\n", offsetof(conv2d_params_t, %s));\n' % n for n in names)))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", str(src), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(P)
+    assert out[1:] == [getattr(P, n).offset for n in names]
 
 
 def test_params_defaults():
@@ -228,3 +241,39 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4 * 64)
     with pytest.raises(ValueError):
         cc().conv2d_forward(d, x, torch.zeros(144), None, None, torch.zeros(256))
+
+
+@pytest.mark.parametrize("bad", ["stride", "dilation", "groups", "kernel", "bf16"])
+def test_winograd_rejects(bad):
+    """algo = WINOGRAD on a shape F(2x2, 3x3) does not cover is refused at
+    descriptor creation (no GPU call is made)."""
+    kw = dict(stride=1, dilation=1, groups=1, dtype="f32")
+    k = (3, 3)
+    if bad == "stride":
+        kw["stride"] = 2
+    elif bad == "dilation":
+        kw["dilation"] = 2
+    elif bad == "groups":
+        kw["groups"] = 2
+    elif bad == "kernel":
+        k = (5, 5)
+    else:
+        kw["dtype"] = "bf16"
+    p = cc().make_params(1, 8, 16, 16, 8, k, pads=1, algo="winograd", **kw)
+    with pytest.raises(cc().ConvError, match="Winograd") as e:
+        cc().conv2d_desc_create(p)
+    assert e.value.status == cc().CONV_ERR_UNSUPPORTED
+
+
+def test_algo_field():
+    """algo defaults to AUTO; an unknown value is refused; WINOGRAD on a 3x3 s1
+    fp32 layer selects the Winograd kernel."""
+    p = cc().conv2d_params_init()
+    assert p.algo == cc().ALGO_AUTO
+    p = cc().make_params(1, 8, 16, 16, 8, (3, 3), pads=1, algo=7)
+    with pytest.raises(cc().ConvError):
+        cc().conv2d_desc_create(p)
+    d = cc().conv2d_desc_create(cc().make_params(1, 8, 16, 16, 8, (3, 3), pads=1, algo="winograd"))
+    assert cc().conv2d_desc_kernel_name(d) == "winograd_f32"
+    d = cc().conv2d_desc_create(cc().make_params(1, 8, 16, 16, 8, (3, 3), pads=1, algo="direct"))
+    assert cc().conv2d_desc_kernel_name(d) != "winograd_f32"

@@ -1,0 +1,89 @@
+"""GPU parity of the Winograd F(2x2, 3x3) path (algo = WINOGRAD) against the
+oracle's direct float64 convolution, fp32 tolerance 1e-4 * (1 + |ref|).
+
+Winograd reaches the convolution's result by a different arithmetic (input,
+filter and output transforms around 16 channel sums), so the oracle stays the
+plain definition; the cases cover partial output tiles (odd sizes), every pad
+layout with a nonzero pad_value, partial channel chunks and channel tiles,
+each activation with bias, batch > 1, concat slices on both sides, and the
+five dense-block layers at full size."""
+import numpy as np
+import pytest
+
+import workloads
+from helpers import FP32_TOL, Guarded, assert_close, layer_params, oracle_layer, to_dev, torch
+
+pytestmark = pytest.mark.gpu
+
+A = workloads
+
+
+def cc():
+    import convolution_conv2d_forward_amd as m
+    return m
+
+
+CASES = [
+    # n, c_in, h, w, c_out, pads (t, l, b, r), act, bias, pad_value
+    (1, 16, 8, 16, 32, (1, 1, 1, 1), A.ACT_NONE, False, 0.0),          # one workgroup, exact tiles
+    (1, 20, 13, 17, 24, (1, 1, 1, 1), A.ACT_RELU, True, 0.0),          # odd sizes: partial tiles, partial chunk
+    (2, 35, 9, 30, 40, (0, 2, 1, 0), A.ACT_LEAKY_RELU, True, 0.5),     # asymmetric pads, pad_value, 2 channel tiles
+    (1, 64, 24, 40, 33, (2, 2, 2, 2), A.ACT_PRELU, True, -1.0),        # pads of 2, PReLU per channel
+    (3, 7, 5, 6, 5, (0, 0, 0, 0), A.ACT_CLIP, True, 0.0),              # no pads, tiny
+    (1, 1, 3, 3, 1, (0, 0, 0, 0), A.ACT_NONE, False, 0.0),             # a single output
+    (1, 48, 33, 65, 64, (1, 0, 0, 1), A.ACT_NONE, True, 0.25),         # several workgroups per row, ragged edges
+]
+
+
+def _run(L, x, w, b, s, *, in_total=0, in_off=0, out_total=0, out_off=0):
+    t = torch()
+    d = cc().conv2d_desc_create(layer_params(L, prelu_slope_count=s.size, in_total_channels=in_total,
+                                             in_channel_offset=in_off, out_total_channels=out_total,
+                                             out_channel_offset=out_off, algo="winograd"))
+    assert cc().conv2d_desc_kernel_name(d) == "winograd_f32"
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
+    y = Guarded(n * ot * ho * wo, t.float32, float("nan"))
+    cc().conv2d_forward(d, to_dev(x), to_dev(w), to_dev(b) if L.has_bias else None,
+                        to_dev(s) if L.act == A.ACT_PRELU else None, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    return y.host().numpy().reshape(n, ot, ho, wo)
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_winograd_cases(i):
+    n, ci, h, w, co, pads, act, bias, pv = CASES[i]
+    L = A.Layer("wino", n, ci, h, w, co, (3, 3), pads=pads, has_bias=bias, act=act, alpha=0.2, clip=(-0.3, 0.4),
+                pad_value=pv)
+    rng = np.random.default_rng(800 + i)
+    x, wt, b, s = A.layer_arrays(rng, L)
+    print(f"case {i}: {L}", flush=True)
+    ref = oracle_layer(L, x, wt, b, s)
+    assert_close(_run(L, x, wt, b, s), ref, FP32_TOL, f"winograd case {i}")
+
+
+def test_winograd_concat_slices():
+    """Input channels [5, 5 + c_in) of a wider buffer, output into channels
+    [3, 3 + c_out) of another; the channels around the slice stay NaN."""
+    L = A.Layer("wino", 2, 24, 10, 18, 20, (3, 3), pads=(1, 1, 1, 1), has_bias=True, act=A.ACT_RELU)
+    rng = np.random.default_rng(880)
+    x, wt, b, s = A.layer_arrays(rng, L)
+    big = rng.standard_normal((L.n, L.c_in + 9, L.h, L.w)).astype(np.float32)
+    big[:, 5:5 + L.c_in] = x
+    y = _run(L, big, wt, b, s, in_total=L.c_in + 9, in_off=5, out_total=L.c_out + 6, out_off=3)
+    assert np.isnan(y[:, :3]).all() and np.isnan(y[:, 3 + L.c_out:]).all()
+    assert_close(y[:, 3:3 + L.c_out], oracle_layer(L, x, wt, b, s), FP32_TOL, "winograd slices")
+
+
+def test_winograd_dense_block_full_size():
+    """The dense-block chain's five layers (1 x Cin x 128 x 128, Cin = 64 + 32k),
+    each fed with the oracle's own previous outputs, at full size."""
+    wl = A.dense_block()
+    a = wl.arrays
+    cur = a["x"]
+    for k, L in enumerate(wl.layers):
+        w = a[f"w{k}"]
+        ref = oracle_layer(L, cur, w, None, None)
+        got = _run(L, cur, w, np.zeros(L.c_out, np.float32), np.zeros(1, np.float32))
+        assert_close(got, ref, FP32_TOL, f"dense block layer {k}")
+        cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
