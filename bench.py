@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default="all",
-                    help="all | dense_block | single_conv | bottleneck | mixed_f32 | mixed_bf16 | int8_chain | copy")
+                    help="all | dense_block | single_conv | bottleneck | mixed_f32 | mixed_bf16 | int8_chain | "
+                         "winograd | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--reps", type=int, default=20, help="timed launches per layer for per_config")
@@ -324,7 +325,7 @@ def float_layer_fns(L, x, w, b, s, dtype, reps, bound=False):
 
 def per_config(reps, only="all"):
     """Per-configuration table; `only` selects one section (single_conv,
-    bottleneck, mixed_f32, mixed_bf16, int8_chain) or all of them."""
+    bottleneck, mixed_f32, mixed_bf16, int8_chain, winograd) or all of them."""
     import convolution_conv2d_forward_amd as cc
     import workloads
     torch = torch_mod()
@@ -451,6 +452,33 @@ def per_config(reps, only="all"):
         res["qfused_dw_pw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "i8"), kernel="qfused_dw_pw")
         log("int8", "qfused_dw_pw", res["qfused_dw_pw"])
         out["int8_chain"] = res
+
+    # dense-block layers, Winograd F(2x2,3x3) beside the implicit GEMM
+    if want("winograd"):
+        wl = workloads.dense_block()
+        total = workloads.DENSE_TOTAL_CHANNELS
+        h, w = wl.layers[0].h, wl.layers[0].w
+        nb = max(1, min(64, -(-ROTATE_BYTES // (total * h * w * 4))))
+        bufs = [torch.zeros((1, total, h, w), device=dev()) for _ in range(nb)]
+        for b in bufs:
+            b[:, :64] = t_(wl.arrays["x"])
+        res = {}
+        for k, L in enumerate(wl.layers):
+            wd = t_(wl.arrays[f"w{k}"])
+            entry = {}
+            for algo in ("direct", "winograd"):
+                p = params_of(L, in_total_channels=total, out_total_channels=total, out_channel_offset=L.c_in)
+                p.algo = cc.ALGOS[algo]
+                d = cc.conv2d_desc_create(p)
+                fns = [lambda d=d, b=b: cc.conv2d_forward(d, b, wd, None, None, b) for b in bufs]
+                t = time_layer(f"{algo}{k}", fns, reps)
+                entry[algo] = dict(roofline_entry(L.flops, 4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w),
+                                                  t, "f32"), kernel=cc.conv2d_desc_kernel_name(d))
+            # the MFMA work Winograd actually issues: 16 products per 2x2 tile and channel pair
+            entry["winograd"]["executed_flops"] = 2 * 16 * L.c_out * L.c_in * ((h + 1) // 2) * ((w + 1) // 2)
+            res[L.name] = entry
+            log("winograd", L.name, {a: e["us"] for a, e in entry.items()})
+        out["dense_block_winograd"] = res
     return out
 
 

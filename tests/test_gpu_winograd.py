@@ -32,6 +32,7 @@ CASES = [
     (3, 7, 5, 6, 5, (0, 0, 0, 0), A.ACT_CLIP, True, 0.0),              # no pads, tiny
     (1, 1, 3, 3, 1, (0, 0, 0, 0), A.ACT_NONE, False, 0.0),             # a single output
     (1, 48, 33, 65, 64, (1, 0, 0, 1), A.ACT_NONE, True, 0.25),         # several workgroups per row, ragged edges
+    (2, 24, 128, 128, 64, (1, 1, 1, 1), A.ACT_RELU, True, 0.0),        # enough workgroups for 64-channel tiles
 ]
 
 
