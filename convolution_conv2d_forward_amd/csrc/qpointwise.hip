@@ -135,6 +135,107 @@ __global__ __launch_bounds__(kThreads) void qpw_kernel(ConvArgs a) {
     }
 }
 
+
+// Fast path for K <= 256 with 4-byte input rows: every chunk's input words
+// and weight fragments are requested up front (loads unconditional, a slot
+// past the channels reads channel 0 and its bytes are zeroed when stored),
+// all chunks are transposed into LDS behind one barrier, then the MFMAs run
+// with the pixel fragment as the first operand, so a lane holds 4
+// consecutive pixels of one output channel and stores them as one word.
+template <int MI, int NCH>
+__global__ __launch_bounds__(kThreads) void qpw_fast_kernel(ConvArgs a) {
+    __shared__ __align__(16) uint8_t xs[NCH][BN * XROW];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int K = a.c_in;
+    const int HW = a.h * a.w;
+
+    uint32_t L = blockIdx.x;
+    const int cot = L % a.co_tiles;  L /= a.co_tiles;
+    const int pt = L % a.tiles_w;    L /= a.tiles_w;
+    const int n = L;
+    const int co0 = cot * MI * 16;
+    const int p0 = pt * BN;
+
+    const int8_t* __restrict__ xg = (const int8_t*)a.xptr + ((int64_t)n * a.in_total + a.in_off) * HW;
+    const int8_t* __restrict__ wg = (const int8_t*)a.wptr;
+    const int kq = tid >> 4;   // this thread's 4 channels of a chunk: 4*kq ..
+    const int pq = tid & 15;   // and 4 pixels: p0 + 4*pq ..
+    const int p = p0 + 4 * pq;
+    const bool pok = p < HW;   // HW % 4 == 0: a word is all in or all out
+
+    uint32_t in[NCH][4];
+    i32x4 wf[NCH][MI];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int ch = 64 * c + 4 * kq + cc;
+            in[c][cc] = *(const uint32_t*)(xg + (ch < K && pok ? (int64_t)ch * HW + p : 0));
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int co = co0 + mi * 16 + (lane & 15);
+            const int k = 64 * c + 16 * (lane >> 4);
+            const bool ok = co < a.c_out && k < K;
+            wf[c][mi] = *(const i32x4*)(wg + (ok ? (int64_t)co * K + k : 0));
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        uint32_t v[4], outw[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) v[cc] = 64 * c + 4 * kq + cc < K && pok ? in[c][cc] : 0u;
+        transpose4x4(v, outw);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) *(uint32_t*)&xs[c][(4 * pq + pp) * XROW + 4 * kq] = outw[pp];
+    }
+    __syncthreads();
+
+    i32x4 acc[MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) acc[mi] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const i32x4 pf = *(const i32x4*)&xs[c][(wave * 16 + (lane & 15)) * XROW + 16 * (lane >> 4)];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int k = 64 * c + 16 * (lane >> 4);
+            const i32x4 w = co0 + mi * 16 + (lane & 15) < a.c_out && k < K ? wf[c][mi] : i32x4{0, 0, 0, 0};
+            acc[mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pf, w, acc[mi], 0, 0, 0);
+        }
+    }
+
+    // Lane: pixels 4*(lane/16) .. +3 of the wave's fragment, channel lane%16.
+    const int px = p0 + wave * 16 + 4 * (lane >> 4);
+    if (px < HW) {
+        int8_t* __restrict__ yg = (int8_t*)a.yptr;
+        const bool relu = a.act == CONV_ACT_RELU;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int co = co0 + mi * 16 + (lane & 15);
+            if (co >= a.c_out) continue;
+            const int32_t b = a.qbias ? a.qbias[co] : 0;
+            uint32_t word = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                word |= (uint32_t)(uint8_t)requant(acc[mi][v] + b, a.composite, a.rounding, a.y_zp, relu) << (8 * v);
+            *(uint32_t*)(yg + ((int64_t)n * a.out_total + a.out_off + co) * HW + px) = word;
+        }
+    }
+}
+
+template <int MI>
+const void* pick_fast_nch(int nch) {
+    switch (nch) {
+    case 1: return (const void*)qpw_fast_kernel<MI, 1>;
+    case 2: return (const void*)qpw_fast_kernel<MI, 2>;
+    case 3: return (const void*)qpw_fast_kernel<MI, 3>;
+    default: return (const void*)qpw_fast_kernel<MI, 4>;
+    }
+}
+
 }  // namespace
 
 bool plan_qpw(Desc& d) {
@@ -158,6 +259,20 @@ hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s) {
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)blocks), block(kThreads);
+    // Fast path: whole 4-byte words of pixels in and out (plane sizes, channel
+    // offsets and the pointers 4-byte aligned) and K <= 256.
+    const int64_t ihw = (int64_t)hw;
+    const bool words = hw % 4 == 0 && (uintptr_t)a.xptr % 4 == 0 && (uintptr_t)a.yptr % 4 == 0 &&
+                       ((int64_t)a.in_total * ihw) % 4 == 0 && ((int64_t)a.out_total * ihw) % 4 == 0 &&
+                       ((int64_t)a.in_off * ihw) % 4 == 0 && ((int64_t)a.out_off * ihw) % 4 == 0;
+    const bool wvec = d.p.c_in % 16 == 0 && (uintptr_t)a.wptr % 16 == 0;
+    if (words && wvec && d.p.c_in <= 4 * KC) {
+        const int nch = (d.p.c_in + KC - 1) / KC;
+        const void* fn = mi == 1 ? pick_fast_nch<1>(nch) : mi == 2 ? pick_fast_nch<2>(nch)
+                         : mi == 3 ? pick_fast_nch<3>(nch) : pick_fast_nch<4>(nch);
+        void* args[] = {&a};
+        return hipLaunchKernel(fn, grid, block, args, 0, s);
+    }
     switch (mi) {
     case 1: hipLaunchKernelGGL(qpw_kernel<1>, grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL(qpw_kernel<2>, grid, block, 0, s, a); break;

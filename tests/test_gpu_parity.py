@@ -419,6 +419,9 @@ INT8_CASES = [
     (2, 144, 10, 10, 48, 1, 1, 0, 1),      # pw K 144
     (1, 20, 7, 9, 30, 1, 1, 0, 1),         # pw K not multiple of 16, HW odd
     (1, 200, 4, 8, 70, 1, 1, 0, 1),        # pw K 200 (4 chunks), M 70
+    (2, 256, 6, 10, 70, 1, 1, 0, 1),       # pw K 256: all four chunks loaded at once, 2 channel tiles
+    (1, 80, 5, 4, 33, 1, 1, 0, 1),         # pw K 80: a partial chunk, one partial pixel tile
+    (1, 288, 4, 4, 16, 1, 1, 0, 1),        # pw K 288: past the load-all-chunks limit
     (2, 6, 9, 11, 10, 3, 1, 1, 2),         # grouped int8 3x3: direct path
     # byte-plane 3x3 kernel: every first-tap byte offset (pad_left mod 4), both strides
     (2, 16, 12, 48, 16, 3, 1, (1, 0, 1, 2), 16),   # s1, pad_left 0
