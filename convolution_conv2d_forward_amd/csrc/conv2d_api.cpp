@@ -47,6 +47,7 @@ const char* kernel_name(const Desc& d) {
     case KC_DIRECT: return "direct";
     case KC_GROUPED: return d.p.dtype == CONV_DTYPE_BF16 ? "grouped_bf16" : "grouped_f32";
     case KC_WINOGRAD_F32: return "winograd_f32";
+    case KC_PW_F32: return "pointwise_f32";
     }
     return "?";
 }
@@ -281,8 +282,11 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
         d->kclass = KC_GROUPED;
         planned = true;
     } else if (p.dtype == CONV_DTYPE_F32) {
+        // The implicit GEMM is planned in every case: it also serves the
+        // pointwise class when a call's tensors are not 16-byte aligned.
         d->kclass = KC_IGEMM_F32;
         planned = plan_igemm_f32(*d);
+        if (planned && plan_pointwise_f32(*d)) d->kclass = KC_PW_F32;
     } else {
         d->kclass = KC_IGEMM_BF16;
         planned = plan_igemm_bf16(*d);
@@ -406,6 +410,9 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     case KC_DW: e = launch_dw(d, a, s); break;
     case KC_GROUPED: e = launch_grouped(d, a, s); break;
     case KC_WINOGRAD_F32: e = launch_winograd_f32(d, a, s); break;
+    case KC_PW_F32:
+        e = pointwise_f32_fits(d, a) ? launch_pointwise_f32(d, a, s) : launch_igemm_f32(d, a, s);
+        break;
     default: e = launch_direct(d, a, s); break;
     }
     return hip_status(e, kernel_name(d));

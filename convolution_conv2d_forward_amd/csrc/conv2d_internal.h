@@ -19,6 +19,7 @@ enum KernelClass : int32_t {
     KC_DIRECT = 5,       // direct convolution, one thread per output (any shape)
     KC_GROUPED = 6,      // grouped 3x3 with 4 or 8 channels per group, VALU
     KC_WINOGRAD_F32 = 7, // Winograd F(2x2, 3x3), fp32 MFMA (3x3, stride 1, dilation 1, one group)
+    KC_PW_F32 = 8,       // pointwise 1x1 with K <= 256, fp32 MFMA, every output channel per workgroup
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -151,6 +152,10 @@ hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s);
+// Needs 16-byte aligned rows (pointers, plane sizes and channel offsets);
+// pointwise_f32_fits says whether a call's tensors allow it.
+hipError_t launch_pointwise_f32(const Desc& d, ConvArgs a, hipStream_t s);
+bool pointwise_f32_fits(const Desc& d, const ConvArgs& a);
 hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw,
                               hipStream_t s);
@@ -168,6 +173,7 @@ bool plan_qdw(Desc& d);
 bool plan_qpw(Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_winograd_f32(const Desc& d);
+bool plan_pointwise_f32(const Desc& d);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 // x: the input pointer (its alignment decides between vector and scalar row loads).

@@ -127,7 +127,8 @@ def test_kernel_choice_for_the_workloads():
                                                      pads=L.pads, dilation=L.dilation, groups=L.groups))
         names[L.name] = cc().conv2d_desc_kernel_name(d)
     assert names["conv0"] == "igemm_f32" and names["conv4"] == "igemm_f32"
-    assert names["pw1"] == "igemm_f32_pointwise" and names["dw"] == "depthwise_f32"
+    assert names["pw1"] == "pointwise_f32" and names["pw2"] == "igemm_f32_pointwise"
+    assert names["dw"] == "depthwise_f32"
     assert names["g32"] == "grouped_f32" and names["pw"] == "igemm_f32_pointwise"
     for L in workloads.int8_chain_layers():
         d = cc().conv2d_desc_create(cc().make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride,

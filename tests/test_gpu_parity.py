@@ -63,6 +63,11 @@ CLASS_CASES = [
     (3, 36, 11, 7, 24, 1, 1, 0, 1, 1, workloads.ACT_RELU),          # pointwise, flattened
     (2, 50, 10, 12, 72, 1, 1, 0, 1, 1, workloads.ACT_PRELU),        # pointwise M 72
     (1, 33, 8, 8, 260, 1, 1, 0, 1, 1, workloads.ACT_NONE),          # pointwise M 260
+    # shallow pointwise (K <= 64, K % 4 == 0, planes of whole 4-pixel words): pointwise_f32
+    (2, 32, 14, 14, 192, 1, 1, 0, 1, 1, workloads.ACT_CLIP),        # the bottleneck expansion shape, partial tile
+    (1, 192, 8, 10, 32, 1, 1, 0, 1, 1, workloads.ACT_PRELU),        # the projection shape (implicit GEMM)
+    (2, 20, 6, 6, 40, 1, 1, 0, 1, 1, workloads.ACT_LEAKY_RELU),     # K 20: partial 16-step, partial channel block
+    (1, 64, 4, 4, 240, 1, 1, 0, 1, 1, workloads.ACT_RELU),          # K 64, weights at the LDS limit
     (2, 8, 12, 12, 16, 1, 2, 1, 1, 1, workloads.ACT_RELU),          # 1x1 strided + padded (not flattened)
     (2, 12, 15, 16, 20, 5, 1, 2, 1, 1, workloads.ACT_LEAKY_RELU),   # 5x5: generic kernel
     (1, 6, 9, 9, 10, (2, 4), (2, 3), (1, 0, 2, 3), (1, 2), 2, workloads.ACT_CLIP),  # 2x4 grouped
@@ -485,3 +490,39 @@ def test_forward_rejects_alias_and_bad_zero_points():
     with pytest.raises(cc().ConvError) as e:
         cc().qconv2d_forward(qd, xi, 0.1, 1, wi, 0.1, 0, None, 0.1, 0, yi)
     assert e.value.status == cc().CONV_ERR_UNSUPPORTED
+
+
+def test_pointwise_f32_slices_and_unaligned_input():
+    """The shallow pointwise kernel reading channels [2, 2 + c_in) of a wider
+    input and writing channels [5, 5 + c_out) of a wider output; then the same
+    layer on an input that is not 16-byte aligned, which the library serves
+    with the implicit GEMM instead (same results within the tolerance)."""
+    import convolution_conv2d_forward_amd as cc
+    t = torch()
+    L = workloads.Layer("pw", 2, 24, 6, 10, 40, (1, 1), has_bias=True, act=workloads.ACT_RELU)
+    rng = np.random.default_rng(990)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    ref = oracle_layer(L, x, wt, b, sl)
+    big = rng.standard_normal((L.n, L.c_in + 5, L.h, L.w)).astype(np.float32)
+    big[:, 2:2 + L.c_in] = x
+    d = cc.conv2d_desc_create(layer_params(L, in_total_channels=L.c_in + 5, in_channel_offset=2,
+                                           out_total_channels=L.c_out + 9, out_channel_offset=5))
+    assert cc.conv2d_desc_kernel_name(d) == "pointwise_f32"
+    n, ot, ho, wo = cc.conv2d_desc_get_output_shape(d)
+    y = Guarded(n * ot * ho * wo, t.float32, float("nan"))
+    cc.conv2d_forward(d, to_dev(big), to_dev(wt), to_dev(b), None, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    got = y.host().numpy().reshape(n, ot, ho, wo)
+    assert np.isnan(got[:, :5]).all() and np.isnan(got[:, 5 + L.c_out:]).all()
+    assert_close(got[:, 5:5 + L.c_out], ref, FP32_TOL, "pointwise_f32 slices")
+    # input one float past a 16-byte boundary
+    d2 = cc.conv2d_desc_create(layer_params(L))
+    raw = t.zeros(x.size + 4, dtype=t.float32, device="cuda")
+    xv = raw[1:1 + x.size]
+    xv.copy_(t.from_numpy(x.reshape(-1)).cuda())
+    y2 = Guarded(L.n * L.c_out * L.h * L.w, t.float32, float("nan"))
+    cc.conv2d_forward(d2, xv, to_dev(wt), to_dev(b), None, y2.view)
+    t.cuda.synchronize()
+    y2.check_guards()
+    assert_close(y2.host().numpy().reshape(ref.shape), ref, FP32_TOL, "pointwise_f32 unaligned input")
