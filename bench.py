@@ -20,8 +20,11 @@ The JSON line also carries:
                 of the same workload's outputs
   per_config    the other synthetic workloads (single conv, inverted
                 bottleneck fused/unfused, mixed sweep fp32/bf16, int8 chain
-                unfused/fused), each layer timed with events the same way,
-                with its binding roofline
+                unfused/fused, dense-block layers with Winograd beside the
+                implicit GEMM), each layer timed with events the same way,
+                with its binding roofline; HBM-bound entries also carry the
+                time of a plain device copy of the same bytes (copy_us) and
+                their speed as a fraction of it (copy_frac)
 Everything on stdout except the final JSON line goes to stderr.
 """
 import argparse
@@ -479,7 +482,38 @@ def per_config(reps, only="all"):
             res[L.name] = entry
             log("winograd", L.name, {a: e["us"] for a, e in entry.items()})
         out["dense_block_winograd"] = res
+    add_copy_context(out, reps)
     return out
+
+
+def copy_us(nbytes, reps):
+    """HIP-event time of a plain device copy moving nbytes in all (half read,
+    half written), cold: rotated over buffer sets like the layers, queued
+    back to back the same way."""
+    torch = torch_mod()
+    n = max(1, nbytes // 8)
+    sets = int(min(64, max(1, ROTATE_BYTES // max(1, 8 * n))))
+    src = [torch.ones(n, device=dev()) for _ in range(sets)]
+    dst = [torch.empty(n, device=dev()) for _ in range(sets)]
+    fns = [lambda s=s_, d=d_: d.copy_(s) for s_, d_ in zip(src, dst)]
+    t = time_layer("copy", fns, reps)
+    del src, dst
+    return t
+
+
+def add_copy_context(out, reps):
+    """Beside every HBM-bound entry: the time a plain device copy of the same
+    bytes takes here, and the entry's speed as a fraction of it (what a copy
+    of that size reaches on this machine, not the 8 TB/s peak)."""
+    cache = {}
+    for sec in out.values():
+        for e in sec.values():
+            if isinstance(e, dict) and e.get("bound") == "hbm" and e.get("bytes"):
+                nb = e["bytes"]
+                if nb not in cache:
+                    cache[nb] = copy_us(nb, reps)
+                e["copy_us"] = round(cache[nb], 3)
+                e["copy_frac"] = round(cache[nb] / e["us"], 4)
 
 
 def copy_probe(reps):
