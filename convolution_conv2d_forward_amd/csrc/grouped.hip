@@ -4,7 +4,9 @@
 // tiles, so the layer is bound by HBM traffic and fp32 FMA issue instead:
 //   * a workgroup owns one (image, group) and a TH x 32 output tile; it
 //     stages the group's input window (all CIG channels, pad_value outside
-//     the image) in LDS as fp32 with coalesced row loads;
+//     the image) in LDS as fp32 with coalesced row loads, every load of a
+//     thread issued before the first LDS write (the whole grid runs in one
+//     round, so a chain of dependent loads per thread would set its time);
 //   * the group's weights are staged in LDS as fp32 in [ci][r][co][s] order
 //     and read as broadcast 16-byte loads (the same address in every lane);
 //   * each thread computes 2 horizontally adjacent output pixels for every
@@ -45,23 +47,60 @@ __global__ __launch_bounds__(TH * 16) void grouped_kernel(ConvArgs a, float pad_
     const int64_t HW = (int64_t)a.h * a.w;
     const T* __restrict__ xg = (const T*)a.xptr + ((int64_t)n * a.in_total + a.in_off + (int64_t)g * CG) * HW;
 
-    // Stage the window: CG planes x PH rows x PW0 columns (pad outside).
-    for (int e = threadIdx.x; e < CG * PH * PW0; e += NT) {
-        const int ci = e / (PH * PW0);
-        const int rem = e - ci * (PH * PW0);
-        const int r = rem / PW0, c = rem - r * PW0;
-        const int ih = ih0 + r, iw = iw0 + c;
-        xs[(ci * PH + r) * PW + c] =
-            ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w) ? ld<T>(xg + ci * HW + ih * a.w + iw)
-                                                                           : pad_v;
+    // Stage the window: CG planes x PH rows x PW0 columns (pad outside), in
+    // batches of up to 24 elements per thread: a batch's loads first
+    // (unconditional: a slot outside the image reads the plane's first
+    // element), then its LDS writes, where the pad is put in.  The weights'
+    // loads go out with the first batch.
+    constexpr int NX = (CG * PH * PW0 + NT - 1) / NT;
+    constexpr int NB = (NX + 23) / 24;
+    constexpr int BX = (NX + NB - 1) / NB;
+    constexpr int NWT = (CG * CG * KH * KW + NT - 1) / NT;
+    const T* __restrict__ wg = (const T*)a.wptr + (int64_t)g * CG * CG * KH * KW;
+    float wv0[NWT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float xv0[BX];
+#pragma unroll
+        for (int i = 0; i < BX; ++i) {
+            const int e = threadIdx.x + (b * BX + i) * NT;
+            const int ci = e / (PH * PW0);
+            const int rem = e - ci * (PH * PW0);
+            const int r = rem / PW0, c = rem - r * PW0;
+            const int ih = ih0 + r, iw = iw0 + c;
+            const bool in = e < CG * PH * PW0 && (unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w;
+            xv0[i] = ld<T>(xg + (in ? ci * HW + ih * a.w + iw : 0));
+        }
+        if (b == 0) {
+#pragma unroll
+            for (int i = 0; i < NWT; ++i) {
+                const int e = threadIdx.x + i * NT;
+                wv0[i] = ld<T>(wg + (e < CG * CG * KH * KW ? e : 0));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BX; ++i) {
+            const int e = threadIdx.x + (b * BX + i) * NT;
+            if (e < CG * PH * PW0) {
+                const int ci = e / (PH * PW0);
+                const int rem = e - ci * (PH * PW0);
+                const int r = rem / PW0, c = rem - r * PW0;
+                const int ih = ih0 + r, iw = iw0 + c;
+                const bool in = (unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w;
+                xs[(ci * PH + r) * PW + c] = in ? xv0[i] : pad_v;
+            }
+        }
     }
     // The group's weights, OIHW -> [ci][r][co][s] in fp32: the 3*CG weights
     // one (ci, r) step needs are contiguous, read as broadcast 16-byte LDS
     // loads (every lane of a wave reads the same address).
-    const T* __restrict__ wg = (const T*)a.wptr + (int64_t)g * CG * CG * KH * KW;
-    for (int e = threadIdx.x; e < CG * CG * KH * KW; e += NT) {
-        const int s = e % KW, r = (e / KW) % KH, ci = (e / (KW * KH)) % CG, co = e / (KW * KH * CG);
-        ws[((ci * KH + r) * CG + co) * KW + s] = ld<T>(wg + e);
+#pragma unroll
+    for (int i = 0; i < NWT; ++i) {
+        const int e = threadIdx.x + i * NT;
+        if (e < CG * CG * KH * KW) {
+            const int s = e % KW, r = (e / KW) % KH, ci = (e / (KW * KH)) % CG, co = e / (KW * KH * CG);
+            ws[((ci * KH + r) * CG + co) * KW + s] = wv0[i];
+        }
     }
     __syncthreads();
 
