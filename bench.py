@@ -161,9 +161,13 @@ def roofline_entry(flops, bytes_, t_us, dtype, bound=None):
 # ------------------------------------------------------------ dense block --
 
 class DenseBlock:
-    """The chain: 5 convs into one concat buffer, rotated over buffer sets."""
+    """The chain: 5 convs into one concat buffer, rotated over buffer sets.
+    bound: each layer's weights are bound to its descriptor once at set-up
+    (conv2d_desc_bind_weights, which packs them for the fp32 implicit GEMM, as
+    ncnn packs weights when a layer's pipeline is created) and every step
+    passes w=None; else every call passes the OIHW weights."""
 
-    def __init__(self, h=128, w=128):
+    def __init__(self, h=128, w=128, bound=True):
         import convolution_conv2d_forward_amd as cc
         import workloads
         torch = torch_mod()
@@ -183,6 +187,12 @@ class DenseBlock:
                                                        out_channel_offset=L.c_in)) for L in self.layers]
         self.kernels = [cc.conv2d_desc_kernel_name(d) for d in self.descs]
         self.w = [t_(wl.arrays[f"w{k}"]) for k in range(len(self.layers))]
+        self.bound = bound
+        if bound:
+            for d, wk in zip(self.descs, self.w):
+                cc.conv2d_desc_bind_weights(d, wk)
+            torch.cuda.synchronize()
+            self.w = [None] * len(self.layers)
         self.flops = [L.flops for L in self.layers]
         # x slice read once + weights + the written slice
         self.bytes = [4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w) for L in self.layers]
@@ -199,10 +209,10 @@ class DenseBlock:
                 timer.run(k, fn)
 
 
-def bench_dense_block(steps, warmup):
+def bench_dense_block(steps, warmup, bound=True):
     torch = torch_mod()
-    db = DenseBlock()
-    log(f"dense block: {db.nsets} buffer sets, kernels {db.kernels}")
+    db = DenseBlock(bound=bound)
+    log(f"dense block: {db.nsets} buffer sets, kernels {db.kernels}, weights {'bound' if bound else 'per call'}")
     for _ in range(warmup):
         db.step()
     torch.cuda.synchronize()
@@ -234,6 +244,8 @@ def dense_roofline(db, per):
     total event time in the step (layers sharing a kernel are pooled)."""
     groups = {}
     for k, name in enumerate(db.kernels):
+        if db.bound and name == "igemm_f32":
+            name = "igemm_f32_packed"
         cfg = f"{name}/M{64 if db.layers[k].c_out > 32 else 32}"
         g = groups.setdefault(cfg, {"layers": [], "flops": 0, "bytes": 0, "us": 0.0})
         g["layers"].append(db.layers[k].name)
@@ -590,7 +602,8 @@ def main():
     step_flops = sum(db.flops)
     value = step_flops * args.steps / wall / 1e9
     dom, g, roof = dense_roofline(db, per)
-    layers = {L.name: dict(roofline_entry(db.flops[k], db.bytes[k], per[k][0], "f32"), kernel=db.kernels[k])
+    kname = lambda k: "igemm_f32_packed" if db.bound and db.kernels[k] == "igemm_f32" else db.kernels[k]
+    layers = {L.name: dict(roofline_entry(db.flops[k], db.bytes[k], per[k][0], "f32"), kernel=kname(k))
               for k, L in enumerate(db.layers)}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -604,6 +617,13 @@ def main():
         "roofline": roof,
         "layers": layers,
     }
+    line["config"]["weights"] = "bound at set-up (packed for the fp32 implicit GEMM)"
+    # The same chain with the OIHW weights passed on every call.
+    db2, wall2, per2 = bench_dense_block(args.steps, args.warmup, bound=False)
+    line["config"]["weights_per_call"] = {
+        "value": round(step_flops * args.steps / wall2 / 1e9, 1), "ms_per_step": round(wall2 / args.steps * 1e3, 4),
+        "layers_us": {L.name: round(per2[k][0], 3) for k, L in enumerate(db2.layers)}}
+    log("dense block, weights per call", line["config"]["weights_per_call"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
         log("cpu_baseline", line["cpu_baseline"])

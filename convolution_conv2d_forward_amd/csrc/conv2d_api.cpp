@@ -333,9 +333,10 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
         return fail(CONV_ERR_INVALID_ARG, "weights were first bound on device %d, current device is %d",
                     d.wbound_device, dev);
     const int64_t wb = w_bytes(d);
-    const bool packs = d.kclass == KC_IGEMM_BF16;
+    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0);
+    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16 ? d.wpack_bytes : d.apack_bytes;
     const int64_t off = packs ? (wb + 255) / 256 * 256 : 0;
-    const int64_t total = packs ? off + d.wpack_bytes : wb;
+    const int64_t total = packs ? off + pack_bytes : wb;
     if (views_overlap(flat(w, wb), flat(d.wbound, d.wbound_bytes)))
         return fail(CONV_ERR_ALIAS, "w is the descriptor's own bound copy");
     if (!d.wbound) {
@@ -351,7 +352,9 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
     d.wbound_pack_off = packs ? off : 0;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(d.wbound, w, (size_t)wb, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess && packs) e = pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s);
+    if (e == hipSuccess && packs)
+        e = d.kclass == KC_IGEMM_BF16 ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
+                                      : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
     if (e != hipSuccess) {
         d.bound = false;
         return hip_status(e, "binding weights");
@@ -403,7 +406,10 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     switch (d.kclass) {
-    case KC_IGEMM_F32: e = launch_igemm_f32(d, a, s); break;
+    case KC_IGEMM_F32:
+        e = launch_igemm_f32(d, a, s, use_bound && d.apack_bytes > 0 ? (const char*)d.wbound + d.wbound_pack_off
+                                                                     : nullptr);
+        break;
     case KC_IGEMM_BF16:
         e = launch_igemm_bf16(d, a, s, use_bound ? (const char*)d.wbound + d.wbound_pack_off : nullptr);
         break;

@@ -127,9 +127,13 @@ struct Desc {
     // column shift, 8-pixel vectors per row, LDS row / plane stride in cells,
     // stride-2 half width)
     int32_t g_ph = 0, g_span = 0, g_shift = 0, g_nvr = 0, g_rs = 0, g_plane = 0, g_half = 0;
+    // fp32 implicit GEMM: bytes of the fragment-order weight image its
+    // packed-weight kernel reads (0 = the configuration has none).
+    int64_t apack_bytes = 0;
     // Weights bound with conv2d_desc_bind_weights: an OIHW copy at wbound,
-    // followed for the bf16 implicit GEMM by the packed image at
-    // wbound + wbound_pack_off (0 = no packed image).
+    // followed for the bf16 implicit GEMM (and the fp32 one when apack_bytes
+    // > 0) by the packed image at wbound + wbound_pack_off (0 = no packed
+    // image).
     void* wbound = nullptr;
     int64_t wbound_bytes = 0;
     int64_t wbound_pack_off = 0;
@@ -139,7 +143,12 @@ struct Desc {
 
 // Launchers (implemented next to their kernels).  Each returns the
 // hipError_t of the launch.
-hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s);
+// wpacked: the bound weights in fragment order (pack_igemm_f32_weights), or
+// null; the packed-weight kernel runs when the configuration has one and the
+// input is 16-byte aligned, else the kernel reading a.wptr (OIHW).
+hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s, const void* wpacked = nullptr);
+// OIHW fp32 weights -> the fragment-order image at dst (d.apack_bytes bytes).
+hipError_t pack_igemm_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 // packed: the weights already in the kernel's layout (bound weights), or
 // null to pack a.wptr (OIHW) into d.wpack first.
 hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed);

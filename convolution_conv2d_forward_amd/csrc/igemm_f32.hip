@@ -61,6 +61,8 @@ struct Cfg {
     static constexpr int AS = (AF4 + 63) / 64;    // weight units per lane
     static constexpr int XS = XS_;                // patch units per lane (upper bound)
     static constexpr int ASZ = WR * KP;           // LDS floats of the weight tile
+    static constexpr int STEPS = KHW * (CW / 4);  // MFMA steps of one chunk
+    static constexpr int AU = (MI * STEPS + 3) / 4;   // packed weights: 16-byte units per lane and chunk
     static constexpr int RS = BN + 4;             // row stride of the reduction tile
     static_assert(WR % 16 == 0 && BN % 16 == 0, "whole 16x16 fragments");
     static_assert(NW % (WM * KS) == 0, "waves split into row halves, K slices and pixel sub-tiles");
@@ -98,7 +100,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <class C>
+// AP (packed weights): a.wptr holds the weights in fragment order, as
+// pack_igemm_f32_weights lays them out: for each group, tile of WR output
+// channels and chunk, AU 16-byte units per lane, unit-major, so that each
+// unit is one coalesced 1 KB load per wave.  The A operands then go from
+// global memory straight into registers, one chunk ahead, and the LDS stages
+// hold the input patch only (a third fewer LDS reads per MFMA step).  Only
+// the two-stage direct-copy pipeline has this form.
+template <class C, bool AP>
 __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     extern __shared__ __align__(16) float lds[];
     constexpr int BM = C::BM, BN = C::BN, TW = C::TW, TH = C::TH, CW = C::CW;
@@ -134,7 +143,8 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     const int PWA = a.patch_w, PS = a.patch_stride;
     const int xf4 = CW * a.patch_h * (PWA >> 2);
     const int HW = a.h * a.w;
-    const int SF = C::ASZ + CW * PS;      // floats of one LDS stage
+    constexpr int XO = AP ? 0 : C::ASZ;   // patch offset in an LDS stage
+    const int SF = XO + CW * PS;          // floats of one LDS stage
     // LDS: the per-wave stages, later reused for the split-K reduction.
     float* pipe = lds;
 
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     constexpr int K4 = C::K / 4;
     int wgo[C::AS];    // weight unit: offset within the co tile at the chunk's first channel, -1 = none
 #pragma unroll
-    for (int i = 0; i < C::AS; ++i) {
+    for (int i = 0; i < (AP ? 0 : C::AS); ++i) {
         const int e = lane + 64 * i;
         const int co = e / K4, j4 = e - (e / K4) * K4;
         wgo[i] = (e < C::AF4 && co0 + co < a.cout_g) ? co * a.cin_g * KHW + 4 * j4 : -1;
@@ -214,7 +224,9 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
                 xr[i] = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
-        if (cl >= CW && vw) {
+        if constexpr (AP) {
+            // Packed weights go to registers separately.
+        } else if (cl >= CW && vw) {
 #pragma unroll
             for (int i = 0; i < C::AS; ++i)
                 wr[i] = wgo[i] >= 0 ? *(const float4*)(wc + wgo[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -233,13 +245,13 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
 
     auto store = [&](float* st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::AS; ++i) {
+        for (int i = 0; i < (AP ? 0 : C::AS); ++i) {
             const int e = lane + 64 * i;
             if (e < C::AF4) *(float4*)(st + (e / K4) * KP + 4 * (e % K4)) = wr[i];
         }
 #pragma unroll
         for (int i = 0; i < C::XS; ++i)
-            if (xlo[i] >= 0) *(float4*)(st + C::ASZ + xlo[i]) = xr[i];
+            if (xlo[i] >= 0) *(float4*)(st + XO + xlo[i]) = xr[i];
     };
 
     // Operand addresses: A lane reads row co = lane%16 at k = (4*step + lane/16)*KHW + rs;
@@ -261,14 +273,14 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
 
     // One MFMA step: tap rs, channels 4q..4q+3 of the chunk.  Operands of
     // step t+1 are fetched from LDS while the MFMAs of step t run.
-    constexpr int STEPS = KHW * (CW / 4);
+    constexpr int STEPS = C::STEPS;
     auto fetch = [&](const float* st, int t, float (&av)[MI], float (&bv)[NI]) __attribute__((always_inline)) {
         const int rs = t / (CW / 4), q = t % (CW / 4);
         const int boff = (rs / KW) * rstep + (rs % KW) * sstep;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) av[mi] = st[a_lane + mi * 16 * KP + q * 4 * KHW + rs];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bv[ni] = st[C::ASZ + b_lane[ni] + q * 4 * PS + boff];
+        for (int ni = 0; ni < NI; ++ni) bv[ni] = st[XO + b_lane[ni] + q * 4 * PS + boff];
     };
     auto mfmas = [&](const float (&av)[MI], const float (&bv)[NI]) __attribute__((always_inline)) {
 #pragma unroll
@@ -305,7 +317,88 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
             }
         }
     };
-    if (C::ST == 2 && a.dma) {
+    if constexpr (AP) {
+        static_assert(C::ST == 2, "packed weights ride the two-stage copy pipeline");
+        // Patch: direct global->LDS copies as below, padding written once per
+        // stage; partial chunks through registers.  Weights: chunk kc's AU
+        // units of this wave's tile, loaded into registers while chunk kc-1
+        // is multiplied out; the wait at the chunk boundary covers both.
+        const int tiles_g = a.co_tiles * C::WM;
+        const f32x4* __restrict__ wp = (const f32x4*)a.wptr +
+            (int64_t)(g * tiles_g + cot * C::WM + wm) * a.chunks * (C::AU * 64) + lane;
+        auto aload = [&](int kc, f32x4 (&dst)[C::AU]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < C::AU; ++u) dst[u] = wp[((int64_t)kc * C::AU + u) * 64];
+        };
+        auto copy_x = [&](int kc, float* st) __attribute__((always_inline)) {
+            if (a.cin_g - kc * CW >= CW) {
+                const float* __restrict__ xc = xg + (int64_t)kc * CW * HW;
+#pragma unroll
+                for (int i = 0; i < C::XS; ++i)
+                    if (xgo[i] >= 0) copy16_to_lds(xc, 4u * (uint32_t)xgo[i], st + 256 * i);
+            } else {
+                load(kc * CW);
+                store(st);
+            }
+        };
+        auto fetch_b = [&](const float* st, int t, float (&bv)[NI]) __attribute__((always_inline)) {
+            const int rs = t / (CW / 4), q = t % (CW / 4);
+            const int boff = (rs / KW) * rstep + (rs % KW) * sstep;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) bv[ni] = st[b_lane[ni] + q * 4 * PS + boff];
+        };
+        if (kb < ke) {
+#pragma unroll
+            for (int i = 0; i < C::XS; ++i)
+                if (xlo[i] >= 0 && xgo[i] < 0) {
+                    *(float4*)(st0 + xlo[i]) = make_float4(pv, pv, pv, pv);
+                    *(float4*)(st1 + xlo[i]) = make_float4(pv, pv, pv, pv);
+                }
+            f32x4 acur[C::AU], anx[C::AU];
+            aload(kb, acur);
+            copy_x(kb, st0);
+            __builtin_amdgcn_s_waitcnt(0);          // chunk kb has landed
+            wave_lds_sync();
+            float b0[NI], b1[NI];
+            fetch_b(st0, 0, b0);
+            for (int kc = kb; kc < ke; ++kc) {
+                const bool odd = (kc - kb) & 1;
+                const float* cur = odd ? st1 : st0;
+                float* nxt = odd ? st0 : st1;
+                const bool more = kc + 1 < ke;
+                if (more) {
+                    copy_x(kc + 1, nxt);
+                    aload(kc + 1, anx);
+                }
+#pragma unroll
+                for (int t = 0; t < STEPS; ++t) {
+                    if (t + 1 < STEPS) {
+                        if (t & 1) fetch_b(cur, t + 1, b0);
+                        else fetch_b(cur, t + 1, b1);
+                    } else if (more) {
+                        __builtin_amdgcn_s_waitcnt(0);   // chunk kc+1 (patch and weights) has landed
+                        wave_lds_sync();
+                        if (t & 1) fetch_b(nxt, 0, b0);
+                        else fetch_b(nxt, 0, b1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    float av[MI];
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi) av[mi] = acur[(mi * STEPS + t) >> 2][(mi * STEPS + t) & 3];
+                    if (t & 1) mfmas(av, b1);
+                    else mfmas(av, b0);
+                }
+                if (STEPS & 1) {
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) b0[ni] = b1[ni];
+                }
+                if (more) {
+#pragma unroll
+                    for (int u = 0; u < C::AU; ++u) acur[u] = anx[u];
+                }
+            }
+        }
+    } else if (C::ST == 2 && a.dma) {
         // Direct global->LDS copies (global_load_lds_dwordx4): lane l of copy
         // unit i writes 16 bytes at stage + 1024*i + 16*l, which is exactly the
         // unit-major layout of both tiles here (weight rows of K = KP floats,
@@ -316,17 +409,17 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
         auto pad_fill = [&](float* st) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < C::XS; ++i)
-                if (xlo[i] >= 0 && xgo[i] < 0) *(float4*)(st + C::ASZ + xlo[i]) = make_float4(pv, pv, pv, pv);
+                if (xlo[i] >= 0 && xgo[i] < 0) *(float4*)(st + XO + xlo[i]) = make_float4(pv, pv, pv, pv);
         };
         auto dma = [&](int c0, float* st) __attribute__((always_inline)) {
             const float* __restrict__ wc = wg + (int64_t)c0 * KHW;
             const float* __restrict__ xc = xg + (int64_t)c0 * HW;
 #pragma unroll
-            for (int i = 0; i < C::AS; ++i)
+            for (int i = 0; i < (AP ? 0 : C::AS); ++i)
                 if (wgo[i] >= 0) copy16_to_lds(wc, 4u * (uint32_t)wgo[i], st + 256 * i);
 #pragma unroll
             for (int i = 0; i < C::XS; ++i)
-                if (xgo[i] >= 0) copy16_to_lds(xc, 4u * (uint32_t)xgo[i], st + C::ASZ + 256 * i);
+                if (xgo[i] >= 0) copy16_to_lds(xc, 4u * (uint32_t)xgo[i], st + XO + 256 * i);
         };
         // Chunks that are not whole (the last one when CW does not divide the
         // group's channels) go through registers.
@@ -465,20 +558,23 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
 // ------------------------------------------------------------ configs ---
 
 struct CfgInfo {
-    int bm, bn, tw, cw, kh, kw, nw, wm, ks, st, xs, asz;
+    int bm, bn, tw, cw, kh, kw, nw, wm, ks, st, xs, asz, mi, steps, au;
     const void* fn;
-    int stage_floats(int ps) const { return asz + cw * ps; }
-    int lds_floats(int ps) const {
-        const int pipe = nw * st * stage_floats(ps);
+    const void* fn_ap;   // packed-weight variant, or null
+    int stage_floats(int ps, bool ap) const { return (ap ? 0 : asz) + cw * ps; }
+    int lds_floats(int ps, bool ap = false) const {
+        const int pipe = nw * st * stage_floats(ps, ap);
         const int red = nw * (bm / wm) * (bn + 4);
         return pipe > red ? pipe : red;
     }
 };
 
-template <class C>
+template <class C, bool AP = false>
 CfgInfo info() {
+    const void* ap = nullptr;
+    if constexpr (AP) ap = (const void*)igemm_f32_kernel<C, true>;
     return CfgInfo{C::BM, C::BN, C::TW, C::CW, C::KH, C::KW, C::NW, C::WM, C::KS, C::ST, C::XS, C::ASZ,
-                   (const void*)igemm_f32_kernel<C>};
+                   C::MI, C::STEPS, C::AU, (const void*)igemm_f32_kernel<C, false>, ap};
 }
 
 // Eight waves (two per SIMD) split K eight ways for the common case, or
@@ -509,7 +605,7 @@ enum {
 
 const CfgInfo& cfg(int i) {
     static const CfgInfo table[NCFG] = {
-        info<K3_M16>(),   info<K3_M32>(),   info<K3_M64>(),    info<K3W_M16>(),  info<K3W_M32>(),
+        info<K3_M16, true>(), info<K3_M32, true>(), info<K3_M64, true>(), info<K3W_M16>(), info<K3W_M32>(),
         info<K3W_M64>(),  info<K3P_M16>(),  info<K3P_M32>(),   info<K1F_M32>(),  info<K1F_M64>(),
         info<K1F_M128>(), info<K1FP_M16>(), info<K1FP_M32>(),  info<K1_M32>(),   info<K1_M64>(),
         info<K5_M16>(),
@@ -584,6 +680,13 @@ bool plan_igemm_f32(Desc& d) {
         if (lds > 160 * 1024) continue;
         d.cfg = cands[k];
         d.flatten_1x1 = flat;
+        // Packed weights (bound weights only): the patch must have the
+        // unit-major layout of the direct copies.
+        d.apack_bytes = 0;
+        if (c.fn_ap && !flat && G.ph * G.pwa == G.ps && p.w % 4 == 0) {
+            const int64_t co_tiles = (d.cout_g + c.bm - 1) / c.bm, chunks = (d.cin_g + c.cw - 1) / c.cw;
+            d.apack_bytes = 4 * (int64_t)p.groups * co_tiles * c.wm * chunks * c.au * 256;
+        }
         d.tile_h = G.th;
         d.tile_w = G.tw;
         d.lds_bytes = lds;
@@ -601,7 +704,7 @@ bool plan_igemm_f32(Desc& d) {
     return false;
 }
 
-hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
+hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s, const void* wpacked) {
     const CfgInfo& c = cfg(d.cfg);
     const conv2d_params_t& p = d.p;
     const Geom G = geom(p, c, d.flatten_1x1);
@@ -631,6 +734,12 @@ hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
     a.dma = c.st == 2 && !d.flatten_1x1 && kdma % 4 == 0 && a_stride(kdma) == kdma &&
             G.ph * G.pwa == G.ps && p.w % 4 == 0 && (d.cin_g * c.kh * c.kw) % 4 == 0 &&
             (uintptr_t)a.xptr % 16 == 0 && (uintptr_t)a.wptr % 16 == 0;
+    const bool ap = wpacked && d.apack_bytes > 0 && c.fn_ap && (uintptr_t)a.xptr % 16 == 0 &&
+                    (uintptr_t)wpacked % 16 == 0;
+    if (ap) {
+        a.wptr = wpacked;
+        a.dma = 1;
+    }
     a.dv_co_tiles = make_divu32((uint32_t)a.co_tiles);
     a.dv_groups = make_divu32((uint32_t)a.groups);
     a.dv_tiles_w = make_divu32((uint32_t)a.tiles_w);
@@ -639,13 +748,66 @@ hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     a.num_blocks = (uint32_t)blocks;
-    if (d.lds_bytes > 64 * 1024) {
-        const hipError_t e =
-            hipFuncSetAttribute(c.fn, hipFuncAttributeMaxDynamicSharedMemorySize, d.lds_bytes);
+    const void* fn = ap ? c.fn_ap : c.fn;
+    const int lds = ap ? 4 * c.lds_floats(G.ps, true) : d.lds_bytes;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
     }
     void* args[] = {&a};
-    return hipLaunchKernel(c.fn, dim3((uint32_t)blocks), dim3(c.nw * 64), args, d.lds_bytes, s);
+    return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(c.nw * 64), args, lds, s);
+}
+
+namespace {
+
+// Fragment-order weights: element i of dst is, with i = ((((g * T + tile) *
+// chunks + kc) * AU + u) * 64 + lane) * 4 + e and f = 4u + e, the A operand of
+// MFMA step t = f % STEPS of row block mi = f / STEPS that lane `lane` feeds
+// for chunk kc of output tile `tile` (WR channels) of group g: output channel
+// tile*WR + 16*mi + lane%16, input channel kc*CW + 4*(t % (CW/4)) + lane/16,
+// tap t / (CW/4); zero past the group's channels and for f >= MI*STEPS.
+__global__ __launch_bounds__(256) void pack_igemm_f32_kernel(const float* __restrict__ w, float* __restrict__ dst,
+                                                             int64_t total, int cin_g, int cout_g, int khw, int cw,
+                                                             int wr, int mi_n, int steps, int au, int chunks,
+                                                             int tiles_g) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int e = (int)(i & 3), lane = (int)((i >> 2) & 63);
+    int64_t r = i >> 8;
+    const int u = (int)(r % au);
+    r /= au;
+    const int kc = (int)(r % chunks);
+    r /= chunks;
+    const int tile = (int)(r % tiles_g);
+    const int g = (int)(r / tiles_g);
+    const int f = 4 * u + e;
+    float v = 0.0f;
+    if (f < mi_n * steps) {
+        const int mi = f / steps, t = f % steps;
+        const int rs = t / (cw / 4), q = t % (cw / 4);
+        const int row = tile * wr + mi * 16 + (lane & 15);
+        const int ch = kc * cw + 4 * q + (lane >> 4);
+        if (row < cout_g && ch < cin_g) v = w[((int64_t)(g * cout_g + row) * cin_g + ch) * khw + rs];
+    }
+    dst[i] = v;
+}
+
+}  // namespace
+
+hipError_t pack_igemm_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s) {
+    if (d.apack_bytes <= 0) return hipErrorInvalidValue;
+    const CfgInfo& c = cfg(d.cfg);
+    const int co_tiles = (d.cout_g + c.bm - 1) / c.bm, chunks = (d.cin_g + c.cw - 1) / c.cw;
+    const int64_t total = d.apack_bytes / 4;
+    const uint64_t blocks = (uint64_t)(total + 255) / 256;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+    const float* src = (const float*)w;
+    float* out = (float*)dst;
+    int64_t tot = total;
+    int cin_g = d.cin_g, cout_g = d.cout_g, khw = d.p.k_h * d.p.k_w, cw = c.cw, wr = c.bm / c.wm, mi = c.mi,
+        steps = c.steps, au = c.au, nch = chunks, tiles_g = co_tiles * c.wm;
+    void* args[] = {&src, &out, &tot, &cin_g, &cout_g, &khw, &cw, &wr, &mi, &steps, &au, &nch, &tiles_g};
+    return hipLaunchKernel((const void*)pack_igemm_f32_kernel, dim3((uint32_t)blocks), dim3(256), args, 0, s);
 }
 
 }  // namespace conv2d
