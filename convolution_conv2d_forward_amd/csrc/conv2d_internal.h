@@ -113,6 +113,7 @@ struct Desc {
     KernelClass kclass;
     // tiling choice for the implicit GEMM / depthwise kernels
     int32_t cfg;                 // kernel variant index within the class
+    int32_t cfg_ap = -1;         // fp32 implicit GEMM: variant that reads packed weights (-1 = none)
     int32_t tile_h, tile_w;
     int32_t lds_bytes;
     int32_t stages;

@@ -64,6 +64,9 @@ struct Cfg {
     static constexpr int STEPS = KHW * (CW / 4);  // MFMA steps of one chunk
     static constexpr int AU = (MI * STEPS + 3) / 4;   // packed weights: 16-byte units per lane and chunk
     static constexpr int RS = BN + 4;             // row stride of the reduction tile
+    // Packed weights: the partial tiles sit behind the (patch-only) pipeline
+    // when both fit beside each other.
+    static constexpr bool RBEHIND = NW * WR * RS * 4 <= 96 * 1024;
     static_assert(WR % 16 == 0 && BN % 16 == 0, "whole 16x16 fragments");
     static_assert(NW % (WM * KS) == 0, "waves split into row halves, K slices and pixel sub-tiles");
     static_assert(TW % 16 == 0 && BN % TW == 0, "a fragment is 16 pixels of one row");
@@ -502,10 +505,15 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
 
     // ---- epilogue: split-K sum through LDS, bias, activation, store ----
     // Wave w parks its WR x BN partial tile at red[w]; wave index is
-    // ((pt * WM) + wm) * KS + wk.
-    __syncthreads();
+    // ((pt * WM) + wm) * KS + wk.  The packed-weight kernel's pipeline is
+    // small enough for the partial tiles to sit behind it, so a wave parks
+    // its tile as soon as it is done; otherwise they reuse the pipeline
+    // stages once every wave has left them.
+    constexpr bool BEHIND = AP && C::RBEHIND;
+    float* const redb = BEHIND ? pipe + C::NW * C::ST * SF : pipe;
+    if constexpr (!BEHIND) __syncthreads();
     {
-        float* red = pipe + wave * C::WR * C::RS;
+        float* red = redb + wave * C::WR * C::RS;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
         const int co = rem / ROW4;                // row within the workgroup's BM
         const int j = 4 * (rem - co * ROW4);
         const int w0 = (p * C::WM + co / C::WR) * C::KS;
-        const float* src = pipe + (co % C::WR) * C::RS + j;
+        const float* src = redb + (co % C::WR) * C::RS + j;
         float4 s = *(const float4*)(src + w0 * C::WR * C::RS);
 #pragma unroll
         for (int k = 1; k < C::KS; ++k) {
@@ -562,19 +570,25 @@ struct CfgInfo {
     const void* fn;
     const void* fn_ap;   // packed-weight variant, or null
     int stage_floats(int ps, bool ap) const { return (ap ? 0 : asz) + cw * ps; }
+    bool rbehind;
     int lds_floats(int ps, bool ap = false) const {
         const int pipe = nw * st * stage_floats(ps, ap);
         const int red = nw * (bm / wm) * (bn + 4);
+        if (ap && rbehind) return pipe + red;   // the partial tiles sit behind the pipeline
         return pipe > red ? pipe : red;
     }
 };
 
-template <class C, bool AP = false>
+// AP: also the packed-weight kernel; AP_ONLY: only that one (the weight
+// tiles of the OIHW kernel would not fit in LDS).
+template <class C, bool AP = false, bool AP_ONLY = false>
 CfgInfo info() {
     const void* ap = nullptr;
+    const void* fn = nullptr;
     if constexpr (AP) ap = (const void*)igemm_f32_kernel<C, true>;
+    if constexpr (!AP_ONLY) fn = (const void*)igemm_f32_kernel<C, false>;
     return CfgInfo{C::BM, C::BN, C::TW, C::CW, C::KH, C::KW, C::NW, C::WM, C::KS, C::ST, C::XS, C::ASZ,
-                   C::MI, C::STEPS, C::AU, (const void*)igemm_f32_kernel<C, false>, ap};
+                   C::MI, C::STEPS, C::AU, fn, ap, C::RBEHIND};
 }
 
 // Eight waves (two per SIMD) split K eight ways for the common case, or
@@ -597,10 +611,14 @@ using K1FP_M32 = Cfg<32,  64, 64, 16, 1, 1, 4, 1, 1, 2, 4>;
 using K1_M32   = Cfg<32,  64, 16,  8, 1, 1, 8, 1, 8, 2, 8>;   // 1x1 with stride or padding
 using K1_M64   = Cfg<64,  64, 16,  8, 1, 1, 8, 2, 4, 2, 8>;
 using K5_M16   = Cfg<16,  64, 16,  4, 5, 5, 8, 1, 8, 1, 4>;
+// Packed weights only: a wave owns all 64 output channels (4 row blocks per
+// patch operand read, K split 8 ways); the OIHW form of its weight tiles
+// would not fit in LDS.
+using K3A_M64  = Cfg<64,  64, 16,  4, 3, 3, 8, 1, 8, 2, 3>;
 
 enum {
     C3_M16, C3_M32, C3_M64, C3W_M16, C3W_M32, C3W_M64, C3P_M16, C3P_M32,
-    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, NCFG
+    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, C3A_M64, NCFG
 };
 
 const CfgInfo& cfg(int i) {
@@ -608,7 +626,7 @@ const CfgInfo& cfg(int i) {
         info<K3_M16, true>(), info<K3_M32, true>(), info<K3_M64, true>(), info<K3W_M16>(), info<K3W_M32>(),
         info<K3W_M64>(),  info<K3P_M16>(),  info<K3P_M32>(),   info<K1F_M32>(),  info<K1F_M64>(),
         info<K1F_M128>(), info<K1FP_M16>(), info<K1FP_M32>(),  info<K1_M32>(),   info<K1_M64>(),
-        info<K5_M16>(),
+        info<K5_M16>(),   info<K3A_M64, true, true>(),
     };
     return table[i];
 }
@@ -682,10 +700,17 @@ bool plan_igemm_f32(Desc& d) {
         d.flatten_1x1 = flat;
         // Packed weights (bound weights only): the patch must have the
         // unit-major layout of the direct copies.
+        // The 64-channel tiles have a packed-only variant in which a wave owns
+        // all 64 rows (same tile and patch geometry, so the same launch grid).
         d.apack_bytes = 0;
-        if (c.fn_ap && !flat && G.ph * G.pwa == G.ps && p.w % 4 == 0) {
-            const int64_t co_tiles = (d.cout_g + c.bm - 1) / c.bm, chunks = (d.cin_g + c.cw - 1) / c.cw;
-            d.apack_bytes = 4 * (int64_t)p.groups * co_tiles * c.wm * chunks * c.au * 256;
+        d.cfg_ap = -1;
+        const int ca = cands[k] == C3_M64 ? C3A_M64 : cands[k];
+        const CfgInfo& cp = cfg(ca);
+        if (cp.fn_ap && !flat && G.ph * G.pwa == G.ps && p.w % 4 == 0 &&
+            4 * cp.lds_floats(G.ps, true) <= 160 * 1024) {
+            const int64_t co_tiles = (d.cout_g + cp.bm - 1) / cp.bm, chunks = (d.cin_g + cp.cw - 1) / cp.cw;
+            d.cfg_ap = ca;
+            d.apack_bytes = 4 * (int64_t)p.groups * co_tiles * cp.wm * chunks * cp.au * 256;
         }
         d.tile_h = G.th;
         d.tile_w = G.tw;
@@ -705,7 +730,9 @@ bool plan_igemm_f32(Desc& d) {
 }
 
 hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s, const void* wpacked) {
-    const CfgInfo& c = cfg(d.cfg);
+    const bool ap = wpacked && d.apack_bytes > 0 && d.cfg_ap >= 0 && (uintptr_t)a.xptr % 16 == 0 &&
+                    (uintptr_t)wpacked % 16 == 0;
+    const CfgInfo& c = cfg(ap ? d.cfg_ap : d.cfg);
     const conv2d_params_t& p = d.p;
     const Geom G = geom(p, c, d.flatten_1x1);
     if (d.flatten_1x1) {
@@ -734,8 +761,6 @@ hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s, const void
     a.dma = c.st == 2 && !d.flatten_1x1 && kdma % 4 == 0 && a_stride(kdma) == kdma &&
             G.ph * G.pwa == G.ps && p.w % 4 == 0 && (d.cin_g * c.kh * c.kw) % 4 == 0 &&
             (uintptr_t)a.xptr % 16 == 0 && (uintptr_t)a.wptr % 16 == 0;
-    const bool ap = wpacked && d.apack_bytes > 0 && c.fn_ap && (uintptr_t)a.xptr % 16 == 0 &&
-                    (uintptr_t)wpacked % 16 == 0;
     if (ap) {
         a.wptr = wpacked;
         a.dma = 1;
@@ -795,8 +820,8 @@ __global__ __launch_bounds__(256) void pack_igemm_f32_kernel(const float* __rest
 }  // namespace
 
 hipError_t pack_igemm_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s) {
-    if (d.apack_bytes <= 0) return hipErrorInvalidValue;
-    const CfgInfo& c = cfg(d.cfg);
+    if (d.apack_bytes <= 0 || d.cfg_ap < 0) return hipErrorInvalidValue;
+    const CfgInfo& c = cfg(d.cfg_ap);
     const int co_tiles = (d.cout_g + c.bm - 1) / c.bm, chunks = (d.cin_g + c.cw - 1) / c.cw;
     const int64_t total = d.apack_bytes / 4;
     const uint64_t blocks = (uint64_t)(total + 255) / 256;

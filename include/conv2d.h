@@ -170,8 +170,10 @@ CONV2D_API const char* conv2d_desc_kernel_name(conv2d_desc_t d);
  * forward calls that use the bound weights skip that step, and for the F32
  * implicit GEMM of 3x3 windows (conv2d_desc_kernel_name "igemm_f32") it packs
  * a second copy in the matrix-core operand order, which forward calls with
- * bound weights read straight into registers (same results, bit for bit;
- * calls whose input is not 16-byte aligned read the OIHW copy).  Forward calls
+ * bound weights read straight into registers (calls whose input is not
+ * 16-byte aligned read the OIHW copy).  The results are those of the OIHW
+ * kernel bit for bit for up to 32 output channels per group; with more, the
+ * packed kernel sums the input channels in another order (same tolerance).  Forward calls
  * (conv2d_forward, fused_pw_dw_forward, qconv2d_forward) use the bound copy
  * when their weight pointer is null.  The copy and the re-layout are queued
  * on `stream` (hipStream_t, null = default stream): forward calls on the same

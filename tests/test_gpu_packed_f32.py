@@ -2,10 +2,13 @@
 fragment order (packed once by conv2d_desc_bind_weights) straight into
 registers instead of staging OIHW weights through LDS.
 
-The packed kernel feeds the matrix cores the same operands in the same order
-and sums the K slices the same way as the kernel given OIHW weights, so the
-bound output must equal the explicit-weight output bit for bit, and both
-must match the oracle at the fp32 tolerance.  Cases reach the three tile
+For tiles of up to 32 output channels the packed kernel feeds the matrix
+cores the same operands in the same order and sums the K slices the same way
+as the kernel given OIHW weights, so the bound output must equal the
+explicit-weight output bit for bit.  For 64-channel tiles the packed kernel
+lets each wave own all 64 channels and splits K eight ways instead of four (a
+different summation order), so there the two agree to the fp32 tolerance.
+Every output must match the oracle at the fp32 tolerance.  Cases reach the three tile
 configurations (<= 16, <= 32, <= 64 output channels per tile), partial
 input-channel chunks and output-channel tiles, padding with a pad value,
 dilation, groups, batch > 1, concat slices on both sides, the layouts that
@@ -46,6 +49,20 @@ def _layer(i):
                    act=act, alpha=0.2, clip=(-0.3, 0.4), pad_value=pv)
 
 
+def _same_split(L):
+    """Bound and explicit weights take the same K split: tiles of <= 32
+    output channels, or the OIHW kernel on both sides (width not a multiple
+    of 4)."""
+    return L.c_out // L.groups <= 32 or L.w % 4 != 0
+
+
+def _agree(bound, explicit, L, what):
+    if _same_split(L):
+        assert_bitexact(bound, explicit, what)
+    else:
+        assert_close(bound, explicit, FP32_TOL, what)
+
+
 def _run(d, xd, wd, bd, sd):
     t = torch()
     n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
@@ -73,11 +90,12 @@ def test_packed_equals_explicit(i):
     cc().conv2d_desc_bind_weights(d, wd)
     wd.fill_(float("nan"))
     bound = _run(d, xd, None, bd, sd)
-    assert_bitexact(bound, explicit, f"case {i} ({kname}): bound vs explicit")
+    _agree(bound, explicit, L, f"case {i} ({kname}): bound vs explicit")
+    assert_close(bound, oracle_layer(L, x, w, b, s), FP32_TOL, f"case {i} bound")
     cc().conv2d_desc_bind_weights(d, w2d)
     rebound = _run(d, xd, None, bd, sd)
     assert_close(rebound, oracle_layer(L, x, w2, b, s), FP32_TOL, f"case {i}: rebound")
-    assert_bitexact(rebound, _run(d, xd, w2d, bd, sd), f"case {i}: rebound vs explicit")
+    _agree(rebound, _run(d, xd, w2d, bd, sd), L, f"case {i}: rebound vs explicit")
 
 
 def test_packed_concat_slices_and_unaligned_input():
@@ -112,7 +130,8 @@ def test_packed_dense_block_full_size():
     buffer, five 3x3 layers appending 32, 32, 32, 32 and 64 channels) with
     every layer's weights bound, run in place like the benchmark; each
     layer's output against the oracle fed with the oracle's own previous
-    outputs, and against the same chain with explicit weights bit for bit."""
+    outputs, and against the same chain with explicit weights (bit for bit
+    for the 32-channel layers)."""
     t = torch()
     wl = A.dense_block()
     a = wl.arrays
@@ -134,9 +153,10 @@ def test_packed_dense_block_full_size():
             cc().conv2d_forward(d, buf, wd, None, None, buf)
         t.cuda.synchronize()
         outs[bound] = buf.cpu().numpy().astype(np.float64)
-    assert_bitexact(outs[True], outs[False], "dense block: bound vs explicit")
     cur = a["x"]
     for k, L in enumerate(wl.layers):
+        sl = slice(L.c_in, L.c_in + L.c_out)
+        _agree(outs[True][:, sl], outs[False][:, sl], L, f"dense block layer {k}: bound vs explicit")
         ref = oracle_layer(L, cur, a[f"w{k}"], None, None)
         assert_close(outs[True][:, L.c_in:L.c_in + L.c_out], ref, FP32_TOL, f"dense block layer {k}")
         cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
