@@ -55,14 +55,36 @@ struct FusedArgs {
     FastDiv div_rw4;       // division by rows*w/4 (load unit -> channel)
 };
 
-__device__ __forceinline__ float act_f(int act, float v, float a0, float a1, float slope) {
-    switch (act) {
-    case CONV_ACT_RELU: return v > 0.0f ? v : 0.0f;
-    case CONV_ACT_LEAKY_RELU: return v >= 0.0f ? v : a0 * v;
-    case CONV_ACT_PRELU: return v >= 0.0f ? v : slope * v;
-    case CONV_ACT_CLIP: return fminf(fmaxf(v, a0), a1);
-    default: return v;
+// The five activations as one branch-free form, y = min(max(v >= 0 ? v : s*v,
+// lo), hi), with (s, lo, hi) = (1, -inf, inf) for none, (1, 0, inf) for ReLU,
+// (alpha, -inf, inf) for LeakyReLU, (slope[c], -inf, inf) for PReLU and
+// (1, lo, hi) for Clip: the same value as each activation's own formula for
+// finite v (ReLU may keep the sign of a zero).  Chosen once per kernel (s per
+// channel for PReLU), it keeps the per-value epilogues free of branches.
+struct ActP {
+    float s, lo, hi;
+};
+
+__device__ __forceinline__ ActP act_params(const ConvArgs& a) {
+    ActP p{1.0f, -INFINITY, INFINITY};
+    if (a.act == CONV_ACT_RELU) {
+        p.lo = 0.0f;
+    } else if (a.act == CONV_ACT_LEAKY_RELU) {
+        p.s = a.act_a;
+    } else if (a.act == CONV_ACT_CLIP) {
+        p.lo = a.act_a;
+        p.hi = a.act_b;
     }
+    return p;
+}
+
+__device__ __forceinline__ float act_apply(float v, float s, float lo, float hi) {
+    return fminf(fmaxf(v >= 0.0f ? v : s * v, lo), hi);
+}
+
+// Slope of channel c: the PReLU slope, else the kernel-wide one.
+__device__ __forceinline__ float act_slope(const ConvArgs& a, const ActP& p, int c) {
+    return a.act == CONV_ACT_PRELU ? a.slope[a.slope_count == 1 ? 0 : c] : p.s;
 }
 
 // NJ: 16-pixel pointwise fragments per wave (register budget: 4 keeps two
@@ -178,29 +200,39 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
     // ---- 2. pointwise epilogue into the expanded tile (aliases xs/ws) ----
     float* es = lds;   // [CE][es_stride], pointwise row r at r*ew, image column c at c + pad_left
     const float dpad = D.pad_value;
+    {
+        // This lane's pixel in each fragment: LDS offset within a channel
+        // (-1 = no pixel) and whether its row is inside the image.
+        int eoff[NJ];
+        bool ein[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int fj = wave + kWaves * j;
-        const int p = fj * 16 + (lane & 15);
-        if (fj < nfn && p < npix) {
-            const int r = (int)fdiv(p, f.div_w);
-            const int c = p - r * W;
-            const bool inside = (unsigned)(ih_lo + r) < (unsigned)H;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int ce = m * 16 + (lane >> 4) * 4 + v;
-                    float val = dpad;
-                    if (inside && ce < ce_valid) {
-                        const int cg = ce0 + ce;
-                        const float t = acc[m][j][v] + (P.bias ? P.bias[cg] : 0.0f);
-                        const float sl = P.act == CONV_ACT_PRELU ? P.slope[P.slope_count == 1 ? 0 : cg] : 0.0f;
-                        val = act_f(P.act, t, P.act_a, P.act_b, sl);
-                    }
-                    es[ce * f.es_stride + r * f.ew + c + D.pad_left] = val;
-                }
+        for (int j = 0; j < NJ; ++j) {
+            const int fj = wave + kWaves * j;
+            const int p = fj * 16 + (lane & 15);
+            eoff[j] = -1;
+            ein[j] = false;
+            if (fj < nfn && p < npix) {
+                const int r = (int)fdiv(p, f.div_w);
+                eoff[j] = r * f.ew + (p - r * W) + D.pad_left;
+                ein[j] = (unsigned)(ih_lo + r) < (unsigned)H;
+            }
         }
+        const ActP pa = act_params(P);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ce = m * 16 + (lane >> 4) * 4 + v;
+                const bool cv = ce < ce_valid;
+                const int cg = ce0 + (cv ? ce : 0);
+                const float bb = P.bias ? P.bias[cg] : 0.0f;
+                const float sl = act_slope(P, pa, cg);
+                float* ech = es + ce * f.es_stride;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    if (eoff[j] >= 0)
+                        ech[eoff[j]] = (ein[j] && cv) ? act_apply(acc[m][j][v] + bb, sl, pa.lo, pa.hi) : dpad;
+            }
     }
     // pad columns of every row
     const int padc = f.ew - W;
@@ -223,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
     float* __restrict__ yg = (float*)D.yptr;
     const float* __restrict__ wdw = (const float*)D.wptr;
     const bool vec_ok = (D.wo % VO) == 0 && (((uintptr_t)D.yptr) % 16) == 0;
+    const ActP da = act_params(D);
     for (int u = tid; u < units; u += kThreads) {
         const int ce = u / (uh * uw);
         const int rem = u - ce * uh * uw;
@@ -237,6 +270,8 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
             for (int q = 0; q < VO; ++q) accd[i][q] = 0.0f;
         const float* ech = es + ce * f.es_stride;
         const float* wch = wdw + (int64_t)cg * kh * kw;
+        const float dbb = D.bias ? D.bias[cg] : 0.0f;
+        const float dsl = act_slope(D, da, cg);
         if constexpr (FIXED) {
             float wt[KH * KW];
 #pragma unroll
@@ -285,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
             if (th >= th_n) break;
             float outv[VO];
 #pragma unroll
-            for (int q = 0; q < VO; ++q) outv[q] = bias_act(D, accd[orow][q], cg);
+            for (int q = 0; q < VO; ++q) outv[q] = act_apply(accd[orow][q] + dbb, dsl, da.lo, da.hi);
             float* dst = yg + ((int64_t)n * D.out_total + D.out_off + cg) * oplane + (int64_t)(ho0 + th) * D.wo + q0;
             if (vec_ok && q0 + VO <= D.wo) {
                 *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
