@@ -33,8 +33,44 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
     return (b & 7u) * per + (b >> 3);
 }
 
+// The five activations as one branch-free form, y = min(max(v >= 0 ? v : s*v,
+// lo), hi), with (s, lo, hi) = (1, -inf, inf) for none, (1, 0, inf) for ReLU,
+// (alpha, -inf, inf) for LeakyReLU, (slope[c], -inf, inf) for PReLU and
+// (1, lo, hi) for Clip: the same value as each activation's own formula for
+// finite v (ReLU may keep the sign of a zero).  Chosen once per kernel (s per
+// channel for PReLU), it keeps the per-value epilogues free of branches; the
+// fused kernels, whose epilogues the compiler did not unswitch, use it.
+struct ActP {
+    float s, lo, hi;
+};
+
+__device__ __forceinline__ ActP act_params(const ConvArgs& a) {
+    ActP p{1.0f, -INFINITY, INFINITY};
+    if (a.act == CONV_ACT_RELU) {
+        p.lo = 0.0f;
+    } else if (a.act == CONV_ACT_LEAKY_RELU) {
+        p.s = a.act_a;
+    } else if (a.act == CONV_ACT_CLIP) {
+        p.lo = a.act_a;
+        p.hi = a.act_b;
+    }
+    return p;
+}
+
+__device__ __forceinline__ float act_apply(float v, float s, float lo, float hi) {
+    return fminf(fmaxf(v >= 0.0f ? v : s * v, lo), hi);
+}
+
+// Slope of channel c: the PReLU slope, else the kernel-wide one.
+__device__ __forceinline__ float act_slope(const ConvArgs& a, const ActP& p, int c) {
+    return a.act == CONV_ACT_PRELU ? a.slope[a.slope_count == 1 ? 0 : c] : p.s;
+}
+
 // Bias add then the fused activation (ncnn convolution: y = act(conv + bias);
-// Go ops ConvLeakyReluOp / ConvPReluOp fuse them into the GEMM write).
+// Go ops ConvLeakyReluOp / ConvPReluOp fuse them into the GEMM write).  The
+// switch on the kernel-wide activation is left to the compiler to hoist out
+// of the callers' loops (measured faster here than the branch-free form for
+// the implicit GEMMs and the depthwise kernels).
 __device__ __forceinline__ float bias_act(const ConvArgs& a, float v, int co) {
     if (a.bias) v += a.bias[co];
     switch (a.act) {

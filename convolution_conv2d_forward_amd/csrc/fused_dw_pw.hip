@@ -209,6 +209,7 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     // window read touch consecutive LDS words (no bank conflicts at stride 1).
     const int cgroups = (WO + 63) / 64;
     const int units = KC * f.th * cgroups * 16;
+    const ActP da = act_params(D);
     auto depthwise = [&](int c, float* es, const float* dp) __attribute__((always_inline)) {
         const int c0 = c * KC;
         for (int u = tid; u < units; u += kT) {
@@ -243,9 +244,10 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
                             for (int v = 0; v < 4; ++v) a[v] = fmaf(rp[16 * v * sw], wv, a[v]);
                         }
                 }
-                const float bb = dp[KC * KHW_MAX + ch], sl = dp[KC * KHW_MAX + KC + ch];
+                const float bb = dp[KC * KHW_MAX + ch];
+                const float sl = D.act == CONV_ACT_PRELU ? dp[KC * KHW_MAX + KC + ch] : da.s;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) outv[v] = apply_act(D, a[v] + bb, sl);
+                for (int v = 0; v < 4; ++v) outv[v] = act_apply(a[v] + bb, sl, da.lo, da.hi);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) outv[v] = 0.0f;   // past the last channel: zero weights too
@@ -321,11 +323,14 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     float* __restrict__ yg = (float*)P.yptr;
     const bool vec_out = WO % 4 == 0 && ((uintptr_t)P.yptr % 16) == 0;
     const int npx_n = th_n * WO;
+    const ActP pa = act_params(P);
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
         const int co = co0 + m * 16 + l16;
         if (m * 16 + l16 >= f.cot || co >= P.c_out) continue;
         float* yc = yg + ((int64_t)n * P.out_total + P.out_off + co) * oplane + (int64_t)ho0 * WO;
+        const float bb = P.bias ? P.bias[co] : 0.0f;
+        const float sl = act_slope(P, pa, co);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int fj = wave + kWaves * j;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
             if (fj >= f.nf || px >= npx_n) continue;
             float v4[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) v4[v] = bias_act(P, acc[m][j][v], co);
+            for (int v = 0; v < 4; ++v) v4[v] = act_apply(acc[m][j][v] + bb, sl, pa.lo, pa.hi);
             if (vec_out) {
                 *(float4*)(yc + px) = make_float4(v4[0], v4[1], v4[2], v4[3]);
             } else {

@@ -55,38 +55,6 @@ struct FusedArgs {
     FastDiv div_rw4;       // division by rows*w/4 (load unit -> channel)
 };
 
-// The five activations as one branch-free form, y = min(max(v >= 0 ? v : s*v,
-// lo), hi), with (s, lo, hi) = (1, -inf, inf) for none, (1, 0, inf) for ReLU,
-// (alpha, -inf, inf) for LeakyReLU, (slope[c], -inf, inf) for PReLU and
-// (1, lo, hi) for Clip: the same value as each activation's own formula for
-// finite v (ReLU may keep the sign of a zero).  Chosen once per kernel (s per
-// channel for PReLU), it keeps the per-value epilogues free of branches.
-struct ActP {
-    float s, lo, hi;
-};
-
-__device__ __forceinline__ ActP act_params(const ConvArgs& a) {
-    ActP p{1.0f, -INFINITY, INFINITY};
-    if (a.act == CONV_ACT_RELU) {
-        p.lo = 0.0f;
-    } else if (a.act == CONV_ACT_LEAKY_RELU) {
-        p.s = a.act_a;
-    } else if (a.act == CONV_ACT_CLIP) {
-        p.lo = a.act_a;
-        p.hi = a.act_b;
-    }
-    return p;
-}
-
-__device__ __forceinline__ float act_apply(float v, float s, float lo, float hi) {
-    return fminf(fmaxf(v >= 0.0f ? v : s * v, lo), hi);
-}
-
-// Slope of channel c: the PReLU slope, else the kernel-wide one.
-__device__ __forceinline__ float act_slope(const ConvArgs& a, const ActP& p, int c) {
-    return a.act == CONV_ACT_PRELU ? a.slope[a.slope_count == 1 ? 0 : c] : p.s;
-}
-
 // NJ: 16-pixel pointwise fragments per wave (register budget: 4 keeps two
 // workgroups per compute unit).
 template <int KH, int KW, int NJ>
