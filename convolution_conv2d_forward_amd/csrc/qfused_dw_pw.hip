@@ -400,8 +400,9 @@ __global__ __launch_bounds__(kT) void qfused_fast_kernel(QFastArgs f) {
     // column group and output row.
     const int du = 16 * th_n * f.wq;
     const float lo_dw = f.relu_dw ? 0.0f : -128.0f;
-    auto depthwise = [&](int c) __attribute__((always_inline)) {
-        const int c0 = c * KC;
+    // The chunk's input tile and filter rows are the ones in LDS (a single
+    // buffer, rewritten each chunk), so the depthwise needs no chunk index.
+    auto depthwise = [&]() __attribute__((always_inline)) {
         for (int u = tid; u < du; u += kT) {
             const int cq = u & 15;
             const int pu = u >> 4;
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(kT) void qfused_fast_kernel(QFastArgs f) {
     // cn (two ahead) into the same registers, depthwise, barrier, MFMAs.
     auto compute = [&](int c, const uint8_t* wt) __attribute__((always_inline)) {
         if (c < nch) {
-            depthwise(c);
+            depthwise();
             __syncthreads();
             pointwise(wt);
         }

@@ -33,7 +33,6 @@ namespace conv2d {
 namespace {
 
 constexpr int kT = 512;
-constexpr int kWaves = kT / 64;
 constexpr int TR = 2, TC = 8;              // output tiles per workgroup (rows, columns)
 constexpr int NT = TR * TC;                // 16: one MFMA column fragment
 constexpr int PH = 2 * TR + 2;             // input patch rows
