@@ -49,6 +49,21 @@ __device__ __forceinline__ uint32_t rq(int32_t acc, float comp, int y_zp, bool r
     return (uint32_t)(uint8_t)(int8_t)q;
 }
 
+// The same requant with the saturation (and ReLU) done on the f32 product:
+// lo = max(-128, relu ? y_zp : -128) - y_zp and hi = 127 - y_zp are integers,
+// and rounding is monotone with integers as fixed points, so clamping before
+// rounding gives the same byte as clamping the rounded value (ReLU after the
+// clamp is the raised lower bound, y_zp <= 127).  One v_med3_f32 replaces the
+// integer clamp, the compare and the select.
+template <int RND>
+__device__ __forceinline__ uint32_t rq_clamped(int32_t acc, float comp, float lo, float hi, int y_zp) {
+    float yf = __fmul_rn((float)acc, comp);
+    asm volatile("" : "+v"(yf));   // as in rq(): no contraction into the rounding
+    yf = __builtin_amdgcn_fmed3f(yf, lo, hi);
+    const float r = RND == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
+    return (uint32_t)(uint8_t)(int8_t)((int)r + y_zp);
+}
+
 template <int SS, int OFF, int RND>
 __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row_bytes, int P) {
     extern __shared__ __align__(16) uint8_t lds8[];
@@ -110,35 +125,44 @@ __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row
     const int64_t oplane = (int64_t)a.ho * a.wo;
     const bool relu = a.act == CONV_ACT_RELU;
     const int q0 = qdw_q0(k, SS, a.pad_left);
+    const float qlo = (float)((relu ? max(-128, a.y_zp) : -128) - a.y_zp), qhi = (float)(127 - a.y_zp);
+    const int lstep = rpi * SS * row_bytes;               // LDS bytes per pass down a plane
+    const int64_t ystep = (int64_t)rpi * a.wo;            // output bytes per pass
+    int8_t* const ybase = (int8_t*)a.yptr + ((int64_t)n * a.out_total + a.out_off + c0) * oplane + 4 * k;
     int p = 0, ho = t0;
     while (ho >= a.ho && p < np) { ho -= a.ho; ++p; }
-    for (; p < np;) {
-        const uint8_t* prow = lds8 + p * plane_bytes + ho * SS * row_bytes + 4 * q0;
-        int32_t acc[4];
+    while (p < np) {
+        // Plane p: its filter rows and bias once, then this thread's rows
+        // ho, ho + rpi, ... with the LDS and output pointers stepping along.
         const int32_t b = bsh[p];
+        const int32_t wrow[3] = {wpk[3 * p], wpk[3 * p + 1], wpk[3 * p + 2]};
+        const uint8_t* prow = lds8 + p * plane_bytes + ho * SS * row_bytes + 4 * q0;
+        int8_t* yrow = ybase + (int64_t)p * oplane + (int64_t)ho * a.wo;
+        for (; ho < a.ho; ho += rpi, prow += lstep, yrow += ystep) {
+            int32_t acc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = b;
+            for (int j = 0; j < 4; ++j) acc[j] = b;
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            const uint32_t* src = (const uint32_t*)(prow + r * row_bytes);
-            uint32_t d[ND];
+            for (int r = 0; r < 3; ++r) {
+                const uint32_t* src = (const uint32_t*)(prow + r * row_bytes);
+                uint32_t d[ND];
 #pragma unroll
-            for (int t = 0; t < ND; ++t) d[t] = src[t];
-            const int32_t wr = wpk[3 * p + r];
+                for (int t = 0; t < ND; ++t) d[t] = src[t];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int idx = OFF + SS * j;              // byte of the first tap, from dword q0
-                const uint32_t lo = d[idx >> 2], hi = d[(idx >> 2) + 1 < ND ? (idx >> 2) + 1 : ND - 1];
-                const uint32_t win = (idx & 3) ? __builtin_amdgcn_alignbyte(hi, lo, idx & 3) : lo;
-                acc[j] = __builtin_amdgcn_sdot4((int)win, wr, acc[j], false);
+                for (int j = 0; j < 4; ++j) {
+                    const int idx = OFF + SS * j;          // byte of the first tap, from dword q0
+                    const uint32_t lo = d[idx >> 2], hi = d[(idx >> 2) + 1 < ND ? (idx >> 2) + 1 : ND - 1];
+                    const uint32_t win = (idx & 3) ? __builtin_amdgcn_alignbyte(hi, lo, idx & 3) : lo;
+                    acc[j] = __builtin_amdgcn_sdot4((int)win, wrow[r], acc[j], false);
+                }
             }
-        }
-        uint32_t packed = 0;
+            uint32_t packed = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) packed |= rq<RND>(acc[j], a.composite, a.y_zp, relu) << (8 * j);
-        int8_t* y = (int8_t*)a.yptr + ((int64_t)n * a.out_total + a.out_off + c0 + p) * oplane + (int64_t)ho * a.wo;
-        *(uint32_t*)(y + 4 * k) = packed;
-        ho += rpi;
+            for (int j = 0; j < 4; ++j) packed |= rq_clamped<RND>(acc[j], a.composite, qlo, qhi, a.y_zp) << (8 * j);
+            *(uint32_t*)yrow = packed;
+        }
+        ho -= a.ho;
+        ++p;
         while (ho >= a.ho && p < np) { ho -= a.ho; ++p; }
     }
 }
