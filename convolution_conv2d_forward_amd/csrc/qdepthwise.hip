@@ -2,10 +2,11 @@
 // QLinearConv (int32 accumulation, + int32 bias, requant) on the VALU
 // dot-product unit.
 //
-//   * A workgroup owns P whole (n, c) planes.  They are staged in LDS as
-//     int8 (not widened), one 16-byte chunk per global load: chunks inside
-//     the image are copied, the margins and the rows outside it are the
-//     zero point (0), so no tap needs a bounds check.
+//   * A workgroup owns P whole (n, c) planes.  They are staged in LDS one at
+//     a time as int8 (not widened), one 16-byte chunk per global load, through
+//     two buffers so that plane p+1's copy runs under plane p's outputs:
+//     chunks inside the image are copied, the margins and the rows outside it
+//     are the zero point (0), so no tap needs a bounds check.
 //   * A thread computes 4 consecutive outputs of one row (one 32-bit store of
 //     4 requantized bytes).  For each filter row it reads the covering LDS
 //     dwords once; the 3 input bytes under output j are cut out with
@@ -22,7 +23,7 @@ namespace {
 
 constexpr int kQT = 256;
 constexpr int kMarg = 16;    // zero bytes left of input column 0 in every LDS row
-constexpr int kNQ = 16;      // 16-byte chunks per thread (bound checked when planning)
+constexpr int kNQ = 16;      // max 16-byte chunks per thread and plane (bound checked when planning)
 
 // LDS geometry of a plane for stride ss, pad_left pl, input width w, output width wo.
 struct QGeom {
@@ -64,11 +65,13 @@ __device__ __forceinline__ uint32_t rq_clamped(int32_t acc, float comp, float lo
     return (uint32_t)(uint8_t)(int8_t)((int)r + y_zp);
 }
 
-template <int SS, int OFF, int RND>
+// NQ: 16-byte chunks per thread and plane (4, 8 or 16; the chunks of the next
+// plane stay in registers while the current one is computed).
+template <int SS, int OFF, int RND, int NQ>
 __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row_bytes, int P) {
     extern __shared__ __align__(16) uint8_t lds8[];
     const int plane_bytes = rows * row_bytes;
-    int32_t* wpk = (int32_t*)(lds8 + P * plane_bytes);     // [P][3] packed filter rows
+    int32_t* wpk = (int32_t*)(lds8 + 2 * plane_bytes);     // [P][3] packed filter rows
     int32_t* bsh = wpk + 3 * P;                             // [P] bias
 
     const int cblocks = (a.c_out + P - 1) / P;
@@ -78,32 +81,36 @@ __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row
     const int64_t HW = (int64_t)a.h * a.w;
     const int8_t* __restrict__ xp = (const int8_t*)a.xptr + ((int64_t)n * a.in_total + a.in_off + c0) * HW;
 
-    // ---- planes -> LDS: all chunk loads first, then the LDS writes ----
+    // One plane at a time through two LDS buffers: the 16-byte chunks of
+    // plane p+1 are requested before plane p's outputs are computed and are
+    // written to the other buffer after them, so their latency runs under
+    // the arithmetic.  Chunks inside the image are copied; the margins and
+    // the rows outside it are the zero point (0), so no tap needs a bounds check.
     const int cpr = row_bytes / 16;                        // chunks per LDS row
-    const int nchunks = np * rows * cpr;
-    uint4 buf[kNQ];
+    const int nchunks = rows * cpr;                        // chunks per plane (<= NQ * kQT)
+    uint4 buf[NQ];
+    auto load_plane = [&](int p) __attribute__((always_inline)) {
+        const int8_t* __restrict__ xq = xp + p * HW;
 #pragma unroll
-    for (int i = 0; i < kNQ; ++i) {
-        const int e = threadIdx.x + i * kQT;
-        buf[i] = make_uint4(0, 0, 0, 0);
-        if (e < nchunks) {
-            const int p = e / (rows * cpr);
-            const int rem = e - p * rows * cpr;
-            const int r = rem / cpr, j = rem - r * cpr;
-            const int ih = r - a.pad_top, iw = 16 * j - kMarg;
-            if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w)
-                buf[i] = *(const uint4*)(xp + p * HW + (int64_t)ih * a.w + iw);
+        for (int i = 0; i < NQ; ++i) {
+            const int e = threadIdx.x + i * kQT;
+            buf[i] = make_uint4(0, 0, 0, 0);
+            if (e < nchunks) {
+                const int r = e / cpr, j = e - r * cpr;
+                const int ih = r - a.pad_top, iw = 16 * j - kMarg;
+                if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w)
+                    buf[i] = *(const uint4*)(xq + (int64_t)ih * a.w + iw);
+            }
         }
-    }
+    };
+    auto store_plane = [&](uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kNQ; ++i) {
-        const int e = threadIdx.x + i * kQT;
-        if (e < nchunks) {
-            const int p = e / (rows * cpr);
-            const int rem = e - p * rows * cpr;
-            *(uint4*)(lds8 + p * plane_bytes + rem * 16) = buf[i];
+        for (int i = 0; i < NQ; ++i) {
+            const int e = threadIdx.x + i * kQT;
+            if (e < nchunks) *(uint4*)(dst + e * 16) = buf[i];
         }
-    }
+    };
+    load_plane(0);
     if (threadIdx.x < np * 3) {
         const int p = threadIdx.x / 3, r = threadIdx.x - p * 3;
         const int8_t* w = (const int8_t*)a.wptr + (int64_t)(c0 + p) * 9 + 3 * r;
@@ -111,77 +118,89 @@ __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row
                                      ((uint32_t)(uint8_t)w[2] << 16));
     }
     if (threadIdx.x < np) bsh[threadIdx.x] = a.qbias ? a.qbias[c0 + threadIdx.x] : 0;
+    store_plane(lds8);
     __syncthreads();
 
     // ---- outputs: 4 consecutive columns of one row per unit ----
-    // A thread keeps one column group k and walks down the rows of the P
-    // planes (rpi rows apart), so its LDS and output addresses only advance.
+    // A thread keeps one column group k and walks down rows t0, t0 + rpi, ...
+    // of each plane, its LDS and output pointers stepping by constants.
     constexpr int ND = SS == 1 ? 3 : 4;                    // dwords covering the taps of 4 outputs
     const int wq = a.wo / 4;
     const int rpi = kQT / wq;                              // rows covered by one pass of the workgroup
     const int t0 = divu((uint32_t)threadIdx.x, a.dv_tiles_w);
-    if (t0 >= rpi) return;                                 // (no barrier follows)
+    const bool active = t0 < rpi;
     const int k = threadIdx.x - t0 * wq;
     const int64_t oplane = (int64_t)a.ho * a.wo;
-    const bool relu = a.act == CONV_ACT_RELU;
     const int q0 = qdw_q0(k, SS, a.pad_left);
+    const bool relu = a.act == CONV_ACT_RELU;
     const float qlo = (float)((relu ? max(-128, a.y_zp) : -128) - a.y_zp), qhi = (float)(127 - a.y_zp);
     const int lstep = rpi * SS * row_bytes;               // LDS bytes per pass down a plane
     const int64_t ystep = (int64_t)rpi * a.wo;            // output bytes per pass
     int8_t* const ybase = (int8_t*)a.yptr + ((int64_t)n * a.out_total + a.out_off + c0) * oplane + 4 * k;
-    int p = 0, ho = t0;
-    while (ho >= a.ho && p < np) { ho -= a.ho; ++p; }
-    while (p < np) {
-        // Plane p: its filter rows and bias once, then this thread's rows
-        // ho, ho + rpi, ... with the LDS and output pointers stepping along.
-        const int32_t b = bsh[p];
-        const int32_t wrow[3] = {wpk[3 * p], wpk[3 * p + 1], wpk[3 * p + 2]};
-        const uint8_t* prow = lds8 + p * plane_bytes + ho * SS * row_bytes + 4 * q0;
-        int8_t* yrow = ybase + (int64_t)p * oplane + (int64_t)ho * a.wo;
-        for (; ho < a.ho; ho += rpi, prow += lstep, yrow += ystep) {
-            int32_t acc[4];
+    for (int p = 0; p < np; ++p) {
+        const bool more = p + 1 < np;
+        if (more) load_plane(p + 1);
+        if (active) {
+            const int32_t b = bsh[p];
+            const int32_t wrow[3] = {wpk[3 * p], wpk[3 * p + 1], wpk[3 * p + 2]};
+            const uint8_t* prow = lds8 + (p & 1) * plane_bytes + t0 * SS * row_bytes + 4 * q0;
+            int8_t* yrow = ybase + (int64_t)p * oplane + (int64_t)t0 * a.wo;
+            for (int ho = t0; ho < a.ho; ho += rpi, prow += lstep, yrow += ystep) {
+                int32_t acc[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = b;
+                for (int j = 0; j < 4; ++j) acc[j] = b;
 #pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                const uint32_t* src = (const uint32_t*)(prow + r * row_bytes);
-                uint32_t d[ND];
+                for (int r = 0; r < 3; ++r) {
+                    const uint32_t* src = (const uint32_t*)(prow + r * row_bytes);
+                    uint32_t d[ND];
 #pragma unroll
-                for (int t = 0; t < ND; ++t) d[t] = src[t];
+                    for (int t = 0; t < ND; ++t) d[t] = src[t];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int idx = OFF + SS * j;          // byte of the first tap, from dword q0
-                    const uint32_t lo = d[idx >> 2], hi = d[(idx >> 2) + 1 < ND ? (idx >> 2) + 1 : ND - 1];
-                    const uint32_t win = (idx & 3) ? __builtin_amdgcn_alignbyte(hi, lo, idx & 3) : lo;
-                    acc[j] = __builtin_amdgcn_sdot4((int)win, wrow[r], acc[j], false);
+                    for (int j = 0; j < 4; ++j) {
+                        const int idx = OFF + SS * j;      // byte of the first tap, from dword q0
+                        const uint32_t lo = d[idx >> 2], hi = d[(idx >> 2) + 1 < ND ? (idx >> 2) + 1 : ND - 1];
+                        const uint32_t win = (idx & 3) ? __builtin_amdgcn_alignbyte(hi, lo, idx & 3) : lo;
+                        acc[j] = __builtin_amdgcn_sdot4((int)win, wrow[r], acc[j], false);
+                    }
                 }
-            }
-            uint32_t packed = 0;
+                uint32_t packed = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) packed |= rq_clamped<RND>(acc[j], a.composite, qlo, qhi, a.y_zp) << (8 * j);
-            *(uint32_t*)yrow = packed;
+                for (int j = 0; j < 4; ++j)
+                    packed |= rq_clamped<RND>(acc[j], a.composite, qlo, qhi, a.y_zp) << (8 * j);
+                *(uint32_t*)yrow = packed;
+            }
         }
-        ho -= a.ho;
-        ++p;
-        while (ho >= a.ho && p < np) { ho -= a.ho; ++p; }
+        if (more) {
+            // Buffer (p+1)&1 was last read by plane p-1's outputs, which every
+            // thread finished before the previous barrier.
+            store_plane(lds8 + ((p + 1) & 1) * plane_bytes);
+            __syncthreads();
+        }
     }
 }
 
 // Byte offset of output 0's first tap inside dword q0: (kMarg - pad_left) & 3.
-template <int SS, int RND>
+template <int SS, int RND, int NQ>
 const void* pick_off(int off) {
     switch (off) {
-    case 0: return (const void*)qdw3_kernel<SS, 0, RND>;
-    case 1: return (const void*)qdw3_kernel<SS, 1, RND>;
-    case 2: return (const void*)qdw3_kernel<SS, 2, RND>;
-    default: return (const void*)qdw3_kernel<SS, 3, RND>;
+    case 0: return (const void*)qdw3_kernel<SS, 0, RND, NQ>;
+    case 1: return (const void*)qdw3_kernel<SS, 1, RND, NQ>;
+    case 2: return (const void*)qdw3_kernel<SS, 2, RND, NQ>;
+    default: return (const void*)qdw3_kernel<SS, 3, RND, NQ>;
     }
 }
 
-template <int SS>
+template <int SS, int NQ>
 const void* pick_rnd(int off, int rounding) {
-    return rounding == CONV_ROUND_HALF_AWAY ? pick_off<SS, CONV_ROUND_HALF_AWAY>(off)
-                                            : pick_off<SS, CONV_ROUND_HALF_EVEN>(off);
+    return rounding == CONV_ROUND_HALF_AWAY ? pick_off<SS, CONV_ROUND_HALF_AWAY, NQ>(off)
+                                            : pick_off<SS, CONV_ROUND_HALF_EVEN, NQ>(off);
+}
+
+template <int SS>
+const void* pick_nq(int nchunks, int off, int rounding) {
+    if (nchunks <= 4 * kQT) return pick_rnd<SS, 4>(off, rounding);
+    if (nchunks <= 8 * kQT) return pick_rnd<SS, 8>(off, rounding);
+    return pick_rnd<SS, 16>(off, rounding);
 }
 
 bool qgeom(const Desc& d, QGeom& G) {
@@ -197,12 +216,13 @@ bool qgeom(const Desc& d, QGeom& G) {
     G.row_bytes = (rb + 15) / 16 * 16;
     G.rows = (d.ho - 1) * ss + 3;
     G.plane_bytes = G.rows * G.row_bytes;
+    // Planes per workgroup: as many as would have fit 32 KB at once (at most
+    // 8), now streamed one at a time through two buffers.
     int P = (32 * 1024) / G.plane_bytes;
     if (P > 8) P = 8;
     if (P < 1) P = 1;
-    while (P > 1 && P * G.rows * (G.row_bytes / 16) > kNQ * kQT) --P;
     G.planes = P;
-    return P * G.rows * (G.row_bytes / 16) <= kNQ * kQT && P * G.plane_bytes + 16 * P <= 64 * 1024;
+    return G.rows * (G.row_bytes / 16) <= kNQ * kQT && 2 * G.plane_bytes + 16 * P <= 160 * 1024;
 }
 
 }  // namespace
@@ -212,6 +232,7 @@ bool plan_qdw3(const Desc& d) {
     if (p.k_h != 3 || p.k_w != 3 || p.dilation_h != 1 || p.dilation_w != 1) return false;
     if (p.stride_h != p.stride_w || (p.stride_h != 1 && p.stride_h != 2)) return false;
     if (p.w % 16 != 0 || d.wo % 4 != 0 || p.pad_left > kMarg) return false;
+    if (d.wo / 4 > kQT) return false;   // a row's column groups must fit one workgroup pass
     if ((int64_t)p.h * p.w >= INT32_MAX / 16) return false;
     QGeom G;
     return qgeom(d, G);
@@ -227,10 +248,15 @@ hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s) {
     const int off = (kMarg - d.p.pad_left) & 3;
     a.dv_tiles_h = make_divu32((uint32_t)(a.ho * (a.wo / 4)));
     a.dv_tiles_w = make_divu32((uint32_t)(a.wo / 4));
-    const void* fn = d.p.stride_h == 1 ? pick_rnd<1>(off, a.rounding) : pick_rnd<2>(off, a.rounding);
+    const int nchunks = G.rows * (G.row_bytes / 16);
+    const void* fn = d.p.stride_h == 1 ? pick_nq<1>(nchunks, off, a.rounding) : pick_nq<2>(nchunks, off, a.rounding);
     int rows = G.rows, rb = G.row_bytes, P = G.planes;
     void* args[] = {&a, &rows, &rb, &P};
-    const size_t lds = (size_t)P * G.plane_bytes + 16 * P;
+    const size_t lds = 2 * (size_t)G.plane_bytes + 16 * P;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
     return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kQT), args, lds, s);
 }
 

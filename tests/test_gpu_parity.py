@@ -434,6 +434,10 @@ INT8_CASES = [
     (2, 8, 17, 64, 8, 3, 2, (1, 2, 1, 0), 8),      # s2, pad_left 2
     (1, 9, 16, 32, 9, 3, 2, 1, 9),                 # s2, pad_left 1, 9 planes (partial last workgroup)
     (3, 5, 9, 16, 5, 3, 1, 1, 5),                  # s1, tiny planes
+    # planes past 1024 and past 2048 16-byte copy units (the 8- and 16-unit register buffers;
+    # the latter two 41 KB LDS buffers)
+    (1, 3, 96, 224, 3, 3, 1, 1, 3),                # s1, 98 rows x 16 units
+    (1, 2, 160, 224, 2, 3, 2, 1, 2),               # s2, 161 rows x 16 units
 ]
 
 
