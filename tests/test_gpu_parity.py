@@ -438,6 +438,7 @@ INT8_CASES = [
     # the latter two 41 KB LDS buffers)
     (1, 3, 96, 224, 3, 3, 1, 1, 3),                # s1, 98 rows x 16 units
     (1, 2, 160, 224, 2, 3, 2, 1, 2),               # s2, 161 rows x 16 units
+    (1, 2, 5, 1056, 2, 3, 1, 1, 2),                # s1, 264 column groups per row: the generic depthwise
 ]
 
 
