@@ -584,8 +584,8 @@ def cpu_baseline(target_s=12.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described, not built).", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(there is no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     torch = torch_mod()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
