@@ -217,7 +217,13 @@ static float round_to_integer(float v, int mode) {
 int8_t oracle_requant(int64_t v, float composite, int rounding, int64_t y_zp, int relu) {
     const float vf = (float)v;       /* exact for |v| < 2^24 */
     volatile float yf = vf * composite;
-    int64_t q = (int64_t)round_to_integer(yf, rounding) + y_zp;
+    float r = round_to_integer(yf, rounding);
+    /* Saturation to int8 makes every |r| beyond 256 equivalent; bounding r
+       first keeps the integer conversion defined for any product, an
+       infinite one (a large composite) included. */
+    if (r > 512.0f) r = 512.0f;
+    if (r < -512.0f) r = -512.0f;
+    int64_t q = (int64_t)r + y_zp;
     if (q < -128) q = -128;
     if (q > 127) q = 127;
     if (relu && q < y_zp) q = y_zp;

@@ -301,6 +301,23 @@ def test_requant_matches_numpy_rint_and_saturates():
     np.testing.assert_array_equal(shifted, np.clip(np.rint(v.astype(np.float32) * comp) + 5, -128, 127))
 
 
+@pytest.mark.parametrize("y_zp", [-100, 0, 100])
+@pytest.mark.parametrize("relu", [False, True])
+def test_requant_saturates_at_extreme_composites(y_zp, relu):
+    """A composite of 1e30 sends every nonzero sum past the int8 range (the
+    largest ones to an infinite f32 product): the result is 127 above zero,
+    -128 below it and the zero point at zero, raised to the zero point under
+    ReLU, whatever y_zp is."""
+    comp = np.float32(1e30)
+    v = np.array([-2**31, -10**9, -5, -1, 0, 1, 7, 10**9, 2**31 - 1], dtype=np.int64)
+    expect = np.where(v > 0, 127, np.where(v < 0, -128, y_zp))
+    if relu:
+        expect = np.maximum(expect, y_zp)
+    for rounding in (oracle.ROUND_HALF_EVEN, oracle.ROUND_HALF_AWAY):
+        got = oracle.requant(v, comp, rounding=rounding, y_zp=y_zp, relu=relu)
+        np.testing.assert_array_equal(got.astype(np.int64), expect)
+
+
 def test_requant_equals_exact_rational_rounding_on_unsaturated_range():
     """Over |acc| <= 32000 the f32 formula with composite 0x3B83126E gives the
     exactly rounded (ties to even) value of acc*sx*sw/sy, sx,sw,sy taken as the
