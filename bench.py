@@ -146,6 +146,33 @@ class EventTimer:
         return float(np.mean(ts)), float(np.median(ts)), len(ts)
 
 
+class BoundaryTimer:
+    """HIP events on the launch stream at the boundaries between consecutive
+    launches of a step: one event before the first launch and one after each
+    launch.  A launch's time is the span between its two neighbouring events,
+    so the spans of a step add up to the step's own event span and nothing is
+    counted twice or left out."""
+
+    def __init__(self):
+        self.steps = []
+        self.cur = []
+
+    def mark(self):
+        torch = torch_mod()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.cur.append(e)
+
+    def end_step(self):
+        self.steps.append(self.cur)
+        self.cur = []
+
+    def spans_us(self):
+        """[step][launch] spans in microseconds."""
+        torch_mod().cuda.synchronize()
+        return [[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(len(ev) - 1)] for ev in self.steps]
+
+
 def roofline_entry(flops, bytes_, t_us, dtype, bound=None):
     t = t_us * 1e-6
     mf = flops / t / PEAK[dtype]
@@ -199,14 +226,19 @@ class DenseBlock:
         self.i = 0
 
     def step(self, timer=None):
+        """One pass of the chain.  timer: a BoundaryTimer that records an event
+        before the first launch and after every launch, so layer k's time is
+        the span between the events on either side of it."""
         buf = self.bufs[self.i % self.nsets]
         self.i += 1
+        if timer is not None:
+            timer.mark()
         for k, (d, w) in enumerate(zip(self.descs, self.w)):
-            fn = lambda d=d, w=w: self.cc.conv2d_forward(d, buf, w, None, None, buf)
-            if timer is None:
-                fn()
-            else:
-                timer.run(k, fn)
+            self.cc.conv2d_forward(d, buf, w, None, None, buf)
+            if timer is not None:
+                timer.mark()
+        if timer is not None:
+            timer.end_step()
 
 
 def bench_dense_block(steps, warmup, bound=True):
@@ -222,9 +254,10 @@ def bench_dense_block(steps, warmup, bound=True):
         db.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Event pass over the same number of steps: per-launch durations, queued
-    # behind a GPU delay so that the launches run back to back.
-    timer = EventTimer()
+    # Event pass over the same number of steps: events at the launch
+    # boundaries, queued behind a GPU delay so that the launches run back to
+    # back as in the wall-clock pass.
+    timer = BoundaryTimer()
     torch.cuda.synchronize()
     delay = 300.0 * steps
     gpu_delay(delay)
@@ -235,7 +268,8 @@ def bench_dense_block(steps, warmup, bound=True):
     torch.cuda.synchronize()
     if t_enq > delay:
         log(f"dense block: host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
-    per = [timer.mean_us(k) for k in range(len(db.layers))]
+    spans = np.array(timer.spans_us())
+    per = [(float(spans[:, k].mean()), float(np.median(spans[:, k])), spans.shape[0]) for k in range(len(db.layers))]
     return db, wall, per
 
 
@@ -291,21 +325,25 @@ def _rotating(make, footprint, target=ROTATE_BYTES, cap=64):
 
 def time_layer(key, fn_sets, reps, warm=3):
     """Mean HIP-event time of one launch.  fn_sets: list of callables (one per
-    rotating buffer set); the timed launches are queued behind a GPU delay."""
+    rotating buffer set); the timed launches are queued back to back behind a
+    GPU delay, with events at the boundaries between them (BoundaryTimer)."""
     torch = torch_mod()
     for i in range(warm):
         fn_sets[i % len(fn_sets)]()
     torch.cuda.synchronize()
-    timer = EventTimer()
+    timer = BoundaryTimer()
     delay = 200.0 * reps
     gpu_delay(delay)
     t0 = time.perf_counter()
+    timer.mark()
     for i in range(reps):
-        timer.run(key, fn_sets[i % len(fn_sets)])
+        fn_sets[i % len(fn_sets)]()
+        timer.mark()
+    timer.end_step()
     t_enq = (time.perf_counter() - t0) * 1e6
     if t_enq > delay:
         log(f"{key}: host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
-    return timer.mean_us(key)[0]
+    return float(np.mean(timer.spans_us()[0]))
 
 
 def float_layer_fns(L, x, w, b, s, dtype, reps, bound=False):
@@ -546,11 +584,16 @@ def copy_probe(reps):
 
 # ------------------------------------------------------------ cpu baseline --
 
-def cpu_baseline(target_s=12.0):
-    """The oracle (as it stands) on whole passes of the same step: the five
-    dense-block layers, each computed in full in float64 from the previous
-    layers' float32 outputs, with the concat buffer assembled by plain
-    concatenation.  Passes repeat until about target_s seconds have run."""
+def cpu_baseline(target_s=6.0):
+    """The oracle (as it stands) on the host cores.
+
+    value: whole passes of the benchmark step (the five dense-block layers,
+    each computed in full in float64 from the previous layers' float32
+    outputs, the concat buffer assembled by plain concatenation), repeated
+    until about target_s seconds have run.  per_config: every layer of the
+    other workloads computed once in full (wall seconds and GFLOP/s each; the
+    mixed sweep's fp32 inputs, whose float64 arithmetic is the same work as
+    its bf16 one; the int8 chain in int64)."""
     import oracle
     import workloads
     layers = workloads.dense_block_layers()
@@ -573,10 +616,54 @@ def cpu_baseline(target_s=12.0):
         if s >= target_s:
             break
     f = passes * step_flops
+
+    per = {}
+
+    def timed(cfg, name, L, fn):
+        t1 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t1
+        per.setdefault(cfg, {})[name] = {"seconds": round(dt, 4), "gflops": round(L.flops / dt / 1e9, 3),
+                                         "gflop": round(L.flops / 1e9, 4)}
+
+    sc = workloads.single_conv()
+    L = sc.layers[0]
+    timed("single_conv", "conv", L, lambda: oracle.conv2d(sc.arrays["x"], sc.arrays["w"], sc.arrays["b"],
+                                                          pads=L.pads, act=L.act))
+    bn = workloads.bottleneck()
+    a = bn.arrays
+    L1, L2, L3 = bn.layers
+    e = oracle.conv2d(a["x"], a["w_pw1"], None, act=L1.act, clip=L1.clip)
+    timed("bottleneck", "pw1", L1, lambda: oracle.conv2d(a["x"], a["w_pw1"], None, act=L1.act, clip=L1.clip))
+    e = e.astype(np.float32)
+    dwo = oracle.conv2d(e, a["w_dw"], None, pads=L2.pads, groups=L2.groups, act=L2.act, clip=L2.clip)
+    timed("bottleneck", "dw", L2, lambda: oracle.conv2d(e, a["w_dw"], None, pads=L2.pads, groups=L2.groups,
+                                                        act=L2.act, clip=L2.clip))
+    dwo = dwo.astype(np.float32)
+    timed("bottleneck", "pw2", L3, lambda: oracle.conv2d(dwo, a["w_pw2"], None))
+    for L in workloads.mixed_sweep_layers():
+        m = workloads.mixed_sweep(which={L.name}).arrays
+        n_ = L.name
+        timed("mixed_sweep", n_, L, lambda: oracle.conv2d(m[f"x_{n_}"], m[f"w_{n_}"], m[f"b_{n_}"], stride=L.stride,
+                                                          pads=L.pads, dilation=L.dilation, groups=L.groups,
+                                                          act=L.act, slope=m[f"s_{n_}"]))
+    q = workloads.int8_chain()
+    cur = q.arrays["x"]
+    for L in q.layers:
+        qa = q.arrays
+        res = {}
+
+        def run(L=L, cur=cur):
+            res["y"] = oracle.qconv2d(cur, qa[f"w_{L.name}"], qa[f"b_{L.name}"], *workloads.INT8_SCALES,
+                                      stride=L.stride, pads=L.pads, groups=L.groups)
+        timed("int8_chain", L.name, L, run)
+        cur = res["y"]
+    total = sum(e["seconds"] for c in per.values() for e in c.values())
     return {"value": round(f / s / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{passes} full pass(es) of the 5-layer dense-block chain "
-                      f"({f / 1e9:.2f} GFLOP in {s:.1f} s, float64 direct loops, OpenMP over (n, c_out))",
-            "seconds": round(s, 2)}
+                      f"({f / 1e9:.2f} GFLOP in {s:.1f} s, float64 direct loops, OpenMP over (n, c_out)); "
+                      f"per_config: every layer of the other workloads once in full ({total:.1f} s)",
+            "seconds": round(s, 2), "per_config": per}
 
 
 # ------------------------------------------------------------------- main --

@@ -1,14 +1,15 @@
 // C ABI of libconv2d.so: descriptor creation and validation, kernel choice,
 // pointer and alias checks, dispatch.  Host code only.
 //
-// The descriptor follows the "validate once, run unchecked" pattern of the
-// onnx-light-cpu "Binary Kernel Design" page (section "Prepared execution":
-// a descriptor built once per node validates attributes and binds the typed
-// function; section "Compute, scheduling, and safety": invalid inputs are
-// rejected before unchecked loops, and an input may alias the output only
-// when nothing is overwritten before its last read).  Status codes mirror
-// the Go "ops" page's error returns (PReluOp rejects a slope it cannot
-// broadcast per channel with ErrIncompatibleShapes).
+// Attributes are checked once, when the descriptor is made, and the forward
+// calls then only check their pointers: the prepared-execution design of the
+// onnx-light-cpu "Binary Kernel Design" page (sections "Prepared execution"
+// and "Compute, scheduling, and safety").  The output may share a buffer
+// with the input only where the two channel ranges are disjoint, so no input
+// element is overwritten before a kernel has read it; any other overlap is
+// refused.  Status codes follow the error returns of the Go "ops" page
+// (section PReluOp: a slope count that is neither 1 nor the channel count is
+// ErrIncompatibleShapes).
 #include <cfloat>
 #include <cmath>
 #include <cstdarg>
@@ -158,6 +159,42 @@ bool winograd_preferred(const Desc& d) {
     return false;
 }
 
+// A bf16 implicit-GEMM forward call given OIHW weights: re-lay them into the
+// descriptor's pack buffer, then convolve.  The buffer is allocated by the
+// first such call, on the current device.  Each call waits, on its own
+// stream, for the event recorded after the previous call's kernels (which
+// read the buffer), refills the buffer, convolves and records the event, all
+// under the descriptor's mutex: calls sharing the descriptor may come from
+// any streams and host threads and each one convolves with its own weights.
+conv_status_t forward_bf16_repack(Desc& d, const ConvArgs& a, hipStream_t s) {
+    std::lock_guard<std::mutex> lock(d.mu);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(CONV_ERR_HIP, "no current HIP device");
+    if (!d.wpack) {
+        hipError_t e = hipMalloc(&d.wpack, (size_t)d.wpack_bytes);
+        if (e != hipSuccess) {
+            d.wpack = nullptr;
+            return fail(CONV_ERR_HIP, "allocating %lld bytes for the packed bf16 weights: %s",
+                        (long long)d.wpack_bytes, hipGetErrorString(e));
+        }
+        e = hipEventCreateWithFlags(&d.wpack_ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            (void)hipFree(d.wpack);
+            d.wpack = nullptr;
+            d.wpack_ev = nullptr;
+            return hip_status(e, "creating the pack buffer's event");
+        }
+        d.wpack_device = dev;
+    } else if (dev != d.wpack_device) {
+        return fail(CONV_ERR_INVALID_ARG, "the bf16 pack buffer lives on device %d, current device is %d",
+                    d.wpack_device, dev);
+    }
+    hipError_t e = hipStreamWaitEvent(s, d.wpack_ev, 0);
+    if (e == hipSuccess) e = launch_igemm_bf16(d, a, s, nullptr, d.wpack);
+    if (e == hipSuccess) e = hipEventRecord(d.wpack_ev, s);
+    return hip_status(e, "igemm_bf16");
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,18 +333,6 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
         d->flatten_1x1 = false;
         d->wpack_bytes = 0;
     }
-    if (d->kclass == KC_IGEMM_BF16) {
-        int dev = -1;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipMalloc(&d->wpack, (size_t)d->wpack_bytes);
-        if (e != hipSuccess) {
-            d->wpack = nullptr;
-            delete d;
-            return fail(CONV_ERR_HIP, "allocating %lld bytes for the packed bf16 weights: %s",
-                        (long long)d->wpack_bytes, hipGetErrorString(e));
-        }
-        d->wpack_device = dev;
-    }
     *out = (conv2d_desc_t)d;
     return ok();
 }
@@ -315,6 +340,11 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
 void conv2d_desc_destroy(conv2d_desc_t dd) {
     Desc* d = (Desc*)dd;
     if (!d) return;
+    if (d->wpack_ev) {
+        // The last call that read the pack buffer may still be running.
+        (void)hipEventSynchronize(d->wpack_ev);
+        (void)hipEventDestroy(d->wpack_ev);
+    }
     free_on(d->wpack, d->wpack_device);
     free_on(d->wbound, d->wbound_device);
     delete d;
@@ -326,9 +356,6 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
     if (!w) return fail(CONV_ERR_INVALID_ARG, "null weights");
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return fail(CONV_ERR_HIP, "no current HIP device");
-    if (d.wpack_device >= 0 && dev != d.wpack_device)
-        return fail(CONV_ERR_INVALID_ARG, "descriptor was created on device %d, current device is %d",
-                    d.wpack_device, dev);
     if (d.wbound && dev != d.wbound_device)
         return fail(CONV_ERR_INVALID_ARG, "weights were first bound on device %d, current device is %d",
                     d.wbound_device, dev);
@@ -382,7 +409,7 @@ const char* conv2d_desc_kernel_name(conv2d_desc_t dd) {
 conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, const float* bias,
                              const float* slope, void* y, void* stream) {
     if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
-    const Desc& d = *(const Desc*)dd;
+    Desc& d = *(Desc*)dd;
     if (d.p.dtype == CONV_DTYPE_I8) return fail(CONV_ERR_INVALID_ARG, "int8 descriptor: use qconv2d_forward");
     if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
     const bool use_bound = !w;
@@ -396,12 +423,6 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
         return fail(CONV_ERR_ALIAS, "y overlaps the bias");
     if (d.p.act_type == CONV_ACT_PRELU && views_overlap(yv, flat(slope, 4 * (int64_t)d.p.prelu_slope_count)))
         return fail(CONV_ERR_ALIAS, "y overlaps the PReLU slopes");
-    if (d.kclass == KC_IGEMM_BF16) {
-        int dev = -1;
-        if (hipGetDevice(&dev) != hipSuccess || dev != d.wpack_device)
-            return fail(CONV_ERR_INVALID_ARG, "bf16 descriptor was created on device %d, current device is %d",
-                        d.wpack_device, dev);
-    }
     ConvArgs a = make_args(d, x, w, bias, slope, y);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -411,7 +432,13 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
                                                                      : nullptr);
         break;
     case KC_IGEMM_BF16:
-        e = launch_igemm_bf16(d, a, s, use_bound ? (const char*)d.wbound + d.wbound_pack_off : nullptr);
+        if (use_bound) {
+            e = launch_igemm_bf16(d, a, s, (const char*)d.wbound + d.wbound_pack_off, nullptr);
+        } else {
+            const conv_status_t st = forward_bf16_repack(d, a, s);
+            if (st != CONV_OK) return st;
+            e = hipSuccess;
+        }
         break;
     case KC_DW: e = launch_dw(d, a, s); break;
     case KC_GROUPED: e = launch_grouped(d, a, s); break;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/conv2d.h"
 
 namespace conv2d {
@@ -119,11 +121,17 @@ struct Desc {
     int32_t stages;
     int32_t pt_vertical;
     bool flatten_1x1;            // 1x1/s1/p0: treat [h][w] as one row of h*w pixels
-    // bf16 implicit GEMM: device buffer for the weights in the kernel's LDS
-    // layout, refilled by every forward call (allocated at creation).
+    // bf16 implicit GEMM, forward calls given OIHW weights: the weights
+    // re-laid into the kernel's per-chunk LDS images before every such call.
+    // The buffer is allocated by the first such call, on the device current
+    // then; wpack_ev is recorded after each call's kernels, and the next call
+    // waits for it on its own stream before it refills the buffer, so calls
+    // on any streams see their own weights; mu serialises the host side.
     void* wpack = nullptr;
     int64_t wpack_bytes = 0;
     int wpack_device = -1;
+    hipEvent_t wpack_ev = nullptr;
+    std::mutex mu;
     // bf16 implicit GEMM: patch geometry fixed at planning (rows, columns,
     // column shift, 8-pixel vectors per row, LDS row / plane stride in cells,
     // stride-2 half width)
@@ -151,8 +159,8 @@ hipError_t launch_igemm_f32(const Desc& d, ConvArgs a, hipStream_t s, const void
 // OIHW fp32 weights -> the fragment-order image at dst (d.apack_bytes bytes).
 hipError_t pack_igemm_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 // packed: the weights already in the kernel's layout (bound weights), or
-// null to pack a.wptr (OIHW) into d.wpack first.
-hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed);
+// null to pack a.wptr (OIHW) into pack_buf (d.wpack_bytes bytes) first.
+hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed, void* pack_buf);
 // OIHW bf16 weights -> the bf16 implicit GEMM's per-chunk LDS images at dst
 // (d.wpack_bytes bytes).
 hipError_t pack_igemm_bf16_weights(const Desc& d, const void* w, void* dst, hipStream_t s);

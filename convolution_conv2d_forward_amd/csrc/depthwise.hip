@@ -297,6 +297,9 @@ const void* pick(const conv2d_params_t& p) {
 
 template <typename T>
 hipError_t launch_t(const Desc& d, ConvArgs a, hipStream_t s) {
+    // The pad enters the input's storage type, as every other bf16 kernel
+    // takes it: padded taps read the bf16 value nearest pad_value.
+    if constexpr (std::is_same<T, __hip_bfloat16>::value) a.pad_value = bf16_to_f32(f32_to_bf16(a.pad_value));
     a.tile_h = d.tile_h;
     a.tile_w = d.tile_w;
     a.tiles_h = (d.ho + d.tile_h - 1) / d.tile_h;

@@ -123,10 +123,13 @@ __device__ __forceinline__ int8_t requant(int32_t acc, float composite, int roun
     // toward zero.
     asm volatile("" : "+v"(yf));
     const float r = rounding == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
-    int q = (int)r + y_zp;
-    q = q < -128 ? -128 : (q > 127 ? 127 : q);
-    if (relu && q < y_zp) q = y_zp;
-    return (int8_t)q;
+    // Saturate on the rounded float before the conversion: clamp(r + y_zp,
+    // -128, 127) is clamp(r, -128 - y_zp, 127 - y_zp) + y_zp for integer r,
+    // and ReLU (q >= y_zp) raises the lower bound to 0.  The float is then at
+    // most 255 in magnitude, so the conversion is exact for any product
+    // (an infinite one included).
+    const float lo = relu ? 0.0f : (float)(-128 - y_zp), hi = (float)(127 - y_zp);
+    return (int8_t)((int)__builtin_amdgcn_fmed3f(r, lo, hi) + y_zp);
 }
 
 __host__ __device__ __forceinline__ float bf16_to_f32(__hip_bfloat16 v) {

@@ -95,23 +95,22 @@ hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s) {
     if (total == 0) return hipSuccess;
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const void* fn;
+    float pv = a.pad_value;
     switch (d.p.dtype) {
-    case CONV_DTYPE_F32:
-        hipLaunchKernelGGL(direct_float_kernel<float>, dim3((uint32_t)blocks), dim3(256), 0, s, a, total,
-                           a.pad_value);
-        break;
-    case CONV_DTYPE_BF16: {
+    case CONV_DTYPE_F32: fn = (const void*)direct_float_kernel<float>; break;
+    case CONV_DTYPE_BF16:
         // The pad enters the same storage type as the input (bf16).
-        const float pv = bf16_to_f32(f32_to_bf16(a.pad_value));
-        hipLaunchKernelGGL(direct_float_kernel<__hip_bfloat16>, dim3((uint32_t)blocks), dim3(256), 0, s,
-                           a, total, pv);
+        fn = (const void*)direct_float_kernel<__hip_bfloat16>;
+        pv = bf16_to_f32(f32_to_bf16(a.pad_value));
         break;
+    default: fn = (const void*)direct_int8_kernel; break;
     }
-    default:
-        hipLaunchKernelGGL(direct_int8_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, a, total);
-        break;
-    }
-    return hipGetLastError();
+    // hipLaunchKernel reports this launch's own status (hipGetLastError would
+    // also return, and clear, an earlier call's error).
+    void* fargs[] = {&a, (void*)&total, &pv};
+    void* iargs[] = {&a, (void*)&total};
+    return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(256), d.p.dtype == CONV_DTYPE_I8 ? iargs : fargs, 0, s);
 }
 
 }  // namespace conv2d

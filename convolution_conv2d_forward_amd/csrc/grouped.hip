@@ -172,9 +172,9 @@ hipError_t launch_t(ConvArgs a, hipStream_t s, float pad_v) {
     const int64_t by = (int64_t)a.n * a.groups;
     if (bx == 0 || by == 0) return hipSuccess;
     if (bx > 0x7FFFFFFF || by > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((grouped_kernel<T, CG, SS, DL, TH>), dim3((uint32_t)bx, (uint32_t)by), dim3(TH * 16), 0, s,
-                       a, pad_v);
-    return hipGetLastError();
+    void* args[] = {&a, &pad_v};
+    return hipLaunchKernel((const void*)grouped_kernel<T, CG, SS, DL, TH>, dim3((uint32_t)bx, (uint32_t)by),
+                           dim3(TH * 16), args, 0, s);
 }
 
 template <typename T, int CG>

@@ -610,7 +610,7 @@ hipError_t pack_igemm_bf16_weights(const Desc& d, const void* w, void* dst, hipS
                            0, s);
 }
 
-hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed) {
+hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const void* packed, void* pack_buf) {
     // The kernel reads input rows as 16-byte vectors.
     if ((uintptr_t)a.xptr % 16 != 0) return launch_direct(d, a, s);
     const CfgInfo& c = cfg(d.cfg);
@@ -640,10 +640,10 @@ hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const voi
     if (d.wpack_bytes != wpack_cells(d, c) * 16) return hipErrorInvalidValue;
     // 1) weights -> per-chunk LDS images (unless they are bound, packed once)
     if (!packed) {
-        if (!d.wpack) return hipErrorInvalidValue;
-        const hipError_t e = pack_igemm_bf16_weights(d, a.wptr, d.wpack, s);
+        if (!pack_buf) return hipErrorInvalidValue;
+        const hipError_t e = pack_igemm_bf16_weights(d, a.wptr, pack_buf, s);
         if (e != hipSuccess) return e;
-        packed = d.wpack;
+        packed = pack_buf;
     }
 
     // 2) the convolution

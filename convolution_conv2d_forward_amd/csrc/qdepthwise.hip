@@ -44,10 +44,10 @@ __device__ __forceinline__ uint32_t rq(int32_t acc, float comp, int y_zp, bool r
     // toward zero.
     asm volatile("" : "+v"(yf));
     const float r = RND == CONV_ROUND_HALF_AWAY ? roundf(yf) : rintf(yf);
-    int q = (int)r + y_zp;
-    q = q < -128 ? -128 : (q > 127 ? 127 : q);
-    if (relu && q < y_zp) q = y_zp;
-    return (uint32_t)(uint8_t)(int8_t)q;
+    // Saturation (and ReLU) on the rounded float, as in requant(): the
+    // conversion then sees at most 255 in magnitude.
+    const float lo = relu ? 0.0f : (float)(-128 - y_zp), hi = (float)(127 - y_zp);
+    return (uint32_t)(uint8_t)(int8_t)((int)__builtin_amdgcn_fmed3f(r, lo, hi) + y_zp);
 }
 
 // The same requant with the saturation (and ReLU) done on the f32 product:

@@ -273,13 +273,10 @@ hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s) {
         void* args[] = {&a};
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
-    switch (mi) {
-    case 1: hipLaunchKernelGGL(qpw_kernel<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(qpw_kernel<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(qpw_kernel<3>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(qpw_kernel<4>, grid, block, 0, s, a); break;
-    }
-    return hipGetLastError();
+    const void* fn = mi == 1 ? (const void*)qpw_kernel<1> : mi == 2 ? (const void*)qpw_kernel<2>
+                     : mi == 3 ? (const void*)qpw_kernel<3> : (const void*)qpw_kernel<4>;
+    void* args[] = {&a};
+    return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
 }  // namespace conv2d

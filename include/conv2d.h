@@ -7,11 +7,11 @@
  * package docs "ops" of github.com/0verkilll/onnx, sections ConvOp,
  * ConvLeakyReluOp, ConvPReluOp, ConcatFusedTailOp, ReluOp, LeakyReluOp,
  * PReluOp, ClipOp; the yscv page "ONNX CPU Kernels (Conv/MatMul) -- Runtime
- * Map", section "Hot kernel paths"):
- *
- *   x2 = pad(x, pads, pad_value)
- *   x3 = correlate(x2, weight, kernel, stride, dilation, group) + bias
- *   y  = activation(x3)     (none, ReLU, LeakyReLU, PReLU, Clip)
+ * Map", section "Hot kernel paths"): every output element is the sum, over
+ * the input channels of its group and the k_h x k_w window taps placed by
+ * stride and dilation, of input times weight, where a tap that falls outside
+ * the input image reads pad_value; the channel's bias is added to that sum
+ * and the activation (none, ReLU, LeakyReLU, PReLU or Clip) is applied last.
  *
  * Layouts (all tensors dense, row-major):
  *   x       [n][in_total_channels][h][w]; the convolution reads channels
@@ -28,19 +28,24 @@
  *
  * Ownership: the caller allocates and owns every input and output buffer;
  * forward calls launch kernels asynchronously on the caller's HIP stream and
- * return, and allocate nothing.  Descriptors are owned by the library from
+ * return, and allocate nothing (one exception, below).  Descriptors are owned by the library from
  * conv2d_desc_create until conv2d_desc_destroy; their attributes are fixed at
  * creation, and the only later change is weights bound with
  * conv2d_desc_bind_weights (a device copy the descriptor owns; see there).
- * Apart from that copy, one exception to "no library device memory": a BF16 descriptor
- * whose kernel is the implicit GEMM (any BF16 dense or grouped convolution
- * that is not depthwise; conv2d_desc_kernel_name starts with "igemm_bf16")
- * allocates, at creation and on the current device, a buffer for the weights
- * in the kernel's layout, freed by conv2d_desc_destroy.  Every forward call
- * refills it from w before the convolution reads it, so forward calls that
- * use one such descriptor must be ordered (one stream, or events); calls on
- * other descriptors are independent.  Such a descriptor must be used with the
- * device it was created on (INVALID_ARG otherwise).
+ * conv2d_desc_create allocates no device memory.  Apart from the bound copy,
+ * one exception to "no library device memory": a BF16 descriptor whose kernel
+ * is the implicit GEMM (any BF16 dense or grouped convolution that is not
+ * depthwise; conv2d_desc_kernel_name starts with "igemm_bf16") re-lays OIHW
+ * weights passed to conv2d_forward into the kernel's layout in a buffer the
+ * descriptor owns.  The first such call allocates it (once, on the current
+ * device; freed by conv2d_desc_destroy); every such call refills it.  The
+ * descriptor orders these calls itself (each one waits, on its own stream,
+ * for the previous one's kernels, through an event the descriptor records),
+ * so calls sharing one descriptor may come from any streams or host threads
+ * and each convolves with its own weights; they then run one after another
+ * on the GPU.  Calls with bound weights (w null) use no such buffer.  The
+ * buffer stays on its device: a later call from another device returns
+ * INVALID_ARG.
  *
  * Errors: every call returns a conv_status_t and never aborts; no C++
  * exception crosses the ABI.  conv2d_last_error() returns a thread-local
@@ -146,9 +151,8 @@ CONV2D_API void conv2d_params_init(conv2d_params_t* p);
  *   INCOMPATIBLE_SHAPES   groups not dividing c_in and c_out; slope count not
  *                         1 or c_out; channel offset + count beyond the total
  *   UNSUPPORTED           I8 with pad_value != 0 or an activation other than
- *                         NONE/RELU; tensors beyond 2^31 elements
- *   HIP                   BF16 implicit-GEMM descriptor: no current device,
- *                         or its packed-weight buffer could not be allocated */
+ *                         NONE/RELU; tensors beyond 2^40 elements, planes
+ *                         beyond 2^31 elements */
 CONV2D_API conv_status_t conv2d_desc_create(const conv2d_params_t* p, conv2d_desc_t* out);
 
 /* Release a descriptor (null is allowed). */
@@ -237,6 +241,11 @@ CONV2D_API conv_status_t fused_dw_pw_forward(conv2d_desc_t desc_dw, conv2d_desc_
  * round = the descriptor's int8_rounding; ReLU (if set) is max(q, y_zp).
  *   x, w, y   device int8 pointers (layouts above); w null = bound weights
  *   bias      device int32[c_out] or null
+ * The sum acc + bias is formed in int32: a bias with |bias[co]| above
+ * 2^31 - 1 - 128*128*(c_in/groups)*k_h*k_w may overflow it, and the output
+ * is then unspecified (no such bias is rejected: the library does not read
+ * device data on the host).  Any positive finite composite is allowed; the
+ * saturation holds for every product, infinite ones included.
  * Errors: UNSUPPORTED if x_zp != 0 or w_zp != 0 (symmetric scheme only);
  * INVALID_ARG if a scale is not finite and positive or dtype is not I8. */
 CONV2D_API conv_status_t qconv2d_forward(conv2d_desc_t d, const int8_t* x, float x_scale, int8_t x_zp,

@@ -100,9 +100,10 @@ def oracle_layer(L: workloads.Layer, x, w, b, s, pad_value=None):
                          slope=s if L.act == workloads.ACT_PRELU else None)
 
 
-def gpu_layer(L: workloads.Layer, x, w, b, s, *, dtype="f32", out_total=None, out_off=0, repeat=1):
+def gpu_layer(L: workloads.Layer, x, w, b, s, *, dtype="f32", out_total=None, out_off=0, repeat=1, bound=False):
     """Run one float layer on the GPU into a NaN-guarded output; returns
-    (host output as float64 [n, out_total, ho, wo], kernel name, all runs)."""
+    (host output as float64 [n, out_total, ho, wo], kernel name, all runs).
+    bound: bind the weights to the descriptor and call with w=None."""
     import convolution_conv2d_forward_amd as cc
     t = torch()
     tdt = t.float32 if dtype == "f32" else t.bfloat16
@@ -114,6 +115,10 @@ def gpu_layer(L: workloads.Layer, x, w, b, s, *, dtype="f32", out_total=None, ou
     wd = to_dev(w.astype(np.float32), tdt)
     bd = to_dev(b.astype(np.float32)) if L.has_bias else None
     sd = to_dev(s.astype(np.float32)) if L.act == workloads.ACT_PRELU else None
+    if bound:
+        cc.conv2d_desc_bind_weights(d, wd)
+        t.cuda.synchronize()
+        wd = None
     runs = []
     for _ in range(repeat):
         y = Guarded(n * ot * ho * wo, tdt, float("nan"))

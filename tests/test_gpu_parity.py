@@ -225,19 +225,40 @@ def test_dense_block_chain_reduced_spatial():
     assert_bitexact(out[:, :64], wl.arrays["x"], "input slice untouched")
 
 
-def test_dense_block_chain_full_size_sampled():
-    """Full 128x128 chain in the launch configuration the benchmark times;
-    each layer is checked at 3000 sampled outputs against the oracle evaluated
-    on the oracle's own chain (full oracle chain, fp32 between layers)."""
-    wl, out = _dense_block(128, 128)
-    rng = np.random.default_rng(0)
+def _dense_block_bound(h, w):
+    """The chain as the benchmark runs it: each layer's weights bound to its
+    descriptor once (packed for the fp32 implicit GEMM), forward calls with
+    w=None."""
+    t = torch()
+    wl = workloads.dense_block(h, w)
+    total = workloads.DENSE_TOTAL_CHANNELS
+    buf = t.full((1, total, h, w), float("nan"), device=dev())
+    buf[:, :64] = to_dev(wl.arrays["x"])
+    descs = []
+    for k, L in enumerate(wl.layers):
+        p = layer_params(L, in_total_channels=total, out_total_channels=total, out_channel_offset=L.c_in)
+        d = cc().conv2d_desc_create(p)
+        cc().conv2d_desc_bind_weights(d, to_dev(wl.arrays[f"w{k}"]))
+        descs.append(d)
+    for d in descs:
+        cc().conv2d_forward(d, buf, None, None, None, buf)
+    t.cuda.synchronize()
+    return wl, buf.cpu().numpy()
+
+
+@pytest.mark.parametrize("bound", [False, True])
+def test_dense_block_chain_full_size(bound):
+    """Full 128x128 chain in the launch configuration the benchmark times
+    (bound: the weights bound and packed, as the benchmark step runs it;
+    else passed on every call), every output of every layer compared with the
+    oracle evaluated on the oracle's own chain (fp32 between layers)."""
+    wl, out = _dense_block_bound(128, 128) if bound else _dense_block(128, 128)
     cur = wl.arrays["x"].astype(np.float32)
     for k, L in enumerate(wl.layers):
-        ref_full = oracle_layer(L, cur, wl.arrays[f"w{k}"], None, None)   # needed for the next layer's input
-        idx = rng.choice(ref_full.size, 3000, replace=False)
-        got = out[:, L.c_in:L.c_in + L.c_out].reshape(-1)[idx]
-        assert_close(got, ref_full.reshape(-1)[idx], FP32_TOL, f"layer {k}")
-        cur = np.concatenate([cur, ref_full.astype(np.float32)], axis=1)
+        ref = oracle_layer(L, cur, wl.arrays[f"w{k}"], None, None)
+        assert_close(out[:, L.c_in:L.c_in + L.c_out], ref, FP32_TOL, f"layer {k}")
+        cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
+    assert_bitexact(out[:, :64], wl.arrays["x"], "input slice untouched")
 
 
 # ------------------------------------------------ inverted bottleneck ----
@@ -352,19 +373,17 @@ def test_mixed_sweep_reduced_batch(name, dtype):
 
 
 @pytest.mark.parametrize("name", ["s2", "d2", "g32", "pw"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_mixed_sweep_full_size_sampled(name, dtype):
-    """Full N=32 layers (the benchmark's launch configuration), 4000 sampled
-    outputs against the oracle evaluated point by point."""
+@pytest.mark.parametrize("dtype,bound", [("f32", False), ("bf16", False), ("bf16", True)])
+def test_mixed_sweep_full_size(name, dtype, bound):
+    """Full N=32 layers in the benchmark's launch configuration, every output
+    compared with the oracle (bound: the bf16 weights bound to the descriptor
+    and re-laid once, as the benchmark times them)."""
     L, x, w, b, s = _mixed(name, 32)
     if dtype == "bf16":
         x, w = bf16_round(x), bf16_round(w)
-    y, kname, _ = gpu_layer(L, x, w, b, s, dtype=dtype)
-    rng = np.random.default_rng(1)
-    idx = rng.choice(y.size, 4000, replace=False)
-    ref = oracle.conv2d_points(x, w, b, idx, stride=L.stride, pads=L.pads, dilation=L.dilation,
-                               groups=L.groups, act=L.act, slope=s)
-    assert_close(y.reshape(-1)[idx], ref, FP32_TOL if dtype == "f32" else BF16_TOL, f"{name} {dtype} ({kname})")
+    y, kname, _ = gpu_layer(L, x, w, b, s, dtype=dtype, bound=bound)
+    ref = oracle_layer(L, x, w, b, s)
+    assert_close(y, ref, FP32_TOL if dtype == "f32" else BF16_TOL, f"{name} {dtype} ({kname})")
 
 
 @pytest.mark.parametrize("seed", range(16))
@@ -475,6 +494,74 @@ def test_int8_ties_exact():
         ref = oracle.qconv2d(x, wt, b, 1.0, 1.0, 2.0, rounding=rounding)
         got, _ = _qrun(L, x, wt, b, (1.0, 1.0, 2.0), rounding=rounding)
         assert_bitexact(got, ref, f"ties rounding={rounding}")
+
+
+# Every int8 kernel class: dot4 depthwise s1 / s2, generic depthwise (5x5),
+# pointwise with all chunks loaded at once and the general pointwise, and the
+# dense / grouped convolutions.
+SAT_CASES = [
+    # n, c, h, w, c_out, k, stride, pads, groups
+    (1, 8, 12, 32, 8, 3, 1, 1, 8),
+    (1, 8, 12, 32, 8, 3, 2, 1, 8),
+    (1, 4, 9, 11, 4, 5, 1, 2, 4),
+    (2, 64, 6, 8, 40, 1, 1, 0, 1),
+    (1, 288, 4, 4, 16, 1, 1, 0, 1),
+    (2, 16, 9, 11, 24, 3, 1, 1, 1),
+    (2, 16, 9, 11, 16, 3, 2, 1, 4),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SAT_CASES)))
+@pytest.mark.parametrize("y_zp", [-100, 100])
+@pytest.mark.parametrize("relu", [False, True])
+def test_int8_saturation_extreme_composite(i, y_zp, relu):
+    """A composite of 1e30 (scales 1e10, 1e10, 1e-10) with a nonzero output
+    zero point: every product leaves the int8 range (many become infinite in
+    f32), and the result must still be the saturated byte the oracle gives."""
+    n, c, h, w, co, k, s, p, g = SAT_CASES[i]
+    L = workloads.Layer("q", n, c, h, w, co, (k, k), stride=(s, s), pads=(p,) * 4, groups=g, has_bias=True)
+    rng = np.random.default_rng(1300 + i)
+    x = rng.integers(-128, 127, size=L.x_shape, endpoint=True).astype(np.int8)
+    x.reshape(-1)[::7] = 0
+    wt = rng.integers(-127, 127, size=L.w_shape, endpoint=True).astype(np.int8)
+    b = rng.integers(-3, 3, size=co, endpoint=True).astype(np.int32)
+    scales = (1e10, 1e10, 1e-10)
+    ref = oracle.qconv2d(x, wt, b, *scales, stride=L.stride, pads=L.pads, groups=g, y_zp=y_zp, relu=relu)
+    got, kname = _qrun(L, x, wt, b, scales, y_zp=y_zp, relu=relu)
+    assert_bitexact(got, ref, f"saturation case {i} ({kname})")
+
+
+BF16_PAD_CASES = [
+    # n, c_in, h, w, c_out, groups: depthwise, grouped 4 and 8 per group, dense 3x3 (implicit GEMM), and a
+    # dense 3x3 whose width the implicit GEMM cannot take (the direct kernel)
+    (1, 8, 8, 16, 8, 8),
+    (1, 16, 8, 16, 16, 4),
+    (1, 16, 8, 16, 16, 2),
+    (1, 16, 8, 16, 32, 1),
+    (1, 16, 7, 13, 32, 1),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BF16_PAD_CASES)))
+def test_bf16_pad_value_enters_as_bf16(i):
+    """Every bf16 kernel reads padded taps as the bf16 value nearest pad_value,
+    the storage type of the input.  With x = 0 and one nonzero weight (3) at
+    the top-left tap of each filter, the top-left output is 3 * pad exactly;
+    pad_value 1.0048828125 is not a bf16 number (bf16 gives 1.0078125), and
+    3 * 1.0078125 = 3.0234375 rounds to the bf16 3.03125 where 3 * 1.0048828125
+    rounds to 3.015625, so the output decides which pad the kernel used."""
+    n, ci, h, w, co, g = BF16_PAD_CASES[i]
+    pv = 1.0048828125
+    L = workloads.Layer("pad", n, ci, h, w, co, (3, 3), pads=(1, 1, 1, 1), groups=g, pad_value=pv)
+    x = np.zeros(L.x_shape, np.float32)
+    wt = np.zeros(L.w_shape, np.float32)
+    wt[:, 0, 0, 0] = 3.0
+    y, kname, _ = gpu_layer(L, x, wt, None, None, dtype="bf16")
+    pv16 = float(bf16_round(np.array([pv], np.float32))[0])
+    assert pv16 == 1.0078125
+    ref = bf16_round(oracle_layer(L, x, wt, None, None, pad_value=pv16).astype(np.float32)).astype(np.float64)
+    assert ref[0, 0, 0, 0] == 3.03125
+    assert_bitexact(y, ref, f"bf16 pad case {i} ({kname})")
 
 
 # ------------------------------------------------------------ errors ----
