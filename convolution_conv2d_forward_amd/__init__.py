@@ -88,6 +88,8 @@ def _load():
     lib.conv2d_desc_bind_weights.restype = i32
     lib.conv2d_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.conv2d_forward.restype = i32
+    lib.conv2d_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.conv2d_forward_noalloc.restype = i32
     lib.fused_pw_dw_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fused_pw_dw_forward.restype = i32
     lib.fused_dw_pw_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -107,7 +109,8 @@ _lib = _load()
 
 # C ABI symbols this binding relies on (the header declares exactly these).
 EXPORTED = ("conv2d_params_init", "conv2d_desc_create", "conv2d_desc_destroy", "conv2d_desc_get_output_shape",
-            "conv2d_desc_kernel_name", "conv2d_desc_bind_weights", "conv2d_forward", "fused_pw_dw_forward",
+            "conv2d_desc_kernel_name", "conv2d_desc_bind_weights", "conv2d_forward", "conv2d_forward_noalloc",
+            "fused_pw_dw_forward",
             "fused_dw_pw_forward", "qconv2d_forward", "qfused_dw_pw_forward", "conv2d_status_string",
             "conv2d_last_error")
 
@@ -269,6 +272,19 @@ def conv2d_forward(desc: Desc, x, w, bias, slope, y, stream=None) -> None:
     et = _ELEM[p.dtype]
     xn, wn, yn = _sizes(desc)
     _check(_lib.conv2d_forward(
+        desc.handle, _ptr(x, "x", et, xn), _ptr(w, "w", et, wn),
+        _ptr(bias, "bias", "float32", p.c_out) if p.has_bias else None,
+        _ptr(slope, "slope", "float32", p.prelu_slope_count) if p.act_type == ACT_PRELU else None,
+        _ptr(y, "y", et, yn), _stream(stream)))
+
+
+def conv2d_forward_noalloc(desc: Desc, x, w, bias, slope, y, stream=None) -> None:
+    """conv2d_forward that allocates no device memory (a fixed per-GPU scratch
+    array holds the bf16 weight re-layout); overlapping calls on one GPU race."""
+    p = desc.params
+    et = _ELEM[p.dtype]
+    xn, wn, yn = _sizes(desc)
+    _check(_lib.conv2d_forward_noalloc(
         desc.handle, _ptr(x, "x", et, xn), _ptr(w, "w", et, wn),
         _ptr(bias, "bias", "float32", p.c_out) if p.has_bias else None,
         _ptr(slope, "slope", "float32", p.prelu_slope_count) if p.act_type == ACT_PRELU else None,

@@ -159,6 +159,38 @@ bool winograd_preferred(const Desc& d) {
     return false;
 }
 
+conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, const float* bias, const float* slope,
+                            void* y, void* stream, bool noalloc);
+
+// Scratch of conv2d_forward_noalloc: the bf16 implicit GEMM's per-call weight
+// re-layout goes here instead of into a buffer the descriptor allocates.  A
+// file-scope device array: every GPU the library runs on holds its own copy,
+// at its own address, until the process ends.  Host code never passes the
+// array's name to a kernel or a copy (on the host it is only a stand-in for
+// the symbol); it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current and kept in g_scratch_ptr.
+constexpr int64_t kScratchBytes = CONV2D_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+conv_status_t scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(CONV_ERR_HIP, "no current HIP device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CONV_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return fail(CONV_ERR_HIP, "address of the scratch array on device %d: %s", dev,
+                                               hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CONV_OK;
+}
+
 // A bf16 implicit-GEMM forward call given OIHW weights: re-lay them into the
 // descriptor's pack buffer, then convolve.  The buffer is allocated by the
 // first such call, on the current device.  Each call waits, on its own
@@ -408,6 +440,20 @@ const char* conv2d_desc_kernel_name(conv2d_desc_t dd) {
 
 conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, const float* bias,
                              const float* slope, void* y, void* stream) {
+    return forward_float(dd, x, w, bias, slope, y, stream, false);
+}
+
+conv_status_t conv2d_forward_noalloc(conv2d_desc_t dd, const void* x, const void* w, const float* bias,
+                                     const float* slope, void* y, void* stream) {
+    return forward_float(dd, x, w, bias, slope, y, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, const float* bias, const float* slope,
+                            void* y, void* stream, bool noalloc) {
     if (check_desc(dd) != CONV_OK) return CONV_ERR_INVALID_ARG;
     Desc& d = *(Desc*)dd;
     if (d.p.dtype == CONV_DTYPE_I8) return fail(CONV_ERR_INVALID_ARG, "int8 descriptor: use qconv2d_forward");
@@ -434,6 +480,18 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     case KC_IGEMM_BF16:
         if (use_bound) {
             e = launch_igemm_bf16(d, a, s, (const char*)d.wbound + d.wbound_pack_off, nullptr);
+        } else if (noalloc) {
+            // The re-layout goes to this GPU's scratch array instead of a
+            // buffer of the descriptor's (nothing allocated, no event).
+            if (d.wpack_bytes > kScratchBytes)
+                return fail(CONV_ERR_UNSUPPORTED,
+                            "the re-laid bf16 weights need %lld bytes, more than the %lld-byte scratch of "
+                            "conv2d_forward_noalloc (bind the weights, or use conv2d_forward)",
+                            (long long)d.wpack_bytes, (long long)kScratchBytes);
+            void* sp = nullptr;
+            const conv_status_t st = scratch_on_current_device(&sp);
+            if (st != CONV_OK) return st;
+            e = launch_igemm_bf16(d, a, s, nullptr, sp);
         } else {
             const conv_status_t st = forward_bf16_repack(d, a, s);
             if (st != CONV_OK) return st;
@@ -450,6 +508,10 @@ conv_status_t conv2d_forward(conv2d_desc_t dd, const void* x, const void* w, con
     }
     return hip_status(e, kernel_name(d));
 }
+
+}  // namespace
+
+extern "C" {
 
 conv_status_t fused_pw_dw_forward(conv2d_desc_t dpw, conv2d_desc_t ddw, const void* x, const void* w_pw,
                                   const float* b_pw, const float* slope_pw, const void* w_dw, const float* b_dw,

@@ -202,6 +202,27 @@ CONV2D_API conv_status_t conv2d_desc_bind_weights(conv2d_desc_t d, const void* w
 CONV2D_API conv_status_t conv2d_forward(conv2d_desc_t d, const void* x, const void* w, const float* bias,
                              const float* slope, void* y, void* stream);
 
+/* Size of the device scratch array that conv2d_forward_noalloc uses on each
+ * GPU (8 MiB). */
+#define CONV2D_NOALLOC_SCRATCH_BYTES (8 << 20)
+
+/* conv2d_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, kernels and results as conv2d_forward, and it
+ * allocates nothing.  The one buffer conv2d_forward may allocate -- the
+ * re-laid weights of a BF16 implicit-GEMM descriptor given OIHW weights --
+ * is replaced by a fixed device array of CONV2D_NOALLOC_SCRATCH_BYTES per
+ * GPU, which the library holds from its first use on that GPU until the
+ * process ends.  A descriptor whose re-laid weights do not fit returns
+ * UNSUPPORTED (bind its weights instead: bound weights need no scratch).
+ * Every such call on one GPU shares that array, and it keeps the last call's
+ * contents (each call refills what it reads): calls that may overlap on one
+ * GPU -- unordered streams, or several host threads -- race and must be
+ * ordered by the caller.  Calls with bound weights (w null) and descriptors of
+ * every other kernel class use no scratch and behave as conv2d_forward. */
+CONV2D_API conv_status_t conv2d_forward_noalloc(conv2d_desc_t d, const void* x, const void* w,
+                                                const float* bias, const float* slope, void* y, void* stream);
+
 /* Fused pointwise 1x1 -> depthwise kxk (the yscv FusedPwDw step).  desc_pw:
  * 1x1, stride 1, pads 0, groups 1; desc_dw: groups == c_in == c_out ==
  * desc_pw.c_out, same n/h/w, same dtype (F32).  The expanded tensor stays in
