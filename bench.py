@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default="all",
                     help="all | dense_block | single_conv | bottleneck | mixed_f32 | mixed_bf16 | int8_chain | "
-                         "winograd | copy")
+                         "int8_bottleneck | winograd | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--reps", type=int, default=20, help="timed launches per layer for per_config")
@@ -378,7 +378,8 @@ def float_layer_fns(L, x, w, b, s, dtype, reps, bound=False):
 
 def per_config(reps, only="all"):
     """Per-configuration table; `only` selects one section (single_conv,
-    bottleneck, mixed_f32, mixed_bf16, int8_chain, winograd) or all of them."""
+    bottleneck, mixed_f32, mixed_bf16, int8_chain, int8_bottleneck, winograd)
+    or all of them."""
     import convolution_conv2d_forward_amd as cc
     import workloads
     torch = torch_mod()
@@ -505,6 +506,46 @@ def per_config(reps, only="all"):
         res["qfused_dw_pw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "i8"), kernel="qfused_dw_pw")
         log("int8", "qfused_dw_pw", res["qfused_dw_pw"])
         out["int8_chain"] = res
+
+    # int8 inverted bottleneck: pw 32->192 and dw 3x3, unfused and fused
+    if want("int8_bottleneck"):
+        res = {}
+        L1 = workloads.Layer("pw", 8, 32, 56, 56, 192, (1, 1), has_bias=True)
+        L2 = workloads.Layer("dw", 8, 192, 56, 56, 192, (3, 3), pads=(1, 1, 1, 1), groups=192, has_bias=True)
+        rng = np.random.default_rng(6)
+        x = rng.integers(-128, 128, size=L1.x_shape).astype(np.int8)
+        w1 = rng.integers(-127, 128, size=L1.w_shape).astype(np.int8)
+        w2 = rng.integers(-127, 128, size=L2.w_shape).astype(np.int8)
+        b1 = rng.integers(-500, 501, size=192).astype(np.int32)
+        b2 = rng.integers(-500, 501, size=192).astype(np.int32)
+        d1 = cc.conv2d_desc_create(params_of(L1, "i8"))
+        d2 = cc.conv2d_desc_create(params_of(L2, "i8"))
+        xq, w1d, w2d, b1d, b2d = t_(x), t_(w1), t_(w2), t_(b1), t_(b2)
+        sc = workloads.INT8_SCALES
+        e_host = rng.integers(-128, 128, size=L2.x_shape).astype(np.int8)
+        eq = t_(e_host)
+        for L, d, xs_, wd, bd in ((L1, d1, xq, w1d, b1d), (L2, d2, eq, w2d, b2d)):
+            def make(d=d, xs_=xs_, wd=wd, bd=bd, L=L):
+                xi = xs_.clone()
+                yi = torch.empty((L.n, L.c_out, L.h, L.w), dtype=torch.int8, device=dev())
+                return lambda: cc.qconv2d_forward(d, xi, 0.02, 0, wd, 0.01, 0, bd, 0.05, 0, yi)
+            fns = _rotating(make, L.n * (L.c_in + L.c_out) * L.h * L.w)
+            t = time_layer(L.name, fns, reps)
+            res[L.name] = dict(roofline_entry(L.flops, layer_bytes(L, 1, extra=4 * L.c_out), t, "i8"),
+                               kernel=cc.conv2d_desc_kernel_name(d))
+
+        def make_f():
+            xi = xq.clone()
+            yi = torch.empty((L2.n, L2.c_out, L2.h, L2.w), dtype=torch.int8, device=dev())
+            return lambda: cc.qfused_pw_dw_forward(d1, d2, xi, w1d, b1d, sc, w2d, b2d, sc, 0, yi)
+
+        fns = _rotating(make_f, L1.n * (L1.c_in + L2.c_out) * L1.h * L1.w)
+        t = time_layer("qfused_pw_dw", fns, reps)
+        fb = (L1.n * L1.c_in * L1.h * L1.w + L1.c_out * L1.c_in + 4 * L1.c_out + L2.c_out * 9 + 4 * L2.c_out
+              + L2.n * L2.c_out * L2.h * L2.w)
+        res["qfused_pw_dw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "i8"), kernel="qfused_pw_dw")
+        log("int8_bottleneck", res)
+        out["int8_bottleneck"] = res
 
     # dense-block layers, Winograd F(2x2,3x3) beside the implicit GEMM
     if want("winograd"):

@@ -11,8 +11,9 @@ built, importing this package raises.
 Names and argument order follow the C ABI:
     conv2d_params_init, conv2d_desc_create, conv2d_desc_destroy,
     conv2d_desc_get_output_shape, conv2d_desc_kernel_name,
-    conv2d_desc_bind_weights, conv2d_forward,
+    conv2d_desc_bind_weights, conv2d_forward, conv2d_forward_noalloc,
     fused_pw_dw_forward, fused_dw_pw_forward, qconv2d_forward, qfused_dw_pw_forward,
+    qfused_pw_dw_forward,
     conv2d_status_string,
     conv2d_last_error
 plus ``make_params`` (keyword construction of a params struct).
@@ -98,6 +99,8 @@ def _load():
     lib.qconv2d_forward.restype = i32
     lib.qfused_dw_pw_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, f32, f32, f32, i8, vp, vp]
     lib.qfused_dw_pw_forward.restype = i32
+    lib.qfused_pw_dw_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, f32, f32, f32, i8, vp, vp]
+    lib.qfused_pw_dw_forward.restype = i32
     lib.conv2d_status_string.argtypes = [i32]
     lib.conv2d_status_string.restype = ctypes.c_char_p
     lib.conv2d_last_error.argtypes = []
@@ -111,7 +114,7 @@ _lib = _load()
 EXPORTED = ("conv2d_params_init", "conv2d_desc_create", "conv2d_desc_destroy", "conv2d_desc_get_output_shape",
             "conv2d_desc_kernel_name", "conv2d_desc_bind_weights", "conv2d_forward", "conv2d_forward_noalloc",
             "fused_pw_dw_forward",
-            "fused_dw_pw_forward", "qconv2d_forward", "qfused_dw_pw_forward", "conv2d_status_string",
+            "fused_dw_pw_forward", "qconv2d_forward", "qfused_dw_pw_forward", "qfused_pw_dw_forward", "conv2d_status_string",
             "conv2d_last_error")
 
 
@@ -349,6 +352,21 @@ def qfused_dw_pw_forward(desc_dw: Desc, desc_pw: Desc, x, w_dw, b_dw, dw_scales,
         _ptr(b_dw, "b_dw", "int32", pd.c_out) if pd.has_bias else None, *(f(v) for v in dw_scales),
         _ptr(w_pw, "w_pw", "int8", wpn), _ptr(b_pw, "b_pw", "int32", pp.c_out) if pp.has_bias else None,
         *(f(v) for v in pw_scales), ctypes.c_int8(int(y_zp)), _ptr(y, "y", "int8", yn), _stream(stream)))
+
+
+def qfused_pw_dw_forward(desc_pw: Desc, desc_dw: Desc, x, w_pw, b_pw, pw_scales, w_dw, b_dw, dw_scales, y_zp, y,
+                         stream=None) -> None:
+    """Fused int8 pointwise -> depthwise: two symmetric QLinearConvs, each with
+    its (x_scale, w_scale, y_scale) triple."""
+    pp, pd = desc_pw.params, desc_dw.params
+    xn, wpn, _ = _sizes(desc_pw)
+    _, wdn, yn = _sizes(desc_dw)
+    f = ctypes.c_float
+    _check(_lib.qfused_pw_dw_forward(
+        desc_pw.handle, desc_dw.handle, _ptr(x, "x", "int8", xn), _ptr(w_pw, "w_pw", "int8", wpn),
+        _ptr(b_pw, "b_pw", "int32", pp.c_out) if pp.has_bias else None, *(f(v) for v in pw_scales),
+        _ptr(w_dw, "w_dw", "int8", wdn), _ptr(b_dw, "b_dw", "int32", pd.c_out) if pd.has_bias else None,
+        *(f(v) for v in dw_scales), ctypes.c_int8(int(y_zp)), _ptr(y, "y", "int8", yn), _stream(stream)))
 
 
 def output_shape(desc: Desc):

@@ -670,6 +670,56 @@ conv_status_t qfused_dw_pw_forward(conv2d_desc_t ddw, conv2d_desc_t dpw, const i
                       "qfused_dw_pw");
 }
 
+conv_status_t qfused_pw_dw_forward(conv2d_desc_t dpw, conv2d_desc_t ddw, const int8_t* x, const int8_t* w_pw,
+                                   const int32_t* b_pw, float pw_x_scale, float pw_w_scale, float pw_y_scale,
+                                   const int8_t* w_dw, const int32_t* b_dw, float dw_x_scale, float dw_w_scale,
+                                   float dw_y_scale, int8_t y_zp, int8_t* y, void* stream) {
+    if (!dpw || !ddw) return fail(CONV_ERR_INVALID_ARG, "null descriptor");
+    const Desc& pw = *(const Desc*)dpw;
+    const Desc& dw = *(const Desc*)ddw;
+    const conv2d_params_t& P = pw.p;
+    const conv2d_params_t& D = dw.p;
+    if (P.dtype != CONV_DTYPE_I8 || D.dtype != CONV_DTYPE_I8)
+        return fail(CONV_ERR_INVALID_ARG, "qfused_pw_dw_forward needs two I8 descriptors");
+    if (P.k_h != 1 || P.k_w != 1 || P.stride_h != 1 || P.stride_w != 1 || P.groups != 1 || P.pad_top ||
+        P.pad_left || P.pad_bottom || P.pad_right)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "first descriptor must be a 1x1, stride 1, unpadded, ungrouped conv");
+    if (!(D.groups == D.c_in && D.groups == D.c_out))
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "second descriptor must be depthwise (groups == c_in == c_out)");
+    if (D.c_in != P.c_out || D.n != P.n || D.h != P.h || D.w != P.w)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "pw output [%d,%d,%d,%d] does not match dw input [%d,%d,%d,%d]",
+                    P.n, P.c_out, P.h, P.w, D.n, D.c_in, D.h, D.w);
+    if (pw.out_total != P.c_out || P.out_channel_offset != 0 || D.in_channel_offset != 0 || dw.in_total != D.c_in)
+        return fail(CONV_ERR_INCOMPATIBLE_SHAPES, "the expanded tensor has no buffer: pw output and dw input must be "
+                                                  "plain (no channel offsets)");
+    if (D.k_h > 5 || D.k_w > 5) return fail(CONV_ERR_UNSUPPORTED, "fused int8 pw->dw supports windows up to 5x5");
+    if (!plan_qfused_pw_dw(pw, dw)) return fail(CONV_ERR_UNSUPPORTED, "image rows too wide for the fused tile");
+    float comp_pw = 0.0f, comp_dw = 0.0f;
+    if (!composite_scale(pw_x_scale, pw_w_scale, pw_y_scale, &comp_pw) ||
+        !composite_scale(dw_x_scale, dw_w_scale, dw_y_scale, &comp_dw))
+        return fail(CONV_ERR_INVALID_ARG, "scales (and their composites) must be finite and positive");
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "null x or y");
+    const void* wpv = w_pw;
+    const void* wdv = w_dw;
+    if (resolve_weights(pw, wpv, "pointwise weights") != CONV_OK || resolve_weights(dw, wdv, "depthwise weights") != CONV_OK)
+        return CONV_ERR_INVALID_ARG;
+    if (P.has_bias && !b_pw) return fail(CONV_ERR_INVALID_ARG, "pw has_bias set but bias is null");
+    if (D.has_bias && !b_dw) return fail(CONV_ERR_INVALID_ARG, "dw has_bias set but bias is null");
+    const View yv = y_view(dw, y);
+    if (views_overlap(yv, x_view(pw, x))) return fail(CONV_ERR_ALIAS, "y overlaps x");
+    if (views_overlap(yv, flat(wpv, w_bytes(pw))) || views_overlap(yv, flat(wdv, w_bytes(dw))))
+        return fail(CONV_ERR_ALIAS, "y overlaps the weights");
+    if ((P.has_bias && views_overlap(yv, flat(b_pw, 4 * (int64_t)P.c_out))) ||
+        (D.has_bias && views_overlap(yv, flat(b_dw, 4 * (int64_t)D.c_out))))
+        return fail(CONV_ERR_ALIAS, "y overlaps a bias");
+    ConvArgs apw = make_args(pw, x, wpv, nullptr, nullptr, nullptr);
+    apw.qbias = P.has_bias ? b_pw : nullptr;
+    ConvArgs adw = make_args(dw, nullptr, wdv, nullptr, nullptr, y);
+    adw.qbias = D.has_bias ? b_dw : nullptr;
+    return hip_status(launch_qfused_pw_dw(pw, dw, apw, adw, comp_pw, comp_dw, y_zp, (hipStream_t)stream),
+                      "qfused_pw_dw");
+}
+
 conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, int8_t x_zp, const int8_t* w,
                               float w_scale, int8_t w_zp, const int32_t* bias, float y_scale, int8_t y_zp,
                               int8_t* y, void* stream) {

@@ -181,6 +181,8 @@ hipError_t launch_fused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, Conv
                               hipStream_t s);
 hipError_t launch_qfused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, ConvArgs apw, float comp_dw,
                                float comp_pw, int y_zp, hipStream_t s);
+hipError_t launch_qfused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, ConvArgs adw, float comp_pw,
+                               float comp_dw, int y_zp, hipStream_t s);
 
 // Tile planners (host): fill the tiling fields of d; return false if the
 // shape cannot use the class (the caller then falls back to KC_DIRECT).
@@ -197,6 +199,7 @@ bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* 
 // x: the input pointer (its alignment decides between vector and scalar row loads).
 bool plan_fused_dw_pw(const Desc& dw, const Desc& pw, const void* x);
 bool plan_qfused_dw_pw(const Desc& dw, const Desc& pw);
+bool plan_qfused_pw_dw(const Desc& pw, const Desc& dw);
 
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.
 

@@ -299,6 +299,33 @@ CONV2D_API conv_status_t qfused_dw_pw_forward(conv2d_desc_t desc_dw, conv2d_desc
                                    const int32_t* b_pw, float pw_x_scale, float pw_w_scale,
                                    float pw_y_scale, int8_t y_zp, int8_t* y, void* stream);
 
+/* Fused int8 pointwise 1x1 -> depthwise kxk (the yscv QuantizedPwDw step):
+ * two symmetric QLinearConvs as in qconv2d_forward, each with its own scale
+ * triple, the int8 expansion kept in on-chip memory.  desc_pw: I8, 1x1,
+ * stride 1, pads 0, groups 1; desc_dw: I8, groups == c_in == c_out ==
+ * desc_pw.c_out, same n/h/w, window up to 5x5, any stride, dilation and
+ * pads.  The pointwise input may be a channel slice (in_channel_offset /
+ * in_total_channels) and the depthwise output may be one (ConcatFusedTail);
+ * the expansion has no buffer, so the pointwise output and depthwise input
+ * carry no channel offsets.  The pointwise stage requantises with the
+ * composite of (pw_x_scale, pw_w_scale, pw_y_scale), zero point 0 and its
+ * descriptor's rounding and ReLU; the depthwise stage reads that int8 tensor,
+ * its taps outside the image reading the intermediate's zero point (0: the
+ * depthwise padding applies to the pointwise output), and requantises with
+ * the composite of (dw_x_scale, dw_w_scale, dw_y_scale), y_zp and its
+ * descriptor's rounding and ReLU.  The output is bitwise that of
+ * qconv2d_forward(desc_pw, x, pw_x_scale, 0, w_pw, pw_w_scale, 0, b_pw,
+ * pw_y_scale, 0, tmp) followed by qconv2d_forward(desc_dw, tmp, dw_x_scale,
+ * 0, w_dw, dw_w_scale, 0, b_dw, dw_y_scale, y_zp, y).  Null w_pw / w_dw
+ * select bound weights; biases are device int32 or null.  Errors as for
+ * qfused_dw_pw_forward (UNSUPPORTED also for image rows too wide for the
+ * on-chip tile). */
+CONV2D_API conv_status_t qfused_pw_dw_forward(conv2d_desc_t desc_pw, conv2d_desc_t desc_dw, const int8_t* x,
+                                   const int8_t* w_pw, const int32_t* b_pw, float pw_x_scale,
+                                   float pw_w_scale, float pw_y_scale, const int8_t* w_dw,
+                                   const int32_t* b_dw, float dw_x_scale, float dw_w_scale,
+                                   float dw_y_scale, int8_t y_zp, int8_t* y, void* stream);
+
 /* Human-readable name of a status code (static string). */
 CONV2D_API const char* conv2d_status_string(conv_status_t s);
 

@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_header_symbols_exported():
     syms = declared_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 15, syms
     lib = ctypes.CDLL(cc().LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), f"{s} declared in conv2d.h but not exported"

@@ -108,3 +108,39 @@ def test_qfused_ties(i):
         t.cuda.synchronize()
         y.check_guards()
         assert_bitexact(y.host().numpy().reshape(ref.shape), ref, f"fused case {i} rounding {r}")
+
+
+FUSED_PW_DW = [
+    # n, c_in, h, w, c_exp, k, stride, pads  (the first two take the 4-byte row path)
+    (2, 32, 12, 16, 48, 3, 1, (1, 1, 1, 1)),
+    (1, 64, 10, 32, 40, 3, 2, (0, 0, 1, 1)),
+    (1, 20, 9, 13, 24, 5, 1, (2, 2, 2, 2)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(FUSED_PW_DW)))
+def test_qfused_pw_dw_ties(i):
+    t = torch()
+    n, c, h, w, ce, k, s, pads = FUSED_PW_DW[i]
+    L1 = workloads.Layer("pw", n, c, h, w, ce, (1, 1), has_bias=True)
+    L2 = workloads.Layer("dw", n, ce, h, w, ce, (k, k), stride=(s, s), pads=pads, groups=ce, has_bias=True)
+    rng = np.random.default_rng(970 + i)
+    x, w1, b1 = _inputs(rng, L1)
+    _, w2, b2 = _inputs(rng, L2)
+    sd = (SC[2], SC[1], SC[2])
+    mids, refs = {}, {}
+    for r in (HALF_EVEN, HALF_AWAY):
+        mids[r] = oracle.qconv2d(x, w1, b1, *SC, rounding=r)
+        refs[r] = oracle.qconv2d(mids[r], w2, b2, *sd, stride=L2.stride, pads=L2.pads, groups=L2.groups,
+                                 rounding=r)
+    assert _ties(mids[HALF_EVEN], mids[HALF_AWAY]) > 0, "no pointwise ties in this case"
+    for r, ref in refs.items():
+        d1 = cc().conv2d_desc_create(layer_params(L1, "i8", int8_rounding=r))
+        d2 = cc().conv2d_desc_create(layer_params(L2, "i8", int8_rounding=r))
+        nn, ot, h2, w2o = cc().conv2d_desc_get_output_shape(d2)
+        y = Guarded(nn * ot * h2 * w2o, t.int8, 0x5A)
+        cc().qfused_pw_dw_forward(d1, d2, to_dev(x), to_dev(w1), to_dev(b1), SC, to_dev(w2), to_dev(b2), sd, 0,
+                                  y.view)
+        t.cuda.synchronize()
+        y.check_guards()
+        assert_bitexact(y.host().numpy().reshape(ref.shape), ref, f"fused pw->dw case {i} rounding {r}")
