@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default="all",
                     help="all | dense_block | single_conv | bottleneck | mixed_f32 | mixed_bf16 | int8_chain | "
-                         "int8_bottleneck | winograd | copy")
+                         "int8_bottleneck | int8_dense | winograd | copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--reps", type=int, default=20, help="timed launches per layer for per_config")
@@ -378,7 +378,8 @@ def float_layer_fns(L, x, w, b, s, dtype, reps, bound=False):
 
 def per_config(reps, only="all"):
     """Per-configuration table; `only` selects one section (single_conv,
-    bottleneck, mixed_f32, mixed_bf16, int8_chain, int8_bottleneck, winograd)
+    bottleneck, mixed_f32, mixed_bf16, int8_chain, int8_bottleneck, int8_dense,
+    winograd)
     or all of them."""
     import convolution_conv2d_forward_amd as cc
     import workloads
@@ -546,6 +547,34 @@ def per_config(reps, only="all"):
         res["qfused_pw_dw"] = dict(roofline_entry(L1.flops + L2.flops, fb, t, "i8"), kernel="qfused_pw_dw")
         log("int8_bottleneck", res)
         out["int8_bottleneck"] = res
+
+    # int8 dense / strided / dilated / grouped convolutions on the i8 matrix cores (the mixed sweep's shapes)
+    if want("int8_dense"):
+        res = {}
+        for L in workloads.mixed_sweep_layers():
+            if L.name == "pw":
+                continue
+            Lq = workloads.Layer(L.name, L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride, pads=L.pads,
+                                 dilation=L.dilation, groups=L.groups, has_bias=True)
+            rng = np.random.default_rng(7)
+            x = rng.integers(-128, 128, size=Lq.x_shape).astype(np.int8)
+            w = rng.integers(-127, 128, size=Lq.w_shape).astype(np.int8)
+            b = rng.integers(-500, 501, size=Lq.c_out).astype(np.int32)
+            d = cc.conv2d_desc_create(params_of(Lq, "i8"))
+            xs_, wd, bd = t_(x), t_(w), t_(b)
+            ho, wo = Lq.out_hw
+
+            def make(d=d, xs_=xs_, wd=wd, bd=bd, Lq=Lq, ho=ho, wo=wo):
+                xi = xs_.clone()
+                yi = torch.empty((Lq.n, Lq.c_out, ho, wo), dtype=torch.int8, device=dev())
+                return lambda: cc.qconv2d_forward(d, xi, 0.02, 0, wd, 0.01, 0, bd, 0.05, 0, yi)
+
+            fns = _rotating(make, x.size + Lq.n * Lq.c_out * ho * wo)
+            t = time_layer(Lq.name, fns, reps)
+            res[Lq.name] = dict(roofline_entry(Lq.flops, layer_bytes(Lq, 1, extra=4 * Lq.c_out), t, "i8"),
+                                kernel=cc.conv2d_desc_kernel_name(d))
+            log("int8_dense", Lq.name, res[Lq.name])
+        out["int8_dense"] = res
 
     # dense-block layers, Winograd F(2x2,3x3) beside the implicit GEMM
     if want("winograd"):

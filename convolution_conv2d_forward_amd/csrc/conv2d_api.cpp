@@ -49,6 +49,7 @@ const char* kernel_name(const Desc& d) {
     case KC_GROUPED: return d.p.dtype == CONV_DTYPE_BF16 ? "grouped_bf16" : "grouped_f32";
     case KC_WINOGRAD_F32: return "winograd_f32";
     case KC_PW_F32: return "pointwise_f32";
+    case KC_IGEMM_I8: return "igemm_i8";
     }
     return "?";
 }
@@ -342,8 +343,16 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
         d->kclass = KC_WINOGRAD_F32;
         planned = true;
     } else if (p.dtype == CONV_DTYPE_I8) {
-        if (depthwise) { d->kclass = KC_QDW; planned = plan_qdw(*d); }
-        else { d->kclass = KC_QPW; planned = plan_qpw(*d); }
+        if (depthwise) {
+            d->kclass = KC_QDW;
+            planned = plan_qdw(*d);
+        } else if (plan_qpw(*d)) {
+            d->kclass = KC_QPW;
+            planned = true;
+        } else {
+            d->kclass = KC_IGEMM_I8;
+            planned = plan_igemm_i8(*d);
+        }
     } else if (depthwise) {
         d->kclass = KC_DW;
         planned = plan_dw(*d);
@@ -756,6 +765,7 @@ conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, 
     switch (d.kclass) {
     case KC_QDW: e = launch_qdw(d, a, s); break;
     case KC_QPW: e = launch_qpw(d, a, s); break;
+    case KC_IGEMM_I8: e = launch_igemm_i8(d, a, s); break;
     default: e = launch_direct(d, a, s); break;
     }
     return hip_status(e, kernel_name(d));

@@ -22,6 +22,7 @@ enum KernelClass : int32_t {
     KC_GROUPED = 6,      // grouped 3x3 with 4 or 8 channels per group, VALU
     KC_WINOGRAD_F32 = 7, // Winograd F(2x2, 3x3), fp32 MFMA (3x3, stride 1, dilation 1, one group)
     KC_PW_F32 = 8,       // pointwise 1x1 with K <= 256, fp32 MFMA, every output channel per workgroup
+    KC_IGEMM_I8 = 9,     // int8 dense / grouped implicit GEMM, i8 MFMA
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -166,6 +167,7 @@ hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const voi
 hipError_t pack_igemm_bf16_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
+hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
@@ -191,6 +193,7 @@ bool plan_igemm_bf16(Desc& d);
 bool plan_dw(Desc& d);
 bool plan_qdw(Desc& d);
 bool plan_qpw(Desc& d);
+bool plan_igemm_i8(const Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_winograd_f32(const Desc& d);
 bool plan_pointwise_f32(const Desc& d);

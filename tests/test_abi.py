@@ -135,6 +135,13 @@ def test_kernel_choice_for_the_workloads():
                                                      pads=L.pads, groups=L.groups, dtype="i8"))
         names[L.name] = cc().conv2d_desc_kernel_name(d)
     assert names["dw_s1"] == names["dw_s2"] == "depthwise_i8_dot4" and names["pw"] == "pointwise_i8_mfma"
+    # int8 dense, strided and grouped convolutions: the i8 implicit GEMM
+    for L in workloads.mixed_sweep_layers():
+        if L.name == "pw":
+            continue
+        d = cc().conv2d_desc_create(cc().make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride,
+                                                     pads=L.pads, dilation=L.dilation, groups=L.groups, dtype="i8"))
+        assert cc().conv2d_desc_kernel_name(d) == "igemm_i8", L.name
 
 
 def _raw(fn, *args):
