@@ -48,7 +48,7 @@ struct I8Args {
     uint32_t num_blocks;
     DivU32 dv_co_tiles, dv_groups, dv_tiles_w, dv_tiles_h;
     DivU32 dv_pw4;          // staging unit -> (quad, patch row)
-    DivU32 dv_ppix;         // staging unit -> channel quad (patch words per quad)
+    DivU32 dv_ppix;         // staging unit / 4 -> channel quad group (patch words per quad)
     DivU32 dv_kw;           // tap -> (r, s)
 };
 
@@ -108,6 +108,9 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
     const int8_t* __restrict__ xg = (const int8_t*)a.xptr + ((int64_t)n * a.in_total + a.in_off + (int64_t)g * cin_g) * HW;
     const int8_t* __restrict__ wg = (const int8_t*)a.wptr + (int64_t)(g * a.cout_g + co0) * cin_g * khw;
 
+    // Patch pixel p (row-major, PW a multiple of 4) lives at slot
+    // (p % 4) * (PH * PW / 4) + p / 4: a thread's four pixels land in four
+    // quarters, and the words of consecutive threads 80 bytes apart.
     uint8_t* xs = lds;                    // [PH * PW][XR]
     uint8_t* ws = lds + f.xs_bytes;       // [khw][BM][XR]
 
@@ -131,14 +134,20 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
         const int kq_n = min(CK, cin_g - c0 + 3) >> 2;   // channel quads holding data
         // ---- patch -> LDS (pixel-major); quads past cin_g are left as they
         // are: their weights are staged as zero ----
-        const int units = kq_n * pq_n;
+        // Unit u: channel quad 4 * (u / (4 * pq_n)) + u % 4 and word rem =
+        // (u / 4) % pq_n of the patch (patch row pr, columns 4 * (rem % pw4)
+        // ..+3).  Four consecutive lanes take four channel quads of one word,
+        // so a wave's LDS stores cover every bank (see slot below).
+        const int kq4 = (kq_n + 3) & ~3;
+        const int units = kq4 * pq_n;
         for (int u0 = 0; u0 < units; u0 += QV * kT) {
             uint32_t in[QV][4];
 #pragma unroll
             for (int i = 0; i < QV; ++i) {
                 const int u = u0 + tid + i * kT;
-                const int cq = (int)divu((uint32_t)u, f.dv_ppix);
-                const int rem = u - cq * pq_n;
+                const int hi = (int)divu((uint32_t)(u >> 2), f.dv_ppix);
+                const int cq = 4 * hi + (u & 3);
+                const int rem = (u >> 2) - hi * pq_n;
                 const int pr = (int)divu((uint32_t)rem, f.dv_pw4);
                 const int pc = 4 * (rem - pr * f.pw4);
                 const int ih = ih0 + pr, iw = iw_a + pc;
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
                 for (int cc = 0; cc < 4; ++cc) {
                     const int ch = c0 + 4 * cq + cc;
                     uint32_t v = 0;
-                    if (u < units && ch < cin_g && (unsigned)ih < (unsigned)H) {
+                    if (u < units && cq < kq_n && ch < cin_g && (unsigned)ih < (unsigned)H) {
                         const int8_t* src = xg + (int64_t)ch * HW + (int64_t)ih * W;
                         if (f.vec_x) {
                             // W % 4 == 0 and iw % 4 == 0: the word is inside the row or outside it.
@@ -163,14 +172,16 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
 #pragma unroll
             for (int i = 0; i < QV; ++i) {
                 const int u = u0 + tid + i * kT;
-                if (u >= units) continue;
-                const int cq = (int)divu((uint32_t)u, f.dv_ppix);
-                const int rem = u - cq * pq_n;
+                const int hi = (int)divu((uint32_t)(u >> 2), f.dv_ppix);
+                const int cq = 4 * hi + (u & 3);
+                if (u >= units || cq >= kq_n) continue;
+                const int rem = (u >> 2) - hi * pq_n;
                 uint32_t outw[4];
                 tr4x4(in[i], outw);
-                // rem = pr * pw4 + pc / 4, so the patch pixel of byte b is 4 * rem + b.
+                // rem = pr * pw4 + pc / 4, so byte b is patch pixel 4 * rem + b,
+                // kept at slot b * pq_n + rem.
 #pragma unroll
-                for (int b = 0; b < 4; ++b) *(uint32_t*)&xs[(4 * rem + b) * XR + 4 * cq] = outw[b];
+                for (int b = 0; b < 4; ++b) *(uint32_t*)&xs[(b * pq_n + rem) * XR + 4 * cq] = outw[b];
             }
         }
         // ---- weights -> LDS [tap][co][64 channels]; zero past the filter ----
@@ -226,7 +237,8 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
                 bw[m] = *(const i32x4*)&ws[((t * BM) + 16 * m + (lane & 15)) * XR + 16 * (lane >> 4)];
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
-                const i32x4 av = *(const i32x4*)&xs[(pbase[j] + toff) * XR + 16 * (lane >> 4)];
+                const int pp = pbase[j] + toff;
+                const i32x4 av = *(const i32x4*)&xs[((pp & 3) * pq_n + (pp >> 2)) * XR + 16 * (lane >> 4)];
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
                     acc[j][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bw[m], acc[j][m], 0, 0, 0);

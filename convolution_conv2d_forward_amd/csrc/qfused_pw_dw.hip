@@ -56,7 +56,7 @@ struct QPDArgs {
     FastDiv div_w;       // pixel -> row
     DivU32 dv_uw;        // depthwise unit -> (channel, row) index: by the VO-column groups per row
     DivU32 dv_th, dv_th_last;   // (channel, row) index -> channel: by tile_h, by the last tile's rows
-    DivU32 dv_pq;        // unit -> channel quad (units reach 16 * npix / 4)
+    DivU32 dv_pq;        // unit / 4 -> channel quad group (by the 4-pixel groups of the tile)
 };
 
 // Transpose a 4x4 byte block: in[c] holds pixels 0..3 of channel c; out[p]
@@ -127,7 +127,10 @@ __global__ __launch_bounds__(kT) void qfused_pw_dw_kernel(QPDArgs f) {
     const int8_t* __restrict__ xg = (const int8_t*)P.xptr + ((int64_t)n * P.in_total + P.in_off) * HW;
     const int8_t* __restrict__ wpw = (const int8_t*)P.wptr;
 
-    uint8_t* xs = lds;   // [npix][XROW]
+    // Pixel p of the staged rows lives at slot (p % 4) * ceil(npix / 4) + p / 4:
+    // a thread's four pixels land in four quarters, and the words of
+    // consecutive threads 80 bytes apart.
+    uint8_t* xs = lds;   // [4 * ceil(npix / 4)][XROW]
 
     i32x4 acc[NF][2];
 #pragma unroll
@@ -142,7 +145,10 @@ __global__ __launch_bounds__(kT) void qfused_pw_dw_kernel(QPDArgs f) {
     const int pq_n = (npix + 3) >> 2;            // 4-pixel groups of the tile
     for (int c0 = 0; c0 < K; c0 += KC) {
         const int kq_n = min(KC, K - c0 + 3) >> 2;
-        const int units = kq_n * pq_n;
+        // Unit u: channel quad 4 * (u / (4 * pq_n)) + u % 4 of the 4-pixel
+        // group (u / 4) % pq_n; four consecutive lanes take four channel
+        // quads of one group, so a wave's LDS stores cover every bank.
+        const int units = ((kq_n + 3) & ~3) * pq_n;
         // B fragments: channel ce0 + 16*cb + lane%16, k = c0 + 16*(lane/16) .. +15.
         i32x4 bw[2];
 #pragma unroll
@@ -167,13 +173,14 @@ __global__ __launch_bounds__(kT) void qfused_pw_dw_kernel(QPDArgs f) {
 #pragma unroll
             for (int i = 0; i < UMAX; ++i) {
                 const int u = u0 + tid + i * kT;
-                const int cq = (int)divu((uint32_t)u, f.dv_pq);
-                const int p = 4 * (u - cq * pq_n);
+                const int hi = (int)divu((uint32_t)(u >> 2), f.dv_pq);
+                const int cq = 4 * hi + (u & 3);
+                const int p = 4 * ((u >> 2) - hi * pq_n);
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
                     const int ch = c0 + 4 * cq + cc;
                     uint32_t v = 0;
-                    if (u < units && ch < K) {
+                    if (u < units && cq < kq_n && ch < K) {
                         const int8_t* src = xg + (int64_t)ch * HW;
                         if (f.vec) {
                             // W % 4 == 0: the 4 pixels share a row.
@@ -197,14 +204,15 @@ __global__ __launch_bounds__(kT) void qfused_pw_dw_kernel(QPDArgs f) {
 #pragma unroll
             for (int i = 0; i < UMAX; ++i) {
                 const int u = u0 + tid + i * kT;
-                if (u >= units) continue;
-                const int cq = (int)divu((uint32_t)u, f.dv_pq);
-                const int p = 4 * (u - cq * pq_n);
+                const int hi = (int)divu((uint32_t)(u >> 2), f.dv_pq);
+                const int cq = 4 * hi + (u & 3);
+                if (u >= units || cq >= kq_n) continue;
+                const int g4 = (u >> 2) - hi * pq_n;
                 uint32_t outw[4];
                 tr4x4(in[i], outw);
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    if (p + b < npix) *(uint32_t*)&xs[(p + b) * XROW + 4 * cq] = outw[b];
+                    if (4 * g4 + b < npix) *(uint32_t*)&xs[(b * pq_n + g4) * XROW + 4 * cq] = outw[b];
             }
         }
         __syncthreads();
@@ -212,9 +220,9 @@ __global__ __launch_bounds__(kT) void qfused_pw_dw_kernel(QPDArgs f) {
         for (int j = 0; j < NF; ++j) {
             const int fj = wave + 4 * j;
             if (fj < nfrag) {
-                const int p = 16 * fj + (lane & 15);
-                // Pixels past the tile read row 0 (their results are never stored).
-                const i32x4 a = *(const i32x4*)&xs[(p < npix ? p : 0) * XROW + 16 * (lane >> 4)];
+                int p = 16 * fj + (lane & 15);
+                p = p < npix ? p : 0;   // pixels past the tile read pixel 0 (their results are never stored)
+                const i32x4 a = *(const i32x4*)&xs[((p & 3) * pq_n + (p >> 2)) * XROW + 16 * (lane >> 4)];
                 acc[j][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw[0], acc[j][0], 0, 0, 0);
                 acc[j][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw[1], acc[j][1], 0, 0, 0);
             }
@@ -462,7 +470,7 @@ bool qpd_plan(const Desc& pw, const Desc& dw, QPDPlan* out) {
         // past the last row (those bytes meet zero weights or feed outputs
         // that are not stored).
         const int etile = (CE * rows * ew + 16 + 15) / 16 * 16;
-        const int dwf_off = max(npix * XROW, etile);
+        const int dwf_off = max((npix + 3) / 4 * 4 * XROW, etile);
         const int lds = dwf_off + CE * 16;            // 3 filter words and a bias per channel
         if (lds > 64 * 1024) break;
         // The kernel is bound by VALU issue: its time follows the expanded
