@@ -53,6 +53,8 @@ struct FusedArgs {
     FastDiv div_w;         // division by the image width (pixel -> row)
     FastDiv div_w4;        // division by w/4 (load unit -> row)
     FastDiv div_rw4;       // division by rows*w/4 (load unit -> channel)
+    DivU32 dv_rows;        // expanded row index -> channel
+    DivU32 dv_uw;          // depthwise thread -> channel (by the VO-column groups per row)
 };
 
 // NJ: 16-pixel pointwise fragments per wave (register budget: 4 keeps two
@@ -202,69 +204,104 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
                         ech[eoff[j]] = (ein[j] && cv) ? act_apply(acc[m][j][v] + bb, sl, pa.lo, pa.hi) : dpad;
             }
     }
-    // pad columns of every row
-    const int padc = f.ew - W;
-    for (int e = tid; e < CE * f.rows * padc; e += kThreads) {
-        const int ce = e / (f.rows * padc);
-        const int rem = e - ce * f.rows * padc;
-        const int r = rem / padc;
-        const int jj = rem - r * padc;
-        const int col = jj < D.pad_left ? jj : W + jj;
-        es[ce * f.es_stride + r * f.ew + col] = dpad;
+    // pad columns of every row (one row per thread)
+    for (int rr = tid; rr < CE * f.rows; rr += kThreads) {
+        const int ce = (int)divu((uint32_t)rr, f.dv_rows);
+        float* row = es + ce * f.es_stride + (rr - ce * f.rows) * f.ew;
+        for (int c = 0; c < D.pad_left; ++c) row[c] = dpad;
+        for (int c = D.pad_left + W; c < f.ew; ++c) row[c] = dpad;
     }
     __syncthreads();
 
-    // ---- 3. depthwise from LDS, R x VO outputs per thread ----
+    // ---- 3. depthwise from LDS ----
     const int th_n = min(f.tile_h, D.ho - ho0);
     const int uw = (D.wo + VO - 1) / VO;
-    const int uh = (th_n + RR - 1) / RR;
-    const int units = ce_valid * uh * uw;
     const int64_t oplane = (int64_t)D.ho * D.wo;
     float* __restrict__ yg = (float*)D.yptr;
     const float* __restrict__ wdw = (const float*)D.wptr;
     const bool vec_ok = (D.wo % VO) == 0 && (((uintptr_t)D.yptr) % 16) == 0;
     const ActP da = act_params(D);
-    for (int u = tid; u < units; u += kThreads) {
-        const int ce = u / (uh * uw);
-        const int rem = u - ce * uh * uw;
-        const int rr = rem / uw;
-        const int q0 = (rem - rr * uw) * VO;
-        const int r0 = rr * RR;
-        const int cg = ce0 + ce;
-        float accd[RR][VO];
+    auto store_row = [&](float* dst, const float (&accd)[VO], float dbb, float dsl, int q0)
+        __attribute__((always_inline)) {
+        float outv[VO];
 #pragma unroll
-        for (int i = 0; i < RR; ++i)
-#pragma unroll
-            for (int q = 0; q < VO; ++q) accd[i][q] = 0.0f;
-        const float* ech = es + ce * f.es_stride;
-        const float* wch = wdw + (int64_t)cg * kh * kw;
-        const float dbb = D.bias ? D.bias[cg] : 0.0f;
-        const float dsl = act_slope(D, da, cg);
-        if constexpr (FIXED) {
-            float wt[KH * KW];
-#pragma unroll
-            for (int i = 0; i < KH * KW; ++i) wt[i] = wch[i];
-            constexpr int RIN = RR + KH - 1, CIN = VO + KW - 1;
-            const int cmax = f.ew - 1;
-#pragma unroll
-            for (int i = 0; i < RIN; ++i) {
-                const int row = r0 + i;
-                if (row >= f.rows) break;
-                const float* src = ech + row * f.ew;
-                float win[CIN];
-#pragma unroll
-                for (int jj = 0; jj < CIN; ++jj) win[jj] = src[q0 + jj <= cmax ? q0 + jj : cmax];
-#pragma unroll
-                for (int orow = 0; orow < RR; ++orow) {
-                    const int r = i - orow;
-                    if (r < 0 || r >= KH) continue;
-#pragma unroll
-                    for (int s2 = 0; s2 < KW; ++s2)
-#pragma unroll
-                        for (int q = 0; q < VO; ++q) accd[orow][q] = fmaf(win[q + s2], wt[r * KW + s2], accd[orow][q]);
-                }
-            }
+        for (int q = 0; q < VO; ++q) outv[q] = act_apply(accd[q] + dbb, dsl, da.lo, da.hi);
+        if (vec_ok && q0 + VO <= D.wo) {
+            *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
         } else {
+#pragma unroll
+            for (int q = 0; q < VO; ++q)
+                if (q0 + q < D.wo) dst[q] = outv[q];
+        }
+    };
+    if constexpr (FIXED) {
+        // 3x3, stride 1: a thread owns one channel and VO output columns and
+        // walks down the tile's output rows with a window of three expanded
+        // rows in registers (each row's VO + 2 floats read once, as a float4
+        // and a float2: rows are 16-byte aligned), so an output costs its 9
+        // FMAs and little else.  Output column q0 + q, tap s reads LDS column
+        // q0 + q + s (LDS column = image column + pad_left).
+        const int pairs = ce_valid * uw;
+        for (int pr = tid; pr < pairs; pr += kThreads) {
+            const int ce = (int)divu((uint32_t)pr, f.dv_uw);
+            const int q0 = (pr - ce * uw) * VO;
+            const int cg = ce0 + ce;
+            const float* wch = wdw + (int64_t)cg * 9;
+            float wt[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) wt[i] = wch[i];
+            const float dbb = D.bias ? D.bias[cg] : 0.0f;
+            const float dsl = act_slope(D, da, cg);
+            const float* ech = es + ce * f.es_stride + q0;
+            auto load = [&](float (&v)[VO + 2], int row) __attribute__((always_inline)) {
+                const float4 a4 = *(const float4*)(ech + row * f.ew);
+                const float2 b2 = *(const float2*)(ech + row * f.ew + 4);
+                v[0] = a4.x; v[1] = a4.y; v[2] = a4.z; v[3] = a4.w; v[4] = b2.x; v[5] = b2.y;
+            };
+            float ra[VO + 2], rb[VO + 2];
+            load(ra, 0);
+            load(rb, 1);
+            float* dst = yg + ((int64_t)n * D.out_total + D.out_off + cg) * oplane + (int64_t)ho0 * D.wo + q0;
+            for (int o = 0; o < th_n; ++o) {
+                float rc[VO + 2];
+                load(rc, o + 2);
+                float accd[VO];
+#pragma unroll
+                for (int q = 0; q < VO; ++q) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int s2 = 0; s2 < 3; ++s2) v = fmaf(ra[q + s2], wt[s2], v);
+#pragma unroll
+                    for (int s2 = 0; s2 < 3; ++s2) v = fmaf(rb[q + s2], wt[3 + s2], v);
+#pragma unroll
+                    for (int s2 = 0; s2 < 3; ++s2) v = fmaf(rc[q + s2], wt[6 + s2], v);
+                    accd[q] = v;
+                }
+                store_row(dst + (int64_t)o * D.wo, accd, dbb, dsl, q0);
+#pragma unroll
+                for (int t = 0; t < VO + 2; ++t) { ra[t] = rb[t]; rb[t] = rc[t]; }
+            }
+        }
+    } else {
+        // Any window, stride and dilation: RR x VO outputs per unit.
+        const int uh = (th_n + RR - 1) / RR;
+        const int units = ce_valid * uh * uw;
+        for (int u = tid; u < units; u += kThreads) {
+            const int ce = u / (uh * uw);
+            const int rem = u - ce * uh * uw;
+            const int rr = rem / uw;
+            const int q0 = (rem - rr * uw) * VO;
+            const int r0 = rr * RR;
+            const int cg = ce0 + ce;
+            float accd[RR][VO];
+#pragma unroll
+            for (int i = 0; i < RR; ++i)
+#pragma unroll
+                for (int q = 0; q < VO; ++q) accd[i][q] = 0.0f;
+            const float* ech = es + ce * f.es_stride;
+            const float* wch = wdw + (int64_t)cg * kh * kw;
+            const float dbb = D.bias ? D.bias[cg] : 0.0f;
+            const float dsl = act_slope(D, da, cg);
 #pragma unroll
             for (int orow = 0; orow < RR; ++orow) {
                 if (r0 + orow >= th_n) break;
@@ -281,21 +318,12 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int orow = 0; orow < RR; ++orow) {
-            const int th = r0 + orow;
-            if (th >= th_n) break;
-            float outv[VO];
-#pragma unroll
-            for (int q = 0; q < VO; ++q) outv[q] = act_apply(accd[orow][q] + dbb, dsl, da.lo, da.hi);
-            float* dst = yg + ((int64_t)n * D.out_total + D.out_off + cg) * oplane + (int64_t)(ho0 + th) * D.wo + q0;
-            if (vec_ok && q0 + VO <= D.wo) {
-                *(float4*)dst = make_float4(outv[0], outv[1], outv[2], outv[3]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < VO; ++q)
-                    if (q0 + q < D.wo) dst[q] = outv[q];
+            for (int orow = 0; orow < RR; ++orow) {
+                const int th = r0 + orow;
+                if (th >= th_n) break;
+                store_row(yg + ((int64_t)n * D.out_total + D.out_off + cg) * oplane + (int64_t)(ho0 + th) * D.wo + q0,
+                          accd[orow], dbb, dsl, q0);
             }
         }
     }
@@ -335,7 +363,9 @@ int cu_count() {
 bool plan(const Desc& pw, const Desc& dw, FusedPlan* out) {
     const conv2d_params_t& d = dw.p;
     const int W = pw.p.w;
-    const int ew = W + d.pad_left + d.pad_right;
+    // Rows of a multiple of 4 floats (16-byte aligned), the columns past the
+    // right pad holding pad_value too.
+    const int ew = (W + d.pad_left + d.pad_right + 3) / 4 * 4;
     const bool vec = W % 4 == 0;
     const long per_image = (long)((pw.p.c_out + CE - 1) / CE) * pw.p.n;
     bool ok = false;
@@ -349,7 +379,7 @@ bool plan(const Desc& pw, const Desc& dw, FusedPlan* out) {
         const int xs = xs_stride_for(npix);
         const int es = es_stride_for(rows * ew);
         const int fl1 = KC * xs + KC * CEP;
-        const int fl2 = CE * es;
+        const int fl2 = CE * es + 8;   // 8 floats of slack: the last column group's window may run past the tile
         const int lds = fl1 > fl2 ? fl1 : fl2;
         if (lds * 4 > 96 * 1024) break;
         // Time ~ rounds of resident workgroups x pointwise rows per workgroup
@@ -397,6 +427,8 @@ hipError_t launch_fused_pw_dw(const Desc& pw, const Desc& dw, ConvArgs apw, Conv
     f.div_w = make_fastdiv((uint32_t)pw.p.w);
     f.div_w4 = make_fastdiv((uint32_t)(pw.p.w / 4 > 0 ? pw.p.w / 4 : 1));
     f.div_rw4 = make_fastdiv((uint32_t)(fp.rows * (pw.p.w / 4) > 0 ? fp.rows * (pw.p.w / 4) : 1));
+    f.dv_rows = make_divu32((uint32_t)fp.rows);
+    f.dv_uw = make_divu32((uint32_t)((dw.wo + VO - 1) / VO));
     f.dv_ce_tiles = make_divu32((uint32_t)f.ce_tiles);
     f.dv_tiles_h = make_divu32((uint32_t)f.tiles_h);
     const uint64_t blocks = (uint64_t)f.ce_tiles * f.tiles_h * apw.n;
