@@ -615,10 +615,15 @@ using K5_M16   = Cfg<16,  64, 16,  4, 5, 5, 8, 1, 8, 1, 4>;
 // patch operand read, K split 8 ways); the OIHW form of its weight tiles
 // would not fit in LDS.
 using K3A_M64  = Cfg<64,  64, 16,  4, 3, 3, 8, 1, 8, 2, 3>;
+// Few input channels on a small image: the four waves split K instead of
+// the pixels, so a workgroup owns one 64-pixel tile and the grid has four
+// times as many workgroups (a 32x32 image: 16 instead of 4).
+using K3S_M16  = Cfg<16,  64, 16,  4, 3, 3, 4, 1, 4, 2, 6>;
+using K3S_M32  = Cfg<32,  64, 16,  4, 3, 3, 4, 1, 4, 2, 6>;
 
 enum {
     C3_M16, C3_M32, C3_M64, C3W_M16, C3W_M32, C3W_M64, C3P_M16, C3P_M32,
-    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, C3A_M64, NCFG
+    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, C3A_M64, C3S_M16, C3S_M32, NCFG
 };
 
 const CfgInfo& cfg(int i) {
@@ -626,7 +631,7 @@ const CfgInfo& cfg(int i) {
         info<K3_M16, true>(), info<K3_M32, true>(), info<K3_M64, true>(), info<K3W_M16>(), info<K3W_M32>(),
         info<K3W_M64>(),  info<K3P_M16>(),  info<K3P_M32>(),   info<K1F_M32>(),  info<K1F_M64>(),
         info<K1F_M128>(), info<K1FP_M16>(), info<K1FP_M32>(),  info<K1_M32>(),   info<K1_M64>(),
-        info<K5_M16>(),   info<K3A_M64, true, true>(),
+        info<K5_M16>(),   info<K3A_M64, true, true>(), info<K3S_M16>(), info<K3S_M32>(),
     };
     return table[i];
 }
@@ -674,6 +679,10 @@ bool plan_igemm_f32(Desc& d) {
     int nc = 0;
     if (is3) {
         if (d.cin_g < 32) {
+            // 64-pixel tiles of the whole batch and all groups; with few of
+            // them the pixel-splitting tiles would leave most CUs idle.
+            const long tiles = (long)p.n * p.groups * ((d.ho + 3) / 4) * ((d.wo + 15) / 16);
+            if (tiles <= 256 && m <= 32) cands[nc++] = m <= 16 ? C3S_M16 : C3S_M32;
             cands[nc++] = m <= 16 ? C3P_M16 : C3P_M32;
         } else {
             cands[nc++] = m <= 16 ? C3_M16 : (m <= 32 ? C3_M32 : C3_M64);
