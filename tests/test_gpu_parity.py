@@ -618,3 +618,67 @@ def test_pointwise_f32_slices_and_unaligned_input():
     t.cuda.synchronize()
     y2.check_guards()
     assert_close(y2.host().numpy().reshape(ref.shape), ref, FP32_TOL, "pointwise_f32 unaligned input")
+
+
+# fp32 depthwise 3x3 stride 1 on rows of whole 16-byte vectors: pads 0-2 on
+# each side (output widths that are and are not multiples of 4), ragged
+# tiles, channel slices in and out, N > 1, a 1024-wide row, a large plane,
+# every activation, nonzero pad values.
+DWS_CASES = [
+    # n, c, h, w, pads (t, l, b, r), act, pad_value
+    (2, 24, 56, 56, (1, 1, 1, 1), workloads.ACT_CLIP, 0.0),
+    (1, 7, 13, 20, (0, 0, 0, 0), workloads.ACT_RELU, 0.0),
+    (3, 5, 9, 12, (2, 1, 0, 2), workloads.ACT_PRELU, -0.5),
+    (1, 4, 33, 16, (2, 2, 2, 2), workloads.ACT_LEAKY_RELU, 0.25),
+    (2, 3, 3, 1024, (1, 1, 1, 1), workloads.ACT_NONE, 0.0),
+    (1, 2, 88, 92, (1, 0, 1, 1), workloads.ACT_CLIP, 1.0),
+    (4, 6, 5, 8, (1, 2, 1, 0), workloads.ACT_RELU, -1.0),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DWS_CASES)))
+def test_depthwise_vector_rows_fp32(i):
+    n, c, h, w, p4, act, pv = DWS_CASES[i]
+    L = workloads.Layer("dws", n, c, h, w, c, (3, 3), pads=p4, groups=c, has_bias=True, act=act, alpha=0.1,
+                        clip=(-0.5, 0.75), pad_value=pv)
+    rng = np.random.default_rng(3100 + i)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    print(f"case {i} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, wt, b, sl, repeat=2)
+    ref = oracle_layer(L, x, wt, b, sl)
+    assert kname == "depthwise_f32"
+    assert_close(y, ref, FP32_TOL, f"dw case {i}")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+def test_depthwise_vector_rows_slices():
+    """Input channels [4, 4 + c) of a wider buffer, output into channels
+    [1, 1 + c) of a wider one; the same layer on an input that is not 16-byte
+    aligned (scalar row loads) agrees."""
+    t = torch()
+    L = workloads.Layer("dws", 2, 12, 16, 24, 12, (3, 3), pads=(1, 1, 1, 1), groups=12, has_bias=True,
+                        act=workloads.ACT_RELU)
+    rng = np.random.default_rng(3199)
+    x, wt, b, _ = workloads.layer_arrays(rng, L)
+    ref = oracle_layer(L, x, wt, b, None)
+    big = rng.standard_normal((L.n, L.c_in + 6, L.h, L.w)).astype(np.float32)
+    big[:, 4:4 + L.c_in] = x
+    d = cc().conv2d_desc_create(layer_params(L, in_total_channels=L.c_in + 6, in_channel_offset=4,
+                                             out_total_channels=L.c_out + 3, out_channel_offset=1))
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
+    y = Guarded(n * ot * ho * wo, t.float32, float("nan"))
+    cc().conv2d_forward(d, to_dev(big), to_dev(wt), to_dev(b), None, y.view)
+    t.cuda.synchronize()
+    y.check_guards()
+    got = y.host().numpy().reshape(n, ot, ho, wo)
+    assert np.isnan(got[:, :1]).all() and np.isnan(got[:, 1 + L.c_out:]).all()
+    assert_close(got[:, 1:1 + L.c_out], ref, FP32_TOL, "dw slices")
+    d2 = cc().conv2d_desc_create(layer_params(L))
+    raw = t.zeros(x.size + 4, dtype=t.float32, device="cuda")
+    xv = raw[1:1 + x.size]
+    xv.copy_(t.from_numpy(x.reshape(-1)).cuda())
+    y2 = Guarded(L.n * L.c_out * L.h * L.w, t.float32, float("nan"))
+    cc().conv2d_forward(d2, xv, to_dev(wt), to_dev(b), None, y2.view)
+    t.cuda.synchronize()
+    y2.check_guards()
+    assert_close(y2.host().numpy().reshape(ref.shape), ref, FP32_TOL, "unaligned input")
