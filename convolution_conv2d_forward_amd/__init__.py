@@ -101,6 +101,8 @@ def _load():
     lib.qfused_dw_pw_forward.restype = i32
     lib.qfused_pw_dw_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, f32, f32, f32, i8, vp, vp]
     lib.qfused_pw_dw_forward.restype = i32
+    lib.conv2d_probe_copy.argtypes = [vp, vp, ctypes.c_int64, vp]
+    lib.conv2d_probe_copy.restype = i32
     lib.conv2d_status_string.argtypes = [i32]
     lib.conv2d_status_string.restype = ctypes.c_char_p
     lib.conv2d_last_error.argtypes = []
@@ -367,6 +369,20 @@ def qfused_pw_dw_forward(desc_pw: Desc, desc_dw: Desc, x, w_pw, b_pw, pw_scales,
         _ptr(b_pw, "b_pw", "int32", pp.c_out) if pp.has_bias else None, *(f(v) for v in pw_scales),
         _ptr(w_dw, "w_dw", "int8", wdn), _ptr(b_dw, "b_dw", "int32", pd.c_out) if pd.has_bias else None,
         *(f(v) for v in dw_scales), ctypes.c_int8(int(y_zp)), _ptr(y, "y", "int8", yn), _stream(stream)))
+
+
+def conv2d_probe_copy(dst, src, stream=None) -> None:
+    """Streaming 16-byte device copy of src into dst (the attainable-bandwidth
+    reference of the benchmark; include/conv2d_probe.h)."""
+    torch = _torch()
+    for t, what in ((dst, "dst"), (src, "src")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{what}: contiguous GPU tensor expected")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check(_lib.conv2d_probe_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                  ctypes.c_int64(nbytes), _stream(stream)))
 
 
 def output_shape(desc: Desc):

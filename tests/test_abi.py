@@ -23,8 +23,11 @@ def cc():
     return m
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "conv2d_probe.h")
+
+
+def declared_symbols(path=HEADER):
+    text = open(path).read()
     return sorted(set(re.findall(r"CONV2D_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
 
 
@@ -35,6 +38,24 @@ def test_header_symbols_exported():
     for s in syms:
         assert hasattr(lib, s), f"{s} declared in conv2d.h but not exported"
     assert sorted(cc().EXPORTED) == syms
+    # every header under include/ (the measurement probe too)
+    probe = declared_symbols(PROBE_HEADER)
+    assert probe == ["conv2d_probe_copy"], probe
+    for s in probe:
+        assert hasattr(lib, s), f"{s} declared in conv2d_probe.h but not exported"
+
+
+def test_probe_copy_rejects_before_launch():
+    """Misaligned or overlapping ranges are refused without a HIP call."""
+    lib = ctypes.CDLL(cc().LIB_PATH)
+    f = lib.conv2d_probe_copy
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    f.restype = ctypes.c_int32
+    assert f(None, ctypes.c_void_p(4096), 64, None) == cc().CONV_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(4096 + 4), ctypes.c_void_p(1 << 20), 64, None) == cc().CONV_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(4096), ctypes.c_void_p(1 << 20), 60, None) == cc().CONV_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 32), 64, None) == cc().CONV_ERR_ALIAS
+    assert f(ctypes.c_void_p(4096), ctypes.c_void_p(1 << 20), 0, None) == cc().CONV_OK
 
 
 def test_params_layout_matches_header(tmp_path):

@@ -90,3 +90,17 @@ def test_bf16_descriptor_shared_by_two_threads():
         for i in range(reps):
             got = ys[k][i].float().cpu().numpy().astype(np.float64)
             assert_close(got, refs[k], BF16_TOL, f"thread {k} call {i}")
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 << 20])
+def test_probe_copy_copies(nbytes):
+    """The measurement copy moves exactly the bytes asked for (the tail past
+    them in dst is untouched)."""
+    t = torch()
+    n = nbytes // 4
+    src = t.arange(n, dtype=t.float32, device="cuda")
+    dst = t.full((n + 64,), -1.0, dtype=t.float32, device="cuda")
+    cc().conv2d_probe_copy(dst, src)
+    t.cuda.synchronize()
+    assert t.equal(dst[:n], src)
+    assert (dst[n:] == -1.0).all()
