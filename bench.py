@@ -20,11 +20,12 @@ The JSON line also carries:
                 of the same workload's outputs
   per_config    the other synthetic workloads (single conv, inverted
                 bottleneck fused/unfused, mixed sweep fp32/bf16, int8 chain
-                unfused/fused, dense-block layers with Winograd beside the
-                implicit GEMM), each layer timed with events the same way,
-                with its binding roofline; HBM-bound entries also carry the
-                time of a plain device copy of the same bytes (copy_us) and
-                their speed as a fraction of it (copy_frac)
+                unfused/fused, int8 bottleneck fused/unfused, int8 dense
+                layers, dense-block layers with Winograd beside the implicit
+                GEMM), each layer timed with events the same way, with its
+                binding roofline; HBM-bound entries also carry the time of the
+                library's streaming 16-byte copy moving the same bytes
+                (copy_us) and their speed as a fraction of it (copy_frac)
 Everything on stdout except the final JSON line goes to stderr.
 """
 import argparse
@@ -589,16 +590,23 @@ def per_config(reps, only="all"):
         for k, L in enumerate(wl.layers):
             wd = t_(wl.arrays[f"w{k}"])
             entry = {}
-            for algo in ("direct", "winograd"):
+            for algo, bound in (("direct", False), ("direct", True), ("winograd", False), ("winograd", True)):
                 p = params_of(L, in_total_channels=total, out_total_channels=total, out_channel_offset=L.c_in)
                 p.algo = cc.ALGOS[algo]
                 d = cc.conv2d_desc_create(p)
-                fns = [lambda d=d, b=b: cc.conv2d_forward(d, b, wd, None, None, b) for b in bufs]
-                t = time_layer(f"{algo}{k}", fns, reps)
-                entry[algo] = dict(roofline_entry(L.flops, 4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w),
-                                                  t, "f32"), kernel=cc.conv2d_desc_kernel_name(d))
+                wuse = wd
+                if bound:
+                    cc.conv2d_desc_bind_weights(d, wd)
+                    torch.cuda.synchronize()
+                    wuse = None
+                fns = [lambda d=d, b=b, wuse=wuse: cc.conv2d_forward(d, b, wuse, None, None, b) for b in bufs]
+                key = algo + ("_bound" if bound else "")
+                t = time_layer(f"{key}{k}", fns, reps)
+                entry[key] = dict(roofline_entry(L.flops, 4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w),
+                                                 t, "f32"), kernel=cc.conv2d_desc_kernel_name(d))
             # the MFMA work Winograd actually issues: 16 products per 2x2 tile and channel pair
-            entry["winograd"]["executed_flops"] = 2 * 16 * L.c_out * L.c_in * ((h + 1) // 2) * ((w + 1) // 2)
+            for key in ("winograd", "winograd_bound"):
+                entry[key]["executed_flops"] = 2 * 16 * L.c_out * L.c_in * ((h + 1) // 2) * ((w + 1) // 2)
             res[L.name] = entry
             log("winograd", L.name, {a: e["us"] for a, e in entry.items()})
         out["dense_block_winograd"] = res
@@ -607,15 +615,17 @@ def per_config(reps, only="all"):
 
 
 def copy_us(nbytes, reps):
-    """HIP-event time of a plain device copy moving nbytes in all (half read,
-    half written), cold: rotated over buffer sets like the layers, queued
-    back to back the same way."""
+    """HIP-event time of the library's streaming 16-byte copy
+    (conv2d_probe_copy) moving nbytes in all (half read, half written), cold:
+    rotated over buffer sets like the layers, queued back to back the same
+    way."""
+    import convolution_conv2d_forward_amd as cc
     torch = torch_mod()
-    n = max(1, nbytes // 8)
+    n = max(4, nbytes // 8 // 4 * 4)      # float32 elements per side, whole 16-byte pieces
     sets = int(min(64, max(1, ROTATE_BYTES // max(1, 8 * n))))
     src = [torch.ones(n, device=dev()) for _ in range(sets)]
     dst = [torch.empty(n, device=dev()) for _ in range(sets)]
-    fns = [lambda s=s_, d=d_: d.copy_(s) for s_, d_ in zip(src, dst)]
+    fns = [lambda s=s_, d=d_: cc.conv2d_probe_copy(d, s) for s_, d_ in zip(src, dst)]
     t = time_layer("copy", fns, reps)
     del src, dst
     return t
@@ -637,19 +647,31 @@ def add_copy_context(out, reps):
 
 
 def copy_probe(reps):
-    """A plain device copy of known size (calibrates the HBM byte counters)."""
+    """The library's streaming copy: one of known size (1 GiB each way, which
+    calibrates the HBM byte counters) and a sweep over the byte counts of the
+    HBM-bound layers (read + written, cold, back to back), as the attainable
+    bandwidth at each size."""
+    import convolution_conv2d_forward_amd as cc
     torch = torch_mod()
     n = 256 << 20   # 1 GiB of float32
     a = torch.ones(n, device=dev())
     b = torch.empty_like(a)
     for _ in range(3):
-        b.copy_(a)
+        cc.conv2d_probe_copy(b, a)
     torch.cuda.synchronize()
     timer = EventTimer()
     for _ in range(reps):
-        timer.run("copy", lambda: b.copy_(a))
+        timer.run("copy", lambda: cc.conv2d_probe_copy(b, a))
     t = timer.mean_us("copy")[0]
-    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "us": t, "gbps": 8 * n / (t * 1e-6) / 1e9}
+    out = {"bytes_read": 4 * n, "bytes_written": 4 * n, "us": t, "gbps": 8 * n / (t * 1e-6) / 1e9}
+    del a, b
+    sweep = {}
+    for mb in (4, 8, 16, 22.5, 38.5, 64, 128, 256, 512):
+        nb = int(mb * 1e6)
+        tu = copy_us(nb, max(reps, 20))
+        sweep[f"{mb}MB"] = {"us": round(tu, 3), "gbps": round(nb / (tu * 1e-6) / 1e9, 1)}
+    out["sweep"] = sweep
+    return out
 
 
 # ------------------------------------------------------------ cpu baseline --

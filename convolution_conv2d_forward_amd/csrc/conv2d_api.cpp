@@ -401,8 +401,11 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
         return fail(CONV_ERR_INVALID_ARG, "weights were first bound on device %d, current device is %d",
                     d.wbound_device, dev);
     const int64_t wb = w_bytes(d);
-    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0);
-    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16 ? d.wpack_bytes : d.apack_bytes;
+    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) ||
+                       d.kclass == KC_WINOGRAD_F32;
+    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16    ? d.wpack_bytes
+                               : d.kclass == KC_WINOGRAD_F32 ? winograd_u_bytes(d)
+                                                             : d.apack_bytes;
     const int64_t off = packs ? (wb + 255) / 256 * 256 : 0;
     const int64_t total = packs ? off + pack_bytes : wb;
     if (views_overlap(flat(w, wb), flat(d.wbound, d.wbound_bytes)))
@@ -421,8 +424,9 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(d.wbound, w, (size_t)wb, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && packs)
-        e = d.kclass == KC_IGEMM_BF16 ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
-                                      : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
+        e = d.kclass == KC_IGEMM_BF16    ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
+            : d.kclass == KC_WINOGRAD_F32 ? pack_winograd_f32_weights(d, d.wbound, (char*)d.wbound + off, s)
+                                          : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
     if (e != hipSuccess) {
         d.bound = false;
         return hip_status(e, "binding weights");
@@ -509,7 +513,9 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
         break;
     case KC_DW: e = launch_dw(d, a, s); break;
     case KC_GROUPED: e = launch_grouped(d, a, s); break;
-    case KC_WINOGRAD_F32: e = launch_winograd_f32(d, a, s); break;
+    case KC_WINOGRAD_F32:
+        e = launch_winograd_f32(d, a, s, use_bound ? (const char*)d.wbound + d.wbound_pack_off : nullptr);
+        break;
     case KC_PW_F32:
         e = pointwise_f32_fits(d, a) ? launch_pointwise_f32(d, a, s) : launch_igemm_f32(d, a, s);
         break;

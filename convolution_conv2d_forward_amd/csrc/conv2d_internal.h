@@ -171,7 +171,13 @@ hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);
-hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s);
+// upacked: the bound weights transformed and packed (pack_winograd_f32_weights),
+// or null to transform a.wptr (OIHW) in the kernel.
+hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s, const void* upacked = nullptr);
+// Bytes of the packed Winograd U image, and the pack (OIHW fp32 -> U in the
+// kernel's per-lane register order).
+int64_t winograd_u_bytes(const Desc& d);
+hipError_t pack_winograd_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 // Needs 16-byte aligned rows (pointers, plane sizes and channel offsets);
 // pointwise_f32_fits says whether a call's tensors allow it.
 hipError_t launch_pointwise_f32(const Desc& d, ConvArgs a, hipStream_t s);

@@ -64,6 +64,68 @@ struct WRegs {
     float g[9];
 };
 
+// U = G g G^T of one 3x3 filter g (row-major): u[4*i + j], i, j = 0..3.  The
+// forward kernel (weights given at each call) and the bound-weight pack use
+// this one function, so both paths multiply the same U.
+__device__ __forceinline__ void filter_u(const float (&g)[9], float (&u)[16]) {
+    float t4[4][3];                                    // G g: rows of the 4x3 product
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const float g0 = g[j], g1 = g[3 + j], g2 = g[6 + j];
+        t4[0][j] = g0;
+        t4[1][j] = 0.5f * (g0 + g1 + g2);
+        t4[2][j] = 0.5f * (g0 - g1 + g2);
+        t4[3][j] = g2;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float r0 = t4[i][0], r1 = t4[i][1], r2 = t4[i][2];
+        u[4 * i + 0] = r0;
+        u[4 * i + 1] = 0.5f * (r0 + r1 + r2);
+        u[4 * i + 2] = 0.5f * (r0 - r1 + r2);
+        u[4 * i + 3] = r2;
+    }
+}
+
+// Packed U (bound weights): for each output-channel tile, chunk, wave and
+// lane, the 16 values the lane's MFMAs take, in the order (e, ks, m):
+// position 2*wave + e, input channel chunk*KC + 4*ks + lane/16, output
+// channel tile*COT + 16*m + lane%16; zero past the channels.  One wave's
+// chunk is 4 KB, read as four coalesced 16-byte loads per lane.
+// MB blocks of 16 output channels per workgroup tile (2 or 4): 8 * MB floats
+// per lane and chunk, in the order (e, ks, m).
+template <int MB>
+__global__ __launch_bounds__(256) void pack_winograd_u(const float* __restrict__ w, float* __restrict__ out,
+                                                       int cin, int cout, int nch, int co_tiles) {
+    constexpr int NPU = 8 * MB;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)co_tiles * nch * 8 * 64;
+    if (idx >= total) return;
+    const int lane = (int)(idx & 63);
+    const int wave = (int)((idx >> 6) & 7);
+    const int64_t rest = idx >> 9;
+    const int c = (int)(rest % nch);
+    const int ct = (int)(rest / nch);
+    const int kq = lane >> 4, l16 = lane & 15;
+    float v[NPU];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int ks = 0; ks < KC / 4; ++ks) {
+            const int co = ct * 16 * MB + 16 * m + l16, ci = c * KC + 4 * ks + kq;
+            float g[9], u[16];
+            const bool ok = co < cout && ci < cin;
+#pragma unroll
+            for (int t = 0; t < 9; ++t) g[t] = ok ? w[((int64_t)co * cin + ci) * 9 + t] : 0.0f;
+            filter_u(g, u);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) v[(e * (KC / 4) + ks) * MB + m] = u[2 * wave + e];
+        }
+    float4* dst = (float4*)(out + idx * NPU);
+#pragma unroll
+    for (int q = 0; q < NPU / 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
 __global__ __launch_bounds__(kT) void winograd_f32_kernel(WinoArgs f) {
     extern __shared__ __align__(16) float lds[];
     const ConvArgs& a = f.a;
@@ -138,30 +200,16 @@ __global__ __launch_bounds__(kT) void winograd_f32_kernel(WinoArgs f) {
     auto filter_transform = [&](int c, Regs& R) __attribute__((always_inline)) {
         const int c0 = c * KC;
         const bool okw = co0 + fco < a.c_out && c0 + fci < C;
-        float g[9];
+        float g[9], u[16];
 #pragma unroll
         for (int t = 0; t < 9; ++t) {
             asm volatile("" : "+v"(R.g[t]));
             g[t] = okw ? R.g[t] : 0.0f;
         }
-        float t4[4][3];                                // G g: rows of the 4x3 product
+        filter_u(g, u);
+        float* dst = us + fci * US + fco;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const float g0 = g[j], g1 = g[3 + j], g2 = g[6 + j];
-            t4[0][j] = g0;
-            t4[1][j] = 0.5f * (g0 + g1 + g2);
-            t4[2][j] = 0.5f * (g0 - g1 + g2);
-            t4[3][j] = g2;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float r0 = t4[i][0], r1 = t4[i][1], r2 = t4[i][2];
-            float* dst = us + (4 * i) * KC * US + fci * US + fco;
-            dst[0 * KC * US] = r0;
-            dst[1 * KC * US] = 0.5f * (r0 + r1 + r2);
-            dst[2 * KC * US] = 0.5f * (r0 - r1 + r2);
-            dst[3 * KC * US] = r2;
-        }
+        for (int pos = 0; pos < 16; ++pos) dst[pos * KC * US] = u[pos];
     };
     // V = B^T d B of one (channel, tile) patch.
     auto input_transform = [&]() __attribute__((always_inline)) {
@@ -297,6 +345,229 @@ __global__ __launch_bounds__(kT) void winograd_f32_kernel(WinoArgs f) {
     }
 }
 
+// Bound weights (U packed by pack_winograd_u<MB>), pipelined: one barrier
+// per input-channel chunk.  Iteration c multiplies chunk c (V from one LDS
+// buffer, U from registers) while every thread transforms half of one
+// (channel, tile) patch of chunk c+1 into the other V buffer and stores the
+// patch of chunk c+2 (loaded one iteration earlier) into the free patch
+// buffer; the loads of chunk c+3 and the U of chunk c+1 are in flight over
+// the same iteration.  MFMAs and transforms share the waves, so the matrix
+// core works while the VALU and LDS transform the next chunk.  The
+// transforms, the 16 channel sums and the output transform are those of
+// winograd_f32_kernel (same U, same V, same order of accumulation), so the
+// results are bitwise equal for the same descriptor.  CO = 16*MB output
+// channels per workgroup.
+template <int MB>
+__global__ __launch_bounds__(kT) void winograd_pu_kernel(WinoArgs f) {
+    constexpr int CO = 16 * MB;
+    constexpr int NPU = 8 * MB;
+    extern __shared__ __align__(16) float lds[];
+    const ConvArgs& a = f.a;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    uint32_t L = xcd_remap(blockIdx.x, f.num_blocks);
+    uint32_t Q = divu(L, f.dv_co_tiles);
+    const int cot = L - Q * f.co_tiles;
+    L = Q;
+    Q = divu(L, f.dv_bw);
+    const int bx = L - Q * f.bw;
+    L = Q;
+    Q = divu(L, f.dv_bh);
+    const int by = L - Q * f.bh;
+    const int n = Q;
+    const int co0 = cot * CO;
+    const int ty0 = by * TR, tx0 = bx * TC;
+    const int ih0 = 2 * ty0 - a.pad_top, iw0 = 2 * tx0 - a.pad_left;
+    const int C = a.c_in, H = a.h, W = a.w;
+    const int64_t HW = (int64_t)H * W;
+    const int nch = (C + KC - 1) / KC;
+
+    float* patch = lds;                                // [2][KC][PH][PW]
+    float* vs = lds + 2 * LDS_PATCH;                   // [2][16][KC][VS]
+    float* ms = lds;                                   // [16][CO][MS] (after the last chunk)
+
+    const float* __restrict__ xg = (const float*)a.xptr + ((int64_t)n * a.in_total + a.in_off) * HW;
+    const float* __restrict__ wu = (const float*)a.wptr;
+    const float pv = a.pad_value;
+
+    // Patch of chunk c -> registers: unconditional loads (slots outside the
+    // patch or the channels read the image's first element, replaced on store).
+    float px[NX];
+    auto load_patch = [&](int c) __attribute__((always_inline)) {
+        const int c0 = c * KC;
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int u = tid + i * kT;
+            const int ch = u / PPL, rem = u - ch * PPL;
+            const int r = rem / PW, col = rem - r * PW;
+            const int ih = ih0 + r, iw = iw0 + col;
+            const bool ok = u < KC * PPL && c0 + ch < C && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+            px[i] = xg[ok ? (int64_t)(c0 + ch) * HW + (int64_t)ih * W + iw : 0];
+        }
+    };
+    auto store_patch = [&](int c, float* dst) __attribute__((always_inline)) {
+        const int c0 = c * KC;
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int u = tid + i * kT;
+            if (u < KC * PPL) {
+                const int ch = u / PPL, rem = u - ch * PPL;
+                const int r = rem / PW, col = rem - r * PW;
+                const int ih = ih0 + r, iw = iw0 + col;
+                float v = px[i];
+                if (c0 + ch >= C) v = 0.0f;                                   // past the channels: no term
+                else if ((unsigned)ih >= (unsigned)H || (unsigned)iw >= (unsigned)W) v = pv;   // padded tap
+                dst[u] = v;
+            }
+        }
+    };
+    // U of chunk c for this wave's lane (NPU floats, order (e, ks, m)).
+    auto load_u = [&](int c, float (&u)[NPU]) __attribute__((always_inline)) {
+        const float4* src = (const float4*)(wu + ((((int64_t)cot * nch + c) * 8 + wave) * 64 + lane) * NPU);
+#pragma unroll
+        for (int q = 0; q < NPU / 4; ++q) {
+            const float4 v = src[q];
+            u[4 * q] = v.x; u[4 * q + 1] = v.y; u[4 * q + 2] = v.z; u[4 * q + 3] = v.w;
+        }
+    };
+    // V = B^T d B, half of one (channel, tile) patch per thread: rows 2h and
+    // 2h+1 of B^T d (B^T rows 0, 1 use patch rows 0..2; rows 2, 3 use 1..3).
+    auto transform = [&](const float* pin, float* vout) __attribute__((always_inline)) {
+        const int ti = tid >> 1, h = tid & 1;
+        const int ci = ti >> 4, t = ti & 15;
+        const int tr = t / TC, tc = t - tr * TC;
+        const float* p = pin + ci * PPL + (2 * tr + h) * PW + 2 * tc;
+        float d[3][4];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) d[i][j] = p[i * PW + j];
+        float b[2][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // h = 0: d rows 0,1,2 -> b0 = d0 - d2, b1 = d1 + d2;  h = 1: d rows 1,2,3 -> b2 = d2 - d1, b3 = d1 - d3
+            b[0][j] = h ? d[1][j] - d[0][j] : d[0][j] - d[2][j];
+            b[1][j] = h ? d[0][j] - d[2][j] : d[1][j] + d[2][j];
+        }
+        float* dst = vout + ci * VS + t;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * h + ii;
+            dst[(4 * i + 0) * KC * VS] = b[ii][0] - b[ii][2];
+            dst[(4 * i + 1) * KC * VS] = b[ii][1] + b[ii][2];
+            dst[(4 * i + 2) * KC * VS] = b[ii][2] - b[ii][1];
+            dst[(4 * i + 3) * KC * VS] = b[ii][1] - b[ii][3];
+        }
+    };
+
+    f32x4 acc[2][MB];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[e][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int kq = lane >> 4, l16 = lane & 15;
+    auto gemm = [&](const float* vin, const float (&u)[NPU]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KC / 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float bv = vin[((2 * wave + e) * KC + 4 * ks + kq) * VS + l16];
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+                    acc[e][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(u[(e * (KC / 4) + ks) * MB + m], bv, acc[e][m],
+                                                                     0, 0, 0);
+            }
+    };
+
+    // ---- prologue: patches of chunks 0 and 1 in LDS, V of chunk 0, patch of
+    // chunk 2 in registers, U of chunk 0 ----
+    float ucur[NPU], unext[NPU];
+    load_patch(0);
+    store_patch(0, patch);
+    if (nch > 1) {
+        load_patch(1);
+        store_patch(1, patch + LDS_PATCH);
+    }
+    load_u(0, ucur);
+    if (nch > 2) load_patch(2);
+    __syncthreads();
+    transform(patch, vs);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nch) load_u(c + 1, unext);
+        gemm(vs + b * LDS_V, ucur);
+        if (c + 1 < nch) transform(patch + (b ^ 1) * LDS_PATCH, vs + (b ^ 1) * LDS_V);
+        if (c + 2 < nch) store_patch(c + 2, patch + b * LDS_PATCH);   // chunk c's patch was transformed last iteration
+        if (c + 3 < nch) load_patch(c + 3);
+        __syncthreads();
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int q = 0; q < NPU; ++q) ucur[q] = unext[q];
+        }
+    }
+
+    // ---- gather M[position][channel][tile] through LDS ----
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int pos = 2 * wave + e;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ms[(pos * CO + 16 * m + 4 * kq + v) * MS + l16] = acc[e][m][v];
+    }
+    __syncthreads();
+
+    // ---- Y = A^T M A, bias, activation, store: one (channel, tile) per pass ----
+    for (int pr = tid; pr < CO * NT; pr += kT) {
+        const int oc = pr >> 4, t = pr & 15;
+        const int co = co0 + oc;
+        const int tr = t / TC, tc = t - tr * TC;
+        const int oy = 2 * (ty0 + tr), ox = 2 * (tx0 + tc);
+        if (co >= a.c_out || oy >= a.ho || ox >= a.wo) continue;
+        float m4[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m4[i][j] = ms[((4 * i + j) * CO + oc) * MS + t];
+        float r[2][4];                                 // A^T M
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r[0][j] = m4[0][j] + m4[1][j] + m4[2][j];
+            r[1][j] = m4[1][j] - m4[2][j] - m4[3][j];
+        }
+        float y[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            y[i][0] = bias_act(a, r[i][0] + r[i][1] + r[i][2], co);
+            y[i][1] = bias_act(a, r[i][1] - r[i][2] - r[i][3], co);
+        }
+        float* yc = (float*)a.yptr + ((int64_t)n * a.out_total + a.out_off + co) * ((int64_t)a.ho * a.wo);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (oy + i >= a.ho) continue;
+            float* row = yc + (int64_t)(oy + i) * a.wo + ox;
+            if (ox + 1 < a.wo && (((uintptr_t)row) & 7) == 0) {
+                *(float2*)row = make_float2(y[i][0], y[i][1]);
+            } else {
+                row[0] = y[i][0];
+                if (ox + 1 < a.wo) row[1] = y[i][1];
+            }
+        }
+    }
+}
+
+// Output channels per workgroup of the bound-weight kernel: 64 when the
+// layer has more than 32 and the 32-channel grid would hold at least eight
+// workgroups per CU of the 256 (the input transform is then shared by twice
+// the output channels without leaving CUs idle), else 32.
+int pu_mb(const Desc& d) {
+    if (d.p.c_out <= 32) return 2;
+    const int64_t tiles = (int64_t)((d.ho + 1) / 2 + TR - 1) / TR * (((d.wo + 1) / 2 + TC - 1) / TC);
+    return (int64_t)d.p.n * tiles * ((d.p.c_out + 31) / 32) >= 8 * 256 ? 4 : 2;
+}
+
 }  // namespace
 
 bool plan_winograd_f32(const Desc& d) {
@@ -310,14 +581,35 @@ bool plan_winograd_f32(const Desc& d) {
     return blocks > 0 && blocks <= 0x7FFFFFFF;
 }
 
-hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s) {
+int64_t winograd_u_bytes(const Desc& d) {
+    const int mb = pu_mb(d);
+    const int64_t co_tiles = (d.p.c_out + 16 * mb - 1) / (16 * mb), nch = (d.p.c_in + KC - 1) / KC;
+    return co_tiles * nch * 8 * 64 * (8 * mb) * 4;
+}
+
+hipError_t pack_winograd_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s) {
+    const int mb = pu_mb(d);
+    const int co_tiles = (d.p.c_out + 16 * mb - 1) / (16 * mb), nch = (d.p.c_in + KC - 1) / KC;
+    const int64_t total = (int64_t)co_tiles * nch * 8 * 64;
+    if (total == 0) return hipSuccess;
+    const float* wp = (const float*)w;
+    float* op = (float*)dst;
+    int cin = d.p.c_in, cout = d.p.c_out, nc = nch, ct = co_tiles;
+    void* args[] = {(void*)&wp, &op, &cin, &cout, &nc, &ct};
+    const void* fn = mb == 4 ? (const void*)pack_winograd_u<4> : (const void*)pack_winograd_u<2>;
+    return hipLaunchKernel(fn, dim3((uint32_t)((total + 255) / 256)), dim3(256), args, 0, s);
+}
+
+hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s, const void* upacked) {
     WinoArgs f;
     f.a = a;
     f.tiles_h = (d.ho + 1) / 2;
     f.tiles_w = (d.wo + 1) / 2;
     f.bh = (f.tiles_h + TR - 1) / TR;
     f.bw = (f.tiles_w + TC - 1) / TC;
-    f.co_tiles = (d.p.c_out + COT - 1) / COT;
+    const int mb = pu_mb(d);
+    const bool pu = upacked && (uintptr_t)upacked % 16 == 0;
+    f.co_tiles = pu ? (d.p.c_out + 16 * mb - 1) / (16 * mb) : (d.p.c_out + COT - 1) / COT;
     const uint64_t blocks = (uint64_t)a.n * f.bh * f.bw * f.co_tiles;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
@@ -325,8 +617,14 @@ hipError_t launch_winograd_f32(const Desc& d, ConvArgs a, hipStream_t s) {
     f.dv_co_tiles = make_divu32((uint32_t)f.co_tiles);
     f.dv_bw = make_divu32((uint32_t)f.bw);
     f.dv_bh = make_divu32((uint32_t)f.bh);
-    const int lds = LDS_FLOATS * 4;
+    int lds = LDS_FLOATS * 4;
     const void* fn = (const void*)winograd_f32_kernel;
+    if (pu) {
+        f.a.wptr = upacked;
+        fn = mb == 4 ? (const void*)winograd_pu_kernel<4> : (const void*)winograd_pu_kernel<2>;
+        const int pipe = 2 * LDS_PATCH + 2 * LDS_V, gather = 16 * 16 * mb * MS;
+        lds = 4 * (pipe > gather ? pipe : gather);
+    }
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;

@@ -36,7 +36,7 @@ CASES = [
 ]
 
 
-def _run(L, x, w, b, s, *, in_total=0, in_off=0, out_total=0, out_off=0):
+def _run(L, x, w, b, s, *, in_total=0, in_off=0, out_total=0, out_off=0, bound=False):
     t = torch()
     d = cc().conv2d_desc_create(layer_params(L, prelu_slope_count=s.size, in_total_channels=in_total,
                                              in_channel_offset=in_off, out_total_channels=out_total,
@@ -44,7 +44,9 @@ def _run(L, x, w, b, s, *, in_total=0, in_off=0, out_total=0, out_off=0):
     assert cc().conv2d_desc_kernel_name(d) == "winograd_f32"
     n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
     y = Guarded(n * ot * ho * wo, t.float32, float("nan"))
-    cc().conv2d_forward(d, to_dev(x), to_dev(w), to_dev(b) if L.has_bias else None,
+    if bound:
+        cc().conv2d_desc_bind_weights(d, to_dev(w))
+    cc().conv2d_forward(d, to_dev(x), None if bound else to_dev(w), to_dev(b) if L.has_bias else None,
                         to_dev(s) if L.act == A.ACT_PRELU else None, y.view)
     t.cuda.synchronize()
     y.check_guards()
@@ -78,13 +80,46 @@ def test_winograd_concat_slices():
 
 def test_winograd_dense_block_full_size():
     """The dense-block chain's five layers (1 x Cin x 128 x 128, Cin = 64 + 32k),
-    each fed with the oracle's own previous outputs, at full size."""
+    each fed with the oracle's own previous outputs, at full size; with the
+    weights passed per call and bound to the descriptor (bitwise equal)."""
     wl = A.dense_block()
     a = wl.arrays
     cur = a["x"]
     for k, L in enumerate(wl.layers):
         w = a[f"w{k}"]
         ref = oracle_layer(L, cur, w, None, None)
-        got = _run(L, cur, w, np.zeros(L.c_out, np.float32), np.zeros(1, np.float32))
+        b0, s0 = np.zeros(L.c_out, np.float32), np.zeros(1, np.float32)
+        got = _run(L, cur, w, b0, s0)
         assert_close(got, ref, FP32_TOL, f"dense block layer {k}")
+        assert np.array_equal(_run(L, cur, w, b0, s0, bound=True), got), f"dense block layer {k}: bound weights"
         cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_winograd_bound_weights(i):
+    """Weights bound to the descriptor: U = G g G^T is computed once and packed
+    in the kernel's register order.  The output is bitwise that of the same
+    descriptor given the OIHW weights (the same transform arithmetic), and
+    matches the oracle."""
+    t = torch()
+    n, ci, h, w, co, pads, act, bias, pv = CASES[i]
+    L = A.Layer("wino", n, ci, h, w, co, (3, 3), pads=pads, has_bias=bias, act=act, alpha=0.2, clip=(-0.3, 0.4),
+                pad_value=pv)
+    rng = np.random.default_rng(850 + i)
+    x, wt, b, s = A.layer_arrays(rng, L)
+    d = cc().conv2d_desc_create(layer_params(L, prelu_slope_count=s.size, algo="winograd"))
+    nn, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
+    xd, wd = to_dev(x), to_dev(wt)
+    bd = to_dev(b) if L.has_bias else None
+    sd = to_dev(s) if L.act == A.ACT_PRELU else None
+    outs = []
+    for bound in (False, True):
+        if bound:
+            cc().conv2d_desc_bind_weights(d, wd)
+        y = Guarded(nn * ot * ho * wo, t.float32, float("nan"))
+        cc().conv2d_forward(d, xd, None if bound else wd, bd, sd, y.view)
+        t.cuda.synchronize()
+        y.check_guards()
+        outs.append(y.host().numpy().reshape(nn, ot, ho, wo))
+    assert np.array_equal(outs[0], outs[1]), "bound weights differ from explicit weights"
+    assert_close(outs[1], oracle_layer(L, x, wt, b, s), FP32_TOL, f"winograd bound case {i}")
