@@ -213,7 +213,6 @@ class DenseBlock:
             self.bufs.append(b)
         self.descs = [cc.conv2d_desc_create(params_of(L, in_total_channels=total, out_total_channels=total,
                                                        out_channel_offset=L.c_in)) for L in self.layers]
-        self.kernels = [cc.conv2d_desc_kernel_name(d) for d in self.descs]
         self.w = [t_(wl.arrays[f"w{k}"]) for k in range(len(self.layers))]
         self.bound = bound
         if bound:
@@ -221,6 +220,8 @@ class DenseBlock:
                 cc.conv2d_desc_bind_weights(d, wk)
             torch.cuda.synchronize()
             self.w = [None] * len(self.layers)
+        # after binding: AUTO runs bound 3x3 layers of this size on Winograd
+        self.kernels = [cc.conv2d_desc_kernel_name(d) for d in self.descs]
         self.flops = [L.flops for L in self.layers]
         # x slice read once + weights + the written slice
         self.bytes = [4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w) for L in self.layers]
@@ -276,27 +277,38 @@ def bench_dense_block(steps, warmup, bound=True):
 
 def dense_roofline(db, per):
     """Roofline of the dominant kernel: the instantiation with the largest
-    total event time in the step (layers sharing a kernel are pooled)."""
+    total event time in the step (layers sharing a kernel are pooled).
+    achieved counts the convolution's own 2*MACs; for Winograd F(2x2,3x3),
+    which issues 16 products per 2x2 output tile and channel pair instead of
+    36, the MFMA flops it executes are given beside it."""
     groups = {}
     for k, name in enumerate(db.kernels):
         if db.bound and name == "igemm_f32":
             name = "igemm_f32_packed"
-        cfg = f"{name}/M{64 if db.layers[k].c_out > 32 else 32}"
-        g = groups.setdefault(cfg, {"layers": [], "flops": 0, "bytes": 0, "us": 0.0})
-        g["layers"].append(db.layers[k].name)
+        L = db.layers[k]
+        cfg = f"{name}/M{64 if L.c_out > 32 else 32}"
+        g = groups.setdefault(cfg, {"layers": [], "flops": 0, "exec": 0, "bytes": 0, "us": 0.0})
+        g["layers"].append(L.name)
         g["flops"] += db.flops[k]
+        g["exec"] += (2 * 16 * L.c_out * L.c_in * ((L.h + 1) // 2) * ((L.w + 1) // 2)
+                      if name == "winograd_f32" else db.flops[k])
         g["bytes"] += db.bytes[k]
         g["us"] += per[k][0]
     dom = max(groups, key=lambda g: groups[g]["us"])
     g = groups[dom]
     n = len(g["layers"])
     achieved = g["flops"] / (g["us"] * 1e-6) / 1e12
-    return dom, g, {
+    roof = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["f32"] / 1e12, "unit": "TFLOP/s",
         "frac": round(achieved * 1e12 / PEAK["f32"], 4), "traffic": traffic_for(dom, n),
         "kernel": dom, "launches_per_step": n, "avg_launch_us": round(g["us"] / n, 3),
         "flops_per_launch": int(g["flops"] / n), "layers": g["layers"],
     }
+    if g["exec"] != g["flops"]:
+        ex = g["exec"] / (g["us"] * 1e-6) / 1e12
+        roof.update(executed_flops_per_launch=int(g["exec"] / n), executed_tflops=round(ex, 2),
+                    executed_frac=round(ex * 1e12 / PEAK["f32"], 4))
+    return dom, g, roof
 
 
 def _source_sha(rel):
@@ -796,7 +808,8 @@ def main():
         "roofline": roof,
         "layers": layers,
     }
-    line["config"]["weights"] = "bound at set-up (packed for the fp32 implicit GEMM)"
+    line["config"]["weights"] = ("bound at set-up (AUTO: 3x3 layers of this size then run Winograd F(2x2,3x3) "
+                                 "with U = G g G^T packed at bind; otherwise packed for the fp32 implicit GEMM)")
     # The same chain with the OIHW weights passed on every call.
     db2, wall2, per2 = bench_dense_block(args.steps, args.warmup, bound=False)
     line["config"]["weights_per_call"] = {

@@ -40,7 +40,7 @@ conv_status_t ok() {
 
 const char* kernel_name(const Desc& d) {
     switch (d.kclass) {
-    case KC_IGEMM_F32: return d.flatten_1x1 ? "igemm_f32_pointwise" : "igemm_f32";
+    case KC_IGEMM_F32: return d.wino_bound ? "winograd_f32" : d.flatten_1x1 ? "igemm_f32_pointwise" : "igemm_f32";
     case KC_IGEMM_BF16: return d.flatten_1x1 ? "igemm_bf16_pointwise" : "igemm_bf16";
     case KC_DW: return d.p.dtype == CONV_DTYPE_BF16 ? "depthwise_bf16" : "depthwise_f32";
     case KC_QDW: return d.cfg == 1 ? "depthwise_i8_dot4" : "depthwise_i8";
@@ -401,11 +401,12 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
         return fail(CONV_ERR_INVALID_ARG, "weights were first bound on device %d, current device is %d",
                     d.wbound_device, dev);
     const int64_t wb = w_bytes(d);
-    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) ||
-                       d.kclass == KC_WINOGRAD_F32;
-    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16    ? d.wpack_bytes
-                               : d.kclass == KC_WINOGRAD_F32 ? winograd_u_bytes(d)
-                                                             : d.apack_bytes;
+    const bool wino = d.kclass == KC_WINOGRAD_F32 ||
+                      (d.kclass == KC_IGEMM_F32 && d.p.algo == CONV_ALGO_AUTO && winograd_bound_preferred(d));
+    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) || wino;
+    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16 ? d.wpack_bytes
+                               : wino                     ? winograd_u_bytes(d)
+                                                          : d.apack_bytes;
     const int64_t off = packs ? (wb + 255) / 256 * 256 : 0;
     const int64_t total = packs ? off + pack_bytes : wb;
     if (views_overlap(flat(w, wb), flat(d.wbound, d.wbound_bytes)))
@@ -424,14 +425,16 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(d.wbound, w, (size_t)wb, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && packs)
-        e = d.kclass == KC_IGEMM_BF16    ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
-            : d.kclass == KC_WINOGRAD_F32 ? pack_winograd_f32_weights(d, d.wbound, (char*)d.wbound + off, s)
-                                          : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
+        e = d.kclass == KC_IGEMM_BF16 ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
+            : wino                     ? pack_winograd_f32_weights(d, d.wbound, (char*)d.wbound + off, s)
+                                       : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
     if (e != hipSuccess) {
         d.bound = false;
+        d.wino_bound = false;
         return hip_status(e, "binding weights");
     }
     d.bound = true;
+    d.wino_bound = wino && d.kclass == KC_IGEMM_F32;
     return ok();
 }
 
@@ -487,8 +490,11 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
     hipError_t e;
     switch (d.kclass) {
     case KC_IGEMM_F32:
-        e = launch_igemm_f32(d, a, s, use_bound && d.apack_bytes > 0 ? (const char*)d.wbound + d.wbound_pack_off
-                                                                     : nullptr);
+        if (use_bound && d.wino_bound)
+            e = launch_winograd_f32(d, a, s, (const char*)d.wbound + d.wbound_pack_off);
+        else
+            e = launch_igemm_f32(d, a, s, use_bound && d.apack_bytes > 0 ? (const char*)d.wbound + d.wbound_pack_off
+                                                                         : nullptr);
         break;
     case KC_IGEMM_BF16:
         if (use_bound) {

@@ -140,10 +140,15 @@ struct Desc {
     // fp32 implicit GEMM: bytes of the fragment-order weight image its
     // packed-weight kernel reads (0 = the configuration has none).
     int64_t apack_bytes = 0;
+    // AUTO fp32 3x3 descriptor whose bound weights run the Winograd kernel:
+    // set at bind when winograd_bound_preferred holds; the packed image is
+    // then U = G g G^T (pack_winograd_f32_weights), and calls that pass
+    // their own weights keep the implicit GEMM.
+    bool wino_bound = false;
     // Weights bound with conv2d_desc_bind_weights: an OIHW copy at wbound,
-    // followed for the bf16 implicit GEMM (and the fp32 one when apack_bytes
-    // > 0) by the packed image at wbound + wbound_pack_off (0 = no packed
-    // image).
+    // followed for the bf16 implicit GEMM, the Winograd kernel (and the fp32
+    // implicit GEMM when apack_bytes > 0) by the packed image at wbound +
+    // wbound_pack_off (0 = no packed image).
     void* wbound = nullptr;
     int64_t wbound_bytes = 0;
     int64_t wbound_pack_off = 0;
@@ -202,6 +207,9 @@ bool plan_qpw(Desc& d);
 bool plan_igemm_i8(const Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_winograd_f32(const Desc& d);
+// AUTO with bound weights: shapes where the packed-U Winograd kernel has
+// been measured faster than the fp32 implicit GEMM with packed weights.
+bool winograd_bound_preferred(const Desc& d);
 bool plan_pointwise_f32(const Desc& d);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);

@@ -138,8 +138,9 @@ def test_packed_dense_block_full_size():
     total = A.DENSE_TOTAL_CHANNELS
     descs = []
     for k, L in enumerate(wl.layers):
+        # algo "direct": AUTO would run these bound layers on Winograd
         d = cc().conv2d_desc_create(layer_params(L, in_total_channels=total, out_total_channels=total,
-                                                 out_channel_offset=L.c_in))
+                                                 out_channel_offset=L.c_in, algo="direct"))
         descs.append(d)
     outs = {}
     for bound in (False, True):

@@ -123,3 +123,44 @@ def test_winograd_bound_weights(i):
         outs.append(y.host().numpy().reshape(nn, ot, ho, wo))
     assert np.array_equal(outs[0], outs[1]), "bound weights differ from explicit weights"
     assert_close(outs[1], oracle_layer(L, x, wt, b, s), FP32_TOL, f"winograd bound case {i}")
+
+
+def test_auto_dense_block_bound_weights_use_winograd():
+    """AUTO descriptors of the dense-block layers (in a 256-channel concat
+    buffer, run in place) keep the implicit GEMM for per-call weights and
+    switch to the packed-U Winograd kernel once their weights are bound: the
+    bound chain equals the chain of algo="winograd" descriptors with bound
+    weights bit for bit, and every layer matches the oracle."""
+    t = torch()
+    wl = A.dense_block()
+    a = wl.arrays
+    total = A.DENSE_TOTAL_CHANNELS
+    outs = {}
+    for algo in ("auto", "winograd"):
+        buf = t.full((1, total, 128, 128), float("nan"), dtype=t.float32, device="cuda")
+        buf[:, :64] = to_dev(a["x"])
+        for k, L in enumerate(wl.layers):
+            d = cc().conv2d_desc_create(layer_params(L, in_total_channels=total, out_total_channels=total,
+                                                     out_channel_offset=L.c_in, algo=algo))
+            if algo == "auto":
+                assert cc().conv2d_desc_kernel_name(d) == "igemm_f32"
+            cc().conv2d_desc_bind_weights(d, to_dev(a[f"w{k}"]))
+            assert cc().conv2d_desc_kernel_name(d) == "winograd_f32", (algo, k)
+            cc().conv2d_forward(d, buf, None, None, None, buf)
+        t.cuda.synchronize()
+        outs[algo] = buf.cpu().numpy().astype(np.float64)
+    assert np.array_equal(outs["auto"], outs["winograd"]), "AUTO bound chain differs from the Winograd chain"
+    cur = a["x"]
+    for k, L in enumerate(wl.layers):
+        ref = oracle_layer(L, cur, a[f"w{k}"], None, None)
+        assert_close(outs["auto"][:, L.c_in:L.c_in + L.c_out], ref, FP32_TOL, f"dense block layer {k}")
+        cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
+
+
+def test_auto_small_bound_layer_keeps_igemm():
+    """A 3x3 layer too small to fill the GPU with Winograd workgroups keeps
+    the implicit GEMM after binding."""
+    L = A.Layer("small", 1, 64, 16, 16, 32, (3, 3), pads=(1, 1, 1, 1))
+    d = cc().conv2d_desc_create(layer_params(L))
+    cc().conv2d_desc_bind_weights(d, to_dev(np.zeros(L.w_shape, np.float32)))
+    assert cc().conv2d_desc_kernel_name(d) == "igemm_f32"
