@@ -226,10 +226,27 @@ def _torch():
 _ELEM = {DTYPE_F32: "float32", DTYPE_BF16: "bfloat16", DTYPE_I8: "int8"}
 
 
+_DTYPES = {}
+
+
+def _dtype(name):
+    dt = _DTYPES.get(name)
+    if dt is None:
+        dt = _DTYPES[name] = getattr(_torch(), name)
+    return dt
+
+
 def _ptr(t, what, dtype_name, min_numel):
     """Raw device pointer of a contiguous GPU tensor holding >= min_numel elements."""
     if t is None:
         return None
+    # Fast path: one pass over the conditions; the checked path below names
+    # the first one that fails.
+    try:
+        if t.is_cuda and t.dtype is _dtype(dtype_name) and t.numel() >= min_numel and t.is_contiguous():
+            return t.data_ptr()
+    except AttributeError:
+        pass
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what}: torch.Tensor expected")
@@ -241,25 +258,40 @@ def _ptr(t, what, dtype_name, min_numel):
         raise TypeError(f"{what}: dtype {t.dtype}, expected torch.{dtype_name}")
     if t.numel() < min_numel:
         raise ValueError(f"{what}: {t.numel()} elements, the descriptor needs {min_numel}")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
+
+
+_RAW_STREAM = None
 
 
 def _stream(stream):
+    """hipStream_t of `stream` (a torch stream or a raw handle); None = the
+    current torch stream of the current device."""
+    global _RAW_STREAM
     if stream is None:
-        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+        if _RAW_STREAM is None:
+            C = _torch()._C
+            get_raw, get_dev = getattr(C, "_cuda_getCurrentRawStream", None), getattr(C, "_cuda_getDevice", None)
+            if get_raw is not None and get_dev is not None:
+                _RAW_STREAM = lambda: get_raw(get_dev())
+            else:
+                _RAW_STREAM = lambda: _torch().cuda.current_stream().cuda_stream
+        return _RAW_STREAM()
     if isinstance(stream, int):
-        return ctypes.c_void_p(stream)
-    return ctypes.c_void_p(stream.cuda_stream)
+        return stream
+    return stream.cuda_stream
 
 
 def _sizes(desc):
-    p = desc.params
-    n, ot, ho, wo = conv2d_desc_get_output_shape(desc)
-    in_total = p.in_total_channels or p.c_in
-    x_numel = p.n * in_total * p.h * p.w
-    w_numel = p.c_out * (p.c_in // p.groups) * p.k_h * p.k_w
-    y_numel = n * ot * ho * wo
-    return x_numel, w_numel, y_numel
+    """(x, w, y) element counts a call on desc reads and writes (cached: a
+    descriptor's shapes never change)."""
+    sz = desc.__dict__.get("_sz")
+    if sz is None:
+        p = desc.params
+        n, ot, ho, wo = conv2d_desc_get_output_shape(desc)
+        in_total = p.in_total_channels or p.c_in
+        sz = desc._sz = (p.n * in_total * p.h * p.w, p.c_out * (p.c_in // p.groups) * p.k_h * p.k_w, n * ot * ho * wo)
+    return sz
 
 
 def conv2d_desc_bind_weights(desc: Desc, w, stream=None) -> None:
