@@ -12,17 +12,18 @@ not from the 256 MB last-level cache.
 
 The JSON line also carries:
   roofline      the dominant kernel of the step against the fp32 MFMA peak;
-                its duration comes from HIP events recorded around every launch
-                on the launch stream, in a pass over the same number of steps
-                queued behind a GPU delay (launches back to back, so no host
-                launch time inside an event pair)
+                its duration comes from HIP events on the launch stream around
+                a run of back-to-back launches of each layer, queued behind a
+                GPU delay (so no host launch time inside the run; the mean
+                per launch is the kernel plus the dispatch gap between
+                kernels)
   cpu_baseline  the float64 CPU oracle timed on this host's cores on a sample
                 of the same workload's outputs
   per_config    the other synthetic workloads (single conv, inverted
                 bottleneck fused/unfused, mixed sweep fp32/bf16, int8 chain
                 unfused/fused, int8 bottleneck fused/unfused, int8 dense
                 layers, dense-block layers with Winograd beside the implicit
-                GEMM), each layer timed with events the same way, with its
+                GEMM), each layer timed in such a run the same way, with its
                 binding roofline; HBM-bound entries also carry the time of the
                 library's streaming 16-byte copy moving the same bytes
                 (copy_us) and their speed as a fraction of it (copy_frac)
@@ -147,31 +148,28 @@ class EventTimer:
         return float(np.mean(ts)), float(np.median(ts)), len(ts)
 
 
-class BoundaryTimer:
-    """HIP events on the launch stream at the boundaries between consecutive
-    launches of a step: one event before the first launch and one after each
-    launch.  A launch's time is the span between its two neighbouring events,
-    so the spans of a step add up to the step's own event span and nothing is
-    counted twice or left out."""
-
-    def __init__(self):
-        self.steps = []
-        self.cur = []
-
-    def mark(self):
-        torch = torch_mod()
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.cur.append(e)
-
-    def end_step(self):
-        self.steps.append(self.cur)
-        self.cur = []
-
-    def spans_us(self):
-        """[step][launch] spans in microseconds."""
-        torch_mod().cuda.synchronize()
-        return [[ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(len(ev) - 1)] for ev in self.steps]
+def run_time_us(fns, reps, delay_per_launch_us=200.0):
+    """Mean HIP-event time of one launch in a run of `reps` back-to-back
+    launches (fns[i % len(fns)] for launch i): two events on the launch
+    stream around the whole run, queued behind a GPU delay so that the host
+    has enqueued every launch before the first one starts.  The mean is the
+    kernel's duration plus the dispatch gap between consecutive kernels; an
+    event between every pair of launches would add its own GPU-side cost to
+    each launch."""
+    torch = torch_mod()
+    delay = delay_per_launch_us * reps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_delay(delay)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    t_enq = (time.perf_counter() - t0) * 1e6
+    torch.cuda.synchronize()
+    if t_enq > delay:
+        log(f"host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
+    return e0.elapsed_time(e1) * 1e3 / reps
 
 
 def roofline_entry(flops, bytes_, t_us, dtype, bound=None):
@@ -227,20 +225,17 @@ class DenseBlock:
         self.bytes = [4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w) for L in self.layers]
         self.i = 0
 
-    def step(self, timer=None):
-        """One pass of the chain.  timer: a BoundaryTimer that records an event
-        before the first launch and after every launch, so layer k's time is
-        the span between the events on either side of it."""
+    def step(self):
+        """One pass of the chain."""
         buf = self.bufs[self.i % self.nsets]
         self.i += 1
-        if timer is not None:
-            timer.mark()
-        for k, (d, w) in enumerate(zip(self.descs, self.w)):
+        for d, w in zip(self.descs, self.w):
             self.cc.conv2d_forward(d, buf, w, None, None, buf)
-            if timer is not None:
-                timer.mark()
-        if timer is not None:
-            timer.end_step()
+
+    def layer_fns(self, k):
+        """Launches of layer k alone, one per buffer set."""
+        d, w = self.descs[k], self.w[k]
+        return [lambda b=b: self.cc.conv2d_forward(d, b, w, None, None, b) for b in self.bufs]
 
 
 def bench_dense_block(steps, warmup, bound=True):
@@ -256,22 +251,13 @@ def bench_dense_block(steps, warmup, bound=True):
         db.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Event pass over the same number of steps: events at the launch
-    # boundaries, queued behind a GPU delay so that the launches run back to
-    # back as in the wall-clock pass.
-    timer = BoundaryTimer()
-    torch.cuda.synchronize()
-    delay = 300.0 * steps
-    gpu_delay(delay)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        db.step(timer)
-    t_enq = (time.perf_counter() - t0) * 1e6
-    torch.cuda.synchronize()
-    if t_enq > delay:
-        log(f"dense block: host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
-    spans = np.array(timer.spans_us())
-    per = [(float(spans[:, k].mean()), float(np.median(spans[:, k])), spans.shape[0]) for k in range(len(db.layers))]
+    # Per-layer times: each layer in a run of back-to-back launches of its
+    # own (inputs from the passes above), events around the run.
+    reps = max(steps, 20)
+    per = []
+    for k in range(len(db.layers)):
+        t = run_time_us(db.layer_fns(k), reps)
+        per.append((t, t, reps))
     return db, wall, per
 
 
@@ -338,25 +324,13 @@ def _rotating(make, footprint, target=ROTATE_BYTES, cap=64):
 
 def time_layer(key, fn_sets, reps, warm=3):
     """Mean HIP-event time of one launch.  fn_sets: list of callables (one per
-    rotating buffer set); the timed launches are queued back to back behind a
-    GPU delay, with events at the boundaries between them (BoundaryTimer)."""
+    rotating buffer set); the timed launches run back to back behind a GPU
+    delay with events around the whole run (run_time_us)."""
     torch = torch_mod()
     for i in range(warm):
         fn_sets[i % len(fn_sets)]()
     torch.cuda.synchronize()
-    timer = BoundaryTimer()
-    delay = 200.0 * reps
-    gpu_delay(delay)
-    t0 = time.perf_counter()
-    timer.mark()
-    for i in range(reps):
-        fn_sets[i % len(fn_sets)]()
-        timer.mark()
-    timer.end_step()
-    t_enq = (time.perf_counter() - t0) * 1e6
-    if t_enq > delay:
-        log(f"{key}: host enqueue {t_enq:.0f} us outran the {delay:.0f} us GPU delay")
-    return float(np.mean(timer.spans_us()[0]))
+    return run_time_us(fn_sets, reps)
 
 
 def float_layer_fns(L, x, w, b, s, dtype, reps, bound=False):
