@@ -100,9 +100,14 @@ typedef enum {
 /* Convolution attributes.  Fill with conv2d_params_init() and then set what
  * differs from the defaults.  Pads are ONNX order (top, left, bottom, right);
  * ncnn's chained defaults (pad_top = pad_left, ...) are the caller's job. */
-/* Algorithm of a float convolution.  AUTO lets the library choose (the
- * direct tiled classes unless Winograd is measured faster for the shape);
- * DIRECT never uses Winograd; WINOGRAD requests the F(2x2, 3x3) minimal
+/* Algorithm of a float convolution.  AUTO lets the library choose: the
+ * direct tiled classes, except that binding weights to an F32 3x3 stride-1
+ * dilation-1 single-group descriptor with >= 32 input channels, <= 64 output
+ * channels and a grid of >= 256 Winograd workgroups (2 x 8 output tiles of
+ * 2 x 2 pixels x 32 output channels each) switches its calls with bound
+ * weights to Winograd, measured faster there (calls passing their own
+ * weights keep the implicit GEMM); DIRECT never uses Winograd; WINOGRAD
+ * requests the F(2x2, 3x3) minimal
  * filtering algorithm (Lavin and Gray, CVPR 2016) for the "Winograd cells"
  * the Go package doc "ops" names among its conv fan-out sites (section
  * WorkerPool): F32 only, 3x3 window, stride 1, dilation 1, one group, any
@@ -177,7 +182,12 @@ CONV2D_API const char* conv2d_desc_kernel_name(conv2d_desc_t d);
  * bound weights read straight into registers (calls whose input is not
  * 16-byte aligned read the OIHW copy).  The results are those of the OIHW
  * kernel bit for bit for up to 32 output channels per group; with more, the
- * packed kernel sums the input channels in another order (same tolerance).  Forward calls
+ * packed kernel sums the input channels in another order (same tolerance).
+ * For a WINOGRAD descriptor, and for an AUTO one in the Winograd regime
+ * (conv_algo_t), it computes the filter transform U = G g G^T once and packs
+ * it in the Winograd kernel's operand order instead; bound-weight calls then
+ * run that kernel (bitwise equal to the WINOGRAD descriptor's per-call
+ * weights) and conv2d_desc_kernel_name reports "winograd_f32".  Forward calls
  * (conv2d_forward, fused_pw_dw_forward, qconv2d_forward) use the bound copy
  * when their weight pointer is null.  The copy and the re-layout are queued
  * on `stream` (hipStream_t, null = default stream): forward calls on the same
