@@ -50,6 +50,7 @@ const char* kernel_name(const Desc& d) {
     case KC_WINOGRAD_F32: return "winograd_f32";
     case KC_PW_F32: return "pointwise_f32";
     case KC_IGEMM_I8: return "igemm_i8";
+    case KC_SMALL_F32: return "small_f32";
     }
     return "?";
 }
@@ -356,6 +357,9 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
     } else if (depthwise) {
         d->kclass = KC_DW;
         planned = plan_dw(*d);
+    } else if (p.algo == CONV_ALGO_AUTO && plan_small_f32(*d)) {
+        d->kclass = KC_SMALL_F32;
+        planned = true;
     } else if (plan_grouped(*d)) {
         d->kclass = KC_GROUPED;
         planned = true;
@@ -525,6 +529,7 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
     case KC_PW_F32:
         e = pointwise_f32_fits(d, a) ? launch_pointwise_f32(d, a, s) : launch_igemm_f32(d, a, s);
         break;
+    case KC_SMALL_F32: e = launch_small_f32(d, a, s); break;
     default: e = launch_direct(d, a, s); break;
     }
     return hip_status(e, kernel_name(d));

@@ -23,6 +23,7 @@ enum KernelClass : int32_t {
     KC_WINOGRAD_F32 = 7, // Winograd F(2x2, 3x3), fp32 MFMA (3x3, stride 1, dilation 1, one group)
     KC_PW_F32 = 8,       // pointwise 1x1 with K <= 256, fp32 MFMA, every output channel per workgroup
     KC_IGEMM_I8 = 9,     // int8 dense / grouped implicit GEMM, i8 MFMA
+    KC_SMALL_F32 = 10,   // small fp32 3x3 layers on the vector units, one thread per output pixel
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -207,6 +208,9 @@ bool plan_qpw(Desc& d);
 bool plan_igemm_i8(const Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_winograd_f32(const Desc& d);
+// Small fp32 3x3 layers (AUTO only): see small_f32.hip.
+bool plan_small_f32(const Desc& d);
+hipError_t launch_small_f32(const Desc& d, ConvArgs a, hipStream_t s);
 // AUTO with bound weights: shapes where the packed-U Winograd kernel has
 // been measured faster than the fp32 implicit GEMM with packed weights.
 bool winograd_bound_preferred(const Desc& d);

@@ -101,12 +101,16 @@ typedef enum {
  * differs from the defaults.  Pads are ONNX order (top, left, bottom, right);
  * ncnn's chained defaults (pad_top = pad_left, ...) are the caller's job. */
 /* Algorithm of a float convolution.  AUTO lets the library choose: the
- * direct tiled classes, except that binding weights to an F32 3x3 stride-1
+ * direct tiled classes; for an F32 3x3 single-group layer with at most 64
+ * input channels and at most 64K output elements, a vector-unit kernel with
+ * one short chain per output pixel (conv2d_desc_kernel_name "small_f32");
+ * and, binding weights to an F32 3x3 stride-1
  * dilation-1 single-group descriptor with >= 32 input channels, <= 64 output
  * channels and a grid of >= 256 Winograd workgroups (2 x 8 output tiles of
  * 2 x 2 pixels x 32 output channels each) switches its calls with bound
  * weights to Winograd, measured faster there (calls passing their own
- * weights keep the implicit GEMM); DIRECT never uses Winograd; WINOGRAD
+ * weights keep the implicit GEMM); DIRECT uses only the tiled classes (no
+ * Winograd, no small-layer kernel); WINOGRAD
  * requests the F(2x2, 3x3) minimal
  * filtering algorithm (Lavin and Gray, CVPR 2016) for the "Winograd cells"
  * the Go package doc "ops" names among its conv fan-out sites (section

@@ -100,7 +100,8 @@ def oracle_layer(L: workloads.Layer, x, w, b, s, pad_value=None):
                          slope=s if L.act == workloads.ACT_PRELU else None)
 
 
-def gpu_layer(L: workloads.Layer, x, w, b, s, *, dtype="f32", out_total=None, out_off=0, repeat=1, bound=False):
+def gpu_layer(L: workloads.Layer, x, w, b, s, *, dtype="f32", out_total=None, out_off=0, repeat=1, bound=False,
+              algo="auto"):
     """Run one float layer on the GPU into a NaN-guarded output; returns
     (host output as float64 [n, out_total, ho, wo], kernel name, all runs).
     bound: bind the weights to the descriptor and call with w=None."""
@@ -108,7 +109,7 @@ def gpu_layer(L: workloads.Layer, x, w, b, s, *, dtype="f32", out_total=None, ou
     t = torch()
     tdt = t.float32 if dtype == "f32" else t.bfloat16
     p = layer_params(L, dtype, prelu_slope_count=(s.size if L.act == workloads.ACT_PRELU else 1),
-                     out_total_channels=out_total or 0, out_channel_offset=out_off)
+                     out_total_channels=out_total or 0, out_channel_offset=out_off, algo=algo)
     d = cc.conv2d_desc_create(p)
     n, ot, ho, wo = cc.conv2d_desc_get_output_shape(d)
     xd = to_dev(x.astype(np.float32), tdt)

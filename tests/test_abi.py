@@ -163,6 +163,16 @@ def test_kernel_choice_for_the_workloads():
         d = cc().conv2d_desc_create(cc().make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride,
                                                      pads=L.pads, dilation=L.dilation, groups=L.groups, dtype="i8"))
         assert cc().conv2d_desc_kernel_name(d) == "igemm_i8", L.name
+    # the single conv: the small-layer kernel under AUTO, the implicit GEMM under DIRECT
+    L = workloads.single_conv().layers[0]
+    for algo, want in (("auto", "small_f32"), ("direct", "igemm_f32")):
+        d = cc().conv2d_desc_create(cc().make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, pads=L.pads, has_bias=True,
+                                                     algo=algo))
+        assert cc().conv2d_desc_kernel_name(d) == want, algo
+    # just past the small-layer limits: 65 input channels, or more than 64K outputs
+    for ci, hw in ((65, 32), (16, 46)):
+        d = cc().conv2d_desc_create(cc().make_params(1, ci, hw, hw, 32, (3, 3), pads=1))
+        assert cc().conv2d_desc_kernel_name(d) == "igemm_f32", (ci, hw)
 
 
 def _raw(fn, *args):

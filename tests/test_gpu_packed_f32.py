@@ -13,7 +13,9 @@ configurations (<= 16, <= 32, <= 64 output channels per tile), partial
 input-channel chunks and output-channel tiles, padding with a pad value,
 dilation, groups, batch > 1, concat slices on both sides, the layouts that
 fall back to the OIHW kernel (width not a multiple of 4, input not 16-byte
-aligned), rebinding, and the dense-block chain at full size."""
+aligned), rebinding, and the dense-block chain at full size.  Descriptors
+ask for the tiled classes (algo "direct"): under AUTO the small 3x3 layers
+here would run the small-layer kernel and bound dense-block layers Winograd."""
 import numpy as np
 import pytest
 
@@ -79,7 +81,7 @@ def test_packed_equals_explicit(i):
     rng = np.random.default_rng(3100 + i)
     x, w, b, s = A.layer_arrays(rng, L)
     _, w2, _, _ = A.layer_arrays(rng, L)
-    d = cc().conv2d_desc_create(layer_params(L, prelu_slope_count=s.size))
+    d = cc().conv2d_desc_create(layer_params(L, prelu_slope_count=s.size, algo="direct"))
     kname = cc().conv2d_desc_kernel_name(d)
     print(f"case {i}: {L} ({kname})", flush=True)
     xd, wd, w2d = to_dev(x), to_dev(w), to_dev(w2)
@@ -110,7 +112,7 @@ def test_packed_concat_slices_and_unaligned_input():
     ref = oracle_layer(L, x, w, b, s)
     big = rng.standard_normal((L.n, L.c_in + 9, L.h, L.w)).astype(np.float32)
     big[:, 5:5 + L.c_in] = x
-    d = cc().conv2d_desc_create(layer_params(L, in_total_channels=L.c_in + 9, in_channel_offset=5,
+    d = cc().conv2d_desc_create(layer_params(L, algo="direct", in_total_channels=L.c_in + 9, in_channel_offset=5,
                                              out_total_channels=L.c_out + 6, out_channel_offset=3))
     assert cc().conv2d_desc_kernel_name(d) == "igemm_f32"
     cc().conv2d_desc_bind_weights(d, to_dev(w))

@@ -24,15 +24,80 @@ def cc():
 
 # --------------------------------------------------------- single conv ----
 
-def test_single_conv_config():
+@pytest.mark.parametrize("algo,kernel", [("auto", "small_f32"), ("direct", "igemm_f32")])
+def test_single_conv_config(algo, kernel):
     wl = workloads.single_conv()
     L = wl.layers[0]
     a = wl.arrays
-    y, kname, runs = gpu_layer(L, a["x"], a["w"], a["b"], None, repeat=2)
+    y, kname, runs = gpu_layer(L, a["x"], a["w"], a["b"], None, repeat=2, algo=algo)
     ref = oracle_layer(L, a["x"], a["w"], a["b"], None)
-    assert kname.startswith("igemm_f32")
+    assert kname == kernel
     assert_close(y, ref, FP32_TOL, "single conv")
     assert_bitexact(runs[1], runs[0], "repeat")
+
+
+# small fp32 3x3 layers (the vector-unit kernel): one, two and four output
+# channels per thread (by grid size), pads 0-2 and asymmetric, stride 2,
+# dilation 2, pad values, every activation, N > 1, ragged pixel counts, and
+# output-channel counts that are not multiples of the per-thread count.
+SMALL_CASES = [
+    # n, c_in, h, w, c_out, stride, pads (t, l, b, r), dilation, act, pad_value
+    (1, 16, 32, 32, 32, 1, (1, 1, 1, 1), 1, workloads.ACT_RELU, 0.0),
+    (2, 3, 17, 23, 5, 1, (0, 0, 0, 0), 1, workloads.ACT_NONE, 0.0),
+    (1, 64, 9, 11, 7, 2, (1, 0, 2, 1), 1, workloads.ACT_LEAKY_RELU, -0.5),
+    (3, 8, 20, 14, 9, 1, (2, 2, 2, 2), 2, workloads.ACT_PRELU, 0.25),
+    (1, 33, 40, 40, 40, 1, (1, 1, 1, 1), 1, workloads.ACT_CLIP, 1.0),      # 64000 outputs: 4 per thread
+    (4, 16, 16, 16, 60, 1, (1, 1, 1, 1), 1, workloads.ACT_RELU, 0.0),      # 61440 outputs, c_out % 4 = 0
+    (1, 5, 3, 3, 3, 1, (1, 1, 1, 1), 1, workloads.ACT_NONE, -1.0),         # image smaller than a wave
+    (2, 12, 31, 29, 34, 2, (0, 1, 1, 0), 2, workloads.ACT_LEAKY_RELU, 0.0),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL_CASES)))
+def test_small_f32_cases(i):
+    n, ci, h, w, co, st, p4, dil, act, pv = SMALL_CASES[i]
+    L = workloads.Layer("small", n, ci, h, w, co, (3, 3), stride=(st, st), pads=p4, dilation=(dil, dil),
+                        has_bias=True, act=act, alpha=0.1, clip=(-0.5, 0.75), pad_value=pv)
+    rng = np.random.default_rng(4100 + i)
+    x, wt, b, sl = workloads.layer_arrays(rng, L)
+    print(f"case {i} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, wt, b, sl, repeat=2)
+    assert kname == "small_f32"
+    assert_close(y, oracle_layer(L, x, wt, b, sl), FP32_TOL, f"small case {i}")
+    assert_bitexact(runs[1], runs[0], "repeat")
+
+
+def test_small_f32_slices_unaligned_and_bound():
+    """Input channels [2, 2 + c_in) of a wider buffer that starts one float
+    past a 16-byte boundary, output into channels [3, 3 + c_out) of a wider
+    one; then the same layer with bound weights (bitwise equal)."""
+    t = torch()
+    L = workloads.Layer("small", 2, 10, 13, 19, 12, (3, 3), pads=(1, 1, 1, 1), has_bias=True, act=workloads.ACT_RELU)
+    rng = np.random.default_rng(4199)
+    x, wt, b, _ = workloads.layer_arrays(rng, L)
+    ref = oracle_layer(L, x, wt, b, None)
+    big = rng.standard_normal((L.n, L.c_in + 5, L.h, L.w)).astype(np.float32)
+    big[:, 2:2 + L.c_in] = x
+    raw = t.zeros(big.size + 1, dtype=t.float32, device="cuda")
+    xv = raw[1:1 + big.size]
+    xv.copy_(t.from_numpy(big.reshape(-1)).cuda())
+    d = cc().conv2d_desc_create(layer_params(L, in_total_channels=L.c_in + 5, in_channel_offset=2,
+                                             out_total_channels=L.c_out + 4, out_channel_offset=3))
+    assert cc().conv2d_desc_kernel_name(d) == "small_f32"
+    n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
+    outs = []
+    for bound in (False, True):
+        y = Guarded(n * ot * ho * wo, t.float32, float("nan"))
+        if bound:
+            cc().conv2d_desc_bind_weights(d, to_dev(wt))
+        cc().conv2d_forward(d, xv, None if bound else to_dev(wt), to_dev(b), None, y.view)
+        t.cuda.synchronize()
+        y.check_guards()
+        got = y.host().numpy().reshape(n, ot, ho, wo)
+        assert np.isnan(got[:, :3]).all() and np.isnan(got[:, 3 + L.c_out:]).all()
+        outs.append(got[:, 3:3 + L.c_out])
+    assert_close(outs[0], ref, FP32_TOL, "small slices")
+    assert_bitexact(outs[1], outs[0], "bound weights")
 
 
 # ---------------------------------------------------- random fp32 sweep ----
@@ -87,7 +152,8 @@ CLASS_CASES = [
 
 @pytest.mark.parametrize("i", range(len(CLASS_CASES)))
 @pytest.mark.parametrize("pad_value", [0.0, -0.75])
-def test_kernel_classes_fp32(i, pad_value):
+@pytest.mark.parametrize("algo", ["auto", "direct"])
+def test_kernel_classes_fp32(i, pad_value, algo):
     n, ci, h, w, co, k, s, p, d, g, act = CLASS_CASES[i]
     k2 = k if isinstance(k, tuple) else (k, k)
     s2 = s if isinstance(s, tuple) else (s, s)
@@ -97,8 +163,10 @@ def test_kernel_classes_fp32(i, pad_value):
                         has_bias=True, act=act, alpha=0.1, clip=(-0.5, 0.75), pad_value=pad_value)
     rng = np.random.default_rng(77 + i)
     x, wt, b, sl = workloads.layer_arrays(rng, L)
-    print(f"case {i} {L}", flush=True)
-    y, kname, runs = gpu_layer(L, x, wt, b, sl, repeat=2)
+    print(f"case {i} {algo} {L}", flush=True)
+    y, kname, runs = gpu_layer(L, x, wt, b, sl, repeat=2, algo=algo)
+    if algo == "direct":
+        assert kname != "small_f32"
     ref = oracle_layer(L, x, wt, b, sl)
     assert_close(y, ref, FP32_TOL, f"case {i} ({kname})")
     assert_bitexact(runs[1], runs[0], "repeat")

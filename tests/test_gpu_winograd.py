@@ -157,10 +157,12 @@ def test_auto_dense_block_bound_weights_use_winograd():
         cur = np.concatenate([cur, ref.astype(np.float32)], axis=1)
 
 
-def test_auto_small_bound_layer_keeps_igemm():
+@pytest.mark.parametrize("algo,kernel", [("auto", "small_f32"), ("direct", "igemm_f32")])
+def test_auto_small_bound_layer_keeps_its_kernel(algo, kernel):
     """A 3x3 layer too small to fill the GPU with Winograd workgroups keeps
-    the implicit GEMM after binding."""
+    its kernel after binding."""
     L = A.Layer("small", 1, 64, 16, 16, 32, (3, 3), pads=(1, 1, 1, 1))
-    d = cc().conv2d_desc_create(layer_params(L))
+    d = cc().conv2d_desc_create(layer_params(L, algo=algo))
+    assert cc().conv2d_desc_kernel_name(d) == kernel
     cc().conv2d_desc_bind_weights(d, to_dev(np.zeros(L.w_shape, np.float32)))
-    assert cc().conv2d_desc_kernel_name(d) == "igemm_f32"
+    assert cc().conv2d_desc_kernel_name(d) == kernel
