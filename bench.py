@@ -437,17 +437,15 @@ def per_config(reps, only="all"):
             a = wl.arrays
             args = (L, a[f"x_{name}"], a[f"w_{name}"], a[f"b_{name}"], a[f"s_{name}"], dtype, reps)
             es = 4 if dtype == "f32" else 2
-            if dtype == "bf16":
-                # The bf16 implicit GEMM re-lays the weights for its kernel: once
-                # at bind time (the timed figure), or on every call when the
-                # weights are passed to forward (reported beside it).
-                t, k = float_layer_fns(*args, bound=True)
-                t_call, _ = float_layer_fns(*args)
-                res[name] = dict(roofline_entry(L.flops, layer_bytes(L, es), t, dtype), kernel=k,
-                                 weights="bound", us_weights_per_call=round(t_call, 3))
-            else:
-                t, k = float_layer_fns(*args)
-                res[name] = dict(roofline_entry(L.flops, layer_bytes(L, es), t, dtype), kernel=k)
+            # Weights bound at set-up (the timed figure), as a layer's weights
+            # are transformed once when it is created: the bf16 implicit GEMM
+            # re-lays them into its per-chunk LDS image, the fp32 one packs the
+            # 3x3 tiles it can read from registers.  Passing them on every call
+            # is reported beside it.
+            t, k = float_layer_fns(*args, bound=True)
+            t_call, _ = float_layer_fns(*args)
+            res[name] = dict(roofline_entry(L.flops, layer_bytes(L, es), t, dtype), kernel=k,
+                             weights="bound", us_weights_per_call=round(t_call, 3))
             log("mixed", dtype, name, res[name])
         out[f"mixed_sweep_{dtype}"] = res
 

@@ -59,6 +59,22 @@ struct FusedArgs {
 
 // NJ: 16-pixel pointwise fragments per wave (register budget: 4 keeps two
 // workgroups per compute unit).
+// 4 bytes per lane from global memory straight into LDS (global_load_lds_dword):
+// lane l reads src (its own address) and writes lds_base + 4*l, lds_base
+// wave-uniform; completion is counted by vmcnt like any load.  Inline
+// assembly, so the compiler does not hold later LDS accesses behind it; the
+// kernel orders it (every wave waits for all of its loads before its first
+// LDS write of the chunk, and a barrier follows).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy4_to_lds(const float* src, const float* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m) : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
 template <int KH, int KW, int NJ>
 __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
     extern __shared__ __align__(16) float lds[];
@@ -101,6 +117,22 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
 
     // ---- 1. pointwise on the matrix cores ----
     for (int k0 = 0; k0 < P.c_in; k0 += KC) {
+        // The chunk's CE x KC weights go straight to LDS first, so their round
+        // trip overlaps the input rows': slot s of ws is (k = s / CEP,
+        // ce = s % CEP).  Columns past CE, channels past the layer's and
+        // inputs past its channels read a valid weight: those columns are
+        // never read, those channels' results are discarded, and those
+        // inputs are zero in xs.
+#pragma unroll
+        for (int k = 0; k < (KC * CEP / 64 + kWaves - 1) / kWaves; ++k) {
+            const int r = wave + kWaves * k;
+            if (r < KC * CEP / 64) {
+                const int sl = 64 * r + lane;
+                const int kc = sl / CEP, ce = sl - (sl / CEP) * CEP;
+                const int cew = min(ce, ce_valid - 1);
+                copy4_to_lds(wpw + (int64_t)(ce0 + cew) * P.c_in + min(k0 + kc, P.c_in - 1), ws + 64 * r);
+            }
+        }
         if (f.vec) {
             // Units of four pixels: (channel, row, column group); all loads first.
             const int w4 = W >> 2;
@@ -139,13 +171,7 @@ __global__ __launch_bounds__(kThreads) void fused_pw_dw_kernel(FusedArgs f) {
                 xs[kc * XS + p] = v;
             }
         }
-        for (int e = tid; e < KC * CE; e += kThreads) {
-            const int ce = e % CE;
-            const int kc = e / CE;
-            float v = 0.0f;
-            if (ce < ce_valid && k0 + kc < P.c_in) v = wpw[(int64_t)(ce0 + ce) * P.c_in + k0 + kc];
-            ws[kc * CEP + ce] = v;
-        }
+        __builtin_amdgcn_s_waitcnt(0x3f70);           // vmcnt(0): this wave's weight copies have landed
         __syncthreads();
         // A lane reads weight row ce = lane%16 (+16) at k = lane/16; B lane reads
         // input plane k = lane/16 at pixel 16*frag + lane%16.
