@@ -12,10 +12,12 @@
 //   1. the 64-pixel input tile (K rows) and the whole weight matrix
 //      (Cout x K) are copied into LDS once, all 16-byte loads issued before
 //      the first LDS write;
-//   2. for each block of 32 output channels, wave w multiplies pixel
-//      fragment w (16 pixels) with the block on the fp32 matrix cores
+//   2. eight waves: wave w multiplies pixel fragment w % 4 (16 pixels) with
+//      every other block of 32 output channels on the fp32 matrix cores
 //      (v_mfma_f32_16x16x4f32, pixels as the first operand, so a lane ends
-//      up holding 4 consecutive pixels of one output channel);
+//      up holding 4 consecutive pixels of one output channel); the pixel
+//      operands are read from LDS once, a block's weight operands before its
+//      first MFMA;
 //   3. bias + activation, one 16-byte store per lane and channel
 //      (ConcatFusedTail offsets included).
 #include "device_common.h"
@@ -24,7 +26,7 @@ namespace conv2d {
 
 namespace {
 
-constexpr int kT = 256;
+constexpr int kT = 512;          // 8 waves: 4 pixel fragments x 2 halves of the channel blocks
 constexpr int PT = 64;           // pixels per workgroup
 constexpr int XS = PT + 16;      // LDS row stride of the input tile (= 16 mod 32)
 constexpr int KMAX = 64;
@@ -91,27 +93,33 @@ __global__ __launch_bounds__(kT) void pointwise_f32_kernel(ConvArgs a, int ws) {
     __syncthreads();
 
     // ---- 2./3. per 32-channel block: MFMAs, bias + activation, store ----
+    // Wave w multiplies pixel fragment w % 4 with every other 32-channel
+    // block (those of parity w / 4).  Its pixel operands are the same for
+    // every block and are read once; a block's weight operands are all read
+    // before its first MFMA.
     const int kq = lane >> 4, l16 = lane & 15;
-    const int px = p0 + wave * 16 + 4 * kq;             // this lane's 4 output pixels
+    const int frag = wave & 3, half = wave >> 2;
+    const int px = p0 + frag * 16 + 4 * kq;             // this lane's 4 output pixels
     float* __restrict__ yg = (float*)a.yptr;
     const int64_t ybase = ((int64_t)n * a.out_total + a.out_off) * HW;
-    for (int cb = 0; cb < M; cb += 32) {
+    const int ksteps = K4 >> 2;
+    float xa[KMAX / 4];
+#pragma unroll
+    for (int s = 0; s < KMAX / 4; ++s) xa[s] = s < ksteps ? xs[(4 * s + kq) * XS + frag * 16 + l16] : 0.0f;
+    for (int cb = 32 * half; cb < M; cb += 64) {
         f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
         const int co_a = cb + l16, co_b = cb + 16 + l16;
         const float* wa = wsm + min(co_a, M - 1) * ws;
         const float* wb = wsm + min(co_b, M - 1) * ws;
-        for (int k0 = 0; k0 < K4; k0 += 16) {
-            float xa[4], fa[4], fb[4];
+        float fa[KMAX / 4], fb[KMAX / 4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = k0 + 4 * s + kq;
-                const bool kin = k < K4;
-                xa[s] = kin ? xs[k * XS + wave * 16 + l16] : 0.0f;
-                fa[s] = kin ? wa[k] : 0.0f;
-                fb[s] = kin ? wb[k] : 0.0f;
-            }
+        for (int s = 0; s < KMAX / 4; ++s) {
+            fa[s] = s < ksteps ? wa[4 * s + kq] : 0.0f;
+            fb[s] = s < ksteps ? wb[4 * s + kq] : 0.0f;
+        }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < KMAX / 4; ++s) {
+            if (s < ksteps) {
                 acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], fa[s], acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[s], fb[s], acc[1], 0, 0, 0);
             }
