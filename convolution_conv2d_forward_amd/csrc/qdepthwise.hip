@@ -3,7 +3,8 @@
 // dot-product unit.
 //
 //   * A workgroup owns P whole (n, c) planes.  They are staged in LDS one at
-//     a time as int8 (not widened), one 16-byte chunk per global load, through
+//     a time as int8 (not widened), one 16-byte chunk per global load (8-byte
+//     chunks for widths that are multiples of 8 but not of 16), through
 //     two buffers so that plane p+1's copy runs under plane p's outputs:
 //     chunks inside the image are copied, the margins and the rows outside it
 //     are the zero point (0), so no tap needs a bounds check.
@@ -65,10 +66,20 @@ __device__ __forceinline__ uint32_t rq_clamped(int32_t acc, float comp, float lo
     return (uint32_t)(uint8_t)(int8_t)((int)r + y_zp);
 }
 
-// NQ: 16-byte chunks per thread and plane (4, 8 or 16; the chunks of the next
-// plane stay in registers while the current one is computed).
-template <int SS, int OFF, int RND, int NQ>
+// NQ: copy chunks per thread and plane (4, 8 or 16; the chunks of the next
+// plane stay in registers while the current one is computed).  CB: bytes per
+// copy chunk, 16, or 8 for images whose width is a multiple of 8 but not of
+// 16 (their rows start 8-byte aligned).
+template <int CB>
+struct QChunk;
+template <>
+struct QChunk<16> { using T = uint4; static __device__ T zero() { return make_uint4(0, 0, 0, 0); } };
+template <>
+struct QChunk<8> { using T = uint2; static __device__ T zero() { return make_uint2(0, 0); } };
+
+template <int SS, int OFF, int RND, int NQ, int CB>
 __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row_bytes, int P) {
+    using CT = typename QChunk<CB>::T;
     extern __shared__ __align__(16) uint8_t lds8[];
     const int plane_bytes = rows * row_bytes;
     int32_t* wpk = (int32_t*)(lds8 + 2 * plane_bytes);     // [P][3] packed filter rows
@@ -86,20 +97,20 @@ __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row
     // written to the other buffer after them, so their latency runs under
     // the arithmetic.  Chunks inside the image are copied; the margins and
     // the rows outside it are the zero point (0), so no tap needs a bounds check.
-    const int cpr = row_bytes / 16;                        // chunks per LDS row
+    const int cpr = row_bytes / CB;                        // chunks per LDS row
     const int nchunks = rows * cpr;                        // chunks per plane (<= NQ * kQT)
-    uint4 buf[NQ];
+    CT buf[NQ];
     auto load_plane = [&](int p) __attribute__((always_inline)) {
         const int8_t* __restrict__ xq = xp + p * HW;
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int e = threadIdx.x + i * kQT;
-            buf[i] = make_uint4(0, 0, 0, 0);
+            buf[i] = QChunk<CB>::zero();
             if (e < nchunks) {
                 const int r = e / cpr, j = e - r * cpr;
-                const int ih = r - a.pad_top, iw = 16 * j - kMarg;
+                const int ih = r - a.pad_top, iw = CB * j - kMarg;
                 if ((unsigned)ih < (unsigned)a.h && iw >= 0 && iw < a.w)
-                    buf[i] = *(const uint4*)(xq + (int64_t)ih * a.w + iw);
+                    buf[i] = *(const CT*)(xq + (int64_t)ih * a.w + iw);
             }
         }
     };
@@ -107,7 +118,7 @@ __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int e = threadIdx.x + i * kQT;
-            if (e < nchunks) *(uint4*)(dst + e * 16) = buf[i];
+            if (e < nchunks) *(CT*)(dst + e * CB) = buf[i];
         }
     };
     load_plane(0);
@@ -180,28 +191,34 @@ __global__ __launch_bounds__(kQT) void qdw3_kernel(ConvArgs a, int rows, int row
 }
 
 // Byte offset of output 0's first tap inside dword q0: (kMarg - pad_left) & 3.
-template <int SS, int RND, int NQ>
+template <int SS, int RND, int NQ, int CB>
 const void* pick_off(int off) {
     switch (off) {
-    case 0: return (const void*)qdw3_kernel<SS, 0, RND, NQ>;
-    case 1: return (const void*)qdw3_kernel<SS, 1, RND, NQ>;
-    case 2: return (const void*)qdw3_kernel<SS, 2, RND, NQ>;
-    default: return (const void*)qdw3_kernel<SS, 3, RND, NQ>;
+    case 0: return (const void*)qdw3_kernel<SS, 0, RND, NQ, CB>;
+    case 1: return (const void*)qdw3_kernel<SS, 1, RND, NQ, CB>;
+    case 2: return (const void*)qdw3_kernel<SS, 2, RND, NQ, CB>;
+    default: return (const void*)qdw3_kernel<SS, 3, RND, NQ, CB>;
     }
 }
 
-template <int SS, int NQ>
+template <int SS, int NQ, int CB>
 const void* pick_rnd(int off, int rounding) {
-    return rounding == CONV_ROUND_HALF_AWAY ? pick_off<SS, CONV_ROUND_HALF_AWAY, NQ>(off)
-                                            : pick_off<SS, CONV_ROUND_HALF_EVEN, NQ>(off);
+    return rounding == CONV_ROUND_HALF_AWAY ? pick_off<SS, CONV_ROUND_HALF_AWAY, NQ, CB>(off)
+                                            : pick_off<SS, CONV_ROUND_HALF_EVEN, NQ, CB>(off);
 }
 
+// 16-byte chunks: up to 16 per thread; 8-byte chunks (planned only for
+// planes of at most 8 * kQT of them): 4 or 8.
 template <int SS>
-const void* pick_nq(int nchunks, int off, int rounding) {
-    if (nchunks <= 4 * kQT) return pick_rnd<SS, 4>(off, rounding);
-    if (nchunks <= 8 * kQT) return pick_rnd<SS, 8>(off, rounding);
-    return pick_rnd<SS, 16>(off, rounding);
+const void* pick_nq(int nchunks, int off, int rounding, int cb) {
+    if (cb == 8) return nchunks <= 4 * kQT ? pick_rnd<SS, 4, 8>(off, rounding) : pick_rnd<SS, 8, 8>(off, rounding);
+    if (nchunks <= 4 * kQT) return pick_rnd<SS, 4, 16>(off, rounding);
+    if (nchunks <= 8 * kQT) return pick_rnd<SS, 8, 16>(off, rounding);
+    return pick_rnd<SS, 16, 16>(off, rounding);
 }
+
+// Copy chunk bytes for an image width: 16 where rows are 16-byte multiples.
+int qdw_cb(int w) { return w % 16 == 0 ? 16 : 8; }
 
 bool qgeom(const Desc& d, QGeom& G) {
     const conv2d_params_t& p = d.p;
@@ -222,7 +239,8 @@ bool qgeom(const Desc& d, QGeom& G) {
     if (P > 8) P = 8;
     if (P < 1) P = 1;
     G.planes = P;
-    return G.rows * (G.row_bytes / 16) <= kNQ * kQT && 2 * G.plane_bytes + 16 * P <= 160 * 1024;
+    const int cb = qdw_cb(p.w);
+    return G.rows * (G.row_bytes / cb) <= (cb == 16 ? kNQ : 8) * kQT && 2 * G.plane_bytes + 16 * P <= 160 * 1024;
 }
 
 }  // namespace
@@ -231,7 +249,7 @@ bool plan_qdw3(const Desc& d) {
     const conv2d_params_t& p = d.p;
     if (p.k_h != 3 || p.k_w != 3 || p.dilation_h != 1 || p.dilation_w != 1) return false;
     if (p.stride_h != p.stride_w || (p.stride_h != 1 && p.stride_h != 2)) return false;
-    if (p.w % 16 != 0 || d.wo % 4 != 0 || p.pad_left > kMarg) return false;
+    if (p.w % 8 != 0 || d.wo % 4 != 0 || p.pad_left > kMarg) return false;
     if (d.wo / 4 > kQT) return false;   // a row's column groups must fit one workgroup pass
     if ((int64_t)p.h * p.w >= INT32_MAX / 16) return false;
     QGeom G;
@@ -239,7 +257,8 @@ bool plan_qdw3(const Desc& d) {
 }
 
 hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s) {
-    if ((uintptr_t)a.xptr % 16 != 0 || (uintptr_t)a.yptr % 4 != 0) return launch_direct(d, a, s);
+    const int cb = qdw_cb(d.p.w);
+    if ((uintptr_t)a.xptr % cb != 0 || (uintptr_t)a.yptr % 4 != 0) return launch_direct(d, a, s);
     QGeom G;
     if (!qgeom(d, G)) return hipErrorInvalidConfiguration;
     const int64_t blocks = (int64_t)a.n * ((a.c_out + G.planes - 1) / G.planes);
@@ -248,8 +267,9 @@ hipError_t launch_qdw3(const Desc& d, ConvArgs a, hipStream_t s) {
     const int off = (kMarg - d.p.pad_left) & 3;
     a.dv_tiles_h = make_divu32((uint32_t)(a.ho * (a.wo / 4)));
     a.dv_tiles_w = make_divu32((uint32_t)(a.wo / 4));
-    const int nchunks = G.rows * (G.row_bytes / 16);
-    const void* fn = d.p.stride_h == 1 ? pick_nq<1>(nchunks, off, a.rounding) : pick_nq<2>(nchunks, off, a.rounding);
+    const int nchunks = G.rows * (G.row_bytes / cb);
+    const void* fn = d.p.stride_h == 1 ? pick_nq<1>(nchunks, off, a.rounding, cb)
+                                       : pick_nq<2>(nchunks, off, a.rounding, cb);
     int rows = G.rows, rb = G.row_bytes, P = G.planes;
     void* args[] = {&a, &rows, &rb, &P};
     const size_t lds = 2 * (size_t)G.plane_bytes + 16 * P;

@@ -156,6 +156,9 @@ def test_kernel_choice_for_the_workloads():
                                                      pads=L.pads, groups=L.groups, dtype="i8"))
         names[L.name] = cc().conv2d_desc_kernel_name(d)
     assert names["dw_s1"] == names["dw_s2"] == "depthwise_i8_dot4" and names["pw"] == "pointwise_i8_mfma"
+    # the int8 bottleneck's depthwise (56-byte rows: 8-byte copy chunks)
+    d = cc().conv2d_desc_create(cc().make_params(8, 192, 56, 56, 192, (3, 3), pads=1, groups=192, dtype="i8"))
+    assert cc().conv2d_desc_kernel_name(d) == "depthwise_i8_dot4"
     # int8 dense, strided and grouped convolutions: the i8 implicit GEMM
     for L in workloads.mixed_sweep_layers():
         if L.name == "pw":

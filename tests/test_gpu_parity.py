@@ -526,6 +526,11 @@ INT8_CASES = [
     (1, 3, 96, 224, 3, 3, 1, 1, 3),                # s1, 98 rows x 16 units
     (1, 2, 160, 224, 2, 3, 2, 1, 2),               # s2, 161 rows x 16 units
     (1, 2, 5, 1056, 2, 3, 1, 1, 2),                # s1, 264 column groups per row: the generic depthwise
+    # widths that are multiples of 8 but not of 16: 8-byte copy chunks
+    (2, 12, 14, 56, 12, 3, 1, 1, 12),              # s1, the int8 bottleneck's width
+    (1, 10, 15, 24, 10, 3, 2, (1, 3, 0, 2), 10),   # s2, pad_left 3
+    (2, 7, 9, 40, 7, 3, 1, (0, 2, 2, 1), 7),       # s1, pad_left 2
+    (1, 3, 90, 88, 3, 3, 1, 1, 3),                 # s1, 92 rows x 16 chunks (the 8-chunk register buffer)
 ]
 
 
