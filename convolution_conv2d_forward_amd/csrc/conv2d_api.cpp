@@ -193,14 +193,15 @@ conv_status_t scratch_on_current_device(void** out) {
     return CONV_OK;
 }
 
-// A bf16 implicit-GEMM forward call given OIHW weights: re-lay them into the
-// descriptor's pack buffer, then convolve.  The buffer is allocated by the
-// first such call, on the current device.  Each call waits, on its own
-// stream, for the event recorded after the previous call's kernels (which
-// read the buffer), refills the buffer, convolves and records the event, all
-// under the descriptor's mutex: calls sharing the descriptor may come from
-// any streams and host threads and each one convolves with its own weights.
-conv_status_t forward_bf16_repack(Desc& d, const ConvArgs& a, hipStream_t s) {
+// A bf16 (or int8 3x3) implicit-GEMM forward call given OIHW weights:
+// re-lay them into the descriptor's pack buffer, then convolve.  The buffer
+// is allocated by the first such call, on the current device.  Each call
+// waits, on its own stream, for the event recorded after the previous call's
+// kernels (which read the buffer), refills the buffer, convolves and records
+// the event, all under the descriptor's mutex: calls sharing the descriptor
+// may come from any streams and host threads and each one convolves with its
+// own weights.
+conv_status_t forward_repack(Desc& d, const ConvArgs& a, hipStream_t s) {
     std::lock_guard<std::mutex> lock(d.mu);
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return fail(CONV_ERR_HIP, "no current HIP device");
@@ -208,7 +209,7 @@ conv_status_t forward_bf16_repack(Desc& d, const ConvArgs& a, hipStream_t s) {
         hipError_t e = hipMalloc(&d.wpack, (size_t)d.wpack_bytes);
         if (e != hipSuccess) {
             d.wpack = nullptr;
-            return fail(CONV_ERR_HIP, "allocating %lld bytes for the packed bf16 weights: %s",
+            return fail(CONV_ERR_HIP, "allocating %lld bytes for the packed weights: %s",
                         (long long)d.wpack_bytes, hipGetErrorString(e));
         }
         e = hipEventCreateWithFlags(&d.wpack_ev, hipEventDisableTiming);
@@ -220,13 +221,18 @@ conv_status_t forward_bf16_repack(Desc& d, const ConvArgs& a, hipStream_t s) {
         }
         d.wpack_device = dev;
     } else if (dev != d.wpack_device) {
-        return fail(CONV_ERR_INVALID_ARG, "the bf16 pack buffer lives on device %d, current device is %d",
+        return fail(CONV_ERR_INVALID_ARG, "the weight pack buffer lives on device %d, current device is %d",
                     d.wpack_device, dev);
     }
     hipError_t e = hipStreamWaitEvent(s, d.wpack_ev, 0);
-    if (e == hipSuccess) e = launch_igemm_bf16(d, a, s, nullptr, d.wpack);
+    if (d.kclass == KC_IGEMM_I8) {
+        if (e == hipSuccess) e = pack_igemm_i8_weights(d, a.wptr, d.wpack, s);
+        if (e == hipSuccess) e = launch_igemm_i8(d, a, s, d.wpack);
+    } else {
+        if (e == hipSuccess) e = launch_igemm_bf16(d, a, s, nullptr, d.wpack);
+    }
     if (e == hipSuccess) e = hipEventRecord(d.wpack_ev, s);
-    return hip_status(e, "igemm_bf16");
+    return hip_status(e, kernel_name(d));
 }
 
 }  // namespace
@@ -353,6 +359,7 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
         } else {
             d->kclass = KC_IGEMM_I8;
             planned = plan_igemm_i8(*d);
+            d->wpack_bytes = planned ? igemm_i8_pack_bytes(*d) : 0;
         }
     } else if (depthwise) {
         d->kclass = KC_DW;
@@ -407,8 +414,9 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
     const int64_t wb = w_bytes(d);
     const bool wino = d.kclass == KC_WINOGRAD_F32 ||
                       (d.kclass == KC_IGEMM_F32 && d.p.algo == CONV_ALGO_AUTO && winograd_bound_preferred(d));
-    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) || wino;
-    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16 ? d.wpack_bytes
+    const bool i8pack = d.kclass == KC_IGEMM_I8 && d.wpack_bytes > 0;
+    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) || wino || i8pack;
+    const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16 || i8pack ? d.wpack_bytes
                                : wino                     ? winograd_u_bytes(d)
                                                           : d.apack_bytes;
     const int64_t off = packs ? (wb + 255) / 256 * 256 : 0;
@@ -430,6 +438,7 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
     hipError_t e = hipMemcpyAsync(d.wbound, w, (size_t)wb, hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess && packs)
         e = d.kclass == KC_IGEMM_BF16 ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
+            : i8pack                   ? pack_igemm_i8_weights(d, d.wbound, (char*)d.wbound + off, s)
             : wino                     ? pack_winograd_f32_weights(d, d.wbound, (char*)d.wbound + off, s)
                                        : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
     if (e != hipSuccess) {
@@ -516,7 +525,7 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
             if (st != CONV_OK) return st;
             e = launch_igemm_bf16(d, a, s, nullptr, sp);
         } else {
-            const conv_status_t st = forward_bf16_repack(d, a, s);
+            const conv_status_t st = forward_repack(d, a, s);
             if (st != CONV_OK) return st;
             e = hipSuccess;
         }
@@ -782,7 +791,15 @@ conv_status_t qconv2d_forward(conv2d_desc_t dd, const int8_t* x, float x_scale, 
     switch (d.kclass) {
     case KC_QDW: e = launch_qdw(d, a, s); break;
     case KC_QPW: e = launch_qpw(d, a, s); break;
-    case KC_IGEMM_I8: e = launch_igemm_i8(d, a, s); break;
+    case KC_IGEMM_I8:
+        if (!igemm_i8_fast(d, x)) {
+            e = launch_igemm_i8(d, a, s);
+        } else if (!w) {
+            e = launch_igemm_i8(d, a, s, (const char*)d.wbound + d.wbound_pack_off);
+        } else {
+            return forward_repack(*(Desc*)dd, a, s);
+        }
+        break;
     default: e = launch_direct(d, a, s); break;
     }
     return hip_status(e, kernel_name(d));

@@ -123,8 +123,9 @@ struct Desc {
     int32_t stages;
     int32_t pt_vertical;
     bool flatten_1x1;            // 1x1/s1/p0: treat [h][w] as one row of h*w pixels
-    // bf16 implicit GEMM, forward calls given OIHW weights: the weights
-    // re-laid into the kernel's per-chunk LDS images before every such call.
+    // bf16 and int8 3x3 implicit GEMM, forward calls given OIHW weights: the
+    // weights re-laid into the kernel's per-chunk LDS images before every
+    // such call.
     // The buffer is allocated by the first such call, on the device current
     // then; wpack_ev is recorded after each call's kernels, and the next call
     // waits for it on its own stream before it refills the buffer, so calls
@@ -147,9 +148,9 @@ struct Desc {
     // their own weights keep the implicit GEMM.
     bool wino_bound = false;
     // Weights bound with conv2d_desc_bind_weights: an OIHW copy at wbound,
-    // followed for the bf16 implicit GEMM, the Winograd kernel (and the fp32
-    // implicit GEMM when apack_bytes > 0) by the packed image at wbound +
-    // wbound_pack_off (0 = no packed image).
+    // followed for the bf16 implicit GEMM, the Winograd kernel, the int8 3x3
+    // implicit GEMM (and the fp32 implicit GEMM when apack_bytes > 0) by the
+    // packed image at wbound + wbound_pack_off (0 = no packed image).
     void* wbound = nullptr;
     int64_t wbound_bytes = 0;
     int64_t wbound_pack_off = 0;
@@ -173,7 +174,17 @@ hipError_t launch_igemm_bf16(const Desc& d, ConvArgs a, hipStream_t s, const voi
 hipError_t pack_igemm_bf16_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_qdw(const Desc& d, ConvArgs a, hipStream_t s);
-hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s);
+// wpacked: the weights re-laid into the 3x3 kernel's per-chunk LDS images
+// (pack_igemm_i8_weights), or null for the kernel that reads a.wptr (OIHW).
+// The 3x3 kernel runs when wpacked is given and igemm_i8_fast holds.
+hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s, const void* wpacked = nullptr);
+// Bytes of the int8 3x3 kernel's weight images (0: the shape has no such kernel).
+int64_t igemm_i8_pack_bytes(const Desc& d);
+// The shape has the 3x3 kernel and x is word-aligned.
+bool igemm_i8_fast(const Desc& d, const void* x);
+// OIHW int8 weights -> the 3x3 kernel's per-chunk LDS images at dst
+// (igemm_i8_pack_bytes bytes).
+hipError_t pack_igemm_i8_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
 hipError_t launch_qpw(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_direct(const Desc& d, ConvArgs a, hipStream_t s);
 hipError_t launch_grouped(const Desc& d, ConvArgs a, hipStream_t s);

@@ -6,22 +6,38 @@
 // fused INT8 chains); the convolution is ncnn's "convolution" definition
 // with the zero point as the pad.
 //
-// GEMM per group: Y[co, p] = sum_k W[co, k] X^[k, p], with K ordered
-// tap-major: k = tap * 64 + c within a chunk of 64 input channels.  An MFMA
-// step is one tap of one chunk, so a lane's 16 consecutive k are 16
-// consecutive channels at one tap:
-//   - the input patch of the tile is staged in LDS pixel-major, [pixel][64
-//     channels] (4 channels x 4 pixels per thread: four 4-byte loads,
-//     transposed with v_perm), so the pixel operand is one 16-byte LDS read
-//     at the tap's patch pixel;
-//   - the weights are re-laid per chunk into [tap][co][64 channels] (a thread
-//     reads one output channel's 4 input channels x all taps, contiguous in
-//     OIHW, and writes one word per tap).
-// Workgroup tile: BM = 16*MB output channels of one group x (4*NFW) output
-// rows x 16 output columns; wave w owns output rows w, w+4, ...  Pixels are
-// the first MFMA operand, so a lane's result is 4 consecutive output columns
-// of one channel: + bias, requant, one packed 4-byte store where the row
-// allows it.
+// GEMM per group: Y[co, p] = sum_k W[co, k] X^[k, p].  K runs over chunks
+// of up to 64 input channels; within a chunk it is a list of items, item i =
+// (tap i / ncg, 16-channel group i % ncg), ncg = 1, 2 or 4 groups of 16
+// channels (enough for the group's channels), and an MFMA K step is four
+// consecutive items: a 3x3 window over 64 channels is one tap per step,
+// over 8 channels four taps per step (instead of a step of 64 channels of
+// which 56 are padding).  A lane's 16 consecutive k are 16 channels at one
+// tap.  The input patch of the tile is staged in LDS pixel-major, [pixel][16
+// * ncg channels] (4 channels x 4 pixels per unit: four 4-byte loads,
+// transposed with v_perm), so the pixel operand is one 16-byte LDS read at
+// the item's patch pixel and channel group.  Pixels are the first MFMA
+// operand, so a lane's result is 4 consecutive output columns of one
+// channel: + bias, requant, one packed 4-byte store where the row allows it.
+//
+// Two kernels:
+//   - igemm_i8_fast_kernel, 3x3 windows over word-aligned input rows: the
+//     weights are re-laid once (at bind, or by a pack kernel before the
+//     call) into per-chunk LDS images, [K step][co][64 bytes] with the four
+//     16-byte pieces of a row rotated by (co / 4) % 4 so that the 16 rows a
+//     B-operand read touches fall on distinct banks; a chunk's image reaches
+//     LDS by direct global->LDS copies, 1 KB per wave instruction.  A
+//     thread holds its share of the next chunk's patch in registers: those
+//     loads are issued as soon as the current chunk is in LDS and land while
+//     its MFMAs run.  The K steps are unrolled (per-lane patch offsets
+//     computed once), and the four waves split the tile 2 x 2 (output
+//     channel halves x output row halves) where it has two or more channel
+//     tiles, so each operand read feeds more MFMAs.
+//   - igemm_i8_kernel, every other window: weights re-laid per chunk from
+//     OIHW by the workgroup ([K step][co][80 bytes], 16 pad bytes per row),
+//     the patch staged in passes, each chunk in turn.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace conv2d {
@@ -29,10 +45,9 @@ namespace conv2d {
 namespace {
 
 constexpr int kT = 256;
-constexpr int CK = 64;          // input channels per chunk (the MFMA's K)
-constexpr int XR = CK + 16;     // LDS bytes per staged pixel / weight row (16 pad bytes spread the banks)
+constexpr int WR = 80;          // igemm_i8_kernel: LDS bytes per weight row (64 + 16 pad bytes)
 constexpr int TW = 16;          // output columns per tile (one MFMA fragment)
-constexpr int QV = 4;           // staged 4x4 blocks per thread and pass
+constexpr int QV = 4;           // igemm_i8_kernel: staged 4x4 blocks per thread and pass
 
 struct I8Args {
     ConvArgs a;
@@ -40,8 +55,12 @@ struct I8Args {
     int32_t th;             // output rows per tile (4 * NFW)
     int32_t ph, pw;         // patch rows, patch columns (a multiple of 4)
     int32_t pw4;            // pw / 4
+    int32_t ncg, lg_nq;     // 16-channel groups per chunk (its 16 * ncg input channels); log2 of its channel quads
+    int32_t xr;             // LDS bytes per staged patch pixel (16 * ncg + 16)
+    int32_t qs;             // patch slots per quarter (see the patch layout)
+    int32_t items, steps;   // (tap, channel group) items per chunk; MFMA K steps, items / 4 rounded up
     int32_t co_tiles, tiles_h, tiles_w, chunks;
-    int32_t xs_bytes;       // LDS bytes of the patch
+    int32_t xs_bytes, ws_bytes;
     int32_t vec_x;          // patch rows move as 4-byte words
     int32_t vec_w;          // filter blocks move as 4-byte words
     int32_t away;           // requant ties away from zero
@@ -50,6 +69,7 @@ struct I8Args {
     DivU32 dv_pw4;          // staging unit -> (quad, patch row)
     DivU32 dv_ppix;         // staging unit / 4 -> channel quad group (patch words per quad)
     DivU32 dv_kw;           // tap -> (r, s)
+    DivU32 dv_ncg;          // item -> (tap, channel group)
 };
 
 __device__ __forceinline__ void tr4x4(const uint32_t in[4], uint32_t out[4]) {
@@ -63,17 +83,339 @@ __device__ __forceinline__ void tr4x4(const uint32_t in[4], uint32_t out[4]) {
     out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
-// Requant, ties to even or (away) away from zero, branch-free; the clamp to
+// Requant, ties to even or (AWAY) away from zero, branch-free; the clamp to
 // [lo, hi] (the int8 range shifted by the zero point, raised to 0 under
 // ReLU) runs on the rounded value.
-__device__ __forceinline__ int rq8(int32_t acc, float comp, bool away, float lo, float hi, int zp) {
+template <bool AWAY>
+__device__ __forceinline__ int rq8(int32_t acc, float comp, float lo, float hi, int zp) {
     float yf = __fmul_rn((float)acc, comp);
     asm volatile("" : "+v"(yf));   // the rounded f32 product decides ties (no fma into the rounding)
-    const float t = truncf(yf);
-    const float r = (away && fabsf(yf - t) == 0.5f) ? t + copysignf(1.0f, yf) : rintf(yf);
+    float r;
+    if constexpr (AWAY) {
+        const float t = truncf(yf);
+        r = fabsf(yf - t) == 0.5f ? t + copysignf(1.0f, yf) : rintf(yf);
+    } else {
+        r = rintf(yf);
+    }
     return (int)__builtin_amdgcn_fmed3f(r, lo, hi) + zp;
 }
 
+// Four requantised values (each in [-128, 127]) as the bytes of one word.
+template <bool AWAY>
+__device__ __forceinline__ uint32_t rq8x4(i32x4 acc, int32_t bb, float comp, float lo, float hi, int zp) {
+    const uint32_t b0 = (uint32_t)rq8<AWAY>(acc[0] + bb, comp, lo, hi, zp);
+    const uint32_t b1 = (uint32_t)rq8<AWAY>(acc[1] + bb, comp, lo, hi, zp);
+    const uint32_t b2 = (uint32_t)rq8<AWAY>(acc[2] + bb, comp, lo, hi, zp);
+    const uint32_t b3 = (uint32_t)rq8<AWAY>(acc[3] + bb, comp, lo, hi, zp);
+    // low bytes of b0, b1 -> bytes 0, 1; of b2, b3 -> bytes 2, 3
+    const uint32_t lo01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+    return lo01 | hi23;
+}
+
+// Block index -> (output-channel tile, group, column tile, row tile, image).
+struct I8Tile {
+    int cot, g, twi, thi, n;
+};
+
+__device__ __forceinline__ I8Tile i8_tile(const I8Args& f) {
+    I8Tile t;
+    uint32_t L = xcd_remap(blockIdx.x, f.num_blocks);
+    uint32_t Q = divu(L, f.dv_co_tiles);
+    t.cot = L - Q * f.co_tiles;
+    L = Q; Q = divu(L, f.dv_groups);
+    t.g = L - Q * f.a.groups;
+    L = Q; Q = divu(L, f.dv_tiles_w);
+    t.twi = L - Q * f.tiles_w;
+    L = Q; Q = divu(L, f.dv_tiles_h);
+    t.thi = L - Q * f.tiles_h;
+    t.n = Q;
+    return t;
+}
+
+// + bias, requant, 4 consecutive columns per lane.  acc[j][m] holds output
+// row ho0 + rbase + rstep * j of channel tile mbase + m.
+template <bool AWAY, int NR, int NM>
+__device__ __forceinline__ void i8_epilogue_r(const I8Args& f, const I8Tile& t, const i32x4 (&acc)[NR][NM], int rbase,
+                                              int rstep, int mbase, int co0, int ho0, int wo0, int lane) {
+    const ConvArgs& a = f.a;
+    const bool relu = a.act == CONV_ACT_RELU;
+    const float lo = relu ? 0.0f : (float)(-128 - a.y_zp), hi = (float)(127 - a.y_zp);
+    int8_t* __restrict__ yg = (int8_t*)a.yptr;
+    const int64_t oplane = (int64_t)a.ho * a.wo;
+    const bool vec_y = (a.wo % 4) == 0 && ((uintptr_t)a.yptr % 4) == 0;
+    const int wo = wo0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int co = co0 + 16 * (mbase + m) + (lane & 15);
+        if (co >= a.cout_g) continue;
+        const int cg = t.g * a.cout_g + co;
+        const int32_t bb = a.qbias ? a.qbias[cg] : 0;
+        int8_t* yc = yg + ((int64_t)t.n * a.out_total + a.out_off + cg) * oplane;
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const int ho = ho0 + rbase + rstep * j;
+            if (ho >= a.ho || wo >= a.wo) continue;
+            const uint32_t word = rq8x4<AWAY>(acc[j][m], bb, a.composite, lo, hi, a.y_zp);
+            int8_t* dst = yc + (int64_t)ho * a.wo + wo;
+            if (vec_y && wo + 4 <= a.wo) {
+                *(uint32_t*)dst = word;
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (wo + v < a.wo) dst[v] = (int8_t)(word >> (8 * v));
+            }
+        }
+    }
+}
+
+template <int NR, int NM>
+__device__ __forceinline__ void i8_epilogue(const I8Args& f, const I8Tile& t, const i32x4 (&acc)[NR][NM], int rbase,
+                                            int rstep, int mbase, int co0, int ho0, int wo0, int lane) {
+    if (f.away)
+        i8_epilogue_r<true>(f, t, acc, rbase, rstep, mbase, co0, ho0, wo0, lane);
+    else
+        i8_epilogue_r<false>(f, t, acc, rbase, rstep, mbase, co0, ho0, wo0, lane);
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l writes lds_base + 16*l
+// (lds_base wave-uniform).  Inline assembly, so that the compiler does not
+// order the workgroup's later LDS reads behind it; the kernel's own
+// s_waitcnt before the barrier is what orders the copy.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
+                 : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
+// ---------------------------------------------------------------------------
+// 3x3 windows over word-aligned rows, weights pre-packed.
+//
+// Packed weights: for each (group, channel tile, chunk) an image of STEPS x
+// BM rows x 64 bytes; row (s, co) holds the four items 4s .. 4s+3, item i =
+// (tap i / ncg, channel group i % ncg) as W[co][16 * cg .. +15][tap], piece
+// kq stored at position kq ^ ((co / 4) % 4).  Items past the last, channels
+// past the group and channels past cout_g are zero.
+template <int NFW, int MB, int NCG>
+__global__ __launch_bounds__(kT, 3) void igemm_i8_fast_kernel(I8Args f, const uint8_t* __restrict__ wpk) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const ConvArgs& a = f.a;
+    constexpr int BM = 16 * MB;
+    constexpr int WM = MB >= 2 ? 2 : 1;         // waves across the channel tiles
+    constexpr int MBW = MB / WM;                // channel tiles per wave
+    constexpr int NFR = NFW * WM;               // output-row fragments per wave
+    constexpr int STEPS = (9 * NCG + 3) / 4;
+    constexpr int XR = 16 * NCG + 16;           // LDS bytes per patch pixel
+    constexpr int NQ = 4 * NCG;                 // channel quads per chunk
+    constexpr int CKC = 16 * NCG;               // input channels per chunk
+    constexpr int UQ = 2 * NCG;                 // patch units per thread held in registers
+    constexpr int WIMG = STEPS * BM * 64;       // bytes of a chunk's weight image
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wr = wave / WM;
+    const int kq = lane >> 4;
+
+    const I8Tile t = i8_tile(f);
+    const int co0 = t.cot * BM;
+    const int ho0 = t.thi * f.th, wo0 = t.twi * TW;
+    const int ih0 = ho0 * a.stride_h - a.pad_top;
+    const int iw_lo = wo0 * a.stride_w - a.pad_left;
+    const int iw_a = iw_lo >= 0 ? iw_lo & ~3 : -((-iw_lo + 3) & ~3);   // patch column 0, a multiple of 4
+    const int shift = iw_lo - iw_a;
+    const int H = a.h, W = a.w;
+    const int64_t HW = (int64_t)H * W;
+    const int cin_g = a.cin_g;
+    const int PW = f.pw;
+    const int pq_n = f.ph * f.pw4;       // 4-pixel words of the patch per channel quad
+    const int QS = f.qs;                 // slots per quarter of the patch (>= pq_n)
+
+    const int8_t* __restrict__ xg = (const int8_t*)a.xptr + ((int64_t)t.n * a.in_total + a.in_off + (int64_t)t.g * cin_g) * HW;
+    const uint8_t* __restrict__ wimg = wpk + ((int64_t)(t.g * f.co_tiles + t.cot) * f.chunks) * WIMG;
+
+    uint8_t* xs = lds;                   // [4 * QS][XR]; pixel p at slot (p % 4) * QS + p / 4
+    uint8_t* ws = lds + f.xs_bytes;      // two buffers of [STEPS][BM][64]
+
+    // This lane's patch offset and channel-group byte per K step: item 4s + kq.
+    int toff[STEPS], cgo[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int i = 4 * s + kq;
+        const int tap = i / NCG, cg = i % NCG;
+        const int r = (tap * 11) >> 5;   // tap / 3 for tap < 12
+        const bool live = i < 9 * NCG;
+        toff[s] = live ? r * a.dilation_h * PW + (tap - 3 * r) * a.dilation_w : 0;
+        cgo[s] = live ? 16 * cg : 0;
+    }
+    int pbase[NFR];
+#pragma unroll
+    for (int j = 0; j < NFR; ++j) pbase[j] = (wr * NFR + j) * a.stride_h * PW + (lane & 15) * a.stride_w + shift;
+    // B-operand read of channel tile m at step s: row s * BM + 16 * m + lane % 16,
+    // piece kq at its rotated position.
+    const int boff = (16 * wm * MBW + (lane & 15)) * 64 + 16 * (kq ^ ((lane >> 2) & 3));
+
+    i32x4 acc[NFR][MBW];
+#pragma unroll
+    for (int j = 0; j < NFR; ++j)
+#pragma unroll
+        for (int m = 0; m < MBW; ++m) acc[j][m] = i32x4{0, 0, 0, 0};
+
+    // Patch unit u: channel quad 4 * (u / (4 * pq_n)) + u % 4 and word rem =
+    // (u / 4) % pq_n (patch row rem / pw4, columns 4 * (rem % pw4) ..+3).
+    // Four consecutive lanes take four channel quads of one word, so a
+    // wave's transposed words fill 16 bytes of each of 16 consecutive slots
+    // (every bank once).  A unit's place in the image and in LDS is the same
+    // for every chunk: its offset within a channel plane (0 outside the
+    // image), channel quad and LDS slot are worked out once.
+    const int units0 = ((min(NQ, (cin_g + 3) >> 2) + 3) & ~3) * pq_n;   // units of the first (largest) chunk
+    uint32_t goff[UQ];
+    int cqs[UQ], sbase[UQ];
+    uint32_t inimg = 0;
+#pragma unroll
+    for (int i = 0; i < UQ; ++i) {
+        const int u = tid + i * kT;
+        const int hi = (int)divu((uint32_t)(u >> 2), f.dv_ppix);
+        const int cq = 4 * hi + (u & 3);
+        const int rem = (u >> 2) - hi * pq_n;
+        const int pr = (int)divu((uint32_t)rem, f.dv_pw4);
+        const int ih = ih0 + pr, iw = iw_a + 4 * (rem - pr * f.pw4);
+        // W % 4 == 0 and iw % 4 == 0: the word is inside the row or outside it.
+        const bool in = u < units0 && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+        goff[i] = in ? (uint32_t)(ih * W + iw) : 0u;
+        cqs[i] = cq;
+        // byte b of the word is patch pixel 4 * rem + b, at slot b * QS + rem
+        sbase[i] = rem * XR + 4 * cq;
+        inimg |= (in ? 1u : 0u) << i;
+    }
+    const uint32_t HW32 = (uint32_t)HW;
+
+    uint32_t pv[UQ][4];
+    uint32_t plive = 0;
+    // Loads at clamped offsets (a unit outside the image, or a channel past
+    // cin_g, reads the chunk's first byte), all issued back to back; the
+    // zeros of units outside the image are chosen when the chunk is stored.
+    auto load_patch = [&](int kc) {
+        const int cleft = cin_g - kc * CKC;              // channels left from this chunk on
+        const int kq_n = min(NQ, (cleft + 3) >> 2);
+        const int8_t* xc = xg + (int64_t)kc * CKC * HW;
+        plive = 0;
+#pragma unroll
+        for (int i = 0; i < UQ; ++i) {
+            if (i * kT >= units0) break;
+            const bool ok = ((inimg >> i) & 1u) && cqs[i] < kq_n;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int ch = 4 * cqs[i] + cc;
+                const uint32_t off = ok && ch < cleft ? goff[i] + (uint32_t)ch * HW32 : 0u;
+                pv[i][cc] = *(const uint32_t*)(xc + off);
+            }
+            plive |= (ok ? 1u : 0u) << i;
+        }
+    };
+    auto store_patch = [&](int kc) {
+        const int kq_n = min(NQ, (cin_g - kc * CKC + 3) >> 2);
+#pragma unroll
+        for (int i = 0; i < UQ; ++i) {
+            if (i * kT >= units0) break;
+            if (tid + i * kT >= units0 || cqs[i] >= kq_n) continue;
+            uint32_t in[4], outw[4];
+            const bool ok = (plive >> i) & 1u;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) in[cc] = ok ? pv[i][cc] : 0u;
+            tr4x4(in, outw);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) *(uint32_t*)&xs[b * QS * XR + sbase[i]] = outw[b];
+        }
+    };
+    // A chunk's weight image (WIMG / 1024 copies of 1 KB, spread over the
+    // waves) into buffer kc % 2.
+    auto copy_weights = [&](int kc) {
+        const uint8_t* src = wimg + (int64_t)kc * WIMG;
+        uint8_t* dst = ws + (kc & 1) * WIMG;
+#pragma unroll
+        for (int p = 0; p < (WIMG / 1024 + 3) / 4; ++p) {
+            const int piece = wave + 4 * p;
+            if (piece < WIMG / 1024) copy16_to_lds(src + piece * 1024 + 16 * lane, dst + piece * 1024);
+        }
+    };
+
+    // Chunk kc+1's weights are copied, and its patch loaded into registers,
+    // while chunk kc's MFMAs run; the weight images alternate between two
+    // LDS buffers, the patch has one (stored after the MFMAs that read it).
+    copy_weights(0);
+    load_patch(0);
+    for (int kc = 0; kc < f.chunks; ++kc) {
+        store_patch(kc);
+        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's copies of chunk kc have landed
+        __syncthreads();                      // ... and every thread's; chunk kc-1's MFMAs are done
+        if (kc + 1 < f.chunks) {
+            copy_weights(kc + 1);
+            load_patch(kc + 1);
+        }
+        const uint8_t* wsc = ws + (kc & 1) * WIMG;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            i32x4 bw[MBW];
+#pragma unroll
+            for (int m = 0; m < MBW; ++m) bw[m] = *(const i32x4*)&wsc[s * BM * 64 + m * 1024 + boff];
+#pragma unroll
+            for (int j = 0; j < NFR; ++j) {
+                const int pp = pbase[j] + toff[s];
+                const i32x4 av = *(const i32x4*)&xs[((pp & 3) * QS + (pp >> 2)) * XR + cgo[s]];
+#pragma unroll
+                for (int m = 0; m < MBW; ++m)
+                    acc[j][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bw[m], acc[j][m], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    i8_epilogue<NFR, MBW>(f, t, acc, wr * NFR, 1, wm * MBW, co0, ho0, wo0, lane);
+}
+
+// OIHW int8 -> the fast kernel's per-chunk weight images, one thread per
+// 4-byte word of the output.
+struct I8PackArgs {
+    int32_t cin_g, cout_g, bm, ncg, steps, co_tiles, chunks;
+    int64_t words;
+};
+
+__global__ __launch_bounds__(256) void pack_i8_kernel(const int8_t* __restrict__ w, uint32_t* __restrict__ dst,
+                                                      I8PackArgs p) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= p.words) return;
+    const int img_words = p.steps * p.bm * 16;
+    const int64_t img = q / img_words;
+    const int ob = (int)(q - img * img_words) * 4;      // byte offset in the image
+    const int kc = (int)(img % p.chunks);
+    const int64_t gt = img / p.chunks;
+    const int cot = (int)(gt % p.co_tiles);
+    const int g = (int)(gt / p.co_tiles);
+    const int s = ob / (p.bm * 64);
+    const int row = (ob / 64) % p.bm;
+    const int pos = ob % 64;
+    const int kq = (pos >> 4) ^ ((row >> 2) & 3);
+    const int i = 4 * s + kq;
+    const int co = cot * p.bm + row;
+    uint32_t v = 0;
+    if (i < 9 * p.ncg && co < p.cout_g) {
+        const int tap = i / p.ncg, cg = i % p.ncg;
+        const int8_t* wc = w + ((int64_t)g * p.cout_g + co) * p.cin_g * 9;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int c = kc * 16 * p.ncg + 16 * cg + (pos & 15) + b;
+            if (c < p.cin_g) v |= (uint32_t)(uint8_t)wc[(int64_t)c * 9 + tap] << (8 * b);
+        }
+    }
+    dst[q] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Every other window: weights re-laid per chunk by the workgroup from OIHW,
+// each chunk staged in turn.  Wave w owns output rows w, w+4, ...
 template <int NFW, int MB>
 __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -82,19 +424,9 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    uint32_t L = xcd_remap(blockIdx.x, f.num_blocks);
-    uint32_t Q = divu(L, f.dv_co_tiles);
-    const int cot = L - Q * f.co_tiles;
-    L = Q; Q = divu(L, f.dv_groups);
-    const int g = L - Q * a.groups;
-    L = Q; Q = divu(L, f.dv_tiles_w);
-    const int twi = L - Q * f.tiles_w;
-    L = Q; Q = divu(L, f.dv_tiles_h);
-    const int thi = L - Q * f.tiles_h;
-    const int n = Q;
-
-    const int co0 = cot * BM;
-    const int ho0 = thi * f.th, wo0 = twi * TW;
+    const I8Tile tl = i8_tile(f);
+    const int co0 = tl.cot * BM;
+    const int ho0 = tl.thi * f.th, wo0 = tl.twi * TW;
     const int ih0 = ho0 * a.stride_h - a.pad_top;
     const int iw_lo = wo0 * a.stride_w - a.pad_left;
     const int iw_a = iw_lo >= 0 ? iw_lo & ~3 : -((-iw_lo + 3) & ~3);   // patch column 0, a multiple of 4
@@ -103,24 +435,42 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
     const int64_t HW = (int64_t)H * W;
     const int cin_g = a.cin_g;
     const int khw = f.khw;
-    const int PH = f.ph, PW = f.pw;
+    const int PW = f.pw;
+    const int XR = f.xr;
+    const int ncg = f.ncg;
+    const int nq = 4 * ncg;               // channel quads per chunk
 
-    const int8_t* __restrict__ xg = (const int8_t*)a.xptr + ((int64_t)n * a.in_total + a.in_off + (int64_t)g * cin_g) * HW;
-    const int8_t* __restrict__ wg = (const int8_t*)a.wptr + (int64_t)(g * a.cout_g + co0) * cin_g * khw;
+    const int8_t* __restrict__ xg = (const int8_t*)a.xptr + ((int64_t)tl.n * a.in_total + a.in_off + (int64_t)tl.g * cin_g) * HW;
+    const int8_t* __restrict__ wg = (const int8_t*)a.wptr + (int64_t)(tl.g * a.cout_g + co0) * cin_g * khw;
 
-    // Patch pixel p (row-major, PW a multiple of 4) lives at slot
-    // (p % 4) * (PH * PW / 4) + p / 4: a thread's four pixels land in four
-    // quarters, and the words of consecutive threads 80 bytes apart.
-    uint8_t* xs = lds;                    // [PH * PW][XR]
-    uint8_t* ws = lds + f.xs_bytes;       // [khw][BM][XR]
+    uint8_t* xs = lds;                                  // [4 * QS][XR]
+    uint8_t* ws = lds + f.xs_bytes;                     // [steps][BM][WR]
+    int* itab = (int*)(lds + f.xs_bytes + f.ws_bytes);  // [4 * steps]: (tap's patch offset << 2) | channel group
+    const int pq_n = f.ph * f.pw4;        // 4-pixel words of the patch per channel quad
+    const int QS = f.qs;                  // slots per quarter of the patch (>= pq_n)
+
+    // Item table; weight rows of the items past the last one (the last K
+    // step's padding) stay zero for the whole kernel.
+    for (int i = tid; i < 4 * f.steps; i += kT) {
+        int e = 0;
+        if (i < f.items) {
+            const int tap = (int)divu((uint32_t)i, f.dv_ncg);
+            const int cg = i - tap * ncg;
+            const int r = (int)divu((uint32_t)tap, f.dv_kw);
+            const int s = tap - r * a.k_w;
+            e = ((r * a.dilation_h * PW + s * a.dilation_w) << 2) | cg;
+        }
+        itab[i] = e;
+    }
+    for (int v = tid; v < (4 * f.steps - f.items) * BM; v += kT) {
+        const int i = f.items + v / BM, co = v % BM;
+        *(i32x4*)&ws[((i >> 2) * BM + co) * WR + 16 * (i & 3)] = i32x4{0, 0, 0, 0};
+    }
 
     // This lane's pixel in each of its fragments: patch pixel of tap (0, 0).
     int pbase[NFW];
 #pragma unroll
-    for (int j = 0; j < NFW; ++j) {
-        const int oh = wave + 4 * j, ow = lane & 15;
-        pbase[j] = oh * a.stride_h * PW + ow * a.stride_w + shift;
-    }
+    for (int j = 0; j < NFW; ++j) pbase[j] = (wave + 4 * j) * a.stride_h * PW + (lane & 15) * a.stride_w + shift;
 
     i32x4 acc[NFW][MB];
 #pragma unroll
@@ -128,18 +478,14 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
 #pragma unroll
         for (int m = 0; m < MB; ++m) acc[j][m] = i32x4{0, 0, 0, 0};
 
-    const int pq_n = PH * f.pw4;          // 4-pixel words of the patch per channel quad
+    const int kq = lane >> 4;
     for (int kc = 0; kc < f.chunks; ++kc) {
-        const int c0 = kc * CK;
-        const int kq_n = min(CK, cin_g - c0 + 3) >> 2;   // channel quads holding data
-        // ---- patch -> LDS (pixel-major); quads past cin_g are left as they
-        // are: their weights are staged as zero ----
-        // Unit u: channel quad 4 * (u / (4 * pq_n)) + u % 4 and word rem =
-        // (u / 4) % pq_n of the patch (patch row pr, columns 4 * (rem % pw4)
-        // ..+3).  Four consecutive lanes take four channel quads of one word,
-        // so a wave's LDS stores cover every bank (see slot below).
-        const int kq4 = (kq_n + 3) & ~3;
-        const int units = kq4 * pq_n;
+        const int c0 = kc * 16 * ncg;
+        const int kq_n = min(nq, (cin_g - c0 + 3) >> 2);
+        // ---- patch -> LDS (pixel-major) in passes; quads past cin_g are
+        // left as they are: their weights are staged as zero.  Unit u: channel
+        // quad 4 * (u / (4 * pq_n)) + u % 4 and word rem = (u / 4) % pq_n. ----
+        const int units = ((kq_n + 3) & ~3) * pq_n;
         for (int u0 = 0; u0 < units; u0 += QV * kT) {
             uint32_t in[QV][4];
 #pragma unroll
@@ -149,8 +495,7 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
                 const int cq = 4 * hi + (u & 3);
                 const int rem = (u >> 2) - hi * pq_n;
                 const int pr = (int)divu((uint32_t)rem, f.dv_pw4);
-                const int pc = 4 * (rem - pr * f.pw4);
-                const int ih = ih0 + pr, iw = iw_a + pc;
+                const int ih = ih0 + pr, iw = iw_a + 4 * (rem - pr * f.pw4);
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
                     const int ch = c0 + 4 * cq + cc;
@@ -178,40 +523,45 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
                 const int rem = (u >> 2) - hi * pq_n;
                 uint32_t outw[4];
                 tr4x4(in[i], outw);
-                // rem = pr * pw4 + pc / 4, so byte b is patch pixel 4 * rem + b,
-                // kept at slot b * pq_n + rem.
+                // byte b of the word is patch pixel 4 * rem + b, at slot b * QS + rem
 #pragma unroll
-                for (int b = 0; b < 4; ++b) *(uint32_t*)&xs[(b * pq_n + rem) * XR + 4 * cq] = outw[b];
+                for (int b = 0; b < 4; ++b) *(uint32_t*)&xs[(b * QS + rem) * XR + 4 * cq] = outw[b];
             }
         }
-        // ---- weights -> LDS [tap][co][64 channels]; zero past the filter ----
-        for (int u = tid; u < BM * (CK / 4); u += kT) {
-            const int co = u >> 4, cq = u & 15;
+        // ---- weights: unit (co, cq) = one output channel's 4 input channels
+        // x all taps; word t (4 channels at tap t) belongs to item t * ncg +
+        // cq / 4, bytes 4 * (cq % 4) ..+3 of its 16 ----
+        auto w_slot = [&](int tap, int co, int cq) {
+            const int i = tap * ncg + (cq >> 2);
+            return &ws[((i >> 2) * BM + co) * WR + 16 * (i & 3) + 4 * (cq & 3)];
+        };
+        for (int u = tid; u < BM * nq; u += kT) {
+            const int co = u >> f.lg_nq, cq = u & (nq - 1);
             const int ci = c0 + 4 * cq;
             const bool live = co0 + co < a.cout_g && ci < cin_g;
             const int8_t* src = wg + ((int64_t)co * cin_g + ci) * khw;
             if (live && f.vec_w && ci + 4 <= cin_g) {
                 // cin_g % 4 == 0 and an aligned base: the 4 channels x khw taps
                 // are 4 * khw contiguous bytes starting on a word.
-                const uint32_t* src32 = (const uint32_t*)src;   // the block's khw words
+                const uint32_t* src32 = (const uint32_t*)src;
                 for (int t0 = 0; t0 < khw; t0 += 4) {
-                    // Taps t0 .. t0+3 of channels ci .. ci+3 sit at bytes c * khw + t.
-                    // Bytes past the block (taps past the window of the
-                    // last channel) are never written below; they read as 0.
-                    uint32_t wv[4];
+                    // Taps t0 .. t0+3 of channels ci .. ci+3 sit at bytes
+                    // c * khw + t.  Bytes past the block (taps past the window
+                    // of the last channel) are never stored below.
+                    uint32_t wv4[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int b0 = c * khw + t0;
                         const int wi = b0 >> 2;
                         const uint32_t lo = wi < khw ? src32[wi] : 0u;
                         const uint32_t hi = ((b0 & 3) && wi + 1 < khw) ? src32[wi + 1] : 0u;
-                        wv[c] = __builtin_amdgcn_alignbyte(hi, lo, b0 & 3);
+                        wv4[c] = __builtin_amdgcn_alignbyte(hi, lo, b0 & 3);
                     }
                     uint32_t outw[4];
-                    tr4x4(wv, outw);      // outw[t] = channels 0..3 at tap t0 + t
+                    tr4x4(wv4, outw);      // outw[t] = channels 0..3 at tap t0 + t
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        if (t0 + t < khw) *(uint32_t*)&ws[((t0 + t) * BM + co) * XR + 4 * cq] = outw[t];
+                        if (t0 + t < khw) *(uint32_t*)w_slot(t0 + t, co, cq) = outw[t];
                 }
             } else {
                 for (int t = 0; t < khw; ++t) {
@@ -221,24 +571,23 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
                         for (int c = 0; c < 4; ++c)
                             if (ci + c < cin_g) v |= (uint32_t)(uint8_t)src[c * khw + t] << (8 * c);
                     }
-                    *(uint32_t*)&ws[(t * BM + co) * XR + 4 * cq] = v;
+                    *(uint32_t*)w_slot(t, co, cq) = v;
                 }
             }
         }
         __syncthreads();
-        // ---- MFMAs: one K step per tap ----
-        for (int t = 0; t < khw; ++t) {
-            const int r = (int)divu((uint32_t)t, f.dv_kw);
-            const int s = t - r * a.k_w;
-            const int toff = r * a.dilation_h * PW + s * a.dilation_w;
+        // ---- MFMAs: four items per K step ----
+        for (int s = 0; s < f.steps; ++s) {
+            const int e = itab[4 * s + kq];
+            const int toff = e >> 2, cgo = (e & 3) << 4;
             i32x4 bw[MB];
 #pragma unroll
             for (int m = 0; m < MB; ++m)
-                bw[m] = *(const i32x4*)&ws[((t * BM) + 16 * m + (lane & 15)) * XR + 16 * (lane >> 4)];
+                bw[m] = *(const i32x4*)&ws[((s * BM) + 16 * m + (lane & 15)) * WR + 16 * kq];
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
                 const int pp = pbase[j] + toff;
-                const i32x4 av = *(const i32x4*)&xs[((pp & 3) * pq_n + (pp >> 2)) * XR + 16 * (lane >> 4)];
+                const i32x4 av = *(const i32x4*)&xs[((pp & 3) * QS + (pp >> 2)) * XR + cgo];
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
                     acc[j][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bw[m], acc[j][m], 0, 0, 0);
@@ -246,68 +595,80 @@ __global__ __launch_bounds__(kT) void igemm_i8_kernel(I8Args f) {
         }
         __syncthreads();
     }
-
-    // ---- epilogue: + bias, requant, 4 consecutive columns per lane ----
-    const bool relu = a.act == CONV_ACT_RELU;
-    const float lo = relu ? 0.0f : (float)(-128 - a.y_zp), hi = (float)(127 - a.y_zp);
-    const bool away = f.away != 0;
-    int8_t* __restrict__ yg = (int8_t*)a.yptr;
-    const int64_t oplane = (int64_t)a.ho * a.wo;
-    const bool vec_y = (a.wo % 4) == 0 && ((uintptr_t)a.yptr % 4) == 0;
-    const int wo = wo0 + 4 * (lane >> 4);
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        const int co = co0 + 16 * m + (lane & 15);
-        if (co >= a.cout_g) continue;
-        const int cg = g * a.cout_g + co;
-        const int32_t bb = a.qbias ? a.qbias[cg] : 0;
-        int8_t* yc = yg + ((int64_t)n * a.out_total + a.out_off + cg) * oplane;
-#pragma unroll
-        for (int j = 0; j < NFW; ++j) {
-            const int ho = ho0 + wave + 4 * j;
-            if (ho >= a.ho || wo >= a.wo) continue;
-            uint32_t word = 0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                word |= (uint32_t)(uint8_t)rq8(acc[j][m][v] + bb, a.composite, away, lo, hi, a.y_zp) << (8 * v);
-            int8_t* dst = yc + (int64_t)ho * a.wo + wo;
-            if (vec_y && wo + 4 <= a.wo) {
-                *(uint32_t*)dst = word;
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (wo + v < a.wo) dst[v] = (int8_t)(word >> (8 * v));
-            }
-        }
-    }
+    i8_epilogue<NFW, MB>(f, tl, acc, wave, 4, 0, co0, ho0, wo0, lane);
 }
 
 struct I8Plan {
-    int nfw, mb, th, ph, pw, xs_bytes, lds;
+    int nfw, mb, ncg, xr, qs, items, steps, th, ph, pw, xs_bytes, ws_bytes, lds;
 };
+
+// Slots per quarter of the patch: pixel p lives at slot (p % 4) * qs + p / 4
+// (a unit's four pixels in four quarters, so its transposed words go to
+// consecutive slots).  A pixel operand read takes 16 bytes at 16 pixels p0 +
+// l * stride; qs is padded so that any 8 of them (stride 1 or 2) fall on 8
+// distinct 16-byte bank groups of a 256-byte bank line: qs = 4 (mod 16)
+// when the slot size in 16-byte units (ncg + 1) is odd, qs = 2 (mod 8) when
+// it is even.
+int i8_qs(int words, int ncg) {
+    const int m = (ncg + 1) % 2 ? 16 : 8, r = (ncg + 1) % 2 ? 4 : 2;
+    return words + ((r - words % m) % m + m) % m;
+}
 
 constexpr int kLdsMax = 160 * 1024;
 
-// The largest tile that fits: 8 output rows (two fragments per wave) when
-// the patch and the weights fit in LDS, else 4; 64 output channels per
-// workgroup for windows of up to 9 taps, 32 for larger ones.
-bool i8_plan(const Desc& d, I8Plan* out) {
+// Output channels per workgroup: 64 for windows of up to 9 taps, 32 for
+// larger ones, and no more than the group has.  Chunks of 16 * ncg input
+// channels: for the generic kernel enough for the group (at most 64); for
+// the 3x3 kernel 16 or 32, which keeps a workgroup's LDS small enough for
+// three or four per CU (a 3x3 step then holds two taps of 32 channels; the
+// last of a chunk's five steps is half padding).  8 output rows (two
+// fragments per wave) when the LDS allows (and, for the 3x3 kernel, the
+// patch fits the prefetch registers), else 4.
+bool i8_plan(const Desc& d, bool fast, I8Plan* out) {
     const conv2d_params_t& p = d.p;
     const int khw = p.k_h * p.k_w;
-    const int mb = khw <= 9 ? 4 : 2;
+    if (fast && !(p.k_h == 3 && p.k_w == 3 && p.w % 4 == 0)) return false;
+    const int mb = d.cout_g <= 16 ? 1 : (d.cout_g <= 32 || khw > 9) ? 2 : 4;
+    const int ncg = fast ? (d.cin_g > 16 ? 2 : 1) : d.cin_g > 32 ? 4 : d.cin_g > 16 ? 2 : 1;
+    const int xr = 16 * ncg + 16;
+    const int items = khw * ncg, steps = (items + 3) / 4;
+    // channel quads of the first chunk, rounded up to 4 (a unit group)
+    const int quads = (std::min(4 * ncg, (d.cin_g + 3) / 4) + 3) / 4 * 4;
     for (int nfw = 2; nfw >= 1; --nfw) {
         const int th = 4 * nfw;
         const int ph = (th - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
         const int pw = ((3 + (TW - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1) + 3) / 4 * 4;
-        const int xs = ph * pw * XR;
-        const int lds = xs + khw * 16 * mb * XR;
-        if (lds <= 64 * 1024 || (nfw == 1 && lds <= kLdsMax)) {
-            *out = I8Plan{nfw, mb, th, ph, pw, xs, lds};
+        const int qs = i8_qs(ph * pw / 4, ncg);
+        const int xs = 4 * qs * xr;
+        // the 3x3 kernel: 64-byte weight rows in two buffers, no item table,
+        // 2 * ncg patch units per thread, 32-bit offsets within the chunk
+        const int wsb = fast ? steps * 16 * mb * 64 : steps * 16 * mb * WR;
+        const int lds = xs + (fast ? 2 * wsb : wsb + 16 * steps);
+        const bool fits = !fast || ((int64_t)quads * (ph * pw / 4) <= 2 * ncg * kT &&
+                                    (int64_t)16 * ncg * p.h * p.w < (1ll << 31));
+        if (fits && lds <= (nfw == 2 ? 80 * 1024 : kLdsMax)) {
+            *out = I8Plan{nfw, mb, ncg, xr, qs, items, steps, th, ph, pw, xs, wsb, lds};
             return true;
         }
     }
     return false;
 }
+
+template <int NFW, int MB>
+const void* i8_fast_fn(int ncg) {
+    return ncg == 2 ? (const void*)igemm_i8_fast_kernel<NFW, MB, 2> : (const void*)igemm_i8_fast_kernel<NFW, MB, 1>;
+}
+
+template <int NFW>
+const void* i8_fn(const I8Plan& ip, bool fast) {
+    if (fast) return ip.mb == 4 ? i8_fast_fn<NFW, 4>(ip.ncg) : ip.mb == 2 ? i8_fast_fn<NFW, 2>(ip.ncg) : i8_fast_fn<NFW, 1>(ip.ncg);
+    return ip.mb == 4 ? (const void*)igemm_i8_kernel<NFW, 4>
+         : ip.mb == 2 ? (const void*)igemm_i8_kernel<NFW, 2>
+                      : (const void*)igemm_i8_kernel<NFW, 1>;
+}
+
+int64_t i8_co_tiles(const Desc& d, const I8Plan& ip) { return (d.cout_g + 16 * ip.mb - 1) / (16 * ip.mb); }
+int64_t i8_chunks(const Desc& d, const I8Plan& ip) { return (d.cin_g + 16 * ip.ncg - 1) / (16 * ip.ncg); }
 
 }  // namespace
 
@@ -316,13 +677,45 @@ bool plan_igemm_i8(const Desc& d) {
     if (p.dtype != CONV_DTYPE_I8) return false;
     if ((int64_t)d.cin_g * p.k_h * p.k_w > (1 << 24)) return false;
     I8Plan ip{};
-    return i8_plan(d, &ip);
+    return i8_plan(d, false, &ip);
 }
 
-hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s) {
+int64_t igemm_i8_pack_bytes(const Desc& d) {
     I8Plan ip{};
-    if (!i8_plan(d, &ip)) return hipErrorInvalidConfiguration;
+    if (!i8_plan(d, true, &ip)) return 0;
+    return (int64_t)d.p.groups * i8_co_tiles(d, ip) * i8_chunks(d, ip) * ip.ws_bytes;
+}
+
+bool igemm_i8_fast(const Desc& d, const void* x) {
+    return igemm_i8_pack_bytes(d) > 0 && ((uintptr_t)x % 4) == 0;
+}
+
+hipError_t pack_igemm_i8_weights(const Desc& d, const void* w, void* dst, hipStream_t s) {
+    I8Plan ip{};
+    if (!i8_plan(d, true, &ip)) return hipErrorInvalidConfiguration;
+    I8PackArgs p;
+    p.cin_g = d.cin_g;
+    p.cout_g = d.cout_g;
+    p.bm = 16 * ip.mb;
+    p.ncg = ip.ncg;
+    p.steps = ip.steps;
+    p.co_tiles = (int32_t)i8_co_tiles(d, ip);
+    p.chunks = (int32_t)i8_chunks(d, ip);
+    p.words = igemm_i8_pack_bytes(d) / 4;
+    if (p.words == 0) return hipSuccess;
+    const int64_t blocks = (p.words + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    void* args[] = {(void*)&w, &dst, &p};
+    return hipLaunchKernel((const void*)pack_i8_kernel, dim3((uint32_t)blocks), dim3(256), args, 0, s);
+}
+
+hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s, const void* wpacked) {
     const conv2d_params_t& p = d.p;
+    const bool vec_x = p.w % 4 == 0 && ((uintptr_t)a.xptr % 4) == 0;
+    // The 3x3 kernel needs the packed image and word-aligned input rows.
+    I8Plan ip{};
+    const bool fast = wpacked && vec_x && i8_plan(d, true, &ip);
+    if (!fast && !i8_plan(d, false, &ip)) return hipErrorInvalidConfiguration;
     I8Args f;
     f.a = a;
     f.khw = p.k_h * p.k_w;
@@ -330,12 +723,19 @@ hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s) {
     f.ph = ip.ph;
     f.pw = ip.pw;
     f.pw4 = ip.pw / 4;
-    f.co_tiles = (d.cout_g + 16 * ip.mb - 1) / (16 * ip.mb);
+    f.ncg = ip.ncg;
+    f.lg_nq = ip.ncg == 1 ? 2 : ip.ncg == 2 ? 3 : 4;
+    f.xr = ip.xr;
+    f.qs = ip.qs;
+    f.items = ip.items;
+    f.steps = ip.steps;
+    f.co_tiles = (int32_t)i8_co_tiles(d, ip);
     f.tiles_h = (d.ho + ip.th - 1) / ip.th;
     f.tiles_w = (d.wo + TW - 1) / TW;
-    f.chunks = (d.cin_g + CK - 1) / CK;
+    f.chunks = (int32_t)i8_chunks(d, ip);
     f.xs_bytes = ip.xs_bytes;
-    f.vec_x = p.w % 4 == 0 && ((uintptr_t)a.xptr % 4) == 0;
+    f.ws_bytes = ip.ws_bytes;
+    f.vec_x = vec_x;
     f.vec_w = d.cin_g % 4 == 0 && ((uintptr_t)a.wptr % 4) == 0;
     f.away = p.int8_rounding == CONV_ROUND_HALF_AWAY;
     f.dv_co_tiles = make_divu32((uint32_t)f.co_tiles);
@@ -345,15 +745,19 @@ hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s) {
     f.dv_pw4 = make_divu32((uint32_t)f.pw4);
     f.dv_ppix = make_divu32((uint32_t)(ip.ph * f.pw4));
     f.dv_kw = make_divu32((uint32_t)p.k_w);
+    f.dv_ncg = make_divu32((uint32_t)ip.ncg);
     const uint64_t blocks = (uint64_t)f.co_tiles * p.groups * f.tiles_w * f.tiles_h * p.n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     f.num_blocks = (uint32_t)blocks;
-    const void* fn = ip.nfw == 2 ? (ip.mb == 4 ? (const void*)igemm_i8_kernel<2, 4> : (const void*)igemm_i8_kernel<2, 2>)
-                                 : (ip.mb == 4 ? (const void*)igemm_i8_kernel<1, 4> : (const void*)igemm_i8_kernel<1, 2>);
+    const void* fn = ip.nfw == 2 ? i8_fn<2>(ip, fast) : i8_fn<1>(ip, fast);
     if (ip.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, ip.lds);
         if (e != hipSuccess) return e;
+    }
+    if (fast) {
+        void* args[] = {&f, (void*)&wpacked};
+        return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kT), args, ip.lds, s);
     }
     void* args[] = {&f};
     return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kT), args, ip.lds, s);

@@ -2,7 +2,8 @@
 bit-exact against the oracle's int64 QLinearConv.
 
 Cases reach every path of the kernel: one and several 64-channel chunks with
-partial ones, output-channel tiles of 64 (windows up to 9 taps) and 32
+partial ones, 3x3 chunks held in registers (one and two fragments per wave,
+1, 2 and 4 sixteen-channel groups per item list), output-channel tiles of 64 (windows up to 9 taps) and 32
 (larger windows), one and two output-row fragments per wave, stride,
 dilation, asymmetric pads, non-square windows, grouped convolutions with 4,
 8, 16 and 72 channels per group and a channel multiplier, rows that are not
@@ -45,6 +46,12 @@ CASES = [
     (1, 144, 8, 8, 144, 3, 1, 1, 1, 2),          # grouped, 72 per group (two chunks per group)
     (1, 6, 9, 11, 12, 3, 1, 1, 1, 6),            # channel multiplier 2 (groups == c_in < c_out)
     (3, 5, 6, 7, 9, 3, 1, 1, 1, 1),              # tiny, odd everything
+    # 3x3 over word-aligned rows and filters: the chunk held in registers
+    (1, 128, 20, 40, 64, 3, 2, 1, 1, 1),         # stride 2, two chunks, one fragment per wave (patch > 2048 units)
+    (2, 8, 16, 24, 16, 3, 1, 1, 1, 1),           # 8 channels: four taps per K step, 16 output channels
+    (1, 48, 9, 16, 24, 3, 1, 1, 1, 1),           # 12 of 16 channel quads, 32-channel tile
+    (1, 36, 8, 12, 20, 3, 1, 1, 1, 2),           # 18 per group: two 16-channel groups per item list
+    (2, 200, 6, 8, 70, 3, 1, (1, 0, 2, 1), 1, 1),  # four chunks (the last 8 channels), ragged channel tile
 ]
 
 
@@ -119,6 +126,22 @@ def test_igemm_i8_unaligned_input_slices_and_bound_weights():
     t.cuda.synchronize()
     y.check_guards()
     assert_bitexact(y.host().numpy().reshape(n, ot, ho, wo), got, "bound weights")
+
+
+@pytest.mark.parametrize("name", ["s2", "d2", "g32"])
+def test_igemm_i8_mixed_sweep_shapes(name):
+    """The mixed sweep's strided, dilated and grouped 3x3 layers at full
+    size (the bench's batch of 32), every output compared."""
+    L0 = next(L for L in workloads.mixed_sweep_layers() if L.name == name)
+    L = workloads.Layer(name, L0.n, L0.c_in, L0.h, L0.w, L0.c_out, L0.k, stride=L0.stride, pads=L0.pads,
+                        dilation=L0.dilation, groups=L0.groups, has_bias=True)
+    rng = np.random.default_rng(2197)
+    x, wt, b = _arrays(rng, L)
+    print(f"{name}: {L}", flush=True)
+    ref = oracle.qconv2d(x, wt, b, *SYM, stride=L.stride, pads=L.pads, dilation=L.dilation, groups=L.groups)
+    got, d = _run(L, to_dev(x), to_dev(wt), to_dev(b), SYM)
+    assert cc().conv2d_desc_kernel_name(d) == "igemm_i8"
+    assert_bitexact(got, ref, f"mixed sweep {name}")
 
 
 def test_igemm_i8_dense_full_size():
