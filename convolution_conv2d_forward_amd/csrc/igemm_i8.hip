@@ -201,8 +201,47 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds_b
 // (tap i / ncg, channel group i % ncg) as W[co][16 * cg .. +15][tap], piece
 // kq stored at position kq ^ ((co / 4) % 4).  Items past the last, channels
 // past the group and channels past cout_g are zero.
+// The kernel is persistent: workgroup b takes tiles b', b' + G, b' + 2G, ...
+// (G workgroups, b' its XCD-grouped index), and the pipeline runs across
+// tile boundaries, so the first chunk of the next tile is in flight during
+// the last chunk's MFMAs and the epilogue.
+struct I8TileGeo {
+    int g, co0, ho0, wo0, ih0, iw_a, n;
+};
+
+__device__ __forceinline__ I8TileGeo i8_geo(const I8Args& f, uint32_t L, int BM) {
+    const ConvArgs& a = f.a;
+    I8TileGeo t;
+    uint32_t Q = divu(L, f.dv_co_tiles);
+    t.co0 = (int)(L - Q * f.co_tiles) * BM;
+    L = Q; Q = divu(L, f.dv_groups);
+    t.g = (int)(L - Q * a.groups);
+    L = Q; Q = divu(L, f.dv_tiles_w);
+    t.wo0 = (int)(L - Q * f.tiles_w) * TW;
+    L = Q; Q = divu(L, f.dv_tiles_h);
+    t.ho0 = (int)(L - Q * f.tiles_h) * f.th;
+    t.n = (int)Q;
+    t.ih0 = t.ho0 * a.stride_h - a.pad_top;
+    const int iw_lo = t.wo0 * a.stride_w - a.pad_left;
+    t.iw_a = iw_lo >= 0 ? iw_lo & ~3 : -((-iw_lo + 3) & ~3);   // patch column 0, a multiple of 4
+    return t;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// base + off and writes lds_base + 16*l (base and lds_base wave-uniform).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16s_to_lds(const uint8_t* base, uint32_t off, const void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m)
+                 : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
 template <int NFW, int MB, int NCG>
-__global__ __launch_bounds__(kT, 3) void igemm_i8_fast_kernel(I8Args f, const uint8_t* __restrict__ wpk) {
+__global__ __launch_bounds__(kT, 2) void igemm_i8_fast_kernel(I8Args f, const uint8_t* __restrict__ wpk) {
     extern __shared__ __align__(16) uint8_t lds[];
     const ConvArgs& a = f.a;
     constexpr int BM = 16 * MB;
@@ -213,68 +252,58 @@ __global__ __launch_bounds__(kT, 3) void igemm_i8_fast_kernel(I8Args f, const ui
     constexpr int XR = 16 * NCG + 16;           // LDS bytes per patch pixel
     constexpr int NQ = 4 * NCG;                 // channel quads per chunk
     constexpr int CKC = 16 * NCG;               // input channels per chunk
-    constexpr int UQ = 2 * NCG;                 // patch units per thread held in registers
+    constexpr int UQ = 3 * NCG;                 // patch units per thread held in registers
     constexpr int WIMG = STEPS * BM * 64;       // bytes of a chunk's weight image
+    constexpr int PIECES = WIMG / 1024;         // 1 KB copies per chunk image
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wr = wave / WM;
     const int kq = lane >> 4;
 
-    const I8Tile t = i8_tile(f);
-    const int co0 = t.cot * BM;
-    const int ho0 = t.thi * f.th, wo0 = t.twi * TW;
-    const int ih0 = ho0 * a.stride_h - a.pad_top;
-    const int iw_lo = wo0 * a.stride_w - a.pad_left;
-    const int iw_a = iw_lo >= 0 ? iw_lo & ~3 : -((-iw_lo + 3) & ~3);   // patch column 0, a multiple of 4
-    const int shift = iw_lo - iw_a;
     const int H = a.h, W = a.w;
     const int64_t HW = (int64_t)H * W;
+    const uint32_t HW32 = (uint32_t)HW;
     const int cin_g = a.cin_g;
     const int PW = f.pw;
     const int pq_n = f.ph * f.pw4;       // 4-pixel words of the patch per channel quad
     const int QS = f.qs;                 // slots per quarter of the patch (>= pq_n)
-
-    const int8_t* __restrict__ xg = (const int8_t*)a.xptr + ((int64_t)t.n * a.in_total + a.in_off + (int64_t)t.g * cin_g) * HW;
-    const uint8_t* __restrict__ wimg = wpk + ((int64_t)(t.g * f.co_tiles + t.cot) * f.chunks) * WIMG;
+    const int chunks = f.chunks;
+    // The patch starts 0-3 columns left of the first input column a tile
+    // reads; tiles start at multiples of 16 output columns, so this shift is
+    // the same for every tile.
+    const int shift = (((-a.pad_left) % 4) + 4) % 4;
 
     uint8_t* xs = lds;                   // [4 * QS][XR]; pixel p at slot (p % 4) * QS + p / 4
     uint8_t* ws = lds + f.xs_bytes;      // two buffers of [STEPS][BM][64]
 
-    // This lane's patch offset and channel-group byte per K step: item 4s + kq.
-    int toff[STEPS], cgo[STEPS];
+    // Per lane, the same for every tile: the LDS address of its pixel
+    // operand for each K step (item 4s + kq) and fragment, and of its weight
+    // operand (row s * BM + 16 * m + lane % 16, piece kq at its rotated place).
+    int aoff[STEPS][NFR];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
         const int i = 4 * s + kq;
         const int tap = i / NCG, cg = i % NCG;
         const int r = (tap * 11) >> 5;   // tap / 3 for tap < 12
         const bool live = i < 9 * NCG;
-        toff[s] = live ? r * a.dilation_h * PW + (tap - 3 * r) * a.dilation_w : 0;
-        cgo[s] = live ? 16 * cg : 0;
+        const int toff = live ? r * a.dilation_h * PW + (tap - 3 * r) * a.dilation_w : 0;
+        const int cgo = live ? 16 * cg : 0;
+#pragma unroll
+        for (int j = 0; j < NFR; ++j) {
+            const int pp = (wr * NFR + j) * a.stride_h * PW + (lane & 15) * a.stride_w + shift + toff;
+            aoff[s][j] = ((pp & 3) * QS + (pp >> 2)) * XR + cgo;
+        }
     }
-    int pbase[NFR];
-#pragma unroll
-    for (int j = 0; j < NFR; ++j) pbase[j] = (wr * NFR + j) * a.stride_h * PW + (lane & 15) * a.stride_w + shift;
-    // B-operand read of channel tile m at step s: row s * BM + 16 * m + lane % 16,
-    // piece kq at its rotated position.
     const int boff = (16 * wm * MBW + (lane & 15)) * 64 + 16 * (kq ^ ((lane >> 2) & 3));
-
-    i32x4 acc[NFR][MBW];
-#pragma unroll
-    for (int j = 0; j < NFR; ++j)
-#pragma unroll
-        for (int m = 0; m < MBW; ++m) acc[j][m] = i32x4{0, 0, 0, 0};
 
     // Patch unit u: channel quad 4 * (u / (4 * pq_n)) + u % 4 and word rem =
     // (u / 4) % pq_n (patch row rem / pw4, columns 4 * (rem % pw4) ..+3).
     // Four consecutive lanes take four channel quads of one word, so a
     // wave's transposed words fill 16 bytes of each of 16 consecutive slots
-    // (every bank once).  A unit's place in the image and in LDS is the same
-    // for every chunk: its offset within a channel plane (0 outside the
-    // image), channel quad and LDS slot are worked out once.
-    const int units0 = ((min(NQ, (cin_g + 3) >> 2) + 3) & ~3) * pq_n;   // units of the first (largest) chunk
-    uint32_t goff[UQ];
-    int cqs[UQ], sbase[UQ];
-    uint32_t inimg = 0;
+    // (every bank once).  Per unit, the same for every tile: patch row and
+    // column, the offset of its first channel, and its LDS place.
+    const int units0 = ((min(NQ, (cin_g + 3) >> 2) + 3) & ~3) * pq_n;   // units of a full chunk
+    int upr[UQ], upc[UQ], ucq[UQ], sbase[UQ];
 #pragma unroll
     for (int i = 0; i < UQ; ++i) {
         const int u = tid + i * kT;
@@ -282,81 +311,96 @@ __global__ __launch_bounds__(kT, 3) void igemm_i8_fast_kernel(I8Args f, const ui
         const int cq = 4 * hi + (u & 3);
         const int rem = (u >> 2) - hi * pq_n;
         const int pr = (int)divu((uint32_t)rem, f.dv_pw4);
-        const int ih = ih0 + pr, iw = iw_a + 4 * (rem - pr * f.pw4);
-        // W % 4 == 0 and iw % 4 == 0: the word is inside the row or outside it.
-        const bool in = u < units0 && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
-        goff[i] = in ? (uint32_t)(ih * W + iw) : 0u;
-        cqs[i] = cq;
-        // byte b of the word is patch pixel 4 * rem + b, at slot b * QS + rem
-        sbase[i] = rem * XR + 4 * cq;
-        inimg |= (in ? 1u : 0u) << i;
+        upr[i] = u < units0 ? pr : -(1 << 20);   // units past the chunk: never inside the image
+        upc[i] = 4 * (rem - pr * f.pw4);
+        ucq[i] = 4 * cq;
+        // byte b of the word is patch pixel 4 * rem + b, at slot b * QS + rem;
+        // units past the chunk store their zeros to slot pq_n of each
+        // quarter, which no pixel uses
+        sbase[i] = u < units0 ? rem * XR + 4 * cq : pq_n * XR;
     }
-    const uint32_t HW32 = (uint32_t)HW;
 
-    uint32_t pv[UQ][4];
-    uint32_t plive = 0;
-    // Loads at clamped offsets (a unit outside the image, or a channel past
-    // cin_g, reads the chunk's first byte), all issued back to back; the
-    // zeros of units outside the image are chosen when the chunk is stored.
-    auto load_patch = [&](int kc) {
-        const int cleft = cin_g - kc * CKC;              // channels left from this chunk on
-        const int kq_n = min(NQ, (cleft + 3) >> 2);
-        const int8_t* xc = xg + (int64_t)kc * CKC * HW;
-        plive = 0;
+    // A tile's patch offsets: channel 4 * cq's word inside the image, or an
+    // offset past every buffer range (the buffer load then returns zero).
+    uint32_t goff[UQ];
+    auto set_units = [&](const I8TileGeo& t) {
 #pragma unroll
         for (int i = 0; i < UQ; ++i) {
-            if (i * kT >= units0) break;
-            const bool ok = ((inimg >> i) & 1u) && cqs[i] < kq_n;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int ch = 4 * cqs[i] + cc;
-                const uint32_t off = ok && ch < cleft ? goff[i] + (uint32_t)ch * HW32 : 0u;
-                pv[i][cc] = *(const uint32_t*)(xc + off);
-            }
-            plive |= (ok ? 1u : 0u) << i;
+            const int ih = t.ih0 + upr[i], iw = t.iw_a + upc[i];
+            // W % 4 == 0 and iw % 4 == 0: the word is inside the row or outside it.
+            const bool in = (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+            goff[i] = in ? (uint32_t)(ih * W + iw) + (uint32_t)ucq[i] * HW32 : 0x80000000u;
         }
     };
-    auto store_patch = [&](int kc) {
-        const int kq_n = min(NQ, (cin_g - kc * CKC + 3) >> 2);
+    uint32_t pv[UQ][4];
+    // Chunk kc of tile t: the patch words through four buffer resources,
+    // resource cc starting at the chunk's channel cc and ending at its last
+    // channel (channels past cin_g and units outside the image read as
+    // zero), the weight image into LDS buffer wb.
+    auto issue = [&](const I8TileGeo& t, int kc, int wb) {
+        const int cleft = min(CKC, cin_g - kc * CKC);
+        const int8_t* xc = (const int8_t*)a.xptr +
+                           ((int64_t)t.n * a.in_total + a.in_off + (int64_t)t.g * cin_g + (int64_t)kc * CKC) * HW;
+        __amdgpu_buffer_rsrc_t rs[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+            rs[cc] = __builtin_amdgcn_make_buffer_rsrc((void*)(xc + cc * HW), (short)0,
+                                                       (int)((uint32_t)max(cleft - cc, 0) * HW32), 0x00020000);
+        const uint8_t* wsrc = wpk + ((int64_t)(t.g * f.co_tiles + t.co0 / BM) * chunks + kc) * WIMG;
+        uint8_t* wdst = ws + wb * WIMG;
+#pragma unroll
+        for (int p = 0; p < (PIECES + 3) / 4; ++p) {
+            const int piece = wave + 4 * p;
+            if (piece < PIECES) copy16s_to_lds(wsrc + 4096 * p, (uint32_t)(wave * 1024 + 16 * lane), wdst + piece * 1024);
+        }
 #pragma unroll
         for (int i = 0; i < UQ; ++i) {
             if (i * kT >= units0) break;
-            if (tid + i * kT >= units0 || cqs[i] >= kq_n) continue;
-            uint32_t in[4], outw[4];
-            const bool ok = (plive >> i) & 1u;
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) in[cc] = ok ? pv[i][cc] : 0u;
-            tr4x4(in, outw);
+            for (int cc = 0; cc < 4; ++cc)
+                pv[i][cc] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs[cc], (int)goff[i], 0, 0);
+        }
+    };
+    auto store_patch = [&]() {
+#pragma unroll
+        for (int i = 0; i < UQ; ++i) {
+            if (i * kT >= units0) break;
+            uint32_t outw[4];
+            tr4x4(pv[i], outw);
 #pragma unroll
             for (int b = 0; b < 4; ++b) *(uint32_t*)&xs[b * QS * XR + sbase[i]] = outw[b];
         }
     };
-    // A chunk's weight image (WIMG / 1024 copies of 1 KB, spread over the
-    // waves) into buffer kc % 2.
-    auto copy_weights = [&](int kc) {
-        const uint8_t* src = wimg + (int64_t)kc * WIMG;
-        uint8_t* dst = ws + (kc & 1) * WIMG;
-#pragma unroll
-        for (int p = 0; p < (WIMG / 1024 + 3) / 4; ++p) {
-            const int piece = wave + 4 * p;
-            if (piece < WIMG / 1024) copy16_to_lds(src + piece * 1024 + 16 * lane, dst + piece * 1024);
-        }
-    };
 
-    // Chunk kc+1's weights are copied, and its patch loaded into registers,
-    // while chunk kc's MFMAs run; the weight images alternate between two
-    // LDS buffers, the patch has one (stored after the MFMAs that read it).
-    copy_weights(0);
-    load_patch(0);
-    for (int kc = 0; kc < f.chunks; ++kc) {
-        store_patch(kc);
-        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's copies of chunk kc have landed
-        __syncthreads();                      // ... and every thread's; chunk kc-1's MFMAs are done
-        if (kc + 1 < f.chunks) {
-            copy_weights(kc + 1);
-            load_patch(kc + 1);
+    i32x4 acc[NFR][MBW];
+#pragma unroll
+    for (int j = 0; j < NFR; ++j)
+#pragma unroll
+        for (int m = 0; m < MBW; ++m) acc[j][m] = i32x4{0, 0, 0, 0};
+
+    const uint32_t ntiles = f.num_blocks, G = gridDim.x;
+    uint32_t tl = xcd_remap(blockIdx.x, G);
+    I8TileGeo cur = i8_geo(f, tl, BM);
+    set_units(cur);
+    issue(cur, 0, 0);
+    int kc = 0, wb = 0;
+    for (;;) {
+        store_patch();
+        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's copies of the chunk have landed
+        __syncthreads();                      // ... and every thread's; the previous chunk's MFMAs are done
+        // the next chunk: of this tile, or the first of the next one
+        const bool last = kc + 1 == chunks;
+        const uint32_t tn = last ? tl + G : tl;
+        const bool more = tn < ntiles;
+        I8TileGeo nxt = cur;
+        if (more) {
+            if (last) {
+                nxt = i8_geo(f, tn, BM);
+                set_units(nxt);
+            }
+            issue(nxt, last ? 0 : kc + 1, wb ^ 1);
         }
-        const uint8_t* wsc = ws + (kc & 1) * WIMG;
+        const uint8_t* wsc = ws + wb * WIMG;
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             i32x4 bw[MBW];
@@ -364,53 +408,64 @@ __global__ __launch_bounds__(kT, 3) void igemm_i8_fast_kernel(I8Args f, const ui
             for (int m = 0; m < MBW; ++m) bw[m] = *(const i32x4*)&wsc[s * BM * 64 + m * 1024 + boff];
 #pragma unroll
             for (int j = 0; j < NFR; ++j) {
-                const int pp = pbase[j] + toff[s];
-                const i32x4 av = *(const i32x4*)&xs[((pp & 3) * QS + (pp >> 2)) * XR + cgo[s]];
+                const i32x4 av = *(const i32x4*)&xs[aoff[s][j]];
 #pragma unroll
                 for (int m = 0; m < MBW; ++m)
                     acc[j][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bw[m], acc[j][m], 0, 0, 0);
             }
         }
+        if (last) {
+            I8Tile t;
+            t.g = cur.g;
+            t.n = cur.n;
+            i8_epilogue<NFR, MBW>(f, t, acc, wr * NFR, 1, wm * MBW, cur.co0, cur.ho0, cur.wo0, lane);
+#pragma unroll
+            for (int j = 0; j < NFR; ++j)
+#pragma unroll
+                for (int m = 0; m < MBW; ++m) acc[j][m] = i32x4{0, 0, 0, 0};
+        }
         __syncthreads();
+        if (!more) break;
+        cur = nxt;
+        tl = tn;
+        kc = last ? 0 : kc + 1;
+        wb ^= 1;
     }
-    i8_epilogue<NFR, MBW>(f, t, acc, wr * NFR, 1, wm * MBW, co0, ho0, wo0, lane);
 }
 
 // OIHW int8 -> the fast kernel's per-chunk weight images, one thread per
-// 4-byte word of the output.
+// 16-byte piece of the output (16 channels of one item).
 struct I8PackArgs {
     int32_t cin_g, cout_g, bm, ncg, steps, co_tiles, chunks;
     int64_t words;
 };
 
-__global__ __launch_bounds__(256) void pack_i8_kernel(const int8_t* __restrict__ w, uint32_t* __restrict__ dst,
+__global__ __launch_bounds__(256) void pack_i8_kernel(const int8_t* __restrict__ w, uint4* __restrict__ dst,
                                                       I8PackArgs p) {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= p.words) return;
-    const int img_words = p.steps * p.bm * 16;
-    const int64_t img = q / img_words;
-    const int ob = (int)(q - img * img_words) * 4;      // byte offset in the image
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;     // 16-byte piece of the output
+    if (q >= p.words / 4) return;
+    const int img_pieces = p.steps * p.bm * 4;
+    const int64_t img = q / img_pieces;
+    const int r = (int)(q - img * img_pieces);
     const int kc = (int)(img % p.chunks);
     const int64_t gt = img / p.chunks;
     const int cot = (int)(gt % p.co_tiles);
     const int g = (int)(gt / p.co_tiles);
-    const int s = ob / (p.bm * 64);
-    const int row = (ob / 64) % p.bm;
-    const int pos = ob % 64;
-    const int kq = (pos >> 4) ^ ((row >> 2) & 3);
+    const int s = r / (p.bm * 4);
+    const int row = (r >> 2) % p.bm;
+    const int kq = (r & 3) ^ ((row >> 2) & 3);          // the item stored at this position
     const int i = 4 * s + kq;
     const int co = cot * p.bm + row;
-    uint32_t v = 0;
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
     if (i < 9 * p.ncg && co < p.cout_g) {
         const int tap = i / p.ncg, cg = i % p.ncg;
-        const int8_t* wc = w + ((int64_t)g * p.cout_g + co) * p.cin_g * 9;
+        const int c0 = kc * 16 * p.ncg + 16 * cg;
+        const int8_t* wc = w + (((int64_t)g * p.cout_g + co) * p.cin_g + c0) * 9 + tap;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int c = kc * 16 * p.ncg + 16 * cg + (pos & 15) + b;
-            if (c < p.cin_g) v |= (uint32_t)(uint8_t)wc[(int64_t)c * 9 + tap] << (8 * b);
-        }
+        for (int b = 0; b < 16; ++b)
+            if (c0 + b < p.cin_g) v[b >> 2] |= (uint32_t)(uint8_t)wc[b * 9] << (8 * (b & 3));
     }
-    dst[q] = v;
+    dst[q] = uint4{v[0], v[1], v[2], v[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -621,9 +676,9 @@ constexpr int kLdsMax = 160 * 1024;
 // channels: for the generic kernel enough for the group (at most 64); for
 // the 3x3 kernel 16 or 32, which keeps a workgroup's LDS small enough for
 // three or four per CU (a 3x3 step then holds two taps of 32 channels; the
-// last of a chunk's five steps is half padding).  8 output rows (two
-// fragments per wave) when the LDS allows (and, for the 3x3 kernel, the
-// patch fits the prefetch registers), else 4.
+// last of a chunk's five steps is half padding).  The tallest tile whose
+// LDS allows two workgroups per CU (and, for the 3x3 kernel, whose patch
+// fits the prefetch registers): 16 output rows (3x3 kernel only), 8 or 4.
 bool i8_plan(const Desc& d, bool fast, I8Plan* out) {
     const conv2d_params_t& p = d.p;
     const int khw = p.k_h * p.k_w;
@@ -634,19 +689,20 @@ bool i8_plan(const Desc& d, bool fast, I8Plan* out) {
     const int items = khw * ncg, steps = (items + 3) / 4;
     // channel quads of the first chunk, rounded up to 4 (a unit group)
     const int quads = (std::min(4 * ncg, (d.cin_g + 3) / 4) + 3) / 4 * 4;
-    for (int nfw = 2; nfw >= 1; --nfw) {
+    // the 3x3 kernel also has 16-row tiles (four fragments per wave)
+    for (int nfw = fast ? 4 : 2; nfw >= 1; nfw /= 2) {
         const int th = 4 * nfw;
         const int ph = (th - 1) * p.stride_h + (p.k_h - 1) * p.dilation_h + 1;
         const int pw = ((3 + (TW - 1) * p.stride_w + (p.k_w - 1) * p.dilation_w + 1) + 3) / 4 * 4;
-        const int qs = i8_qs(ph * pw / 4, ncg);
+        const int qs = i8_qs(ph * pw / 4 + 1, ncg);   // + a slot no pixel uses
         const int xs = 4 * qs * xr;
         // the 3x3 kernel: 64-byte weight rows in two buffers, no item table,
-        // 2 * ncg patch units per thread, 32-bit offsets within the chunk
+        // 3 * ncg patch units per thread, 32-bit offsets within the chunk
         const int wsb = fast ? steps * 16 * mb * 64 : steps * 16 * mb * WR;
         const int lds = xs + (fast ? 2 * wsb : wsb + 16 * steps);
-        const bool fits = !fast || ((int64_t)quads * (ph * pw / 4) <= 2 * ncg * kT &&
+        const bool fits = !fast || ((int64_t)quads * (ph * pw / 4) <= 3 * ncg * kT &&
                                     (int64_t)16 * ncg * p.h * p.w < (1ll << 31));
-        if (fits && lds <= (nfw == 2 ? 80 * 1024 : kLdsMax)) {
+        if (fits && lds <= (nfw >= 2 ? 80 * 1024 : kLdsMax)) {
             *out = I8Plan{nfw, mb, ncg, xr, qs, items, steps, th, ph, pw, xs, wsb, lds};
             return true;
         }
@@ -665,6 +721,24 @@ const void* i8_fn(const I8Plan& ip, bool fast) {
     return ip.mb == 4 ? (const void*)igemm_i8_kernel<NFW, 4>
          : ip.mb == 2 ? (const void*)igemm_i8_kernel<NFW, 2>
                       : (const void*)igemm_i8_kernel<NFW, 1>;
+}
+
+const void* i8_fast_nfw4(const I8Plan& ip) {
+    return ip.mb == 4 ? i8_fast_fn<4, 4>(ip.ncg) : ip.mb == 2 ? i8_fast_fn<4, 2>(ip.ncg) : i8_fast_fn<4, 1>(ip.ncg);
+}
+
+// Compute units of the current device (256 on MI355X).
+int i8_cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cached = v;
+        else
+            cached = 256;
+    }
+    return cached;
 }
 
 int64_t i8_co_tiles(const Desc& d, const I8Plan& ip) { return (d.cout_g + 16 * ip.mb - 1) / (16 * ip.mb); }
@@ -703,7 +777,7 @@ hipError_t pack_igemm_i8_weights(const Desc& d, const void* w, void* dst, hipStr
     p.chunks = (int32_t)i8_chunks(d, ip);
     p.words = igemm_i8_pack_bytes(d) / 4;
     if (p.words == 0) return hipSuccess;
-    const int64_t blocks = (p.words + 255) / 256;
+    const int64_t blocks = (p.words / 4 + 255) / 256;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     void* args[] = {(void*)&w, &dst, &p};
     return hipLaunchKernel((const void*)pack_i8_kernel, dim3((uint32_t)blocks), dim3(256), args, 0, s);
@@ -750,14 +824,22 @@ hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s, const void*
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
     f.num_blocks = (uint32_t)blocks;
-    const void* fn = ip.nfw == 2 ? i8_fn<2>(ip, fast) : i8_fn<1>(ip, fast);
+    const void* fn = ip.nfw == 4 ? i8_fast_nfw4(ip) : ip.nfw == 2 ? i8_fn<2>(ip, fast) : i8_fn<1>(ip, fast);
     if (ip.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, ip.lds);
         if (e != hipSuccess) return e;
     }
     if (fast) {
+        // persistent: as many workgroups as fit on the device at once (each
+        // then takes every G-th tile), a multiple of 8 for the XCD grouping
+        int per_cu = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kT, ip.lds);
+        if (e != hipSuccess) return e;
+        uint64_t g = (uint64_t)std::max(per_cu, 1) * i8_cu_count();
+        g = std::min<uint64_t>(g, blocks);
+        if (g > 8) g &= ~7ull;
         void* args[] = {&f, (void*)&wpacked};
-        return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kT), args, ip.lds, s);
+        return hipLaunchKernel(fn, dim3((uint32_t)g), dim3(kT), args, ip.lds, s);
     }
     void* args[] = {&f};
     return hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kT), args, ip.lds, s);
