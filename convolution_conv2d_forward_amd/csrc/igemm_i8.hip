@@ -351,7 +351,9 @@ __global__ __launch_bounds__(kT, 2) void igemm_i8_fast_kernel(I8Args f, const ui
 #pragma unroll
         for (int p = 0; p < (PIECES + 3) / 4; ++p) {
             const int piece = wave + 4 * p;
-            if (piece < PIECES) copy16s_to_lds(wsrc + 4096 * p, (uint32_t)(wave * 1024 + 16 * lane), wdst + piece * 1024);
+            // (every wave copies PIECES / 4 pieces when 4 divides PIECES)
+            if (PIECES % 4 == 0 || piece < PIECES)
+                copy16s_to_lds(wsrc + 4096 * p, (uint32_t)(wave * 1024 + 16 * lane), wdst + piece * 1024);
         }
 #pragma unroll
         for (int i = 0; i < UQ; ++i) {

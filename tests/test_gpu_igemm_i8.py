@@ -128,10 +128,12 @@ def test_igemm_i8_unaligned_input_slices_and_bound_weights():
     assert_bitexact(y.host().numpy().reshape(n, ot, ho, wo), got, "bound weights")
 
 
+@pytest.mark.parametrize("bound", [False, True])
 @pytest.mark.parametrize("name", ["s2", "d2", "g32"])
-def test_igemm_i8_mixed_sweep_shapes(name):
+def test_igemm_i8_mixed_sweep_shapes(name, bound):
     """The mixed sweep's strided, dilated and grouped 3x3 layers at full
-    size (the bench's batch of 32), every output compared."""
+    size (the bench's batch of 32), every output compared; with the weights
+    passed per call and bound to the descriptor (as the bench times them)."""
     L0 = next(L for L in workloads.mixed_sweep_layers() if L.name == name)
     L = workloads.Layer(name, L0.n, L0.c_in, L0.h, L0.w, L0.c_out, L0.k, stride=L0.stride, pads=L0.pads,
                         dilation=L0.dilation, groups=L0.groups, has_bias=True)
@@ -139,9 +141,20 @@ def test_igemm_i8_mixed_sweep_shapes(name):
     x, wt, b = _arrays(rng, L)
     print(f"{name}: {L}", flush=True)
     ref = oracle.qconv2d(x, wt, b, *SYM, stride=L.stride, pads=L.pads, dilation=L.dilation, groups=L.groups)
-    got, d = _run(L, to_dev(x), to_dev(wt), to_dev(b), SYM)
+    if not bound:
+        got, d = _run(L, to_dev(x), to_dev(wt), to_dev(b), SYM)
+    else:
+        t = torch()
+        d = cc().conv2d_desc_create(layer_params(L, "i8"))
+        cc().conv2d_desc_bind_weights(d, to_dev(wt))
+        n, ot, ho, wo = cc().conv2d_desc_get_output_shape(d)
+        y = Guarded(n * ot * ho * wo, t.int8, 0x5A)
+        cc().qconv2d_forward(d, to_dev(x), SYM[0], 0, None, SYM[1], 0, to_dev(b), SYM[2], 0, y.view)
+        t.cuda.synchronize()
+        y.check_guards()
+        got = y.host().numpy().reshape(n, ot, ho, wo)
     assert cc().conv2d_desc_kernel_name(d) == "igemm_i8"
-    assert_bitexact(got, ref, f"mixed sweep {name}")
+    assert_bitexact(got, ref, f"mixed sweep {name} ({'bound' if bound else 'per call'})")
 
 
 def test_igemm_i8_dense_full_size():

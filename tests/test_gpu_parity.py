@@ -441,11 +441,11 @@ def test_mixed_sweep_reduced_batch(name, dtype):
 
 
 @pytest.mark.parametrize("name", ["s2", "d2", "g32", "pw"])
-@pytest.mark.parametrize("dtype,bound", [("f32", False), ("bf16", False), ("bf16", True)])
+@pytest.mark.parametrize("dtype,bound", [("f32", False), ("f32", True), ("bf16", False), ("bf16", True)])
 def test_mixed_sweep_full_size(name, dtype, bound):
     """Full N=32 layers in the benchmark's launch configuration, every output
-    compared with the oracle (bound: the bf16 weights bound to the descriptor
-    and re-laid once, as the benchmark times them)."""
+    compared with the oracle (bound: the weights bound to the descriptor and
+    re-laid once, as the benchmark times them)."""
     L, x, w, b, s = _mixed(name, 32)
     if dtype == "bf16":
         x, w = bf16_round(x), bf16_round(w)
