@@ -21,6 +21,17 @@
 
 using namespace conv2d;
 
+int conv2d::device_cu_count() {
+    static const int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            return v;
+        return 256;
+    }();
+    return n;
+}
+
 namespace {
 
 thread_local char g_last_error[512] = "";

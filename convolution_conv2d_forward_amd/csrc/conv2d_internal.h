@@ -233,6 +233,11 @@ bool plan_fused_dw_pw(const Desc& dw, const Desc& pw, const void* x);
 bool plan_qfused_dw_pw(const Desc& dw, const Desc& pw);
 bool plan_qfused_pw_dw(const Desc& pw, const Desc& dw);
 
+// Compute units of the current device (256 on MI355X; also the answer when
+// no device is visible, e.g. when a descriptor is planned on a host without
+// one).  Read once per process.
+int device_cu_count();
+
 // Fill the tile-dependent ConvArgs fields from a planned descriptor.
 
 

@@ -354,19 +354,6 @@ struct Plan {
     int th, ir, xoff, xw, xs_plane, npx, nf, nj, nx, es_stride, cot, cop, lds_floats;
 };
 
-int cu_count_dwpw() {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cached = v;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 // vec: the input moves as 16-byte vectors (row width and pointer allow it).
 bool plan(const Desc& dw, const Desc& pw, bool vec, Plan* out, int cot = 0) {
     const conv2d_params_t& d = dw.p;
@@ -408,7 +395,7 @@ bool plan(const Desc& dw, const Desc& pw, bool vec, Plan* out, int cot = 0) {
         if (lds * 4 > 160 * 1024) break;
         // One workgroup per compute unit: 8 waves of up to 256 registers.
         const long blocks = (long)d.n * ((dw.ho + th - 1) / th) * co_tiles;
-        const long rounds = (blocks + cu_count_dwpw() - 1) / cu_count_dwpw();
+        const long rounds = (blocks + device_cu_count() - 1) / device_cu_count();
         // Time ~ rounds x input rows a workgroup stages (halo included).
         const long cost = rounds * ir;
         if (!ok || cost < best) {

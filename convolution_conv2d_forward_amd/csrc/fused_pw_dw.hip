@@ -371,21 +371,6 @@ struct FusedPlan {
     int tile_h, rows, xs_stride, ew, es_stride, lds_floats, vec;
 };
 
-// Compute units of the current device (256 on MI355X; also the answer when
-// no device is visible, e.g. when descriptors are built on a host without one).
-int cu_count() {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cached = v;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 bool plan(const Desc& pw, const Desc& dw, FusedPlan* out) {
     const conv2d_params_t& d = dw.p;
     const int W = pw.p.w;
@@ -414,7 +399,7 @@ bool plan(const Desc& pw, const Desc& dw, FusedPlan* out) {
         long per_cu = (160 * 1024) / (lds * 4) > 0 ? (160 * 1024) / (lds * 4) : 1;
         const long per_cu_regs = (npix + 15) / 16 <= 4 * kWaves ? 2 : 1;   // NJ = 4 or 8 register budget
         if (per_cu > per_cu_regs) per_cu = per_cu_regs;
-        const long rounds = (blocks + per_cu * cu_count() - 1) / (per_cu * cu_count());
+        const long rounds = (blocks + per_cu * device_cu_count() - 1) / (per_cu * device_cu_count());
         const long cost = rounds * rows;
         if (!ok || cost < best_cost) {
             *out = FusedPlan{th, rows, xs, ew, es, lds, vec ? 1 : 0};

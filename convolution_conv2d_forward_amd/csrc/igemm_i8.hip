@@ -729,20 +729,6 @@ const void* i8_fast_nfw4(const I8Plan& ip) {
     return ip.mb == 4 ? i8_fast_fn<4, 4>(ip.ncg) : ip.mb == 2 ? i8_fast_fn<4, 2>(ip.ncg) : i8_fast_fn<4, 1>(ip.ncg);
 }
 
-// Compute units of the current device (256 on MI355X).
-int i8_cu_count() {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cached = v;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 int64_t i8_co_tiles(const Desc& d, const I8Plan& ip) { return (d.cout_g + 16 * ip.mb - 1) / (16 * ip.mb); }
 int64_t i8_chunks(const Desc& d, const I8Plan& ip) { return (d.cin_g + 16 * ip.ncg - 1) / (16 * ip.ncg); }
 
@@ -837,7 +823,7 @@ hipError_t launch_igemm_i8(const Desc& d, ConvArgs a, hipStream_t s, const void*
         int per_cu = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kT, ip.lds);
         if (e != hipSuccess) return e;
-        uint64_t g = (uint64_t)std::max(per_cu, 1) * i8_cu_count();
+        uint64_t g = (uint64_t)std::max(per_cu, 1) * device_cu_count();
         g = std::min<uint64_t>(g, blocks);
         if (g > 8) g &= ~7ull;
         void* args[] = {&f, (void*)&wpacked};

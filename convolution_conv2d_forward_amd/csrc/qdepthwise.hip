@@ -2,10 +2,11 @@
 // QLinearConv (int32 accumulation, + int32 bias, requant) on the VALU
 // dot-product unit.
 //
-//   * A workgroup owns P whole (n, c) planes.  They are staged in LDS one at
-//     a time as int8 (not widened), one 16-byte chunk per global load (8-byte
-//     chunks for widths that are multiples of 8 but not of 16), through
-//     two buffers so that plane p+1's copy runs under plane p's outputs:
+//   * A workgroup owns P whole (n, c) planes, P sized for three workgroups
+//     per compute unit.  They are staged in LDS one at a time as int8 (not
+//     widened), one 16-byte chunk per global load (8-byte chunks for widths
+//     that are multiples of 8 but not of 16), through two buffers so that
+//     plane p+1's copy runs under plane p's outputs:
 //     chunks inside the image are copied, the margins and the rows outside it
 //     are the zero point (0), so no tap needs a bounds check.
 //   * A thread computes 4 consecutive outputs of one row (one 32-bit store of
@@ -233,12 +234,18 @@ bool qgeom(const Desc& d, QGeom& G) {
     G.row_bytes = (rb + 15) / 16 * 16;
     G.rows = (d.ho - 1) * ss + 3;
     G.plane_bytes = G.rows * G.row_bytes;
-    // Planes per workgroup: as many as would have fit 32 KB at once (at most
-    // 8), now streamed one at a time through two buffers.
-    int P = (32 * 1024) / G.plane_bytes;
+    // Planes per workgroup: enough for three workgroups per compute unit
+    // (at most 8).  Each streams its planes through two buffers, so fewer,
+    // longer workgroups hide the latency of each plane's copy behind the
+    // previous plane's outputs, while three per CU keep every CU busy with
+    // independent copies; measured on 56x56 and 80x80 planes (s1 and s2),
+    // three per CU beat one, two, or five to eight planes per workgroup.
+    const int64_t planes = (int64_t)p.n * p.c_out;
+    const int64_t slots = 3 * (int64_t)device_cu_count();
+    int64_t P = (planes + slots - 1) / slots;
     if (P > 8) P = 8;
     if (P < 1) P = 1;
-    G.planes = P;
+    G.planes = (int)P;
     const int cb = qdw_cb(p.w);
     return G.rows * (G.row_bytes / cb) <= (cb == 16 ? kNQ : 8) * kQT && 2 * G.plane_bytes + 16 * P <= 160 * 1024;
 }

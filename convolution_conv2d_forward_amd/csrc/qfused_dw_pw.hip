@@ -205,19 +205,6 @@ struct QPlan {
     int th, ir, xw, xplane, npx, nf, nj, lds;
 };
 
-int cu_count_q() {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cached = v;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 // ---------------------------------------------------------------------------
 // Fast path: 3x3 or 5x5 window, stride 1 or 2, dilation 1, input rows a
 // multiple of 16 bytes, 16-byte aligned input and pointwise weights.
@@ -588,7 +575,7 @@ bool qfast_plan(const Desc& dw, const Desc& pw, const void* x, const void* w_dw,
         const int lds = KC * pb + nf * 16 * FROW + 2 * 64 * FROW + 4 * KC * kk * nwin + 4 * KC;
         if (lds > 80 * 1024) break;
         const long blocks = (long)d.n * ((dw.ho + th - 1) / th) * co_tiles;
-        const long cost = (blocks + cu_count_q() - 1) / cu_count_q() * (ir + th);
+        const long cost = (blocks + device_cu_count() - 1) / device_cu_count() * (ir + th);
         if (!ok || cost < best) {
             *out = QFastPlan{th, cot, mt, nf, ir, rb, pb, q0, (FM - d.pad_left) & 3, wq, units <= 4 * kT ? 4 : 8, lds};
             best = cost;
@@ -677,7 +664,7 @@ bool qplan(const Desc& dw, const Desc& pw, QPlan* out) {
         const long blocks = (long)d.n * ((dw.ho + th - 1) / th) * co_tiles;
         long per_cu = (160 * 1024) / lds;
         if (per_cu > 4) per_cu = 4;
-        const long rounds = (blocks + per_cu * cu_count_q() - 1) / (per_cu * cu_count_q());
+        const long rounds = (blocks + per_cu * device_cu_count() - 1) / (per_cu * device_cu_count());
         const long cost = rounds * ir;
         if (!ok || cost < best) {
             *out = QPlan{th, ir, xw, xplane, npx, nf, nj <= 1 ? 1 : (nj <= 2 ? 2 : 4), lds};

@@ -438,19 +438,6 @@ struct QPDPlan {
     int tile_h, rows, off, ew, lds, nf, dwf_off;
 };
 
-int cu_count_q() {
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cached = v;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 // Output rows per tile: the fewest rounds of resident workgroups times
 // expanded rows per workgroup (the halo recompute included).
 bool qpd_plan(const Desc& pw, const Desc& dw, QPDPlan* out) {
@@ -477,7 +464,7 @@ bool qpd_plan(const Desc& pw, const Desc& dw, QPDPlan* out) {
         // rows the busiest compute unit processes (workgroups per CU, rounded
         // up, times rows per workgroup); ties go to more workgroups.
         const long blocks = ce_tiles * pw.p.n * ((dw.ho + th - 1) / th);
-        const long cost = (blocks + cu_count_q() - 1) / cu_count_q() * rows;
+        const long cost = (blocks + device_cu_count() - 1) / device_cu_count() * rows;
         if (!ok || cost < best) {
             *out = QPDPlan{th, rows, off, ew, lds, nf, dwf_off};
             best = cost;
