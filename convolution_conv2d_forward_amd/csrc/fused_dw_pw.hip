@@ -51,6 +51,7 @@ struct DwPwArgs {
     uint32_t num_blocks;
     DivU32 dv_co_tiles, dv_tiles_h;
     FastDiv div_cg, div_th;   // 64-column groups per row; output rows per tile
+    FastDiv div_q4, div_rp;   // 4-column groups per output row; output row pairs per tile
 };
 
 // Smallest s >= n with s % 32 == 16: four rows s apart start 16 or 48 banks
@@ -113,11 +114,16 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     const float pv = D.pad_value;
 
     // Pad rows (outside the image) and pad columns of the input tile: the
-    // same for every chunk, written once.
-    for (int e = tid; e < KC * f.ir * f.xw; e += kT) {
-        const int row = (e / f.xw) % f.ir, col = e % f.xw;
-        const int ih = ih0 + row, iw = col - f.xoff;
-        if ((unsigned)ih >= (unsigned)H || (unsigned)iw >= (unsigned)W) xs[e] = pv;
+    // same for every chunk, written once, one LDS row per thread.
+    for (int rr = tid; rr < KC * f.ir; rr += kT) {
+        const int row = rr % f.ir;
+        float* dst = xs + rr * f.xw;
+        if ((unsigned)(ih0 + row) >= (unsigned)H) {
+            for (int col = 0; col < f.xw; ++col) dst[col] = pv;
+        } else {
+            for (int col = 0; col < f.xoff; ++col) dst[col] = pv;
+            for (int col = f.xoff + W; col < f.xw; ++col) dst[col] = pv;
+        }
     }
 
     // ---- chunk loads ----
@@ -128,22 +134,42 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     const int per_ch = VEC ? f.ir * (W >> 2) : f.ir * W;    // load units per channel
     const int units_x = KC * per_ch;
     using Regs = ChunkRegs<VEC, NX>;
-    auto load_chunk = [&](int c, Regs& R) __attribute__((always_inline)) {
+    // Load unit u = tid + i*kT is the same (channel, row, column) of every
+    // chunk: its offset in the chunk's first plane (ch*HW + row*W + col,
+    // < KC*HW < 2^31) and its LDS offset are worked out once; -1 marks units
+    // past the tile or on rows outside the image.  A unit's channel exists
+    // when its offset is below (C - c0)*HW.
+    int xoff_g[NX], xoff_l[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        const int u = tid + i * kT;
+        const int ch = u / per_ch, rem = u - ch * per_ch;
+        int row, col;
+        if (VEC) { row = rem / (W >> 2); col = 4 * (rem - row * (W >> 2)); }
+        else { row = rem / W; col = rem - row * W; }
+        const bool ok = u < units_x && (unsigned)(ih0 + row) < (unsigned)H;
+        xoff_g[i] = ok ? ch * (int)HW + (ih0 + row) * W + col : -1;
+        xoff_l[i] = ok ? ch * f.xs_plane + row * f.xw + f.xoff + col : -1;
+    }
+    auto load_x = [&](int c, Regs& R) __attribute__((always_inline)) {
         const int c0 = c * KC;
+        // A chunk past the last channel (the loop's padding step) reads
+        // element 0 of the first plane for every unit.
+        const float* __restrict__ xc = xg + (c0 < C ? (int64_t)c0 * HW : 0);
+        const int64_t lim = c0 < C ? (int64_t)(C - c0) * HW : 0;
+        const int lim32 = lim < INT32_MAX ? (int)lim : INT32_MAX;
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
-            const int u = tid + i * kT;
-            const int ch = u / per_ch, rem = u - ch * per_ch;
-            int row, col;
-            if (VEC) { row = rem / (W >> 2); col = 4 * (rem - row * (W >> 2)); }
-            else { row = rem / W; col = rem - row * W; }
-            const bool ok = u < units_x && c0 + ch < C && (unsigned)(ih0 + row) < (unsigned)H;
-            const int64_t off = ok ? (int64_t)(c0 + ch) * HW + (int64_t)(ih0 + row) * W + col : 0;
-            if constexpr (VEC) R.x[i] = *(const f32x4*)(xg + off);
-            else R.x[i] = xg[off];
+            const int off = (unsigned)xoff_g[i] < (unsigned)lim32 ? xoff_g[i] : 0;
+            if constexpr (VEC) R.x[i] = *(const f32x4*)(xc + off);
+            else R.x[i] = xc[off];
         }
-        // The loaded values are not touched here: masking them now would make
-        // the compiler wait for every load in flight, the next chunk's included.
+    };
+    // The chunk's pointwise and depthwise weights, depthwise bias and slope.
+    // The loaded values are not touched here: masking them now would make
+    // the compiler wait for every load in flight, the next chunk's included.
+    auto load_w = [&](int c, Regs& R) __attribute__((always_inline)) {
+        const int c0 = c * KC;
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             const int e = tid + i * kT;                     // k-major: e = k * 64 + co
@@ -167,13 +193,8 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
         const int c0 = c * KC;
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
-            const int u = tid + i * kT;
-            const int ch = u / per_ch, rem = u - ch * per_ch;
-            int row, col;
-            if (VEC) { row = rem / (W >> 2); col = 4 * (rem - row * (W >> 2)); }
-            else { row = rem / W; col = rem - row * W; }
-            if (u < units_x && (unsigned)(ih0 + row) < (unsigned)H) {
-                float* dst = xs + ch * f.xs_plane + row * f.xw + f.xoff + col;
+            if (xoff_l[i] >= 0) {
+                float* dst = xs + xoff_l[i];
                 if constexpr (VEC) *(f32x4*)dst = R.x[i];
                 else *dst = R.x[i];
             }
@@ -210,7 +231,72 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     const int cgroups = (WO + 63) / 64;
     const int units = KC * f.th * cgroups * 16;
     const ActP da = act_params(D);
+    // 3x3 stride 1 with pad_left 1 and whole 4-column groups: a unit is one
+    // (channel, output row pair, 4 columns); each of its four input rows is
+    // read once as float2 + float4 + float2 (the LDS column of output column
+    // 4l sits at xoff + 4l, a multiple of 4) into a 6-column register window.
+    const bool quad = FIXED && SS == 1 && KH == 3 && KW == 3 && D.pad_left == 1 && WO % 4 == 0;
+    const int nq = WO >> 2, nrp = (f.th + 1) >> 1;
+    const int units_q = KC * nrp * nq;
+    auto depthwise_quad = [&](int c, float* es, const float* dp) __attribute__((always_inline)) {
+        const int c0 = c * KC;
+        for (int u = tid; u < units_q; u += kT) {
+            const int rest = (int)fdiv((uint32_t)u, f.div_q4);      // ch * nrp + row pair
+            const int l = u - rest * nq;
+            const int ch = (int)fdiv((uint32_t)rest, f.div_rp);
+            const int r0 = 2 * (rest - ch * nrp);
+            if (r0 >= th_n) continue;
+            const bool two = r0 + 1 < th_n;
+            float o[2][4];
+            if (c0 + ch < C) {
+                float wv[9];
+#pragma unroll
+                for (int t = 0; t < 9; ++t) wv[t] = dp[ch * 9 + t];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[m][v] = 0.0f;
+                const float* base = xs + ch * f.xs_plane + r0 * f.xw + f.xoff + 4 * l;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (i == 3 && !two) break;
+                    const float* rp = base + i * f.xw;
+                    const float2 lo = *(const float2*)(rp - 2);
+                    const float4 mid = *(const float4*)rp;
+                    const float2 hi = *(const float2*)(rp + 4);
+                    const float win[6] = {lo.y, mid.x, mid.y, mid.z, mid.w, hi.x};
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const int r = i - m;                       // filter row feeding output row r0+m
+                        if (r < 0 || r > 2) continue;
+#pragma unroll
+                        for (int s2 = 0; s2 < 3; ++s2)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) o[m][v] = fmaf(win[v + s2], wv[3 * r + s2], o[m][v]);
+                    }
+                }
+                const float bb = dp[KC * KHW_MAX + ch];
+                const float sl = D.act == CONV_ACT_PRELU ? dp[KC * KHW_MAX + KC + ch] : da.s;
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[m][v] = act_apply(o[m][v] + bb, sl, da.lo, da.hi);
+            } else {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[m][v] = 0.0f;   // past the last channel: zero weights too
+            }
+            float* dst = es + ch * f.es_stride + r0 * WO + 4 * l;
+            *(float4*)dst = make_float4(o[0][0], o[0][1], o[0][2], o[0][3]);
+            if (two) *(float4*)(dst + WO) = make_float4(o[1][0], o[1][1], o[1][2], o[1][3]);
+        }
+    };
     auto depthwise = [&](int c, float* es, const float* dp) __attribute__((always_inline)) {
+        if (quad) {
+            depthwise_quad(c, es, dp);
+            return;
+        }
         const int c0 = c * KC;
         for (int u = tid; u < units; u += kT) {
             const int l = u & 15;
@@ -261,7 +347,10 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
 
     // ---- 3. pointwise on the matrix cores ----
     // The operands of k step t+1 are read from LDS while the MFMAs of step t run.
-    auto pointwise = [&](const float* es, const float* ws) __attribute__((always_inline)) {
+    // between(t) runs after the MFMAs of k step t are issued (the next
+    // chunk's loads go there, so their address work and issue overlap the
+    // matrix cores).
+    auto pointwise = [&](const float* es, const float* ws, auto&& between) __attribute__((always_inline)) {
         float bv[2][MI], av[2][NJ];
         auto fetch = [&](int kq, int set) __attribute__((always_inline)) {
             const int kr = kq + q;
@@ -286,23 +375,27 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
                         acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t & 1][j], bv[t & 1][m], acc[m][j], 0, 0, 0);
                 }
             }
+            between(t);
         }
     };
 
     // Chunk c: its registers -> LDS (the input tile is free: the depthwise of
     // chunk c-1 finished before the last barrier; the weight and result
-    // buffers c%2 were last read by chunk c-2's MFMAs), barrier, loads of
-    // chunk cn (two ahead) into the same registers, depthwise, barrier, MFMAs.
+    // buffers c%2 were last read by chunk c-2's MFMAs), barrier, depthwise,
+    // barrier, MFMAs with the loads of chunk cn (two ahead) into the same
+    // registers issued between them.
     auto step = [&](int c, Regs& R, int cn) __attribute__((always_inline)) {
         float* es = es0 + (c & 1) * KC * f.es_stride;
         float* ws = ws0 + (c & 1) * KC * f.cop;
         float* dp = dp0 + (c & 1) * DWP;
         store_chunk(c, R, ws, dp);
         __syncthreads();
-        load_chunk(cn, R);
         depthwise(c, es, dp);
         __syncthreads();
-        pointwise(es, ws);
+        pointwise(es, ws, [&](int t) __attribute__((always_inline)) {
+            if (t == 0) load_x(cn, R);
+            if (t == 2) load_w(cn, R);
+        });
     };
     // An even number of steps, two per iteration with fixed register sets, and
     // loads in every step (the last two reload the last chunk; with an odd
@@ -310,8 +403,10 @@ __global__ __launch_bounds__(kT) void fused_dw_pw_kernel(DwPwArgs f) {
     // load sits behind a condition, so the waits stay exact.
     const int nch2 = (nch + 1) & ~1;
     Regs R0, R1;
-    load_chunk(0, R0);
-    load_chunk(1, R1);
+    load_x(0, R0);
+    load_w(0, R0);
+    load_x(1, R1);
+    load_w(1, R1);
     for (int c = 0; c < nch2; c += 2) {
         step(c, R0, min(c + 2, nch2 - 1));
         step(c + 1, R1, min(c + 3, nch2 - 1));
@@ -430,7 +525,7 @@ bool vec_ok(const Desc& dw, const void* x) {
 
 bool plan_fused_dw_pw(const Desc& dw, const Desc& pw, const void* x) {
     if (dw.p.k_h > 5 || dw.p.k_w > 5) return false;
-    if ((int64_t)dw.p.h * dw.p.w >= INT32_MAX / 2 || (int64_t)dw.ho * dw.wo >= INT32_MAX / 2) return false;
+    if ((int64_t)KC * dw.p.h * dw.p.w >= INT32_MAX || (int64_t)dw.ho * dw.wo >= INT32_MAX / 2) return false;
     Plan pl{};
     return plan(dw, pw, vec_ok(dw, x), &pl);
 }
@@ -458,6 +553,8 @@ hipError_t launch_fused_dw_pw(const Desc& dw, const Desc& pw, ConvArgs adw, Conv
     f.dv_tiles_h = make_divu32((uint32_t)f.tiles_h);
     f.div_cg = make_fastdiv((uint32_t)((dw.wo + 63) / 64));
     f.div_th = make_fastdiv((uint32_t)pl.th);
+    f.div_q4 = make_fastdiv((uint32_t)(dw.wo >= 4 ? dw.wo / 4 : 1));
+    f.div_rp = make_fastdiv((uint32_t)((pl.th + 1) / 2));
     const uint64_t blocks = (uint64_t)f.co_tiles * f.tiles_h * adw.n;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
