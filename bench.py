@@ -583,7 +583,8 @@ def per_config(reps, only="all"):
         for k, L in enumerate(wl.layers):
             wd = t_(wl.arrays[f"w{k}"])
             entry = {}
-            for algo, bound in (("direct", False), ("direct", True), ("winograd", False), ("winograd", True)):
+            for algo, bound in (("direct", False), ("direct", True), ("winograd", False), ("winograd", True),
+                                ("winograd4", True)):
                 p = params_of(L, in_total_channels=total, out_total_channels=total, out_channel_offset=L.c_in)
                 p.algo = cc.ALGOS[algo]
                 d = cc.conv2d_desc_create(p)
@@ -597,12 +598,39 @@ def per_config(reps, only="all"):
                 t = time_layer(f"{key}{k}", fns, reps)
                 entry[key] = dict(roofline_entry(L.flops, 4 * (L.c_in * h * w + L.c_out * L.c_in * 9 + L.c_out * h * w),
                                                  t, "f32"), kernel=cc.conv2d_desc_kernel_name(d))
-            # the MFMA work Winograd actually issues: 16 products per 2x2 tile and channel pair
+            # the MFMA work Winograd actually issues: 16 products per 2x2 tile and
+            # channel pair, 36 per 4x4 tile for F(4x4)
             for key in ("winograd", "winograd_bound"):
                 entry[key]["executed_flops"] = 2 * 16 * L.c_out * L.c_in * ((h + 1) // 2) * ((w + 1) // 2)
+            entry["winograd4_bound"]["executed_flops"] = 2 * 36 * L.c_out * L.c_in * ((h + 3) // 4) * ((w + 3) // 4)
             res[L.name] = entry
             log("winograd", L.name, {a: e["us"] for a, e in entry.items()})
         out["dense_block_winograd"] = res
+        # a batched 3x3 layer (8 x 128 x 64 x 64 -> 128), whose F(4x4) grid
+        # fills the GPU: the shape where the larger tile pays
+        L = workloads.Layer("batched_3x3", 8, 128, 64, 64, 128, (3, 3), pads=(1, 1, 1, 1))
+        rng = np.random.default_rng(5)
+        xs = t_(rng.standard_normal((L.n, L.c_in, L.h, L.w), dtype=np.float32))
+        wd = t_((0.05 * rng.standard_normal((L.c_out, L.c_in, 3, 3))).astype(np.float32))
+        bufs = _rotating(lambda: (xs.clone(), torch.empty((L.n, L.c_out, L.h, L.w), device=dev())),
+                         4 * L.n * (L.c_in + L.c_out) * L.h * L.w)
+        entry = {}
+        for algo in ("direct", "winograd", "winograd4"):
+            p = params_of(L)
+            p.algo = cc.ALGOS[algo]
+            d = cc.conv2d_desc_create(p)
+            cc.conv2d_desc_bind_weights(d, wd)
+            torch.cuda.synchronize()
+            fns = [lambda d=d, x=x, y=y: cc.conv2d_forward(d, x, None, None, None, y) for x, y in bufs]
+            t = time_layer(f"batched_{algo}", fns, reps)
+            entry[algo + "_bound"] = dict(roofline_entry(L.flops, 4 * (L.n * L.c_in * L.h * L.w + L.c_out * L.c_in * 9
+                                                                       + L.n * L.c_out * L.h * L.w), t, "f32"),
+                                          kernel=cc.conv2d_desc_kernel_name(d))
+        tiles2, tiles4 = L.n * (L.h // 2) * (L.w // 2), L.n * (L.h // 4) * (L.w // 4)
+        entry["winograd_bound"]["executed_flops"] = 2 * 16 * L.c_out * L.c_in * tiles2
+        entry["winograd4_bound"]["executed_flops"] = 2 * 36 * L.c_out * L.c_in * tiles4
+        log("winograd", L.name, {a: e["us"] for a, e in entry.items()})
+        out["batched_3x3_winograd"] = {L.name: entry}
     add_copy_context(out, reps)
     return out
 

@@ -30,8 +30,8 @@ CONV_OK, CONV_ERR_INVALID_ARG, CONV_ERR_INCOMPATIBLE_SHAPES, CONV_ERR_UNSUPPORTE
 ACT_NONE, ACT_RELU, ACT_LEAKY_RELU, ACT_PRELU, ACT_CLIP = range(5)
 DTYPE_F32, DTYPE_BF16, DTYPE_I8 = range(3)
 ROUND_HALF_EVEN, ROUND_HALF_AWAY = range(2)
-ALGO_AUTO, ALGO_DIRECT, ALGO_WINOGRAD = range(3)
-ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "winograd": ALGO_WINOGRAD}
+ALGO_AUTO, ALGO_DIRECT, ALGO_WINOGRAD, ALGO_WINOGRAD4 = range(4)
+ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "winograd": ALGO_WINOGRAD, "winograd4": ALGO_WINOGRAD4}
 
 _ACT_NAMES = {"none": ACT_NONE, "relu": ACT_RELU, "leaky_relu": ACT_LEAKY_RELU, "prelu": ACT_PRELU,
               "clip": ACT_CLIP}

@@ -51,7 +51,11 @@ conv_status_t ok() {
 
 const char* kernel_name(const Desc& d) {
     switch (d.kclass) {
-    case KC_IGEMM_F32: return d.wino_bound ? "winograd_f32" : d.flatten_1x1 ? "igemm_f32_pointwise" : "igemm_f32";
+    case KC_IGEMM_F32:
+        return d.wino4_bound ? "winograd4_f32"
+               : d.wino_bound ? "winograd_f32"
+               : d.flatten_1x1 ? "igemm_f32_pointwise"
+                               : "igemm_f32";
     case KC_IGEMM_BF16: return d.flatten_1x1 ? "igemm_bf16_pointwise" : "igemm_bf16";
     case KC_DW: return d.p.dtype == CONV_DTYPE_BF16 ? "depthwise_bf16" : "depthwise_f32";
     case KC_QDW: return d.cfg == 1 ? "depthwise_i8_dot4" : "depthwise_i8";
@@ -59,6 +63,7 @@ const char* kernel_name(const Desc& d) {
     case KC_DIRECT: return "direct";
     case KC_GROUPED: return d.p.dtype == CONV_DTYPE_BF16 ? "grouped_bf16" : "grouped_f32";
     case KC_WINOGRAD_F32: return "winograd_f32";
+    case KC_WINOGRAD4_F32: return "winograd4_f32";
     case KC_PW_F32: return "pointwise_f32";
     case KC_IGEMM_I8: return "igemm_i8";
     case KC_SMALL_F32: return "small_f32";
@@ -295,7 +300,7 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
     if (p.int8_rounding != CONV_ROUND_HALF_EVEN && p.int8_rounding != CONV_ROUND_HALF_AWAY)
         return fail(CONV_ERR_INVALID_ARG, "unknown rounding %d", p.int8_rounding);
     if (p.has_bias != 0 && p.has_bias != 1) return fail(CONV_ERR_INVALID_ARG, "has_bias must be 0 or 1");
-    if (p.algo < CONV_ALGO_AUTO || p.algo > CONV_ALGO_WINOGRAD) return fail(CONV_ERR_INVALID_ARG, "unknown algo %d", p.algo);
+    if (p.algo < CONV_ALGO_AUTO || p.algo > CONV_ALGO_WINOGRAD4) return fail(CONV_ERR_INVALID_ARG, "unknown algo %d", p.algo);
     if (!std::isfinite(p.pad_value)) return fail(CONV_ERR_INVALID_ARG, "pad_value must be finite");
     if (p.groups <= 0) return fail(CONV_ERR_INVALID_ARG, "groups must be >= 1");
     if (p.c_in % p.groups || p.c_out % p.groups)
@@ -356,6 +361,14 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
                                               "and one group");
         }
         d->kclass = KC_WINOGRAD_F32;
+        planned = true;
+    } else if (p.algo == CONV_ALGO_WINOGRAD4) {
+        if (!plan_winograd4_f32(*d)) {
+            delete d;
+            return fail(CONV_ERR_UNSUPPORTED, "Winograd F(4x4,3x3) needs F32, a 3x3 window, stride 1, dilation 1 "
+                                              "and one group");
+        }
+        d->kclass = KC_WINOGRAD4_F32;
         planned = true;
     } else if (p.algo == CONV_ALGO_AUTO && winograd_preferred(*d)) {
         d->kclass = KC_WINOGRAD_F32;
@@ -423,12 +436,17 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
         return fail(CONV_ERR_INVALID_ARG, "weights were first bound on device %d, current device is %d",
                     d.wbound_device, dev);
     const int64_t wb = w_bytes(d);
-    const bool wino = d.kclass == KC_WINOGRAD_F32 ||
-                      (d.kclass == KC_IGEMM_F32 && d.p.algo == CONV_ALGO_AUTO && winograd_bound_preferred(d));
+    // AUTO fp32 3x3 layers switch to Winograd with bound weights where it was
+    // measured faster: F(4x4) on grids that fill the GPU, else F(2x2).
+    const bool auto_f32 = d.kclass == KC_IGEMM_F32 && d.p.algo == CONV_ALGO_AUTO;
+    const bool wino4 = d.kclass == KC_WINOGRAD4_F32 || (auto_f32 && winograd4_bound_preferred(d));
+    const bool wino = !wino4 && (d.kclass == KC_WINOGRAD_F32 || (auto_f32 && winograd_bound_preferred(d)));
     const bool i8pack = d.kclass == KC_IGEMM_I8 && d.wpack_bytes > 0;
-    const bool packs = d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) || wino || i8pack;
+    const bool packs =
+        d.kclass == KC_IGEMM_BF16 || (d.kclass == KC_IGEMM_F32 && d.apack_bytes > 0) || wino || i8pack || wino4;
     const int64_t pack_bytes = d.kclass == KC_IGEMM_BF16 || i8pack ? d.wpack_bytes
                                : wino                     ? winograd_u_bytes(d)
+                               : wino4                    ? winograd4_u_bytes(d)
                                                           : d.apack_bytes;
     const int64_t off = packs ? (wb + 255) / 256 * 256 : 0;
     const int64_t total = packs ? off + pack_bytes : wb;
@@ -451,14 +469,17 @@ conv_status_t conv2d_desc_bind_weights(conv2d_desc_t dd, const void* w, void* st
         e = d.kclass == KC_IGEMM_BF16 ? pack_igemm_bf16_weights(d, d.wbound, (char*)d.wbound + off, s)
             : i8pack                   ? pack_igemm_i8_weights(d, d.wbound, (char*)d.wbound + off, s)
             : wino                     ? pack_winograd_f32_weights(d, d.wbound, (char*)d.wbound + off, s)
+            : wino4                    ? pack_winograd4_f32_weights(d, d.wbound, (char*)d.wbound + off, s)
                                        : pack_igemm_f32_weights(d, d.wbound, (char*)d.wbound + off, s);
     if (e != hipSuccess) {
         d.bound = false;
         d.wino_bound = false;
+        d.wino4_bound = false;
         return hip_status(e, "binding weights");
     }
     d.bound = true;
     d.wino_bound = wino && d.kclass == KC_IGEMM_F32;
+    d.wino4_bound = wino4 && d.kclass == KC_IGEMM_F32;
     return ok();
 }
 
@@ -514,7 +535,9 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
     hipError_t e;
     switch (d.kclass) {
     case KC_IGEMM_F32:
-        if (use_bound && d.wino_bound)
+        if (use_bound && d.wino4_bound)
+            e = launch_winograd4_f32(d, a, s, (const char*)d.wbound + d.wbound_pack_off);
+        else if (use_bound && d.wino_bound)
             e = launch_winograd_f32(d, a, s, (const char*)d.wbound + d.wbound_pack_off);
         else
             e = launch_igemm_f32(d, a, s, use_bound && d.apack_bytes > 0 ? (const char*)d.wbound + d.wbound_pack_off
@@ -545,6 +568,13 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
     case KC_GROUPED: e = launch_grouped(d, a, s); break;
     case KC_WINOGRAD_F32:
         e = launch_winograd_f32(d, a, s, use_bound ? (const char*)d.wbound + d.wbound_pack_off : nullptr);
+        break;
+    case KC_WINOGRAD4_F32:
+        // U exists only as the image packed when the weights were bound.
+        if (!use_bound)
+            return fail(CONV_ERR_UNSUPPORTED, "Winograd F(4x4,3x3) runs on bound weights: bind them with "
+                                              "conv2d_desc_bind_weights and pass w = NULL");
+        e = launch_winograd4_f32(d, a, s, (const char*)d.wbound + d.wbound_pack_off);
         break;
     case KC_PW_F32:
         e = pointwise_f32_fits(d, a) ? launch_pointwise_f32(d, a, s) : launch_igemm_f32(d, a, s);

@@ -24,6 +24,7 @@ enum KernelClass : int32_t {
     KC_PW_F32 = 8,       // pointwise 1x1 with K <= 256, fp32 MFMA, every output channel per workgroup
     KC_IGEMM_I8 = 9,     // int8 dense / grouped implicit GEMM, i8 MFMA
     KC_SMALL_F32 = 10,   // small fp32 3x3 layers on the vector units, one thread per output pixel
+    KC_WINOGRAD4_F32 = 11, // Winograd F(4x4, 3x3), fp32 MFMA, bound weights only
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -147,6 +148,7 @@ struct Desc {
     // then U = G g G^T (pack_winograd_f32_weights), and calls that pass
     // their own weights keep the implicit GEMM.
     bool wino_bound = false;
+    bool wino4_bound = false;   // AUTO fp32 3x3 with bound weights: Winograd F(4x4)
     // Weights bound with conv2d_desc_bind_weights: an OIHW copy at wbound,
     // followed for the bf16 implicit GEMM, the Winograd kernel, the int8 3x3
     // implicit GEMM (and the fp32 implicit GEMM when apack_bytes > 0) by the
@@ -219,6 +221,15 @@ bool plan_qpw(Desc& d);
 bool plan_igemm_i8(const Desc& d);
 bool plan_grouped(const Desc& d);
 bool plan_winograd_f32(const Desc& d);
+// Winograd F(4x4, 3x3): U packed once at bind (winograd4_u_bytes of it) and
+// read by the kernel (upacked must be that image).
+bool plan_winograd4_f32(const Desc& d);
+// AUTO with bound weights: shapes where F(4x4) has been measured faster
+// than F(2x2) and the implicit GEMM with packed weights.
+bool winograd4_bound_preferred(const Desc& d);
+int64_t winograd4_u_bytes(const Desc& d);
+hipError_t pack_winograd4_f32_weights(const Desc& d, const void* w, void* dst, hipStream_t s);
+hipError_t launch_winograd4_f32(const Desc& d, ConvArgs a, hipStream_t s, const void* upacked);
 // Small fp32 3x3 layers (AUTO only): see small_f32.hip.
 bool plan_small_f32(const Desc& d);
 hipError_t launch_small_f32(const Desc& d, ConvArgs a, hipStream_t s);

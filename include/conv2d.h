@@ -104,12 +104,14 @@ typedef enum {
  * direct tiled classes; for an F32 3x3 single-group layer with at most 64
  * input channels and at most 64K output elements, a vector-unit kernel with
  * one short chain per output pixel (conv2d_desc_kernel_name "small_f32");
- * and, binding weights to an F32 3x3 stride-1
- * dilation-1 single-group descriptor with >= 32 input channels, <= 64 output
- * channels and a grid of >= 256 Winograd workgroups (2 x 8 output tiles of
- * 2 x 2 pixels x 32 output channels each) switches its calls with bound
- * weights to Winograd, measured faster there (calls passing their own
- * weights keep the implicit GEMM); DIRECT uses only the tiled classes (no
+ * and, binding weights to an F32 3x3 stride-1 dilation-1 single-group
+ * descriptor with >= 32 input channels switches its calls with bound weights
+ * to Winograd where it was measured faster (calls passing their own weights
+ * keep the implicit GEMM): F(4x4, 3x3) when that grid has >= one workgroup
+ * per compute unit (2 x 8 output tiles of 4 x 4 pixels x 32 output channels
+ * each; conv2d_desc_kernel_name "winograd4_f32"), else F(2x2, 3x3) for <= 64
+ * output channels and a grid of >= 256 workgroups (2 x 8 tiles of 2 x 2
+ * pixels x 32 output channels; "winograd_f32"); DIRECT uses only the tiled classes (no
  * Winograd, no small-layer kernel); WINOGRAD
  * requests the F(2x2, 3x3) minimal
  * filtering algorithm (Lavin and Gray, CVPR 2016) for the "Winograd cells"
@@ -117,11 +119,18 @@ typedef enum {
  * WorkerPool): F32 only, 3x3 window, stride 1, dilation 1, one group, any
  * pads, bias, activation and channel offsets; conv2d_desc_create returns
  * CONV_ERR_UNSUPPORTED for any other shape.  Its results differ from the
- * direct sum by fp32 rounding only. */
+ * direct sum by fp32 rounding only.  WINOGRAD4 requests the larger tile of
+ * the same paper, F(4x4, 3x3) (36 multiplies per 4x4 output tile and input
+ * channel instead of 144), for the same shapes; its filter transform is
+ * computed once, when the weights are bound, so conv2d_forward and
+ * conv2d_forward_noalloc take only w = NULL on such a descriptor (a call
+ * with weights returns CONV_ERR_UNSUPPORTED).  Its rounding differs from the
+ * direct sum more than F(2x2)'s: the tests bound it by 1e-4 * (1 + |y|). */
 typedef enum {
     CONV_ALGO_AUTO = 0,
     CONV_ALGO_DIRECT = 1,
-    CONV_ALGO_WINOGRAD = 2
+    CONV_ALGO_WINOGRAD = 2,
+    CONV_ALGO_WINOGRAD4 = 3
 } conv_algo_t;
 
 typedef struct {
