@@ -620,10 +620,19 @@ using K3A_M64  = Cfg<64,  64, 16,  4, 3, 3, 8, 1, 8, 2, 3>;
 // times as many workgroups (a 32x32 image: 16 instead of 4).
 using K3S_M16  = Cfg<16,  64, 16,  4, 3, 3, 4, 1, 4, 2, 6>;
 using K3S_M32  = Cfg<32,  64, 16,  4, 3, 3, 4, 1, 4, 2, 6>;
+// Large grids (at least two workgroups per compute unit with these): the
+// waves split K fewer ways and cover more pixel sub-tiles instead, so each
+// wave runs a longer K loop and the split-K reduction shrinks or vanishes.
+// Measured on the batch-32 sweep: 3x3 d2 494 -> 453 us, 3x3 s2 255 -> 241
+// us, 1x1 256 -> 512 148 -> 127 us; on small grids they leave CUs idle.
+using K3L_M64   = Cfg<64,  64, 16,  4, 3, 3, 8, 2, 1, 2, 3>;
+using K3WL_M64  = Cfg<64,  64, 16,  4, 3, 3, 8, 2, 2, 1, 6>;
+using K1FL_M128 = Cfg<128, 64, 64, 16, 1, 1, 8, 2, 1, 1, 4>;
 
 enum {
     C3_M16, C3_M32, C3_M64, C3W_M16, C3W_M32, C3W_M64, C3P_M16, C3P_M32,
-    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, C3A_M64, C3S_M16, C3S_M32, NCFG
+    C1F_M32, C1F_M64, C1F_M128, C1FP_M16, C1FP_M32, C1_M32, C1_M64, C5_M16, C3A_M64, C3S_M16, C3S_M32,
+    C3L_M64, C3WL_M64, C1FL_M128, NCFG
 };
 
 const CfgInfo& cfg(int i) {
@@ -632,6 +641,7 @@ const CfgInfo& cfg(int i) {
         info<K3W_M64>(),  info<K3P_M16>(),  info<K3P_M32>(),   info<K1F_M32>(),  info<K1F_M64>(),
         info<K1F_M128>(), info<K1FP_M16>(), info<K1FP_M32>(),  info<K1_M32>(),   info<K1_M64>(),
         info<K5_M16>(),   info<K3A_M64, true, true>(), info<K3S_M16>(), info<K3S_M32>(),
+        info<K3L_M64>(),  info<K3WL_M64>(), info<K1FL_M128>(),
     };
     return table[i];
 }
@@ -665,6 +675,19 @@ Geom geom(const conv2d_params_t& p, const CfgInfo& c, bool flat) {
     return G;
 }
 
+// Workgroups of a launch with config c (pixel sub-tiles stacked the cheaper
+// way, as the planner below picks).
+int64_t grid_blocks(const Desc& d, const CfgInfo& c, bool flat) {
+    const conv2d_params_t& p = d.p;
+    const int pt = c.nw / (c.wm * c.ks);
+    const int64_t co = p.n * (int64_t)p.groups * ((d.cout_g + c.bm - 1) / c.bm);
+    if (flat) return co * ((d.ho * d.wo + c.tw * pt - 1) / (c.tw * pt));
+    const int th = c.bn / c.tw;
+    const int64_t v = (int64_t)((d.ho + th * pt - 1) / (th * pt)) * ((d.wo + c.tw - 1) / c.tw);
+    const int64_t h = (int64_t)((d.ho + th - 1) / th) * ((d.wo + c.tw * pt - 1) / (c.tw * pt));
+    return co * (v < h ? v : h);
+}
+
 }  // namespace
 
 bool plan_igemm_f32(Desc& d) {
@@ -675,7 +698,7 @@ bool plan_igemm_f32(Desc& d) {
     const bool flat = is1 && p.stride_h == 1 && p.stride_w == 1 && p.pad_top == 0 && p.pad_left == 0 &&
                       p.pad_bottom == 0 && p.pad_right == 0;
     const int m = d.cout_g;
-    int cands[4];
+    int cands[6];
     int nc = 0;
     if (is3) {
         if (d.cin_g < 32) {
@@ -696,9 +719,22 @@ bool plan_igemm_f32(Desc& d) {
     } else if (is5) {
         cands[nc++] = C5_M16;
     }
+    // Large grids try the variant with fewer K slices first.
+    for (int k = 0; k < nc; ++k) {
+        const int l = cands[k] == C3_M64 ? C3L_M64 : cands[k] == C3W_M64 ? C3WL_M64
+                      : cands[k] == C1F_M128 ? C1FL_M128 : -1;
+        if (l < 0 || grid_blocks(d, cfg(l), flat) < 2 * (int64_t)device_cu_count()) continue;
+        for (int j = nc; j > k; --j) cands[j] = cands[j - 1];
+        cands[k] = l;
+        ++nc;
+        ++k;
+    }
     for (int k = 0; k < nc; ++k) {
         const CfgInfo& c = cfg(cands[k]);
         const Geom G = geom(p, c, flat);
+        // Where the packed-weight variant applies (same geometry as C3_M64),
+        // keep the config that has it.
+        if (cands[k] == C3L_M64 && G.ph * G.pwa == G.ps && p.w % 4 == 0) continue;
         if (c.cw * G.ph * G.pwa / 4 > 64 * c.xs) continue;            // patch units per lane
         if (c.cw * G.ph * G.pwa / 4 >= 65536 || G.ph * G.pwa >= 65536) continue;   // magic division range
         if ((int64_t)c.cw * p.h * p.w >= INT32_MAX / 2) continue;      // 32-bit patch offsets
