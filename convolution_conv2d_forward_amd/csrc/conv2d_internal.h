@@ -25,6 +25,7 @@ enum KernelClass : int32_t {
     KC_IGEMM_I8 = 9,     // int8 dense / grouped implicit GEMM, i8 MFMA
     KC_SMALL_F32 = 10,   // small fp32 3x3 layers on the vector units, one thread per output pixel
     KC_WINOGRAD4_F32 = 11, // Winograd F(4x4, 3x3), fp32 MFMA, bound weights only
+    KC_PWG_F32 = 12,     // pointwise 1x1 with a deep reduction, 128 x 128 GEMM tiles shared in LDS
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -237,6 +238,10 @@ hipError_t launch_small_f32(const Desc& d, ConvArgs a, hipStream_t s);
 // been measured faster than the fp32 implicit GEMM with packed weights.
 bool winograd_bound_preferred(const Desc& d);
 bool plan_pointwise_f32(const Desc& d);
+// fp32 pointwise 1x1 as shared 128-pixel x 128-channel GEMM tiles (pw_gemm_f32.hip);
+// launch_pw_gemm_f32 needs the 16-byte alignment pointwise_f32_fits checks.
+bool plan_pw_gemm_f32(const Desc& d);
+hipError_t launch_pw_gemm_f32(const Desc& d, ConvArgs a, hipStream_t s);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 // x: the input pointer (its alignment decides between vector and scalar row loads).

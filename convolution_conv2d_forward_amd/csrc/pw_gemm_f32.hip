@@ -1,0 +1,188 @@
+// fp32 pointwise 1x1 convolution (stride 1, no pads, one group) with a deep
+// reduction and many output channels: Y[co, p] = act(sum_k W[co, k] X[k, p]
+// + b[co]) per image (ncnn convolution with a 1x1 kernel; ONNX Conv with
+// kernel_shape 1x1), as one GEMM tile per workgroup.
+//
+// The implicit GEMM gives every wave a private LDS pipeline, so the waves of
+// a workgroup each fetch their own copy of the weight and pixel chunks.  For
+// a plain 1x1 GEMM with many output channels and a long K the workgroup
+// shares its tiles instead:
+//   - a workgroup owns 128 pixels of one image x 128 output channels; four
+//     waves (2 x 2), each 64 pixels x 64 channels = 4 x 4 fragments of
+//     v_mfma_f32_16x16x4f32, pixels as the first operand so that a lane ends
+//     up holding 4 consecutive pixels of one channel (16-byte stores);
+//   - K runs in chunks of 16 input channels through two LDS buffers: the
+//     next chunk's 16-byte loads are issued before the current chunk's
+//     MFMAs and written to the other buffer after them, one barrier per
+//     chunk;
+//   - within a chunk, MFMA step s of lane group q takes input channel
+//     4q + s (the order of a sum's terms is free), so a lane's four weight
+//     operands of a chunk are one 16-byte LDS read;
+//   - block indices are remapped so that the output-channel tiles of one
+//     pixel tile run on the same XCD and share its L2 copy of the input.
+// On the mixed sweep's 1x1 256 -> 512 layer (batch 32, 32 x 32) this takes
+// ~102 us against 127 us for the implicit GEMM's best configuration.
+#include "device_common.h"
+
+namespace conv2d {
+
+namespace {
+
+constexpr int kT = 256;
+constexpr int TP = 128;          // pixels per workgroup
+constexpr int TC = 128;          // output channels per workgroup
+constexpr int KC = 16;           // input channels per chunk
+constexpr int XST = TP + 4;      // LDS row stride of the pixel tile [k][pixel]
+constexpr int WST = KC + 4;      // LDS row stride of the weight tile [co][k]
+constexpr int XBUF = KC * XST;
+constexpr int WBUF = TC * WST;
+constexpr int LDS_FLOATS = 2 * (XBUF + WBUF);
+
+// Four workgroups per CU (four waves per SIMD: at most 128 registers, and
+// 4 x 37 KB of LDS), so that a 1024-workgroup grid runs in one round.
+__global__ __launch_bounds__(kT, 4) void pw_gemm_f32_kernel(ConvArgs a, int px_tiles, int co_tiles) {
+    __shared__ __align__(16) float lds[LDS_FLOATS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r = lane & 15;
+    const int K = a.c_in, M = a.c_out, HW = a.w;
+
+    // XCD remap: consecutive logical blocks land on one XCD.
+    const uint32_t nb = a.num_blocks;
+    uint32_t b = blockIdx.x;
+    if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+    const int ct = (int)(b % (uint32_t)co_tiles);
+    const uint32_t rest = b / (uint32_t)co_tiles;
+    const int pt = (int)(rest % (uint32_t)px_tiles);
+    const int n = (int)(rest / (uint32_t)px_tiles);
+    const int p0 = pt * TP, c0 = ct * TC;
+
+    const float* __restrict__ xg = (const float*)a.xptr + ((int64_t)n * a.in_total + a.in_off) * HW;
+    const float* __restrict__ wg = (const float*)a.wptr;
+
+    // Loader roles: two 16-byte pixel units and two 16-byte weight units per
+    // thread and chunk.  Pixel unit u: channel u >> 5, pixels 4 (u & 31) ..;
+    // weight unit u: channel row u >> 2, input channels 4 (u & 3) ...
+    int xk[2], xp[2], wr[2], wk[2];
+    bool xin[2], win[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = tid + kT * i;
+        xk[i] = u >> 5;
+        xp[i] = 4 * (u & 31);
+        xin[i] = p0 + xp[i] < HW;
+        wr[i] = u >> 2;
+        wk[i] = 4 * (u & 3);
+        win[i] = c0 + wr[i] < M;
+    }
+    const int nch = (K + KC - 1) / KC;
+    f32x4 xv[2], wv[2];
+    auto fetch = [&](int ch) {
+        const int k0 = ch * KC;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = k0 + xk[i];
+            xv[i] = (xin[i] && k < K) ? *(const f32x4*)(xg + (int64_t)k * HW + p0 + xp[i])
+                                      : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int kw = k0 + wk[i];
+            wv[i] = (win[i] && kw < K) ? *(const f32x4*)(wg + (int64_t)(c0 + wr[i]) * K + kw)
+                                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    auto stash = [&](int buf) {
+        float* xs = lds + buf * XBUF;
+        float* ws = lds + 2 * XBUF + buf * WBUF;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *(f32x4*)(xs + xk[i] * XST + xp[i]) = xv[i];
+            *(f32x4*)(ws + wr[i] * WST + wk[i]) = wv[i];
+        }
+    };
+
+    const int wp = (wave & 1) * 64, wc = (wave >> 1) * 64;   // this wave's 64 pixels x 64 channels
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < nch) fetch(ch + 1);
+        const float* xs = lds + buf * XBUF;
+        const float* ws = lds + 2 * XBUF + buf * WBUF;
+        f32x4 wo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wo[j] = *(const f32x4*)(ws + (wc + 16 * j + r) * WST + 4 * q);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float xo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xo[i] = xs[(4 * q + s) * XST + wp + 16 * i + r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[i], wo[j][s], acc[i][j], 0, 0, 0);
+        }
+        if (ch + 1 < nch) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Bias + activation; lane (q, r) of fragment (i, j) holds pixels
+    // wp + 16 i + 4 q .. + 3 of channel wc + 16 j + r.
+    float* __restrict__ yg = (float*)a.yptr + ((int64_t)n * a.out_total + a.out_off) * HW;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int co = c0 + wc + 16 * j + r;
+        if (co >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int px = p0 + wp + 16 * i + 4 * q;
+            if (px >= HW) continue;
+            f32x4 o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = bias_act(a, acc[i][j][v], co);
+            // streamed past the caches (measured 3% faster on 64 MB of output)
+            __builtin_nontemporal_store(o, (f32x4*)(yg + (int64_t)co * HW + px));
+        }
+    }
+}
+
+int64_t pw_gemm_blocks(const Desc& d) {
+    const int64_t hw = (int64_t)d.p.h * d.p.w;
+    return (int64_t)d.p.n * ((hw + TP - 1) / TP) * ((d.p.c_out + TC - 1) / TC);
+}
+
+}  // namespace
+
+// Deep reductions with many output channels, on grids that fill the GPU at
+// least twice over; shallower or smaller layers stay with the implicit GEMM.
+bool plan_pw_gemm_f32(const Desc& d) {
+    const conv2d_params_t& p = d.p;
+    if (p.dtype != CONV_DTYPE_F32 || p.k_h != 1 || p.k_w != 1 || p.stride_h != 1 || p.stride_w != 1) return false;
+    if (p.pad_top || p.pad_left || p.pad_bottom || p.pad_right || p.groups != 1) return false;
+    if (p.c_in < 128 || p.c_in % 4 != 0 || p.c_out < 128) return false;
+    const int64_t hw = (int64_t)p.h * p.w;
+    if (hw % 4 != 0 || (int64_t)p.c_in * hw >= INT32_MAX || (int64_t)p.c_out * hw >= INT32_MAX) return false;
+    if ((int64_t)p.c_out * p.c_in >= INT32_MAX) return false;
+    return pw_gemm_blocks(d) >= 2 * (int64_t)device_cu_count();
+}
+
+hipError_t launch_pw_gemm_f32(const Desc& d, ConvArgs a, hipStream_t s) {
+    if (!pointwise_f32_fits(d, a)) return hipErrorInvalidValue;
+    const int64_t hw = (int64_t)d.p.h * d.p.w;
+    a.h = 1;
+    a.w = (int32_t)hw;
+    const int px_tiles = (int)((hw + TP - 1) / TP), co_tiles = (d.p.c_out + TC - 1) / TC;
+    const int64_t blocks = pw_gemm_blocks(d);
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    a.num_blocks = (uint32_t)blocks;
+    void* args[] = {&a, (void*)&px_tiles, (void*)&co_tiles};
+    return hipLaunchKernel((const void*)pw_gemm_f32_kernel, dim3((uint32_t)blocks), dim3(kT), args, 0, s);
+}
+
+}  // namespace conv2d

@@ -150,7 +150,7 @@ def test_kernel_choice_for_the_workloads():
     assert names["conv0"] == "igemm_f32" and names["conv4"] == "igemm_f32"
     assert names["pw1"] == "pointwise_f32" and names["pw2"] == "igemm_f32_pointwise"
     assert names["dw"] == "depthwise_f32"
-    assert names["g32"] == "grouped_f32" and names["pw"] == "igemm_f32_pointwise"
+    assert names["g32"] == "grouped_f32" and names["pw"] == "pw_gemm_f32"
     for L in workloads.int8_chain_layers():
         d = cc().conv2d_desc_create(cc().make_params(L.n, L.c_in, L.h, L.w, L.c_out, L.k, stride=L.stride,
                                                      pads=L.pads, groups=L.groups, dtype="i8"))
