@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["conv2d_api.cpp", "igemm_f32.hip", "igemm_bf16.hip", "depthwise.hip", "qpointwise.hip",
            "direct.hip", "fused_pw_dw.hip", "fused_dw_pw.hip", "grouped.hip", "qdepthwise.hip",
            "qfused_dw_pw.hip", "qfused_pw_dw.hip", "igemm_i8.hip", "probe_copy.hip", "winograd_f32.hip",
-           "winograd4_f32.hip", "pointwise_f32.hip", "pw_gemm_f32.hip", "small_f32.hip"]
+           "winograd4_f32.hip", "pointwise_f32.hip", "pw_gemm_f32.hip", "pw_narrow_f32.hip", "small_f32.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -66,6 +66,7 @@ const char* kernel_name(const Desc& d) {
     case KC_WINOGRAD4_F32: return "winograd4_f32";
     case KC_PW_F32: return "pointwise_f32";
     case KC_PWG_F32: return "pw_gemm_f32";
+    case KC_PWN_F32: return "pw_narrow_f32";
     case KC_IGEMM_I8: return "igemm_i8";
     case KC_SMALL_F32: return "small_f32";
     }
@@ -402,6 +403,7 @@ conv_status_t conv2d_desc_create(const conv2d_params_t* pin, conv2d_desc_t* out)
         planned = plan_igemm_f32(*d);
         if (planned && plan_pointwise_f32(*d)) d->kclass = KC_PW_F32;
         else if (planned && plan_pw_gemm_f32(*d)) d->kclass = KC_PWG_F32;
+        else if (planned && plan_pw_narrow_f32(*d)) d->kclass = KC_PWN_F32;
     } else {
         d->kclass = KC_IGEMM_BF16;
         planned = plan_igemm_bf16(*d);
@@ -583,6 +585,9 @@ conv_status_t forward_float(conv2d_desc_t dd, const void* x, const void* w, cons
         break;
     case KC_PWG_F32:
         e = pointwise_f32_fits(d, a) ? launch_pw_gemm_f32(d, a, s) : launch_igemm_f32(d, a, s);
+        break;
+    case KC_PWN_F32:
+        e = pointwise_f32_fits(d, a) ? launch_pw_narrow_f32(d, a, s) : launch_igemm_f32(d, a, s);
         break;
     case KC_SMALL_F32: e = launch_small_f32(d, a, s); break;
     default: e = launch_direct(d, a, s); break;

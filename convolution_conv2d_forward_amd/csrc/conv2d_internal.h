@@ -26,6 +26,7 @@ enum KernelClass : int32_t {
     KC_SMALL_F32 = 10,   // small fp32 3x3 layers on the vector units, one thread per output pixel
     KC_WINOGRAD4_F32 = 11, // Winograd F(4x4, 3x3), fp32 MFMA, bound weights only
     KC_PWG_F32 = 12,     // pointwise 1x1 with a deep reduction, 128 x 128 GEMM tiles shared in LDS
+    KC_PWN_F32 = 13,     // pointwise 1x1 with 64 < K <= 256 and <= 32 output channels, 32-pixel tiles
 };
 
 // Fast unsigned division by a runtime constant d (1 <= d < 2^16) for
@@ -242,6 +243,10 @@ bool plan_pointwise_f32(const Desc& d);
 // launch_pw_gemm_f32 needs the 16-byte alignment pointwise_f32_fits checks.
 bool plan_pw_gemm_f32(const Desc& d);
 hipError_t launch_pw_gemm_f32(const Desc& d, ConvArgs a, hipStream_t s);
+// fp32 pointwise 1x1 narrowing a deep input to <= 32 channels (pw_narrow_f32.hip);
+// same alignment needs.
+bool plan_pw_narrow_f32(const Desc& d);
+hipError_t launch_pw_narrow_f32(const Desc& d, ConvArgs a, hipStream_t s);
 bool plan_qdw3(const Desc& d);
 bool plan_fused_pw_dw(const Desc& pw, const Desc& dw, int32_t* tile_h, int32_t* lds_bytes);
 // x: the input pointer (its alignment decides between vector and scalar row loads).

@@ -148,7 +148,7 @@ def test_kernel_choice_for_the_workloads():
                                                      pads=L.pads, dilation=L.dilation, groups=L.groups))
         names[L.name] = cc().conv2d_desc_kernel_name(d)
     assert names["conv0"] == "igemm_f32" and names["conv4"] == "igemm_f32"
-    assert names["pw1"] == "pointwise_f32" and names["pw2"] == "igemm_f32_pointwise"
+    assert names["pw1"] == "pointwise_f32" and names["pw2"] == "pw_narrow_f32"
     assert names["dw"] == "depthwise_f32"
     assert names["g32"] == "grouped_f32" and names["pw"] == "pw_gemm_f32"
     for L in workloads.int8_chain_layers():
