@@ -244,6 +244,193 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(ConvArgs a) {
     }
 }
 
+// fp32 3x3 stride-1 depthwise over whole planes (ncnn "convolutiondepthwise",
+// one filter per channel).  The tile kernel above gives every (n, c) plane a
+// workgroup of its own: all of a launch's reads are in flight together, then
+// all of its writes, so reads and writes barely overlap.  Here a smaller grid
+// of persistent workgroups walks the planes (plane p, p + grid, ...) through
+// two LDS buffers: the next plane's 16-byte loads are issued before the
+// current plane's taps, so its reads run under the current plane's stores.
+// LDS column pad_left + iw holds input column iw, so output column wo reads
+// columns wo .. wo + 2 and four outputs read one float4 and one float2 per
+// row; pad cells never change from plane to plane and are written once.
+constexpr int PNV = 4;          // 16-byte input vectors per thread and plane (planes <= 4096 elements)
+constexpr int kPlaneWgPerCu = 3;  // persistent workgroups per compute unit
+
+__global__ __launch_bounds__(kThreads) void dw3s1_planes_kernel(ConvArgs a) {
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    float* lds = (float*)lds_raw;
+    const int tid = threadIdx.x;
+    const int H = a.h, W = a.w, Ho = a.ho, Wo = a.wo;
+    const int pt = a.pad_top, pl = a.pad_left;
+    const int LW = a.patch_w, RHA = a.patch_h;   // LDS row stride, rows per buffer
+    const int bufsz = RHA * LW;
+    const int C = a.c_out;
+    const int P = a.n * C;
+    const int G = gridDim.x;
+    const int64_t HW = (int64_t)H * W;
+    const int64_t oplane = (int64_t)Ho * Wo;
+
+    // This thread's input vectors: the same plane-relative offsets for every plane.
+    const int wv = W >> 2;
+    const int nvec = H * wv;
+    int goff[PNV], loff[PNV];
+    bool ok[PNV];
+#pragma unroll
+    for (int i = 0; i < PNV; ++i) {
+        const int v = tid + i * kThreads;
+        const int r = v / wv;
+        const int cq = v - r * wv;
+        ok[i] = v < nvec;
+        goff[i] = ok[i] ? r * W + 4 * cq : 0;   // spare lanes reload the first vector
+        loff[i] = (r + pt) * LW + pl + 4 * cq;
+    }
+
+    // The next plane in flight: its 16-byte vectors, taps, bias and PReLU
+    // slope, copied out at the top of its plane after the one wait for the
+    // vectors, so the taps and the stores never wait for a load still in
+    // flight.
+    const ActP ap = act_params(a);
+    uint4 buf[PNV];
+    float wn[9], bn, sn;
+    auto issue = [&](int pp) {
+        const int nn = (int)divu((uint32_t)pp, a.dv_co_tiles);
+        const int cc = pp - nn * C;
+        const float* xp = (const float*)a.xptr + ((int64_t)nn * a.in_total + a.in_off + cc) * HW;
+#pragma unroll
+        for (int i = 0; i < PNV; ++i) buf[i] = *(const uint4*)(xp + goff[i]);
+        const float* wq = (const float*)a.wptr + (int64_t)cc * 9;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) wn[k] = wq[k];
+        bn = a.bias ? a.bias[cc] : 0.0f;
+        sn = act_slope(a, ap, cc);
+    };
+
+    int p = blockIdx.x;
+    if (p < P) issue(p);
+
+    // Pad cells of both buffers: whole rows above and below the image, then
+    // the columns left and right of it on the image rows.
+    const float padv = a.pad_value;
+    const int prow = RHA - H;
+    for (int idx = tid; idx < 2 * prow * LW; idx += kThreads) {
+        const int b = idx >= prow * LW;
+        const int j = idx - b * prow * LW;
+        const int rr = j / LW;
+        const int col = j - rr * LW;
+        lds[b * bufsz + (rr < pt ? rr : rr + H) * LW + col] = padv;
+    }
+    const int pc = LW - W;
+    for (int idx = tid; idx < 2 * H * pc; idx += kThreads) {
+        const int b = idx >= H * pc;
+        const int j = idx - b * H * pc;
+        const int rr = j / pc;
+        const int k = j - rr * pc;
+        lds[b * bufsz + (rr + pt) * LW + (k < pl ? k : k + W)] = padv;
+    }
+
+    const int gw = Wo >> 2;
+    const int units = ((Ho + 3) >> 2) * gw;
+    for (int it = 0; p < P; ++it, p += G) {
+        float* T = lds + (it & 1) * bufsz;
+#pragma unroll
+        for (int i = 0; i < PNV; ++i) {
+            if (!ok[i]) continue;
+            float* dst = T + loff[i];
+            if ((pl & 3) == 0) {
+                *(uint4*)dst = buf[i];
+            } else if ((pl & 1) == 0) {
+                *(uint2*)dst = make_uint2(buf[i].x, buf[i].y);
+                *(uint2*)(dst + 2) = make_uint2(buf[i].z, buf[i].w);
+            } else {
+                dst[0] = __uint_as_float(buf[i].x);
+                dst[1] = __uint_as_float(buf[i].y);
+                dst[2] = __uint_as_float(buf[i].z);
+                dst[3] = __uint_as_float(buf[i].w);
+            }
+        }
+        float wt[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) wt[k] = wn[k];
+        const float bv = bn, slope = sn;
+        const int n = (int)divu((uint32_t)p, a.dv_co_tiles);
+        const int c = p - n * C;
+        float* yp = (float*)a.yptr + ((int64_t)n * a.out_total + a.out_off + c) * oplane;
+        if (p + G < P) issue(p + G);
+        __syncthreads();
+
+        for (int u = tid; u < units; u += kThreads) {
+            const int rb = (int)fdiv((uint32_t)u, a.div_tile_w);
+            const int r0 = rb * 4;
+            const int wo0 = (u - rb * gw) * 4;
+            float acc[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
+            const float* src = T + r0 * LW + wo0;
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const float4 lo = *(const float4*)(src + i * LW);
+                const float2 hi = *(const float2*)(src + i * LW + 4);
+                const float win[6] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y};
+#pragma unroll
+                for (int orow = 0; orow < 4; ++orow) {
+                    const int r = i - orow;
+                    if (r < 0 || r > 2) continue;
+#pragma unroll
+                    for (int s = 0; s < 3; ++s)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[orow][q] = fmaf(win[q + s], wt[r * 3 + s], acc[orow][q]);
+                }
+            }
+#pragma unroll
+            for (int orow = 0; orow < 4; ++orow) {
+                const int ho = r0 + orow;
+                if (ho >= Ho) break;
+                float4 o;
+                o.x = act_apply(acc[orow][0] + bv, slope, ap.lo, ap.hi);
+                o.y = act_apply(acc[orow][1] + bv, slope, ap.lo, ap.hi);
+                o.z = act_apply(acc[orow][2] + bv, slope, ap.lo, ap.hi);
+                o.w = act_apply(acc[orow][3] + bv, slope, ap.lo, ap.hi);
+                *(float4*)(yp + (int64_t)ho * Wo + wo0) = o;
+            }
+        }
+    }
+}
+
+// Shapes the plane kernel takes (fp32, 3x3, stride 1, dilation 1, rows of
+// whole 16-byte vectors in and out, a plane of at most PNV * 256 vectors and
+// two plane buffers in 64 KB of LDS); the call also needs 16-byte aligned x
+// and y.
+bool dw_planes_fit(const Desc& d, int* lds_bytes) {
+    const conv2d_params_t& p = d.p;
+    if (p.dtype != CONV_DTYPE_F32 || p.k_h != 3 || p.k_w != 3 || p.stride_h != 1 || p.stride_w != 1 ||
+        p.dilation_h != 1 || p.dilation_w != 1)
+        return false;
+    if (p.w % 4 != 0 || d.wo % 4 != 0 || d.ho < 1 || (int64_t)p.h * p.w > (int64_t)PNV * kThreads * 4)
+        return false;
+    const int64_t bytes = 2 * (int64_t)((d.ho + 3) / 4 * 4 + 2) * (d.wo + 4) * 4;
+    if (bytes > 64 * 1024) return false;
+    *lds_bytes = (int)bytes;
+    return true;
+}
+
+hipError_t launch_dw_planes(const Desc& d, ConvArgs a, hipStream_t s) {
+    const int64_t planes = (int64_t)a.n * a.c_out;
+    if (planes == 0) return hipSuccess;
+    if (planes > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    a.patch_w = d.wo + 4;
+    a.patch_h = (d.ho + 3) / 4 * 4 + 2;
+    a.div_tile_w = make_fastdiv((uint32_t)(d.wo / 4));
+    a.dv_co_tiles = make_divu32((uint32_t)a.c_out);
+    const int64_t cap = (int64_t)kPlaneWgPerCu * device_cu_count();
+    const uint32_t grid = (uint32_t)(planes < cap ? planes : cap);
+    const size_t lds = (size_t)2 * a.patch_h * a.patch_w * sizeof(float);
+    void* args[] = {&a};
+    return hipLaunchKernel((const void*)dw3s1_planes_kernel, dim3(grid), dim3(kThreads), args, lds, s);
+}
+
 // LDS bytes of the window of a tile (worst-case alignment slack).
 template <typename T>
 size_t window_bytes(const conv2d_params_t& p, int tile_h, int tile_w, int ho, int wo) {
@@ -321,8 +508,14 @@ hipError_t launch_t(const Desc& d, ConvArgs a, hipStream_t s) {
 
 }  // namespace
 
+// cfg 1: the shape also fits the fp32 plane kernel (launch_dw takes it when
+// x and y are 16-byte aligned); the tile kernel is planned in every case.
 bool plan_dw(Desc& d) {
-    return d.p.dtype == CONV_DTYPE_BF16 ? plan_dw_t<__hip_bfloat16>(d) : plan_dw_t<float>(d);
+    if (d.p.dtype == CONV_DTYPE_BF16) return plan_dw_t<__hip_bfloat16>(d);
+    if (!plan_dw_t<float>(d)) return false;
+    int lds = 0;
+    d.cfg = dw_planes_fit(d, &lds) ? 1 : 0;
+    return true;
 }
 
 // int8: the byte-plane dot-product kernel for 3x3 s1/s2 (cfg 1), else the
@@ -337,6 +530,8 @@ bool plan_qdw(Desc& d) {
 }
 
 hipError_t launch_dw(const Desc& d, ConvArgs a, hipStream_t s) {
+    if (d.p.dtype == CONV_DTYPE_F32 && d.cfg == 1 && ((uintptr_t)a.xptr % 16) == 0 && ((uintptr_t)a.yptr % 16) == 0)
+        return launch_dw_planes(d, a, s);
     return d.p.dtype == CONV_DTYPE_BF16 ? launch_t<__hip_bfloat16>(d, a, s) : launch_t<float>(d, a, s);
 }
 

@@ -706,6 +706,12 @@ DWS_CASES = [
     (2, 3, 3, 1024, (1, 1, 1, 1), workloads.ACT_NONE, 0.0),
     (1, 2, 88, 92, (1, 0, 1, 1), workloads.ACT_CLIP, 1.0),
     (4, 6, 5, 8, (1, 2, 1, 0), workloads.ACT_RELU, -1.0),
+    # whole planes streamed through LDS: the largest plane, pad_left 0 / 3,
+    # ragged row blocks, more planes than workgroups
+    (3, 40, 64, 64, (1, 1, 1, 1), workloads.ACT_LEAKY_RELU, 0.5),
+    (1, 5, 12, 12, (0, 0, 2, 2), workloads.ACT_NONE, -2.0),
+    (2, 9, 7, 20, (2, 3, 0, 3), workloads.ACT_CLIP, 0.125),
+    (16, 96, 14, 16, (1, 1, 1, 1), workloads.ACT_PRELU, 0.0),
 ]
 
 
