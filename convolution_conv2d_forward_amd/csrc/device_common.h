@@ -94,6 +94,43 @@ __device__ __forceinline__ float bias_act(const ConvArgs& a, float v, int co) {
     return v;
 }
 
+// A channel's bias and PReLU slope, read before an epilogue's first store.
+// bias_act re-reads them for every value, and since a store may alias them
+// the compiler keeps each read after the stores before it: every read then
+// waits for all earlier stores to be acknowledged.  bias_act_pre computes
+// exactly what bias_act does from the preloaded pair.
+struct ChanEpi {
+    float b, s;
+};
+
+__device__ __forceinline__ ChanEpi chan_epi(const ConvArgs& a, int co) {
+    ChanEpi e;
+    e.b = a.bias ? a.bias[co] : 0.0f;
+    e.s = a.act == CONV_ACT_PRELU ? a.slope[a.slope_count == 1 ? 0 : co] : 0.0f;
+    return e;
+}
+
+__device__ __forceinline__ float bias_act_pre(const ConvArgs& a, float v, ChanEpi e) {
+    if (a.bias) v += e.b;
+    switch (a.act) {
+    case CONV_ACT_RELU:
+        v = v > 0.0f ? v : 0.0f;
+        break;
+    case CONV_ACT_LEAKY_RELU:
+        v = v >= 0.0f ? v : a.act_a * v;
+        break;
+    case CONV_ACT_PRELU:
+        v = v >= 0.0f ? v : e.s * v;
+        break;
+    case CONV_ACT_CLIP:
+        v = fminf(fmaxf(v, a.act_a), a.act_b);
+        break;
+    default:
+        break;
+    }
+    return v;
+}
+
 // The activation alone, with the channel's PReLU slope already loaded.
 __device__ __forceinline__ float apply_act(const ConvArgs& a, float v, float slope) {
     switch (a.act) {

@@ -528,36 +528,53 @@ __global__ __launch_bounds__(C::NT) void igemm_f32_kernel(ConvArgs a) {
     const int64_t out_plane = (int64_t)a.ho * a.wo;
     constexpr int UNITS = C::PT * BM * BN / 4;
     constexpr int ROW4 = BN / 4;
+    constexpr int ITERS = (UNITS + C::NT - 1) / C::NT;
+    constexpr int CH = ITERS < 8 ? ITERS : 8;   // units whose bias and slope are read at once
 #pragma unroll
-    for (int u0 = 0; u0 < UNITS; u0 += C::NT) {
-        const int u = u0 + threadIdx.x;
-        if (UNITS % C::NT != 0 && u >= UNITS) break;
-        const int p = u / (BM * ROW4);
-        const int rem = u - p * (BM * ROW4);
-        const int co = rem / ROW4;                // row within the workgroup's BM
-        const int j = 4 * (rem - co * ROW4);
-        const int w0 = (p * C::WM + co / C::WR) * C::KS;
-        const float* src = redb + (co % C::WR) * C::RS + j;
-        float4 s = *(const float4*)(src + w0 * C::WR * C::RS);
+    for (int i0 = 0; i0 < ITERS; i0 += CH) {
+        // Bias and slope of the next CH units before their stores (one wait
+        // for earlier stores per CH units instead of one per unit).
+        ChanEpi ce[CH];
 #pragma unroll
-        for (int k = 1; k < C::KS; ++k) {
-            const float4 t = *(const float4*)(src + (w0 + k) * C::WR * C::RS);
-            s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+        for (int k = 0; k < CH; ++k) {
+            const int u = (i0 + k) * C::NT + threadIdx.x;
+            const int rem = u % (BM * ROW4);
+            const int cog = cot * BM + rem / ROW4;
+            ce[k] = chan_epi(a, (u < UNITS && cog < a.cout_g) ? g * a.cout_g + cog : 0);
         }
-        const int cog = cot * BM + co;
-        const int pho = a.pt_vertical ? (thi * C::PT + p) * TH : thi * TH;
-        const int pwo = a.pt_vertical ? twi * TW : (twi * C::PT + p) * TW;
-        const int ho = pho + j / TW, wo = pwo + (j % TW);
-        if (cog < a.cout_g && ho < a.ho) {
-            const int cg = g * a.cout_g + cog;
-            float v[4] = {bias_act(a, s.x, cg), bias_act(a, s.y, cg), bias_act(a, s.z, cg), bias_act(a, s.w, cg)};
-            float* dst = yg + ((int64_t)n * a.out_total + a.out_off + cg) * out_plane + (int64_t)ho * a.wo + wo;
-            if (a.vec_store && wo + 3 < a.wo) {
-                *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (wo + t < a.wo) dst[t] = v[t];
+        for (int k = 0; k < CH; ++k) {
+            if (i0 + k >= ITERS) break;
+            const int u = (i0 + k) * C::NT + threadIdx.x;
+            if (UNITS % C::NT != 0 && u >= UNITS) break;
+            const int p = u / (BM * ROW4);
+            const int rem = u - p * (BM * ROW4);
+            const int co = rem / ROW4;                // row within the workgroup's BM
+            const int j = 4 * (rem - co * ROW4);
+            const int w0 = (p * C::WM + co / C::WR) * C::KS;
+            const float* src = redb + (co % C::WR) * C::RS + j;
+            float4 s = *(const float4*)(src + w0 * C::WR * C::RS);
+#pragma unroll
+            for (int kk = 1; kk < C::KS; ++kk) {
+                const float4 t = *(const float4*)(src + (w0 + kk) * C::WR * C::RS);
+                s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+            }
+            const int cog = cot * BM + co;
+            const int pho = a.pt_vertical ? (thi * C::PT + p) * TH : thi * TH;
+            const int pwo = a.pt_vertical ? twi * TW : (twi * C::PT + p) * TW;
+            const int ho = pho + j / TW, wo = pwo + (j % TW);
+            if (cog < a.cout_g && ho < a.ho) {
+                const int cg = g * a.cout_g + cog;
+                float v[4] = {bias_act_pre(a, s.x, ce[k]), bias_act_pre(a, s.y, ce[k]), bias_act_pre(a, s.z, ce[k]),
+                              bias_act_pre(a, s.w, ce[k])};
+                float* dst = yg + ((int64_t)n * a.out_total + a.out_off + cg) * out_plane + (int64_t)ho * a.wo + wo;
+                if (a.vec_store && wo + 3 < a.wo) {
+                    *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (wo + t < a.wo) dst[t] = v[t];
+                }
             }
         }
     }

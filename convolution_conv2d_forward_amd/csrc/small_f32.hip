@@ -106,10 +106,13 @@ __global__ __launch_bounds__(256) void small3x3_f32_kernel(SmallArgs sa) {
     for (int j = 0; j < CO; ++j) acc[j] += part[j][threadIdx.x];
     const int64_t plane = (int64_t)a.ho * a.wo;
     float* __restrict__ yb = (float*)a.yptr + ((int64_t)n * a.out_total + a.out_off) * plane + (int64_t)oy * a.wo + ox;
+    ChanEpi ce[CO];   // every channel's bias and slope before the first store
+#pragma unroll
+    for (int j = 0; j < CO; ++j) ce[j] = chan_epi(a, co0 + j < a.c_out ? co0 + j : 0);
 #pragma unroll
     for (int j = 0; j < CO; ++j) {
         const int co = co0 + j;
-        if (co < a.c_out) yb[(int64_t)co * plane] = bias_act(a, acc[j], co);
+        if (co < a.c_out) yb[(int64_t)co * plane] = bias_act_pre(a, acc[j], ce[j]);
     }
 }
 
