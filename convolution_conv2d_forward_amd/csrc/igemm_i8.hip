@@ -145,12 +145,20 @@ __device__ __forceinline__ void i8_epilogue_r(const I8Args& f, const I8Tile& t, 
     const int64_t oplane = (int64_t)a.ho * a.wo;
     const bool vec_y = (a.wo % 4) == 0 && ((uintptr_t)a.yptr % 4) == 0;
     const int wo = wo0 + 4 * (lane >> 4);
+    // Every channel's bias before the first store: a read behind a store
+    // waits for all earlier memory operations, the next tile's loads included.
+    int32_t bias[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int co = co0 + 16 * (mbase + m) + (lane & 15);
+        bias[m] = (a.qbias && co < a.cout_g) ? a.qbias[t.g * a.cout_g + co] : 0;
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int co = co0 + 16 * (mbase + m) + (lane & 15);
         if (co >= a.cout_g) continue;
         const int cg = t.g * a.cout_g + co;
-        const int32_t bb = a.qbias ? a.qbias[cg] : 0;
+        const int32_t bb = bias[m];
         int8_t* yc = yg + ((int64_t)t.n * a.out_total + a.out_off + cg) * oplane;
 #pragma unroll
         for (int j = 0; j < NR; ++j) {

@@ -121,13 +121,23 @@ __global__ __launch_bounds__(kThreads) void qpw_kernel(ConvArgs a) {
     if (p < HW) {
         int8_t* __restrict__ yg = (int8_t*)a.yptr;
         const bool relu = a.act == CONV_ACT_RELU;
+        // Biases read before the first store (a read behind a store waits
+        // for every earlier store).
+        int32_t bias[MI][4];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int co = co0 + mi * 16 + (lane >> 4) * 4 + v;
+                bias[mi][v] = (a.qbias && co < a.c_out) ? a.qbias[co] : 0;
+            }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int co = co0 + mi * 16 + (lane >> 4) * 4 + v;
                 if (co < a.c_out) {
-                    const int32_t val = acc[mi][v] + (a.qbias ? a.qbias[co] : 0);
+                    const int32_t val = acc[mi][v] + bias[mi][v];
                     yg[((int64_t)n * a.out_total + a.out_off + co) * HW + p] =
                         requant(val, a.composite, a.rounding, a.y_zp, relu);
                 }
@@ -212,11 +222,17 @@ __global__ __launch_bounds__(kThreads) void qpw_fast_kernel(ConvArgs a) {
     if (px < HW) {
         int8_t* __restrict__ yg = (int8_t*)a.yptr;
         const bool relu = a.act == CONV_ACT_RELU;
+        int32_t bias[MI];   // read before the first store
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int co = co0 + mi * 16 + (lane & 15);
+            bias[mi] = (a.qbias && co < a.c_out) ? a.qbias[co] : 0;
+        }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const int co = co0 + mi * 16 + (lane & 15);
             if (co >= a.c_out) continue;
-            const int32_t b = a.qbias ? a.qbias[co] : 0;
+            const int32_t b = bias[mi];
             uint32_t word = 0;
 #pragma unroll
             for (int v = 0; v < 4; ++v)
