@@ -262,15 +262,16 @@ __global__ __launch_bounds__(kT) void winograd4_kernel(Wino4Args f) {
             r[3][j] = m6[1] - m6[2] + 8.0f * (m6[3] - m6[4]) + m6[5];
         }
         float* yc = (float*)a.yptr + ((int64_t)n * a.out_total + a.out_off + co) * ((int64_t)a.ho * a.wo);
+        const ChanEpi ce = chan_epi(a, co);   // before the first row's store
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (oy + i >= a.ho) continue;
             const float* q = r[i];
             float y[4];
-            y[0] = bias_act(a, q[0] + q[1] + q[2] + q[3] + q[4], co);
-            y[1] = bias_act(a, q[1] - q[2] + 2.0f * (q[3] - q[4]), co);
-            y[2] = bias_act(a, q[1] + q[2] + 4.0f * (q[3] + q[4]), co);
-            y[3] = bias_act(a, q[1] - q[2] + 8.0f * (q[3] - q[4]) + q[5], co);
+            y[0] = bias_act_pre(a, q[0] + q[1] + q[2] + q[3] + q[4], ce);
+            y[1] = bias_act_pre(a, q[1] - q[2] + 2.0f * (q[3] - q[4]), ce);
+            y[2] = bias_act_pre(a, q[1] + q[2] + 4.0f * (q[3] + q[4]), ce);
+            y[3] = bias_act_pre(a, q[1] - q[2] + 8.0f * (q[3] - q[4]) + q[5], ce);
             float* row = yc + (int64_t)(oy + i) * a.wo + ox;
             if (ox + 3 < a.wo && (((uintptr_t)row) & 15) == 0) {
                 *(float4*)row = make_float4(y[0], y[1], y[2], y[3]);
